@@ -1,0 +1,423 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each ``pin_*`` takes an oracle module and raises AssertionError when that
+module disagrees with a closed form, an invariant, a library routine or brute
+force.  ``test_oracle.py`` runs them on the real oracle; ``test_oracle_mutants.py``
+runs them on copies of the oracle with planted mistakes and requires that
+every mistake is caught by at least one pin.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import scipy.special
+import torch
+
+from dynamic_block_sparse_tile_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_tiles.json")
+
+
+def _lay(o, S, N, P, nsp):
+    return o.Layout(S, N, P, nsp)
+
+
+def _rand_inputs(S, N, P, nsp, H=2, d=8, seed=0, pad=np.nan):
+    rng = np.random.default_rng(seed)
+    L = S * P
+    Q = rng.standard_normal((H, L, d))
+    K = rng.standard_normal((H, L, d))
+    V = rng.standard_normal((H, L, d))
+    j = np.arange(L) % P
+    for X in (Q, K, V):
+        X[:, j >= N] = pad
+    return Q, K, V
+
+
+# --------------------------------------------------------------------------- pool + score
+def pin_block_mean_identity(o):
+    """sigma[tq, tk] is the mean of the dense logit block over valid queries x member keys.
+
+    By bilinearity mean_{i,j} s*q_i.k_j = s*mean(q).mean(k); the block means are taken
+    here from a separately computed dense logit matrix with row sets written out by
+    position (valid query: in-frame < N; member key: nsp <= in-frame < N).
+    """
+    for (S, N, P, nsp, tile) in [(2, 256, 256, 0, 64), (3, 37, 48, 5, 16), (2, 10, 32, 3, 8),
+                                 (2, 5, 16, 2, 8)]:
+        Q, K, _ = _rand_inputs(S, N, P, nsp, seed=S * 100 + N)
+        lay = _lay(o, S, N, P, nsp)
+        scale = 0.3
+        qbar, qc = o.tile_pool(Q, lay, tile, "query")
+        kbar, kc = o.tile_pool(K, lay, tile, "key")
+        sig = o.tile_scores(qbar, qc, kbar, kc, scale)
+        T = S * P // tile
+        for h in range(Q.shape[0]):
+            Qz = np.nan_to_num(Q[h])
+            Kz = np.nan_to_num(K[h])
+            logits = scale * (Qz @ Kz.T)
+            for tq in range(T):
+                R = [r for r in range(tq * tile, (tq + 1) * tile) if r % P < N]
+                for tk in range(T):
+                    M = [r for r in range(tk * tile, (tk + 1) * tile) if nsp <= r % P < N]
+                    if not R or not M:
+                        assert sig[h, tq, tk] == -np.inf
+                    else:
+                        want = logits[np.ix_(R, M)].mean()
+                        assert abs(sig[h, tq, tk] - want) <= 1e-12 * (1 + abs(want)), (tq, tk)
+
+
+def pin_tile_constant_pool(o):
+    """Rows equal to c_t inside every tile pool to exactly c_t (pad holds NaN)."""
+    S, N, P, nsp, tile = 2, 50, 64, 4, 16
+    lay = _lay(o, S, N, P, nsp)
+    T = S * P // tile
+    c = np.arange(T * 3, dtype=np.float64).reshape(1, T, 3) * 0.25 - 1.0
+    X = np.repeat(c, tile, axis=1)
+    j = np.arange(S * P) % P
+    X[:, j >= N] = np.nan
+    qbar, qc = o.tile_pool(X, lay, tile, "query")
+    kbar, kc = o.tile_pool(X, lay, tile, "key")
+    for t in range(T):
+        rows = np.arange(t * tile, (t + 1) * tile) % P
+        nq = int(np.sum(rows < N))
+        nk = int(np.sum((rows >= nsp) & (rows < N)))
+        assert qc[t] == nq and kc[t] == nk
+        if nq:
+            assert np.array_equal(qbar[0, t], c[0, t])
+        if nk:
+            assert np.array_equal(kbar[0, t], c[0, t])
+
+
+def pin_symmetric_scores(o):
+    """With Q = K and no specials or pad, query and key tiles coincide: sigma is symmetric."""
+    w = synth.WORKLOADS["tiny_s2"]
+    inp = synth.make_inputs(w, seed=3)
+    lay = o.Layout(*w.layout)
+    qbar, qc = o.tile_pool(inp.q, lay, 64, "query")
+    kbar, kc = o.tile_pool(inp.k, lay, 64, "key")
+    sig = o.tile_scores(qbar, qc, kbar, kc, 0.125)
+    assert np.allclose(sig, np.swapaxes(sig, 1, 2), rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- select
+def _brute_topk(row, k):
+    """argmax over all k-subsets of the score sum; ties to the lexicographically smallest set."""
+    best, best_set = None, None
+    for comb in itertools.combinations(range(len(row)), k):
+        s = float(np.sum(row[list(comb)]))
+        if best is None or s > best + 1e-12:
+            best, best_set = s, comb
+    return np.array(best_set, dtype=np.int64)
+
+
+def pin_select_brute_force(o):
+    rng = np.random.default_rng(7)
+    for trial in range(60):
+        Tk = int(rng.integers(2, 11))
+        # small integers: plenty of exact ties between tiles
+        row = rng.integers(-3, 4, size=Tk).astype(np.float64) * 0.5
+        k = int(rng.integers(0, Tk + 1))
+        tpf = [t for t in (1, 2, Tk) if Tk % t == 0][int(rng.integers(0, 2))]
+        anchor = int(rng.integers(-1, Tk // tpf))
+        want = set(_brute_topk(row, k).tolist()) if k else set()
+        if anchor >= 0:
+            want |= set(range(anchor * tpf, (anchor + 1) * tpf))
+        got = o.select_tiles(row, k, tpf, anchor)
+        assert got.tolist() == sorted(want), (row, k, tpf, anchor, got)
+
+
+def pin_select_invariants(o):
+    rng = np.random.default_rng(11)
+    for trial in range(40):
+        Tk = int(rng.integers(1, 40))
+        row = rng.standard_normal(Tk)
+        prev = set()
+        for k in range(Tk + 2):
+            s = o.select_tiles(row, k, 1, -1)
+            assert list(s) == sorted(set(s.tolist()))             # ascending, unique
+            assert len(s) == min(k, Tk)
+            assert prev <= set(s.tolist())                        # nested in k
+            prev = set(s.tolist())
+            if k <= Tk and k > 0:                                 # the k largest, by value
+                thr = np.sort(row)[::-1][k - 1]
+                assert np.all(row[s] >= thr)
+        assert o.select_tiles(row, Tk + 5, 1, -1).tolist() == list(range(Tk))
+    # an empty tile scores -inf: it is only picked once the finite ones run out (lowest index first)
+    row = np.array([-np.inf, 2.0, -np.inf, 1.0, -np.inf])
+    assert o.select_tiles(row, 2, 1, -1).tolist() == [1, 3]
+    assert o.select_tiles(row, 3, 1, -1).tolist() == [0, 1, 3]
+    assert o.select_tiles(row, 4, 1, -1).tolist() == [0, 1, 2, 3]
+    # -0.0 and +0.0 are the same score: the lower index wins
+    assert o.select_tiles(np.array([0.0, -0.0, 0.0]), 1, 1, -1).tolist() == [0]
+    assert o.select_tiles(np.array([-0.0, 0.0]), 1, 1, -1).tolist() == [0]
+    # the anchor union and the padded table
+    sc = np.array([[[5.0, 4.0, 3.0, 2.0, 1.0, 0.0]]])
+    idx, cnt = o.select_topk(sc, 2, 3, 1)
+    assert idx.shape == (1, 1, 5) and cnt[0, 0] == 5 and idx[0, 0].tolist() == [0, 1, 3, 4, 5]
+    idx, cnt = o.select_topk(sc, 2, 3, 0)
+    assert cnt[0, 0] == 3 and idx[0, 0].tolist() == [0, 1, 2, -1, -1]
+
+
+# --------------------------------------------------------------------------- attend
+def _sdpa_dense(Q, K, V, qlay, klay, scale):
+    """Dense attention through torch's library routine, fp64 on the CPU, key-padding mask."""
+    H, Lq, d = Q.shape
+    kvalid = (np.arange(K.shape[1]) % klay.stride) < klay.tokens
+    qt = torch.from_numpy(np.nan_to_num(Q)).double()
+    kt = torch.from_numpy(np.nan_to_num(K)).double()
+    vt = torch.from_numpy(np.nan_to_num(V)).double()
+    mask = torch.from_numpy(np.broadcast_to(kvalid, (Lq, K.shape[1])).copy())
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+    logits = scale * np.einsum("hqd,hkd->hqk", np.nan_to_num(Q), np.nan_to_num(K))
+    lse = scipy.special.logsumexp(np.where(kvalid[None, None, :], logits, -np.inf), axis=2)
+    return out.numpy(), lse
+
+
+def pin_dense_matches_library(o):
+    for (S, N, P, nsp) in [(2, 60, 64, 5), (3, 100, 128, 2), (2, 64, 64, 0)]:
+        Q, K, V = _rand_inputs(S, N, P, nsp, H=2, d=16, seed=N)
+        lay = o.Layout(S, N, P, nsp)
+        O, lse = o.dense_attend(Q, K, V, lay, lay, 0.25)
+        ref, rlse = _sdpa_dense(Q, K, V, lay, lay, 0.25)
+        qv = (np.arange(S * P) % P) < N
+        assert np.allclose(O[:, qv], ref[:, qv], rtol=0, atol=1e-12)
+        assert np.allclose(lse[:, qv], rlse[:, qv], rtol=0, atol=1e-12)
+        assert np.all(O[:, ~qv] == 0) and np.all(lse[:, ~qv] == 0)
+
+
+def _selection(o, Q, K, lay, tile, k, anchor, scale):
+    qbar, qc = o.tile_pool(Q, lay, tile, "query")
+    kbar, kc = o.tile_pool(K, lay, tile, "key")
+    sig = o.tile_scores(qbar, qc, kbar, kc, scale)
+    idx, cnt = o.select_topk(sig, k, lay.stride // tile, anchor)
+    return idx, cnt, kbar, kc
+
+
+def pin_all_tiles_is_dense(o):
+    """k >= Tk keeps every tile: specials + all member keys = every valid key."""
+    for (S, N, P, nsp, tile) in [(2, 60, 64, 5, 16), (3, 37, 48, 5, 16), (2, 64, 64, 0, 32)]:
+        Q, K, V = _rand_inputs(S, N, P, nsp, H=2, d=16, seed=P + N)
+        lay = o.Layout(S, N, P, nsp)
+        Tk = S * P // tile
+        idx, cnt, _, _ = _selection(o, Q, K, lay, tile, Tk, 0, 0.25)
+        O, lse = o.sparse_attend(Q, K, V, lay, lay, tile, idx, cnt, 0.25)
+        ref, rlse = _sdpa_dense(Q, K, V, lay, lay, 0.25)
+        qv = (np.arange(S * P) % P) < N
+        assert np.allclose(O[:, qv], ref[:, qv], rtol=0, atol=1e-12)
+        assert np.allclose(lse[:, qv], rlse[:, qv], rtol=0, atol=1e-12)
+
+
+def _explicit_key_set(lay, tile, sel):
+    """Key rows attended by a query tile, written out by position."""
+    S, N, P, nsp = lay
+    J = [s * P + j for s in range(S) for j in range(min(nsp, N))]
+    for t in sel:
+        J += [r for r in range(t * tile, (t + 1) * tile) if nsp <= r % P < N]
+    return J
+
+
+def pin_closed_forms(o):
+    """V = c gives O = c; Q = 0 gives the plain (landmark-weighted) mean; convexity."""
+    S, N, P, nsp, tile = 3, 45, 64, 5, 16
+    lay = o.Layout(S, N, P, nsp)
+    Q, K, V = _rand_inputs(S, N, P, nsp, H=2, d=8, seed=5)
+    T = S * P // tile
+    qv = (np.arange(S * P) % P) < N
+    for k, anchor, lm in [(3, 0, False), (2, -1, False), (1, 2, True), (5, 1, True)]:
+        idx, cnt, kbar, kc = _selection(o, Q, K, lay, tile, k, anchor, 0.5)
+        vbar, _ = o.tile_pool(V, lay, tile, "key")
+        kw = dict(kbar=kbar, vbar=vbar, kcount=kc) if lm else {}
+        # constant V
+        c = np.array([1.5, -2.25, 0.0, 3.0, 7.0, -1.0, 0.5, 2.0])
+        Vc = np.broadcast_to(c, V.shape).copy()
+        Vc[:, ~qv] = np.nan
+        vbc, _ = o.tile_pool(Vc, lay, tile, "key")
+        kwc = dict(kbar=kbar, vbar=vbc, kcount=kc) if lm else {}
+        O, _ = o.sparse_attend(Q, K, Vc, lay, lay, tile, idx, cnt, 0.5, **kwc)
+        assert np.allclose(O[:, qv], c, rtol=1e-13, atol=1e-13)
+        # Q = 0: uniform weights; each landmark stands for 64 keys
+        Qz = np.zeros_like(Q)
+        O, lse = o.sparse_attend(Qz, K, V, lay, lay, tile, idx, cnt, 0.5, **kw)
+        for h in range(2):
+            for tq in range(T):
+                rows = [r for r in range(tq * tile, (tq + 1) * tile) if r % P < N]
+                if not rows:
+                    continue
+                sel = idx[h, tq, :cnt[h, tq]]
+                J = _explicit_key_set(lay, tile, sel)
+                num = V[h, J].sum(axis=0)
+                den = float(len(J))
+                if lm:
+                    for t in range(T):
+                        if t not in set(sel.tolist()) and kc[t] > 0:
+                            num = num + 64.0 * vbar[h, t]
+                            den += 64.0
+                assert np.allclose(O[h, rows], num / den, rtol=0, atol=1e-12)
+                assert np.allclose(lse[h, rows], math.log(den), rtol=0, atol=1e-12)
+        # convexity over the attended values
+        O, _ = o.sparse_attend(Q, K, V, lay, lay, tile, idx, cnt, 0.5)
+        for h in range(2):
+            for tq in range(T):
+                rows = [r for r in range(tq * tile, (tq + 1) * tile) if r % P < N]
+                if not rows:
+                    continue
+                J = _explicit_key_set(lay, tile, idx[h, tq, :cnt[h, tq]])
+                lo, hi = V[h, J].min(axis=0), V[h, J].max(axis=0)
+                assert np.all(O[h, rows] >= lo - 1e-12) and np.all(O[h, rows] <= hi + 1e-12)
+
+
+def pin_frame_permutation(o):
+    """Permuting frames (the anchor moves with its frame) permutes the outputs."""
+    w = synth.with_frames(synth.WORKLOADS["vggt_s8"], 3, heads=2)
+    inp = synth.make_inputs(w, seed=2)
+    lay = o.Layout(*w.layout)
+    perm = np.array([2, 0, 1])                 # new frame s holds old frame perm[s]
+    P = w.stride
+
+    def permute(X):
+        return X.reshape(X.shape[0], w.frames, P, -1)[:, perm].reshape(X.shape)
+
+    base = o.layer(inp.q, inp.k, inp.v, lay, lay, 64, 3, anchor=0, landmarks=True)
+    new_anchor = int(np.nonzero(perm == 0)[0][0])
+    moved = o.layer(permute(inp.q), permute(inp.k), permute(inp.v), lay, lay, 64, 3,
+                    anchor=new_anchor, landmarks=True)
+    assert np.allclose(moved["O"], permute(base["O"]), rtol=0, atol=1e-12)
+
+
+def pin_query_tiles_independent(o):
+    w = synth.with_frames(synth.WORKLOADS["vggt_s8"], 2, heads=2)
+    inp = synth.make_inputs(w, seed=4)
+    lay = o.Layout(*w.layout)
+    full = o.layer(inp.q, inp.k, inp.v, lay, lay, 64, 4, anchor=0, landmarks=True)
+    some = [3, 17, 30]
+    part = o.layer(inp.q, inp.k, inp.v, lay, lay, 64, 4, anchor=0, landmarks=True,
+                   query_tiles=some, heads=[1])
+    for t in some:
+        r = slice(t * 64, (t + 1) * 64)
+        assert np.array_equal(part["O"][1, r], full["O"][1, r])
+
+
+def pin_landmarks_exact_on_constant_tiles(o):
+    """K, V constant inside every full 64-row tile: a landmark (mean K, mean V, +ln 64)
+    carries exactly the softmax mass of its tile, so sparse + landmarks = dense for any
+    selection (64 * e^{q.k} = sum over the tile's 64 equal keys)."""
+    S, N, P, nsp, tile = 2, 256, 256, 0, 64
+    rng = np.random.default_rng(9)
+    H, d = 2, 8
+    T = S * P // tile
+    Q = rng.standard_normal((H, S * P, d))
+    K = np.repeat(rng.standard_normal((H, T, d)), tile, axis=1)
+    V = np.repeat(rng.standard_normal((H, T, d)), tile, axis=1)
+    lay = o.Layout(S, N, P, nsp)
+    ref, rlse = _sdpa_dense(Q, K, V, lay, lay, 0.4)
+    kbar, kc = o.tile_pool(K, lay, tile, "key")
+    vbar, _ = o.tile_pool(V, lay, tile, "key")
+    for k, anchor in [(0, -1), (1, -1), (2, 0), (3, 1)]:
+        idx, cnt, _, _ = _selection(o, Q, K, lay, tile, k, anchor, 0.4)
+        O, lse = o.sparse_attend(Q, K, V, lay, lay, tile, idx, cnt, 0.4,
+                                 kbar=kbar, vbar=vbar, kcount=kc)
+        assert np.allclose(O, ref, rtol=0, atol=1e-12)
+        assert np.allclose(lse, rlse, rtol=0, atol=1e-12)
+
+
+def pin_landmarks_vanish_when_all_selected(o):
+    S, N, P, nsp, tile = 2, 60, 64, 5, 16
+    lay = o.Layout(S, N, P, nsp)
+    Q, K, V = _rand_inputs(S, N, P, nsp, H=2, d=8, seed=13)
+    Tk = S * P // tile
+    idx, cnt, kbar, kc = _selection(o, Q, K, lay, tile, Tk, -1, 0.3)
+    vbar, _ = o.tile_pool(V, lay, tile, "key")
+    a, la = o.sparse_attend(Q, K, V, lay, lay, tile, idx, cnt, 0.3, kbar=kbar, vbar=vbar, kcount=kc)
+    b, lb = o.sparse_attend(Q, K, V, lay, lay, tile, idx, cnt, 0.3)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def pin_empty_key_set(o):
+    """No specials, k = 0, no anchor: nothing to attend; O = 0, lse = -inf."""
+    S, N, P, nsp, tile = 2, 64, 64, 0, 32
+    lay = o.Layout(S, N, P, nsp)
+    Q, K, V = _rand_inputs(S, N, P, nsp, H=1, d=4, seed=1)
+    idx, cnt, _, _ = _selection(o, Q, K, lay, tile, 0, -1, 0.5)
+    assert np.all(cnt == 0)
+    O, lse = o.sparse_attend(Q, K, V, lay, lay, tile, idx, cnt, 0.5)
+    assert np.all(O == 0) and np.all(lse == -np.inf)
+
+
+# --------------------------------------------------------------------------- subsample
+def pin_subsample(o):
+    # closed form on a 5x5 grid, window 2, 2 specials: rows/cols 0, 2, 4 of the grid
+    pos = o.subsample_positions(2, (5, 5), 2)
+    assert pos.tolist() == [0, 1] + [2 + p for p in (0, 2, 4, 10, 12, 14, 20, 22, 24)]
+    pos = o.subsample_positions(5, (37, 37), 2)
+    assert pos.size == 5 + 19 * 19
+    assert pos.tolist()[:8] == [0, 1, 2, 3, 4, 5, 7, 9] and pos[-1] == 5 + 36 * 37 + 36
+    pos = o.subsample_positions(1, (4, 3), 3)
+    assert pos.tolist() == [0, 1 + 0, 1 + 9]
+    # attention over all subsampled tiles is dense attention over exactly the kept keys
+    S, gh, gw, nsp, tile = 2, 6, 6, 3, 16
+    N, P = nsp + gh * gw, 48
+    lay = o.Layout(S, N, P, nsp)
+    Q, K, V = _rand_inputs(S, N, P, nsp, H=2, d=8, seed=21)
+    K2, V2, lay2 = o.subsample_keys(K, V, lay, (gh, gw), 2, tile)
+    assert tuple(lay2) == (S, nsp + 9, 16, nsp)
+    Tk = S * lay2.stride // tile
+    qbar, qc = o.tile_pool(Q, lay, tile, "query")
+    kbar, kc = o.tile_pool(K2, lay2, tile, "key")
+    idx, cnt = o.select_topk(o.tile_scores(qbar, qc, kbar, kc, 0.3), Tk, lay2.stride // tile, 0)
+    O, _ = o.sparse_attend(Q, K2, V2, lay, lay2, tile, idx, cnt, 0.3)
+    kept = [s * P + p for s in range(S) for p in
+            list(range(nsp)) + [nsp + y * gw + x for y in (0, 2, 4) for x in (0, 2, 4)]]
+    qv = np.nonzero((np.arange(S * P) % P) < N)[0]
+    qt = torch.from_numpy(Q[:, qv]).double()
+    kt = torch.from_numpy(K[:, kept]).double()
+    vt = torch.from_numpy(V[:, kept]).double()
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=0.3).numpy()
+    assert np.allclose(O[:, qv], ref, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- hand-worked cases
+def _arr(rows):
+    return np.array([[float(x) for x in r] for r in rows])
+
+
+def pin_hand_worked(o):
+    spec = json.load(open(GOLDEN))
+    env = {"e": math.e, "ln64": math.log(64.0), "__builtins__": {}}
+    for case in spec["cases"]:
+        L = case["layout"]
+        lay = o.Layout(L["frames"], L["tokens"], L["stride"], L["specials"])
+        tile, scale = case["tile"], case["scale"]
+        Q = _arr(case["q"])[None]
+        V = _arr(case["v"])[None]
+        qbar, qc = o.tile_pool(Q, lay, tile, "query")
+        kbar, kc = o.tile_pool(Q, lay, tile, "key")
+        vbar, _ = o.tile_pool(V, lay, tile, "key")
+        sig = o.tile_scores(qbar, qc, kbar, kc, scale)
+        assert np.allclose(sig[0], np.array(case["sigma"], dtype=float), rtol=0, atol=1e-15)
+        for run in case["runs"]:
+            want = np.array([eval(s, env) for s in run["o0"]])
+            if run["k"] == "dense":
+                O, _ = o.dense_attend(Q, Q, V, lay, lay, scale)
+            else:
+                idx, cnt = o.select_topk(sig, run["k"], lay.stride // tile, run["anchor"])
+                got_sel = [idx[0, t, :cnt[0, t]].tolist() for t in range(idx.shape[1])]
+                assert got_sel == run["sel"], (case["name"], run, got_sel)
+                kw = dict(kbar=kbar, vbar=vbar, kcount=kc) if run["landmarks"] else {}
+                O, _ = o.sparse_attend(Q, Q, V, lay, lay, tile, idx, cnt, scale, **kw)
+            assert np.allclose(O[0, :, 0], want, rtol=0, atol=1e-12), (case["name"], run, O[0, :, 0])
+            qv = (np.arange(lay.rows) % lay.stride) < lay.tokens
+            assert np.allclose(O[0, qv, 1], 1.0, rtol=0, atol=1e-12)
+
+
+ALL_PINS = [
+    pin_block_mean_identity, pin_tile_constant_pool, pin_symmetric_scores,
+    pin_select_brute_force, pin_select_invariants,
+    pin_dense_matches_library, pin_all_tiles_is_dense, pin_closed_forms,
+    pin_frame_permutation, pin_query_tiles_independent,
+    pin_landmarks_exact_on_constant_tiles, pin_landmarks_vanish_when_all_selected,
+    pin_empty_key_set, pin_subsample, pin_hand_worked,
+]

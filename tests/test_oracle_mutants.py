@@ -1,0 +1,55 @@
+"""Planted mistakes in copies of the oracle must each be caught by some pin.
+
+The mistakes are the plausible ones: a dropped term, a wrong sign, index or
+constant, a transposed operand.  Each mutant is a fresh module built from the
+oracle's source with one textual change; the real oracle is never modified.
+"""
+import os
+import types
+
+import pytest
+
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "sparse3d_oracle.py")
+
+MUTANTS = {
+    "landmark_bias_ln63": ("LN64 = math.log(64.0)", "LN64 = math.log(63.0)"),
+    "key_pool_keeps_specials": ("return (j >= lay.specials) & (j < lay.tokens)",
+                                "return (j < lay.tokens)"),
+    "query_pool_drops_specials": ("return _inframe(lay) < lay.tokens\n\n\ndef member_rows",
+                                  "return (_inframe(lay) < lay.tokens) & (_inframe(lay) >= lay.specials)\n\n\ndef member_rows"),
+    "ties_to_higher_index": ("np.lexsort((np.arange(Tk), -row))", "np.lexsort((-np.arange(Tk), -row))"),
+    "smallest_scores": ("np.lexsort((np.arange(Tk), -row))", "np.lexsort((np.arange(Tk), row))"),
+    "specials_dropped": ("keys = [spec] + ", "keys = [spec[:0]] + "),
+    "scores_transposed": ("np.matmul(qbar, np.swapaxes(kbar, 1, 2))", "np.matmul(kbar, np.swapaxes(qbar, 1, 2))"),
+    "landmark_unscaled": ("scale * (q @ kbar[h, lm].T) + landmark_bias", "(q @ kbar[h, lm].T) + landmark_bias"),
+    "anchor_short": ("(anchor + 1) * tiles_per_frame)\n", "(anchor + 1) * tiles_per_frame - 1)\n"),
+    "landmarks_include_selected": ("~chosen & (kcount > 0)", "(kcount > 0)"),
+    "dense_reads_pad": ("return _inframe(lay) < lay.tokens\n\n\n# ---", "return _inframe(lay) <= lay.tokens\n\n\n# ---"),
+    "lse_without_log": ("(m + np.log(den))[:, 0]", "(m + den)[:, 0]"),
+    "subsample_odd_rows": ("for y in range(0, gh, window)", "for y in range(1, gh, window)"),
+    "empty_tiles_not_masked": ("sig[:, :, kcount == 0] = -np.inf", "pass"),
+    "mean_over_tile_size": ("mean[h, nz] = s[nz] / count[nz, None]", "mean[h, nz] = s[nz] / Xh.shape[1]"),
+}
+
+
+def _mutant(name):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique/present"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    exec(compile(src.replace(old, new), SRC, "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = _mutant(name)
+    for pin in ALL_PINS:
+        try:
+            pin(mod)
+        except Exception:
+            return
+    pytest.fail(f"planted mistake {name!r} passed every oracle pin")
