@@ -1,0 +1,105 @@
+// The extern "C" entry points declared in include/sparse3d.h: validate on the host
+// (validate.cpp, no HIP), then enqueue the kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include "launch.h"
+#include "sparse3d.h"
+#include "validate.h"
+
+using namespace s3d;
+
+#define S3D_HIP(expr)                                       \
+    do {                                                    \
+        if ((expr) != hipSuccess) return SPARSE3D_ERR_HIP;   \
+    } while (0)
+
+extern "C" {
+
+int sparse3d_abi_version(void) { return SPARSE3D_ABI_VERSION; }
+
+const char* sparse3d_status_string(int status) {
+    switch (status) {
+        case SPARSE3D_OK: return "ok";
+        case SPARSE3D_ERR_NULL: return "a required pointer is NULL";
+        case SPARSE3D_ERR_SHAPE: return "inconsistent sizes or layout";
+        case SPARSE3D_ERR_UNSUPPORTED: return "unsupported size, dtype or option";
+        case SPARSE3D_ERR_HIP: return "HIP runtime error at launch";
+        case SPARSE3D_ERR_ALIAS: return "an output overlaps an input";
+        default: return "unknown status";
+    }
+}
+
+int sparse3d_tile_scores(const void* q, const void* k, const void* v, sparse3d_dtype dtype,
+                         int32_t heads, int32_t head_dim, int32_t tile,
+                         const sparse3d_layout* qlay, const sparse3d_layout* klay, float scale,
+                         float* qbar, float* kbar, float* vbar, float* scores, void* stream) {
+    const int st = validate_tile_scores(q, k, v, dtype, heads, head_dim, tile, qlay, klay, qbar,
+                                        kbar, vbar, scores);
+    if (st != SPARSE3D_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const LayH ql = to_lay(*qlay), kl = to_lay(*klay);
+    S3D_HIP(launch_tile_pool(q, dtype, heads, ql, false, qbar, s));
+    S3D_HIP(launch_tile_pool(k, dtype, heads, kl, true, kbar, s));
+    if (v) S3D_HIP(launch_tile_pool(v, dtype, heads, kl, true, vbar, s));
+    S3D_HIP(launch_tile_scores(qbar, kbar, heads, ql, kl, scale, scores, s));
+    return SPARSE3D_OK;
+}
+
+int sparse3d_select_topk(const float* scores, int32_t heads, int32_t q_tiles, int32_t k_tiles,
+                         int32_t k, int32_t tiles_per_frame, int32_t anchor_frame, int32_t* idx,
+                         int32_t* cnt, int32_t kmax, void* stream) {
+    const int st = validate_select_topk(scores, heads, q_tiles, k_tiles, k, tiles_per_frame,
+                                        anchor_frame, idx, cnt, kmax);
+    if (st != SPARSE3D_OK) return st;
+    S3D_HIP(launch_select_topk(scores, heads, q_tiles, k_tiles, k, tiles_per_frame, anchor_frame,
+                               idx, cnt, kmax, static_cast<hipStream_t>(stream)));
+    return SPARSE3D_OK;
+}
+
+int sparse3d_sparse_attn_fwd(const void* q, const void* k, const void* v, sparse3d_dtype dtype,
+                             int32_t heads, int32_t head_dim, int32_t tile,
+                             const sparse3d_layout* qlay, const sparse3d_layout* klay,
+                             const int32_t* idx, const int32_t* cnt, int32_t kmax,
+                             const float* kbar, const float* vbar, float landmark_bias,
+                             float scale, void* out, sparse3d_dtype out_dtype, float* lse,
+                             void* stream) {
+    const int st = validate_attn(true, q, k, v, dtype, heads, head_dim, tile, qlay, klay, idx, cnt,
+                                 kmax, kbar, vbar, out, out_dtype, lse);
+    if (st != SPARSE3D_OK) return st;
+    AttnArgs a{q, k, v, dtype, out_dtype, heads, to_lay(*qlay), to_lay(*klay), false, idx, cnt,
+               kmax, kbar, vbar, landmark_bias, scale, out, lse};
+    S3D_HIP(launch_attn(a, static_cast<hipStream_t>(stream)));
+    return SPARSE3D_OK;
+}
+
+int sparse3d_dense_attn_fwd(const void* q, const void* k, const void* v, sparse3d_dtype dtype,
+                            int32_t heads, int32_t head_dim, const sparse3d_layout* qlay,
+                            const sparse3d_layout* klay, float scale, void* out,
+                            sparse3d_dtype out_dtype, float* lse, void* stream) {
+    const int st = validate_attn(false, q, k, v, dtype, heads, head_dim, kTile, qlay, klay, nullptr,
+                                 nullptr, 0, nullptr, nullptr, out, out_dtype, lse);
+    if (st != SPARSE3D_OK) return st;
+    AttnArgs a{q, k, v, dtype, out_dtype, heads, to_lay(*qlay), to_lay(*klay), true, nullptr,
+               nullptr, 0, nullptr, nullptr, 0.f, scale, out, lse};
+    S3D_HIP(launch_attn(a, static_cast<hipStream_t>(stream)));
+    return SPARSE3D_OK;
+}
+
+int sparse3d_subsample_layout(const sparse3d_layout* lay, int32_t grid_h, int32_t grid_w,
+                              int32_t window, int32_t tile, sparse3d_layout* out_lay) {
+    return subsample_layout(lay, grid_h, grid_w, window, tile, out_lay);
+}
+
+int sparse3d_grid_subsample_kv(const void* k, const void* v, sparse3d_dtype dtype, int32_t heads,
+                               int32_t head_dim, const sparse3d_layout* lay, int32_t grid_h,
+                               int32_t grid_w, int32_t window, void* k_out, void* v_out,
+                               const sparse3d_layout* out_lay, void* stream) {
+    const int st = validate_subsample(k, v, dtype, heads, head_dim, lay, grid_h, grid_w, window,
+                                      k_out, v_out, out_lay);
+    if (st != SPARSE3D_OK) return st;
+    S3D_HIP(launch_grid_subsample(k, v, dtype, heads, to_lay(*lay), grid_w, window,
+                                  to_lay(*out_lay), k_out, v_out, static_cast<hipStream_t>(stream)));
+    return SPARSE3D_OK;
+}
+
+}  // extern "C"

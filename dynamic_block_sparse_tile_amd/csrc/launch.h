@@ -1,0 +1,49 @@
+// Kernel launchers (host functions, one per kernel family).  Arguments are
+// already validated by the entry points; each returns the launch's hipError_t.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "sparse3d.h"
+
+namespace s3d {
+
+struct LayH {
+    int S, N, P, nsp;
+};
+inline LayH to_lay(const sparse3d_layout& l) { return {l.frames, l.tokens, l.stride, l.specials}; }
+
+hipError_t launch_tile_pool(const void* x, int dtype, int heads, LayH lay, bool key_rows,
+                            float* out, hipStream_t st);
+hipError_t launch_tile_scores(const float* qbar, const float* kbar, int heads, LayH ql, LayH kl,
+                              float scale, float* scores, hipStream_t st);
+hipError_t launch_select_topk(const float* scores, int heads, int tq, int tk, int k, int tpf,
+                              int anchor, int32_t* idx, int32_t* cnt, int kmax, hipStream_t st);
+
+struct AttnArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    int dtype, out_dtype;
+    int heads;
+    LayH ql, kl;
+    bool dense;
+    const int32_t* idx;
+    const int32_t* cnt;
+    int kmax;
+    const float* kbar;  // landmarks on iff non-null
+    const float* vbar;
+    float landmark_bias;
+    float scale;
+    void* out;
+    float* lse;
+};
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+
+hipError_t launch_grid_subsample(const void* k, const void* v, int dtype, int heads, LayH lay,
+                                 int grid_w, int window, LayH out_lay, void* k_out, void* v_out,
+                                 hipStream_t st);
+
+}  // namespace s3d

@@ -1,0 +1,212 @@
+// Per-row top-k tile selection united with the anchor frame (SAF3R abstract: keep
+// only the most promising interactions for this input; Zebra3D abstract: tile-sparse
+// attention).  One workgroup per (head, query tile) row of the score matrix.
+//
+// Scores become order-preserving unsigned keys (-0 folded into +0, so equal values
+// give equal keys).  The k-th largest key T is found by a radix select whose digit
+// range adapts to the live key interval: each round histograms the candidates of
+// [lo, hi] into 2048 bins (LDS atomics), a suffix scan finds the bin holding the k-th
+// largest, and the interval shrinks to that bin -- at most three rounds for 32-bit
+// keys.  Then every key > T is selected, plus the (k - #greater) lowest-index keys
+// equal to T, plus every anchor-frame tile, and the selection is compacted in
+// ascending tile order.  Integer-only after the key transform: bit-exact and
+// deterministic for a given score row.
+#include "device.h"
+#include "launch.h"
+
+namespace s3d {
+
+constexpr int TK_THREADS = 256;
+constexpr int TK_WAVES = TK_THREADS / 64;
+constexpr int NBINS = 2048;
+constexpr int BIN_BITS = 11;
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) == 0) u = 0;            // -0.0 and +0.0 are one value
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Block-wide exclusive prefix sum over thread order; also returns the total.
+__device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) s_tmp[wave] = x;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < TK_WAVES; ++w) {
+        const int t = s_tmp[w];
+        before += (w < wave) ? t : 0;
+        tot += t;
+    }
+    __syncthreads();
+    total = tot;
+    return before + x - v;
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, off));
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
+    return v;
+}
+
+__global__ __launch_bounds__(TK_THREADS) void k_select_topk(const float* __restrict__ scores, int Tk,
+                                                            int k, int tpf, int anchor,
+                                                            int32_t* __restrict__ idx,
+                                                            int32_t* __restrict__ cnt, int kmax) {
+    extern __shared__ uint32_t s_keys[];           // Tk keys
+    __shared__ uint32_t s_hist[NBINS];
+    __shared__ int s_tmp[TK_WAVES];
+    __shared__ uint32_t s_mm[2 * TK_WAVES];
+    __shared__ uint32_t s_bin;
+    __shared__ int s_above;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const size_t row = blockIdx.x;
+    const float* src = scores + row * (size_t)Tk;
+
+    uint32_t kmin = 0xffffffffu, kmaxk = 0u;
+    for (int i = tid; i < Tk; i += TK_THREADS) {
+        const uint32_t key = order_key(src[i]);
+        s_keys[i] = key;
+        kmin = min(kmin, key);
+        kmaxk = max(kmaxk, key);
+    }
+    kmin = wave_min(kmin);
+    kmaxk = wave_max(kmaxk);
+    if (lane == 0) {
+        s_mm[wave] = kmin;
+        s_mm[TK_WAVES + wave] = kmaxk;
+    }
+    __syncthreads();
+    uint32_t lo = s_mm[0], hi = s_mm[TK_WAVES];
+#pragma unroll
+    for (int w = 1; w < TK_WAVES; ++w) {
+        lo = min(lo, s_mm[w]);
+        hi = max(hi, s_mm[TK_WAVES + w]);
+    }
+
+    // mode: 0 = nothing from top-k, 1 = everything, 2 = threshold (thr, need_eq)
+    int mode = 2;
+    if (k <= 0) mode = 0;
+    else if (k >= Tk) mode = 1;
+    int above = 0;
+    if (mode == 2) {
+        while (lo != hi) {
+            const uint32_t span = hi - lo;
+            const int bits = 32 - __clz(span);
+            const int shift = bits > BIN_BITS ? bits - BIN_BITS : 0;
+            for (int b = tid; b < NBINS; b += TK_THREADS) s_hist[b] = 0;
+            __syncthreads();
+            for (int i = tid; i < Tk; i += TK_THREADS) {
+                const uint32_t key = s_keys[i];
+                if (key >= lo && key <= hi) atomicAdd(&s_hist[(key - lo) >> shift], 1u);
+            }
+            __syncthreads();
+            // thread t owns bins [8t, 8t+8); count from the top: scan over reversed threads
+            constexpr int PER = NBINS / TK_THREADS;
+            const int myb = (TK_THREADS - 1 - tid) * PER;   // reversed: thread 0 owns the top bins
+            int local = 0;
+#pragma unroll
+            for (int j = 0; j < PER; ++j) local += (int)s_hist[myb + j];
+            int total;
+            const int before = block_excl_scan(local, s_tmp, total);
+            const int run0 = above + before;
+            if (run0 < k && k <= run0 + local) {
+                int run = run0;
+                for (int j = PER - 1; j >= 0; --j) {
+                    const int c = (int)s_hist[myb + j];
+                    if (run + c >= k) {
+                        s_bin = (uint32_t)(myb + j);
+                        s_above = run;
+                        break;
+                    }
+                    run += c;
+                }
+            }
+            __syncthreads();
+            const uint32_t b = s_bin;
+            above = s_above;
+            const uint64_t nlo = (uint64_t)lo + ((uint64_t)b << shift);
+            const uint64_t nhi = nlo + ((1ull << shift) - 1ull);
+            lo = (uint32_t)nlo;
+            hi = (uint32_t)(nhi < (uint64_t)hi ? nhi : (uint64_t)hi);
+            __syncthreads();
+        }
+    }
+    const uint32_t thr = lo;
+    const int need_eq = k - above;                   // how many keys equal to thr to take
+
+    // contiguous chunk of tile indices per thread, so selection order = index order
+    const int E = (Tk + TK_THREADS - 1) / TK_THREADS;
+    const int i0 = min(tid * E, Tk), i1 = min(i0 + E, Tk);
+    int eq_local = 0;
+    if (mode == 2)
+        for (int i = i0; i < i1; ++i) eq_local += (s_keys[i] == thr);
+    int eq_total;
+    int eq_rank = block_excl_scan(eq_local, s_tmp, eq_total);
+    const int a0 = anchor >= 0 ? anchor * tpf : 0, a1 = anchor >= 0 ? a0 + tpf : 0;
+    int sel_local = 0;
+    {
+        int r = eq_rank;
+        for (int i = i0; i < i1; ++i) {
+            const uint32_t key = s_keys[i];
+            bool s = (i >= a0 && i < a1);
+            if (mode == 1) s = true;
+            else if (mode == 2) {
+                if (key > thr) s = true;
+                else if (key == thr) {
+                    s = s || (r < need_eq);
+                    ++r;
+                }
+            }
+            sel_local += s;
+        }
+    }
+    int total;
+    int pos = block_excl_scan(sel_local, s_tmp, total);
+    int32_t* out = idx + row * (size_t)kmax;
+    {
+        int r = eq_rank;
+        for (int i = i0; i < i1; ++i) {
+            const uint32_t key = s_keys[i];
+            bool s = (i >= a0 && i < a1);
+            if (mode == 1) s = true;
+            else if (mode == 2) {
+                if (key > thr) s = true;
+                else if (key == thr) {
+                    s = s || (r < need_eq);
+                    ++r;
+                }
+            }
+            if (s) {
+                if (pos < kmax) out[pos] = i;
+                ++pos;
+            }
+        }
+    }
+    for (int p = total + tid; p < kmax; p += TK_THREADS) out[p] = -1;
+    if (tid == 0) cnt[row] = min(total, kmax);
+}
+
+hipError_t launch_select_topk(const float* scores, int heads, int tq, int tk, int k, int tpf,
+                              int anchor, int32_t* idx, int32_t* cnt, int kmax, hipStream_t st) {
+    const unsigned rows = (unsigned)heads * (unsigned)tq;
+    const size_t shm = (size_t)tk * sizeof(uint32_t);
+    hipLaunchKernelGGL(k_select_topk, dim3(rows), dim3(TK_THREADS), shm, st, scores, tk, k, tpf,
+                       anchor, idx, cnt, kmax);
+    return hipGetLastError();
+}
+
+}  // namespace s3d

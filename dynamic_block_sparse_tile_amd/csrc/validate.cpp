@@ -1,0 +1,165 @@
+// Host-side argument checks (no HIP).  Every entry point runs these before it
+// launches anything, so a rejected call has no side effects.
+#include "validate.h"
+
+#include <algorithm>
+#include <cstdint>
+
+namespace s3d {
+
+int check_layout(const sparse3d_layout* l) {
+    if (!l) return SPARSE3D_ERR_NULL;
+    if (l->frames < 1 || l->tokens < 1 || l->stride < 1) return SPARSE3D_ERR_SHAPE;
+    if (l->tokens > l->stride) return SPARSE3D_ERR_SHAPE;
+    if (l->specials < 0 || l->specials >= l->tokens) return SPARSE3D_ERR_SHAPE;
+    if (l->stride % kTile != 0) return SPARSE3D_ERR_SHAPE;
+    // row indices are int32 inside the kernels
+    if (lay_rows(*l) > (int64_t(1) << 30)) return SPARSE3D_ERR_UNSUPPORTED;
+    return SPARSE3D_OK;
+}
+
+int check_dtype(int dt) {
+    return (dt == SPARSE3D_F32 || dt == SPARSE3D_BF16) ? SPARSE3D_OK : SPARSE3D_ERR_UNSUPPORTED;
+}
+
+int check_heads_dims(int32_t heads, int32_t head_dim, int32_t tile) {
+    if (heads < 1 || head_dim < 1 || tile < 1) return SPARSE3D_ERR_SHAPE;
+    if (head_dim != kHeadDim || tile != kTile) return SPARSE3D_ERR_UNSUPPORTED;
+    if (heads > 65535) return SPARSE3D_ERR_UNSUPPORTED;
+    return SPARSE3D_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    auto pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+#define S3D_TRY(expr)                      \
+    do {                                   \
+        int _st = (expr);                  \
+        if (_st != SPARSE3D_OK) return _st; \
+    } while (0)
+
+int validate_tile_scores(const void* q, const void* k, const void* v, int dtype, int32_t heads,
+                         int32_t head_dim, int32_t tile, const sparse3d_layout* qlay,
+                         const sparse3d_layout* klay, const float* qbar, const float* kbar,
+                         const float* vbar, const float* scores) {
+    if (!q || !k || !qbar || !kbar || !scores) return SPARSE3D_ERR_NULL;
+    if ((v == nullptr) != (vbar == nullptr)) return SPARSE3D_ERR_NULL;
+    S3D_TRY(check_dtype(dtype));
+    S3D_TRY(check_heads_dims(heads, head_dim, tile));
+    S3D_TRY(check_layout(qlay));
+    S3D_TRY(check_layout(klay));
+    if (qlay->frames != klay->frames) return SPARSE3D_ERR_SHAPE;
+    const size_t eb = dtype_bytes(sparse3d_dtype(dtype));
+    const size_t qb = size_t(heads) * lay_rows(*qlay) * head_dim * eb;
+    const size_t kb = size_t(heads) * lay_rows(*klay) * head_dim * eb;
+    const size_t Tq = lay_tiles(*qlay), Tk = lay_tiles(*klay);
+    const size_t qbar_b = size_t(heads) * Tq * head_dim * 4;
+    const size_t kbar_b = size_t(heads) * Tk * head_dim * 4;
+    const size_t sc_b = size_t(heads) * Tq * Tk * 4;
+    const void* outs[4] = {qbar, kbar, vbar, scores};
+    const size_t outn[4] = {qbar_b, kbar_b, vbar ? kbar_b : 0, sc_b};
+    for (int i = 0; i < 4; ++i) {
+        if (overlaps(outs[i], outn[i], q, qb) || overlaps(outs[i], outn[i], k, kb) ||
+            overlaps(outs[i], outn[i], v, kb))
+            return SPARSE3D_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], outn[i], outs[j], outn[j])) return SPARSE3D_ERR_ALIAS;
+    }
+    return SPARSE3D_OK;
+}
+
+int validate_select_topk(const float* scores, int32_t heads, int32_t q_tiles, int32_t k_tiles,
+                         int32_t k, int32_t tiles_per_frame, int32_t anchor_frame,
+                         const int32_t* idx, const int32_t* cnt, int32_t kmax) {
+    if (!scores || !cnt) return SPARSE3D_ERR_NULL;
+    if (kmax > 0 && !idx) return SPARSE3D_ERR_NULL;
+    if (heads < 1 || q_tiles < 1 || k_tiles < 1 || k < 0 || tiles_per_frame < 1 || kmax < 0)
+        return SPARSE3D_ERR_SHAPE;
+    if (k_tiles % tiles_per_frame != 0) return SPARSE3D_ERR_SHAPE;
+    if (anchor_frame < -1 || anchor_frame >= k_tiles / tiles_per_frame) return SPARSE3D_ERR_SHAPE;
+    const int64_t need = std::min<int64_t>(
+        k_tiles, int64_t(k) + (anchor_frame >= 0 ? tiles_per_frame : 0));
+    if (kmax < need) return SPARSE3D_ERR_SHAPE;
+    if (k_tiles > kMaxTopkTiles) return SPARSE3D_ERR_UNSUPPORTED;
+    if (heads > 65535) return SPARSE3D_ERR_UNSUPPORTED;
+    const size_t sb = size_t(heads) * q_tiles * k_tiles * 4;
+    const size_t ib = size_t(heads) * q_tiles * kmax * 4;
+    const size_t cb = size_t(heads) * q_tiles * 4;
+    if (overlaps(idx, ib, scores, sb) || overlaps(cnt, cb, scores, sb) || overlaps(idx, ib, cnt, cb))
+        return SPARSE3D_ERR_ALIAS;
+    return SPARSE3D_OK;
+}
+
+int validate_attn(bool sparse, const void* q, const void* k, const void* v, int dtype,
+                  int32_t heads, int32_t head_dim, int32_t tile, const sparse3d_layout* qlay,
+                  const sparse3d_layout* klay, const int32_t* idx, const int32_t* cnt,
+                  int32_t kmax, const float* kbar, const float* vbar, const void* out,
+                  int out_dtype, const float* lse) {
+    if (!q || !k || !v || !out) return SPARSE3D_ERR_NULL;
+    if (sparse) {
+        if (!cnt) return SPARSE3D_ERR_NULL;
+        if (kmax > 0 && !idx) return SPARSE3D_ERR_NULL;
+        if (kmax < 0) return SPARSE3D_ERR_SHAPE;
+        if ((kbar == nullptr) != (vbar == nullptr)) return SPARSE3D_ERR_NULL;
+    }
+    S3D_TRY(check_dtype(dtype));
+    S3D_TRY(check_dtype(out_dtype));
+    S3D_TRY(check_heads_dims(heads, head_dim, tile));
+    S3D_TRY(check_layout(qlay));
+    S3D_TRY(check_layout(klay));
+    if (qlay->frames != klay->frames) return SPARSE3D_ERR_SHAPE;
+    if (sparse && lay_tiles(*klay) > kMaxTopkTiles) return SPARSE3D_ERR_UNSUPPORTED;
+    if (int64_t(heads) * lay_tiles(*qlay) > (int64_t(1) << 31) - 1) return SPARSE3D_ERR_UNSUPPORTED;
+    const size_t eb = dtype_bytes(sparse3d_dtype(dtype));
+    const size_t qb = size_t(heads) * lay_rows(*qlay) * head_dim * eb;
+    const size_t kb = size_t(heads) * lay_rows(*klay) * head_dim * eb;
+    const size_t ob = size_t(heads) * lay_rows(*qlay) * head_dim * dtype_bytes(sparse3d_dtype(out_dtype));
+    const size_t lb = size_t(heads) * lay_rows(*qlay) * 4;
+    if (overlaps(out, ob, q, qb) || overlaps(out, ob, k, kb) || overlaps(out, ob, v, kb))
+        return SPARSE3D_ERR_ALIAS;
+    if (overlaps(lse, lb, q, qb) || overlaps(lse, lb, k, kb) || overlaps(lse, lb, v, kb) ||
+        overlaps(lse, lb, out, ob))
+        return SPARSE3D_ERR_ALIAS;
+    return SPARSE3D_OK;
+}
+
+int subsample_layout(const sparse3d_layout* lay, int32_t grid_h, int32_t grid_w, int32_t window,
+                     int32_t tile, sparse3d_layout* out) {
+    if (!lay || !out) return SPARSE3D_ERR_NULL;
+    S3D_TRY(check_layout(lay));
+    if (grid_h < 1 || grid_w < 1 || window < 1 || tile < 1) return SPARSE3D_ERR_SHAPE;
+    if (tile != kTile) return SPARSE3D_ERR_UNSUPPORTED;
+    if (int64_t(lay->specials) + int64_t(grid_h) * grid_w != lay->tokens) return SPARSE3D_ERR_SHAPE;
+    const int32_t kh = (grid_h + window - 1) / window, kw = (grid_w + window - 1) / window;
+    const int32_t tokens = lay->specials + kh * kw;
+    out->frames = lay->frames;
+    out->tokens = tokens;
+    out->stride = (tokens + tile - 1) / tile * tile;
+    out->specials = lay->specials;
+    return SPARSE3D_OK;
+}
+
+int validate_subsample(const void* k, const void* v, int dtype, int32_t heads, int32_t head_dim,
+                       const sparse3d_layout* lay, int32_t grid_h, int32_t grid_w, int32_t window,
+                       const void* k_out, const void* v_out, const sparse3d_layout* out_lay) {
+    if (!k || !v || !k_out || !v_out || !out_lay) return SPARSE3D_ERR_NULL;
+    S3D_TRY(check_dtype(dtype));
+    S3D_TRY(check_heads_dims(heads, head_dim, kTile));
+    sparse3d_layout want;
+    S3D_TRY(subsample_layout(lay, grid_h, grid_w, window, kTile, &want));
+    if (out_lay->frames != want.frames || out_lay->tokens != want.tokens ||
+        out_lay->stride != want.stride || out_lay->specials != want.specials)
+        return SPARSE3D_ERR_SHAPE;
+    const size_t eb = dtype_bytes(sparse3d_dtype(dtype));
+    const size_t ib = size_t(heads) * lay_rows(*lay) * head_dim * eb;
+    const size_t ob = size_t(heads) * lay_rows(want) * head_dim * eb;
+    if (overlaps(k_out, ob, k, ib) || overlaps(k_out, ob, v, ib) || overlaps(v_out, ob, k, ib) ||
+        overlaps(v_out, ob, v, ib) || overlaps(k_out, ob, v_out, ob))
+        return SPARSE3D_ERR_ALIAS;
+    return SPARSE3D_OK;
+}
+
+}  // namespace s3d

@@ -1,0 +1,48 @@
+// Host-side argument checks for every entry point.  Plain C++ with no HIP
+// dependency: each function returns a sparse3d_status and touches nothing.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "sparse3d.h"
+
+namespace s3d {
+
+constexpr int kTile = 64;
+constexpr int kHeadDim = 64;
+constexpr int kMaxTopkTiles = 12288;   // row keys live in LDS (48 KiB)
+
+inline int64_t lay_rows(const sparse3d_layout& l) { return int64_t(l.frames) * l.stride; }
+inline int64_t lay_tiles(const sparse3d_layout& l) { return lay_rows(l) / kTile; }
+inline size_t dtype_bytes(sparse3d_dtype d) { return d == SPARSE3D_BF16 ? 2 : 4; }
+
+int check_layout(const sparse3d_layout* l);
+int check_dtype(int dt);
+int check_heads_dims(int32_t heads, int32_t head_dim, int32_t tile);
+// Byte ranges [a, a+na) and [b, b+nb) overlap (both non-empty).
+bool overlaps(const void* a, size_t na, const void* b, size_t nb);
+
+int validate_tile_scores(const void* q, const void* k, const void* v, int dtype, int32_t heads,
+                         int32_t head_dim, int32_t tile, const sparse3d_layout* qlay,
+                         const sparse3d_layout* klay, const float* qbar, const float* kbar,
+                         const float* vbar, const float* scores);
+
+int validate_select_topk(const float* scores, int32_t heads, int32_t q_tiles, int32_t k_tiles,
+                         int32_t k, int32_t tiles_per_frame, int32_t anchor_frame,
+                         const int32_t* idx, const int32_t* cnt, int32_t kmax);
+
+int validate_attn(bool sparse, const void* q, const void* k, const void* v, int dtype,
+                  int32_t heads, int32_t head_dim, int32_t tile, const sparse3d_layout* qlay,
+                  const sparse3d_layout* klay, const int32_t* idx, const int32_t* cnt,
+                  int32_t kmax, const float* kbar, const float* vbar, const void* out,
+                  int out_dtype, const float* lse);
+
+int subsample_layout(const sparse3d_layout* lay, int32_t grid_h, int32_t grid_w, int32_t window,
+                     int32_t tile, sparse3d_layout* out);
+
+int validate_subsample(const void* k, const void* v, int dtype, int32_t heads, int32_t head_dim,
+                       const sparse3d_layout* lay, int32_t grid_h, int32_t grid_w, int32_t window,
+                       const void* k_out, const void* v_out, const sparse3d_layout* out_lay);
+
+}  // namespace s3d

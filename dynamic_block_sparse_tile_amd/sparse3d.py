@@ -1,0 +1,237 @@
+"""Python binding of libsparse3d.so (argument marshalling only).
+
+Every function here has the name of the C entry point it wraps.  Torch provides
+device memory and the current stream; all computation happens in the library's
+HIP kernels.  If the library is not built, loading fails with an ImportError:
+there is no fallback path.
+
+Layouts are plain tuples ``(frames, tokens, stride, specials)``.  Tensors are
+contiguous ``[heads, frames*stride, 64]`` on one HIP device.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+__all__ = [
+    "Sparse3dError", "library", "sparse3d_abi_version", "sparse3d_status_string",
+    "sparse3d_tile_scores", "sparse3d_select_topk", "sparse3d_sparse_attn_fwd",
+    "sparse3d_dense_attn_fwd", "sparse3d_subsample_layout", "sparse3d_grid_subsample_kv",
+    "kmax_for", "LN64",
+]
+
+LN64 = math.log(64.0)
+TILE = 64
+HEAD_DIM = 64
+F32, BF16 = 0, 1
+_LIBPATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparse3d.so")
+_lib = None
+
+
+class Sparse3dError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"sparse3d status {status}: {msg}")
+        self.status = status
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("frames", ctypes.c_int32), ("tokens", ctypes.c_int32),
+                ("stride", ctypes.c_int32), ("specials", ctypes.c_int32)]
+
+
+_i32, _f32, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+_LP = ctypes.POINTER(_Layout)
+
+_SIGS = {
+    "sparse3d_abi_version": ([], ctypes.c_int),
+    "sparse3d_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "sparse3d_tile_scores": ([_vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32, _LP, _LP, _f32,
+                              _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "sparse3d_select_topk": ([_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp],
+                             ctypes.c_int),
+    "sparse3d_sparse_attn_fwd": ([_vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32, _LP, _LP, _vp,
+                                  _vp, _i32, _vp, _vp, _f32, _f32, _vp, ctypes.c_int, _vp, _vp],
+                                 ctypes.c_int),
+    "sparse3d_dense_attn_fwd": ([_vp, _vp, _vp, ctypes.c_int, _i32, _i32, _LP, _LP, _f32, _vp,
+                                 ctypes.c_int, _vp, _vp], ctypes.c_int),
+    "sparse3d_subsample_layout": ([_LP, _i32, _i32, _i32, _i32, _LP], ctypes.c_int),
+    "sparse3d_grid_subsample_kv": ([_vp, _vp, ctypes.c_int, _i32, _i32, _LP, _i32, _i32, _i32,
+                                    _vp, _vp, _LP, _vp], ctypes.c_int),
+}
+
+
+def library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libsparse3d.so once (ImportError if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or _LIBPATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: build it with `python -m dynamic_block_sparse_tile_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (args, res) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise Sparse3dError(status, library().sparse3d_status_string(status).decode())
+
+
+def _lay(t: Sequence[int]) -> _Layout:
+    f, n, p, s = (int(x) for x in t)
+    return _Layout(f, n, p, s)
+
+
+def _dt(x: torch.Tensor) -> int:
+    if x.dtype == torch.bfloat16:
+        return BF16
+    if x.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {x.dtype} (bfloat16 or float32)")
+
+
+def _dev(x: torch.Tensor, name: str) -> torch.Tensor:
+    if not x.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return x
+
+
+def _stream(x: torch.Tensor) -> int:
+    return torch.cuda.current_stream(x.device).cuda_stream
+
+
+def _ptr(x: Optional[torch.Tensor]) -> Optional[int]:
+    return None if x is None else x.data_ptr()
+
+
+def sparse3d_abi_version() -> int:
+    return library().sparse3d_abi_version()
+
+
+def sparse3d_status_string(status: int) -> str:
+    return library().sparse3d_status_string(status).decode()
+
+
+def _tiles(lay) -> int:
+    return lay[0] * lay[2] // TILE
+
+
+def sparse3d_tile_scores(q: torch.Tensor, k: torch.Tensor, qlay, klay=None,
+                         v: Optional[torch.Tensor] = None, scale: Optional[float] = None):
+    """Pooled tile summaries and tile scores.  Returns (qbar, kbar, vbar|None, scores)."""
+    klay = qlay if klay is None else klay
+    _dev(q, "q"), _dev(k, "k")
+    if v is not None:
+        _dev(v, "v")
+    H = q.shape[0]
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else scale
+    Tq, Tk = _tiles(qlay), _tiles(klay)
+    f = dict(device=q.device, dtype=torch.float32)
+    qbar = torch.empty((H, Tq, HEAD_DIM), **f)
+    kbar = torch.empty((H, Tk, HEAD_DIM), **f)
+    vbar = torch.empty((H, Tk, HEAD_DIM), **f) if v is not None else None
+    scores = torch.empty((H, Tq, Tk), **f)
+    ql, kl = _lay(qlay), _lay(klay)
+    _check(library().sparse3d_tile_scores(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), H, q.shape[2], TILE, ctypes.byref(ql), ctypes.byref(kl),
+        scale, _ptr(qbar), _ptr(kbar), _ptr(vbar), _ptr(scores), _stream(q)))
+    return qbar, kbar, vbar, scores
+
+
+def kmax_for(k_tiles: int, k: int, tiles_per_frame: int, anchor_frame: int) -> int:
+    """Size of the index table's last axis: min(Tk, k + anchor tiles)."""
+    return min(k_tiles, max(k, 0) + (tiles_per_frame if anchor_frame >= 0 else 0))
+
+
+def sparse3d_select_topk(scores: torch.Tensor, k: int, tiles_per_frame: int, anchor_frame: int = 0,
+                         kmax: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Top-k key tiles per query tile united with the anchor frame.  Returns (idx, cnt)."""
+    _dev(scores, "scores")
+    H, Tq, Tk = scores.shape
+    kmax = kmax_for(Tk, k, tiles_per_frame, anchor_frame) if kmax is None else kmax
+    idx = torch.empty((H, Tq, max(kmax, 0)), device=scores.device, dtype=torch.int32)
+    cnt = torch.empty((H, Tq), device=scores.device, dtype=torch.int32)
+    _check(library().sparse3d_select_topk(
+        _ptr(scores), H, Tq, Tk, k, tiles_per_frame, anchor_frame,
+        _ptr(idx) if kmax > 0 else None, _ptr(cnt), kmax, _stream(scores)))
+    return idx, cnt
+
+
+def _out_dtype(q, out_dtype):
+    od = q.dtype if out_dtype is None else out_dtype
+    return od, (BF16 if od == torch.bfloat16 else F32)
+
+
+def sparse3d_sparse_attn_fwd(q, k, v, qlay, klay, idx, cnt, kbar=None, vbar=None,
+                             landmark_bias: float = LN64, scale: Optional[float] = None,
+                             out_dtype=None, return_lse: bool = False):
+    """Attention over specials + selected tiles (+ landmarks when kbar/vbar are given)."""
+    for x, n in ((q, "q"), (k, "k"), (v, "v"), (idx, "idx"), (cnt, "cnt")):
+        _dev(x, n)
+    if (kbar is None) != (vbar is None):
+        raise ValueError("kbar and vbar go together")
+    H = q.shape[0]
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else scale
+    od, odc = _out_dtype(q, out_dtype)
+    out = torch.empty(q.shape, device=q.device, dtype=od)
+    lse = torch.empty(q.shape[:2], device=q.device, dtype=torch.float32) if return_lse else None
+    ql, kl = _lay(qlay), _lay(klay)
+    kmax = idx.shape[2]
+    _check(library().sparse3d_sparse_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), H, q.shape[2], TILE, ctypes.byref(ql), ctypes.byref(kl),
+        _ptr(idx) if kmax > 0 else None, _ptr(cnt), kmax, _ptr(kbar), _ptr(vbar), landmark_bias,
+        scale, _ptr(out), odc, _ptr(lse), _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+def sparse3d_dense_attn_fwd(q, k, v, qlay, klay=None, scale: Optional[float] = None,
+                            out_dtype=None, return_lse: bool = False):
+    """Dense global attention over every valid key (the library's own baseline)."""
+    klay = qlay if klay is None else klay
+    for x, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(x, n)
+    H = q.shape[0]
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else scale
+    od, odc = _out_dtype(q, out_dtype)
+    out = torch.empty(q.shape, device=q.device, dtype=od)
+    lse = torch.empty(q.shape[:2], device=q.device, dtype=torch.float32) if return_lse else None
+    ql, kl = _lay(qlay), _lay(klay)
+    _check(library().sparse3d_dense_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), H, q.shape[2], ctypes.byref(ql), ctypes.byref(kl),
+        scale, _ptr(out), odc, _ptr(lse), _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+def sparse3d_subsample_layout(lay, grid_h: int, grid_w: int, window: int, tile: int = TILE):
+    """Key/value layout after the grid subsample, as a (frames, tokens, stride, specials) tuple."""
+    src, dst = _lay(lay), _Layout()
+    _check(library().sparse3d_subsample_layout(ctypes.byref(src), grid_h, grid_w, window, tile,
+                                               ctypes.byref(dst)))
+    return (dst.frames, dst.tokens, dst.stride, dst.specials)
+
+
+def sparse3d_grid_subsample_kv(k, v, lay, grid: Tuple[int, int], window: int):
+    """Thin keys/values on the patch grid.  Returns (k_sub, v_sub, layout_sub)."""
+    _dev(k, "k"), _dev(v, "v")
+    H = k.shape[0]
+    out_lay = sparse3d_subsample_layout(lay, grid[0], grid[1], window)
+    rows = out_lay[0] * out_lay[2]
+    k2 = torch.empty((H, rows, k.shape[2]), device=k.device, dtype=k.dtype)
+    v2 = torch.empty_like(k2)
+    il, ol = _lay(lay), _lay(out_lay)
+    _check(library().sparse3d_grid_subsample_kv(
+        _ptr(k), _ptr(v), _dt(k), H, k.shape[2], ctypes.byref(il), grid[0], grid[1], window,
+        _ptr(k2), _ptr(v2), ctypes.byref(ol), _stream(k)))
+    return k2, v2, out_lay

@@ -1,0 +1,139 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and
+rejects bad arguments on the host before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dynamic_block_sparse_tile_amd import sparse3d as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse3d.h")
+
+NULL = None
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_HIP, ERR_ALIAS = 0, 1, 2, 3, 4, 5
+FAKE = 0x7F0000000000        # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparse3d_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return S.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(S._SIGS), "binding signatures must cover the header exactly"
+
+
+def test_version_and_status(lib):
+    assert lib.sparse3d_abi_version() == 1
+    for st in range(6):
+        assert lib.sparse3d_status_string(st)
+    assert lib.sparse3d_status_string(99) == b"unknown status"
+
+
+def L(f=2, n=256, p=256, s=0):
+    return ctypes.byref(S._Layout(f, n, p, s))
+
+
+def scores_call(lib, q=FAKE, k=FAKE, v=NULL, dt=1, H=2, d=64, tile=64, ql=None, kl=None,
+                qbar=FAKE + 10**9, kbar=FAKE + 2 * 10**9, vbar=NULL, sc=FAKE + 3 * 10**9):
+    return lib.sparse3d_tile_scores(q, k, v, dt, H, d, tile, ql or L(), kl or L(), 0.125,
+                                    qbar, kbar, vbar, sc, NULL)
+
+
+def test_tile_scores_validation(lib):
+    assert scores_call(lib, q=NULL) == ERR_NULL
+    assert scores_call(lib, sc=NULL) == ERR_NULL
+    assert scores_call(lib, v=FAKE + 4 * 10**9) == ERR_NULL            # v without vbar
+    assert scores_call(lib, d=32) == ERR_UNSUP
+    assert scores_call(lib, tile=32) == ERR_UNSUP
+    assert scores_call(lib, dt=7) == ERR_UNSUP
+    assert scores_call(lib, H=0) == ERR_SHAPE
+    assert scores_call(lib, ql=L(p=200)) == ERR_SHAPE                   # stride % 64
+    assert scores_call(lib, ql=L(n=300)) == ERR_SHAPE                   # tokens > stride
+    assert scores_call(lib, ql=L(s=256)) == ERR_SHAPE                   # specials >= tokens
+    assert scores_call(lib, kl=L(f=3, n=256, p=256)) == ERR_SHAPE       # frame counts differ
+    assert scores_call(lib, sc=FAKE + 100) == ERR_ALIAS                 # scores overlaps q
+    assert lib.sparse3d_tile_scores(FAKE, FAKE, NULL, 1, 2, 64, 64, NULL, L(), 0.1, FAKE + 10**9,
+                                    FAKE + 2 * 10**9, NULL, FAKE + 3 * 10**9, NULL) == ERR_NULL
+
+
+def topk_call(lib, sc=FAKE, H=2, tq=8, tk=8, k=4, tpf=4, anchor=0, idx=FAKE + 10**9,
+              cnt=FAKE + 2 * 10**9, kmax=8):
+    return lib.sparse3d_select_topk(sc, H, tq, tk, k, tpf, anchor, idx, cnt, kmax, NULL)
+
+
+def test_select_validation(lib):
+    assert topk_call(lib, sc=NULL) == ERR_NULL
+    assert topk_call(lib, cnt=NULL) == ERR_NULL
+    assert topk_call(lib, idx=NULL) == ERR_NULL
+    assert topk_call(lib, kmax=7) == ERR_SHAPE                          # k + anchor tiles = 8
+    assert topk_call(lib, anchor=-1, kmax=3) == ERR_SHAPE
+    assert topk_call(lib, tpf=3) == ERR_SHAPE                           # 8 % 3
+    assert topk_call(lib, anchor=2) == ERR_SHAPE                        # only 2 frames
+    assert topk_call(lib, anchor=-2) == ERR_SHAPE
+    assert topk_call(lib, k=-1) == ERR_SHAPE
+    assert topk_call(lib, tk=12289 * 1, tpf=12289, kmax=8, anchor=-1) == ERR_UNSUP
+    assert topk_call(lib, idx=FAKE + 64) == ERR_ALIAS
+
+
+def attn_call(lib, q=FAKE, k=FAKE + 10**9, v=FAKE + 2 * 10**9, dt=1, H=2, d=64, tile=64,
+              ql=None, kl=None, idx=FAKE + 3 * 10**9, cnt=FAKE + 4 * 10**9, kmax=8, kbar=NULL,
+              vbar=NULL, out=FAKE + 5 * 10**9, odt=1, lse=NULL):
+    return lib.sparse3d_sparse_attn_fwd(q, k, v, dt, H, d, tile, ql or L(), kl or L(), idx, cnt,
+                                        kmax, kbar, vbar, 4.1588830833596715, 0.125, out, odt,
+                                        lse, NULL)
+
+
+def test_attn_validation(lib):
+    assert attn_call(lib, v=NULL) == ERR_NULL
+    assert attn_call(lib, out=NULL) == ERR_NULL
+    assert attn_call(lib, cnt=NULL) == ERR_NULL
+    assert attn_call(lib, idx=NULL) == ERR_NULL
+    assert attn_call(lib, kbar=FAKE + 6 * 10**9) == ERR_NULL            # kbar without vbar
+    assert attn_call(lib, kmax=-1) == ERR_SHAPE
+    assert attn_call(lib, odt=5) == ERR_UNSUP
+    assert attn_call(lib, d=128) == ERR_UNSUP
+    assert attn_call(lib, kl=L(f=3)) == ERR_SHAPE
+    assert attn_call(lib, out=FAKE + 64) == ERR_ALIAS                   # out overlaps q
+    assert attn_call(lib, lse=FAKE + 5 * 10**9 + 128) == ERR_ALIAS      # lse overlaps out
+    assert lib.sparse3d_dense_attn_fwd(FAKE, FAKE, NULL, 1, 2, 64, L(), L(), 0.1, FAKE + 10**9, 1,
+                                       NULL, NULL) == ERR_NULL
+    assert lib.sparse3d_dense_attn_fwd(FAKE, FAKE, FAKE, 1, 2, 64, L(), L(), 0.1, FAKE + 64, 1,
+                                       NULL, NULL) == ERR_ALIAS
+
+
+def test_subsample_layout_host_only(lib):
+    out = S._Layout()
+    lay = S._Layout(256, 1374, 1408, 5)
+    assert lib.sparse3d_subsample_layout(ctypes.byref(lay), 37, 37, 2, 64, ctypes.byref(out)) == OK
+    assert (out.frames, out.tokens, out.stride, out.specials) == (256, 366, 384, 5)
+    assert lib.sparse3d_subsample_layout(ctypes.byref(lay), 37, 37, 3, 64, ctypes.byref(out)) == OK
+    assert (out.tokens, out.stride) == (5 + 13 * 13, 192)
+    assert lib.sparse3d_subsample_layout(ctypes.byref(lay), 36, 37, 2, 64, ctypes.byref(out)) == ERR_SHAPE
+    assert lib.sparse3d_subsample_layout(ctypes.byref(lay), 37, 37, 0, 64, ctypes.byref(out)) == ERR_SHAPE
+    assert lib.sparse3d_subsample_layout(NULL, 37, 37, 2, 64, ctypes.byref(out)) == ERR_NULL
+    bad = S._Layout(256, 366, 384, 5)
+    assert lib.sparse3d_grid_subsample_kv(FAKE, FAKE + 10**10, 1, 16, 64, ctypes.byref(lay), 37, 37, 2,
+                                          FAKE + 2 * 10**10, FAKE + 3 * 10**10, ctypes.byref(S._Layout(256, 366, 448, 5)),
+                                          NULL) == ERR_SHAPE
+    assert lib.sparse3d_grid_subsample_kv(FAKE, FAKE + 10**10, 1, 16, 64, ctypes.byref(lay), 37, 37, 2,
+                                          FAKE + 64, FAKE + 3 * 10**10, ctypes.byref(bad), NULL) == ERR_ALIAS
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(2, 256, 64)
+    with pytest.raises(ValueError):
+        S.sparse3d_tile_scores(x, x, (2, 256, 256, 0))

@@ -1,0 +1,39 @@
+"""Host-side bookkeeping of the layer (no GPU): pseudo-tiles, sparsity, k calibration, FLOPs."""
+import numpy as np
+
+from dynamic_block_sparse_tile_amd import layer as LY
+
+
+def test_special_tiles_and_tpf():
+    assert LY.special_tiles((128, 1374, 1408, 5)) == 10
+    assert LY.special_tiles((256, 1374, 1408, 5)) == 20
+    assert LY.special_tiles((8, 1374, 1408, 5)) == 1
+    assert LY.special_tiles((2, 256, 256, 0)) == 0
+    assert LY.tiles_per_frame((128, 1374, 1408, 5)) == 22
+
+
+def test_measured_sparsity():
+    # 10 pseudo-tiles + 159 selected of 2816 -> 94.0 %
+    assert abs(LY.measured_sparsity(159 * 100, 100, 10, 2816) - (1 - 169 / 2816)) < 1e-12
+
+
+def test_calibrate_k_monotone_search():
+    rng = np.random.default_rng(0)
+    for trial in range(50):
+        tk = int(rng.integers(5, 400))
+        rows = int(rng.integers(1, 50))
+        ts = int(rng.integers(0, 4))
+        # selection size per row: k plus a data-dependent overlap with 'anchor' tiles, capped
+        extra = rng.integers(0, 6, size=rows)
+        count = lambda k: int(np.minimum(k + np.where(k > 0, extra, extra), tk).sum())
+        target = float(rng.uniform(0.0, 1.0))
+        k = LY.calibrate_k(count, rows, ts, tk, target)
+        sp = lambda kk: LY.measured_sparsity(count(kk), rows, ts, tk)
+        best = min(range(tk + 1), key=lambda kk: (abs(sp(kk) - target), -sp(kk)))
+        assert abs(sp(k) - target) <= abs(sp(best) - target) + 1e-12
+
+
+def test_flops():
+    assert LY.pair_flops() == 4 * 64 ** 3 == 1048576
+    assert LY.selected_flops(total_cnt=5, rows=2, ts=1) == 7 * 1048576
+    assert LY.selected_flops(total_cnt=0, rows=1, ts=0, landmarks=10) == 10 * 64 * 4 * 64

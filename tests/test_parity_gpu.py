@@ -1,0 +1,290 @@
+"""HIP path vs the fp64 oracle, through the C ABI, on seeded inputs (needs an MI355X).
+
+Selections: bit-exact against the oracle's rule applied to the GPU's fp32 scores,
+and equal to the oracle's own fp64 selection wherever the k-th/(k+1)-th score gap
+exceeds 1e-3 relative.  Outputs, given the GPU's selection: max-abs 1e-4 for fp32
+inputs, 2e-2 for bf16.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dynamic_block_sparse_tile_amd import layer as LY
+from dynamic_block_sparse_tile_amd import sparse3d as S
+from dynamic_block_sparse_tile_amd import synth
+from parity_helpers import (TOL, check_scores, check_selection, compare_outputs, dev,
+                            oracle_pool_scores, sample_tiles, say, tdt, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_full_case(w, seed=0, k=None, landmarks=None, out_f32=True, pad=0.0):
+    """Whole layer on the GPU, everything compared with the oracle (small workloads)."""
+    k = w.k if k is None else k
+    lm = w.landmarks if landmarks is None else landmarks
+    say(f"[case] {w.name} seed={seed} k={k} landmarks={lm} dtype={w.dtype}")
+    inp = synth.make_inputs(w, seed=seed, pad_value=pad)
+    dt = tdt(w)
+    q, v = to_dev(inp.q, dt), to_dev(inp.v, dt)
+    lay = w.layout
+    res = LY.sparse_global_attention(q, q, v, lay, top_k=k, anchor_frame=w.anchor, landmarks=lm,
+                                     out_dtype=torch.float32 if out_f32 else None, return_lse=True)
+    torch.cuda.synchronize()
+    ol = oracle.Layout(*lay)
+    ref = oracle_pool_scores(inp, ol, ol, landmarks=lm)
+    g = {n: getattr(res, n).cpu().numpy() for n in ("qbar", "kbar", "scores", "idx", "cnt")}
+    check_scores(g["qbar"], g["kbar"], g["scores"], ref)
+    tpf = w.stride // 64
+    nm, n = check_selection(g["scores"], g["idx"], g["cnt"], ref["scores"], k, tpf, w.anchor)
+    kw = dict(kbar=ref["kbar"], vbar=ref["vbar"], kcount=ref["kcount"]) if lm else {}
+    O, lse = oracle.sparse_attend(inp.q, inp.k, inp.v, ol, ol, 64, g["idx"], g["cnt"], 0.125, **kw)
+    out = res.out.float().cpu().numpy()
+    tol = TOL[w.dtype] if out_f32 or w.dtype == "f32" else 2e-2
+    H, L, _ = out.shape
+    pairs = [(h, t) for h in range(H) for t in range(L // 64)]
+    worst = compare_outputs(out, O, pairs, tol=tol, g_lse=res.lse.cpu().numpy(), ref_lse=lse,
+                            lse_tol=1e-3 if w.dtype == "bf16" else 1e-5)
+    qv = (np.arange(L) % w.stride) < w.tokens
+    assert np.all(out[:, ~qv] == 0)
+    say(f"  ok: margin rows {nm}/{n}, max|dO| = {worst:.2e}")
+    return res, inp
+
+
+def test_tiny_fp32_layer():
+    run_full_case(synth.WORKLOADS["tiny_s2"])
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_tiny_fp32_seeds_and_k(seed):
+    w = synth.WORKLOADS["tiny_s2"]
+    for k in (0, 1, 3, 8):
+        run_full_case(w, seed=seed, k=k)
+
+
+def test_tiny_fp32_landmarks():
+    run_full_case(synth.WORKLOADS["tiny_s2"], landmarks=True)
+
+
+def test_tiny_fp32_dense():
+    w = synth.WORKLOADS["tiny_s2"]
+    inp = synth.make_inputs(w, seed=0)
+    q, v = to_dev(inp.q, torch.float32), to_dev(inp.v, torch.float32)
+    out, lse = S.sparse3d_dense_attn_fwd(q, q, v, w.layout, return_lse=True)
+    torch.cuda.synchronize()
+    ol = oracle.Layout(*w.layout)
+    O, L = oracle.dense_attend(inp.q, inp.k, inp.v, ol, ol, 0.125)
+    assert float(np.max(np.abs(out.cpu().numpy() - O))) <= 1e-4
+    assert float(np.max(np.abs(lse.cpu().numpy() - L))) <= 1e-5
+
+
+def test_vggt_s8_bf16_layer_f32_out():
+    run_full_case(synth.WORKLOADS["vggt_s8"])
+
+
+def test_vggt_s8_bf16_layer_bf16_out():
+    run_full_case(synth.WORKLOADS["vggt_s8"], out_f32=False, seed=3)
+
+
+def test_vggt_s8_landmarks():
+    run_full_case(synth.WORKLOADS["vggt_s8"], landmarks=True, seed=4)
+
+
+def test_vggt_s8_dense_sampled():
+    w = synth.WORKLOADS["vggt_s8"]
+    inp = synth.make_inputs(w, seed=5)
+    q, v = to_dev(inp.q, torch.bfloat16), to_dev(inp.v, torch.bfloat16)
+    out, lse = S.sparse3d_dense_attn_fwd(q, q, v, w.layout, out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    ol = oracle.Layout(*w.layout)
+    rows = np.concatenate([np.arange(0, 200), np.arange(5000, 5400), np.arange(11000, 11264)])
+    O, L = oracle.dense_attend(inp.q, inp.k, inp.v, ol, ol, 0.125, query_rows_subset=rows)
+    g, gl = out.cpu().numpy(), lse.cpu().numpy()
+    qv = rows[(rows % w.stride) < w.tokens]
+    assert float(np.max(np.abs(g[:, qv] - O[:, qv]))) <= 2e-2
+    assert float(np.max(np.abs(gl[:, qv] - L[:, qv]))) <= 1e-3
+    pad = rows[(rows % w.stride) >= w.tokens]
+    assert np.all(g[:, pad] == 0) and np.all(gl[:, pad] == 0)
+
+
+# ------------------------------------------------------------------ edge cases
+def _custom(frames, tokens, stride, specials, heads=2, dtype="bf16", k=3, **kw):
+    return synth.Workload(name=f"custom_{frames}x{tokens}_{stride}_{specials}", frames=frames,
+                          tokens=tokens, stride=stride, specials=specials, heads=heads, dtype=dtype,
+                          structure="cyclic1d", bank=max(tokens - specials, 1), k=k, **kw)
+
+
+def test_ragged_and_empty_tiles():
+    # tile 2 of every frame has no valid rows (empty query and key tile, scores -inf)
+    run_full_case(_custom(3, 70, 192, 5, k=2))
+    run_full_case(_custom(3, 70, 192, 5, k=2, dtype="f32"))
+
+
+def test_specials_span_tiles():
+    # 70 specials per frame: key tile 0 holds only specials (no members) and the
+    # special pseudo-tiles run past 64 rows
+    run_full_case(_custom(2, 150, 192, 70, k=2))
+    run_full_case(_custom(2, 150, 192, 70, k=2), landmarks=True)
+
+
+def test_single_frame_and_anchor_off():
+    run_full_case(_custom(1, 100, 128, 3, k=1, anchor=-1))
+    run_full_case(_custom(4, 64, 64, 0, k=2, anchor=-1))
+
+
+def test_k_all_tiles_equals_dense():
+    w = synth.with_frames(synth.WORKLOADS["vggt_s8"], 2, heads=2)
+    inp = synth.make_inputs(w, seed=7)
+    q, v = to_dev(inp.q, torch.bfloat16), to_dev(inp.v, torch.bfloat16)
+    Tk = w.rows // 64
+    res = LY.sparse_global_attention(q, q, v, w.layout, top_k=Tk, out_dtype=torch.float32)
+    dense = S.sparse3d_dense_attn_fwd(q, q, v, w.layout, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.all(res.cnt == Tk)
+    # same keys, different tile order and pseudo-tiles: equal within accumulation rounding
+    assert float((res.out - dense).abs().max()) <= 5e-3
+    ol = oracle.Layout(*w.layout)
+    O, _ = oracle.dense_attend(inp.q, inp.k, inp.v, ol, ol, 0.125)
+    assert float(np.max(np.abs(res.out.cpu().numpy() - O))) <= 2e-2
+
+
+def test_empty_key_set():
+    w = _custom(2, 128, 128, 0, dtype="f32", k=0, anchor=-1)
+    inp = synth.make_inputs(w, seed=1)
+    q, v = to_dev(inp.q, torch.float32), to_dev(inp.v, torch.float32)
+    res = LY.sparse_global_attention(q, q, v, w.layout, top_k=0, anchor_frame=-1, return_lse=True)
+    torch.cuda.synchronize()
+    assert res.idx.shape[2] == 0 and torch.all(res.cnt == 0)
+    assert torch.all(res.out == 0) and torch.all(torch.isneginf(res.lse))
+
+
+def test_nan_pad_is_never_read():
+    w = synth.with_frames(synth.WORKLOADS["vggt_s8"], 3, heads=2, k=5)
+    a = synth.make_inputs(w, seed=11, pad_value=0.0)
+    b = synth.make_inputs(w, seed=11, pad_value=float("nan"))
+    outs = []
+    for inp in (a, b):
+        q, v = to_dev(inp.q, torch.bfloat16), to_dev(inp.v, torch.bfloat16)
+        r = LY.sparse_global_attention(q, q, v, w.layout, top_k=5, landmarks=True, return_lse=True)
+        d = S.sparse3d_dense_attn_fwd(q, q, v, w.layout)
+        torch.cuda.synchronize()
+        outs.append((r, d))
+    (ra, da), (rb, db) = outs
+    for x, y in ((ra.out, rb.out), (ra.lse, rb.lse), (ra.scores, rb.scores), (ra.idx, rb.idx),
+                 (ra.kbar, rb.kbar), (ra.vbar, rb.vbar), (da, db)):
+        assert torch.equal(x, y)
+
+
+def test_deterministic():
+    w = synth.with_frames(synth.WORKLOADS["vggt_s32"], 6, heads=4, k=12)
+    inp = synth.make_inputs(w, seed=2)
+    q, v = to_dev(inp.q, torch.bfloat16), to_dev(inp.v, torch.bfloat16)
+    r1 = LY.sparse_global_attention(q, q, v, w.layout, top_k=12, landmarks=True)
+    r2 = LY.sparse_global_attention(q, q, v, w.layout, top_k=12, landmarks=True)
+    torch.cuda.synchronize()
+    for n in ("out", "scores", "idx", "cnt", "qbar", "kbar", "vbar"):
+        assert torch.equal(getattr(r1, n), getattr(r2, n)), n
+
+
+def test_constant_v_and_convexity():
+    w = synth.with_frames(synth.WORKLOADS["vggt_s8"], 2, heads=2, k=4)
+    inp = synth.make_inputs(w, seed=3)
+    q = to_dev(inp.q, torch.bfloat16)
+    vc = torch.full_like(q, 1.5)
+    r = LY.sparse_global_attention(q, q, vc, w.layout, top_k=4, landmarks=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    qv = torch.from_numpy((np.arange(w.rows) % w.stride) < w.tokens).to(q.device)
+    o = r.out[:, qv]
+    assert float((o - 1.5).abs().max()) <= 1.5 * 2 ** -8
+    v = to_dev(inp.v, torch.bfloat16)
+    r = LY.sparse_global_attention(q, q, v, w.layout, top_k=4, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    vmax = float(v.float().abs().max())
+    assert float(r.out.abs().max()) <= vmax * (1 + 2 ** -8)
+
+
+def test_frame_permutation():
+    w = synth.with_frames(synth.WORKLOADS["vggt_s32"], 4, heads=2, k=10)
+    inp = synth.make_inputs(w, seed=8)
+    perm = np.array([2, 0, 3, 1])
+    P = w.stride
+
+    def permute(x):
+        return np.ascontiguousarray(x.reshape(x.shape[0], w.frames, P, -1)[:, perm].reshape(x.shape))
+
+    outs = []
+    for (qq, vv, anchor) in ((inp.q, inp.v, 0), (permute(inp.q), permute(inp.v), int(np.nonzero(perm == 0)[0][0]))):
+        q, v = to_dev(qq, torch.bfloat16), to_dev(vv, torch.bfloat16)
+        r = LY.sparse_global_attention(q, q, v, w.layout, top_k=10, anchor_frame=anchor,
+                                       landmarks=True, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        outs.append(r.out.cpu().numpy())
+    # accumulation order follows tile order, so equal within fp32 rounding, not bitwise
+    assert float(np.max(np.abs(outs[1] - permute(outs[0])))) <= 1e-3
+
+
+# ------------------------------------------------------------------ full-size workloads
+def _full_size(name, n_tiles=48, seed=0):
+    w = synth.WORKLOADS[name]
+    say(f"[full] {name}: generating inputs")
+    inp = synth.make_inputs(w, seed=seed)
+    q, v = to_dev(inp.q, torch.bfloat16), to_dev(inp.v, torch.bfloat16)
+    lay, klay = w.layout, w.layout
+    K, V = q, v
+    if w.kv_window > 1:
+        K, V, klay = S.sparse3d_grid_subsample_kv(q, v, lay, w.grid, w.kv_window)
+    qbar, kbar, vbar, scores = S.sparse3d_tile_scores(q, K, lay, klay, v=V if w.landmarks else None)
+    tpf = klay[2] // 64
+    Tq, Tk = scores.shape[1], scores.shape[2]
+    ts = LY.special_tiles(klay)
+    k = LY.calibrate_k(LY.device_count_fn(scores, tpf, w.anchor), w.heads * Tq, ts, Tk,
+                       w.target_sparsity)
+    idx, cnt = S.sparse3d_select_topk(scores, k, tpf, w.anchor)
+    out = S.sparse3d_sparse_attn_fwd(q, K, V, lay, klay, idx, cnt,
+                                     kbar=kbar if w.landmarks else None,
+                                     vbar=vbar if w.landmarks else None)
+    torch.cuda.synchronize()
+    sp = LY.measured_sparsity(int(cnt.sum()), w.heads * Tq, ts, Tk)
+    say(f"[full] {name}: k={k} sparsity={sp:.4f}")
+    assert abs(sp - w.target_sparsity) < 0.01
+    ol = oracle.Layout(*lay)
+    okl = oracle.Layout(*klay)
+    Kn, Vn = inp.k, inp.v
+    if w.kv_window > 1:
+        Kn, Vn, okl2 = oracle.subsample_keys(inp.k, inp.v, ol, w.grid, w.kv_window, 64)
+        assert tuple(okl2) == tuple(klay)
+        assert np.array_equal(K.float().cpu().numpy(), Kn) and np.array_equal(V.float().cpu().numpy(), Vn)
+    ref = oracle_pool_scores(inp, ol, okl, K=Kn, V=Vn, landmarks=w.landmarks)
+    pairs = sample_tiles(w.heads, Tq, n_tiles, seed=seed)
+    g_scores = scores.cpu().numpy()
+    # scores on the sampled rows, pooled summaries everywhere
+    check_scores(qbar.cpu().numpy(), kbar.cpu().numpy(),
+                 np.stack([g_scores[h, t] for h, t in pairs])[None],
+                 dict(qbar=ref["qbar"], kbar=ref["kbar"],
+                      scores=np.stack([ref["scores"][h, t] for h, t in pairs])[None]))
+    g_idx, g_cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    nm, n = check_selection(g_scores, g_idx, g_cnt, ref["scores"], k, tpf, w.anchor, rows=pairs)
+    kw = dict(kbar=ref["kbar"], vbar=ref["vbar"], kcount=ref["kcount"]) if w.landmarks else {}
+    heads = sorted({h for h, _ in pairs})
+    O, _ = oracle.sparse_attend(inp.q, Kn, Vn, ol, okl, 64, g_idx, g_cnt, 0.125,
+                                query_tiles=sorted({t for _, t in pairs}), heads=heads, **kw)
+    worst = compare_outputs(out.cpu().numpy(), O, pairs, tol=2e-2)
+    say(f"[full] {name}: margin rows {nm}/{n}, max|dO| = {worst:.2e}")
+
+
+def test_full_vggt_s32():
+    _full_size("vggt_s32")
+
+
+def test_full_vggt_s128():
+    _full_size("vggt_s128", n_tiles=32)
+
+
+def test_full_vggt_s256_landmarks():
+    _full_size("vggt_s256_lm", n_tiles=16)
+
+
+def test_full_vggt_s256_landmarks_subsampled():
+    _full_size("vggt_s256_lm_sub2", n_tiles=16)
