@@ -205,8 +205,7 @@ def test_constant_v_and_convexity():
     assert float(r.out.abs().max()) <= vmax * (1 + 2 ** -8)
 
 
-def test_frame_permutation():
-    w = synth.with_frames(synth.WORKLOADS["vggt_s32"], 4, heads=2, k=10)
+def _permutation_case(w, k, tol, dtype):
     inp = synth.make_inputs(w, seed=8)
     perm = np.array([2, 0, 3, 1])
     P = w.stride
@@ -215,14 +214,29 @@ def test_frame_permutation():
         return np.ascontiguousarray(x.reshape(x.shape[0], w.frames, P, -1)[:, perm].reshape(x.shape))
 
     outs = []
-    for (qq, vv, anchor) in ((inp.q, inp.v, 0), (permute(inp.q), permute(inp.v), int(np.nonzero(perm == 0)[0][0]))):
-        q, v = to_dev(qq, torch.bfloat16), to_dev(vv, torch.bfloat16)
-        r = LY.sparse_global_attention(q, q, v, w.layout, top_k=10, anchor_frame=anchor,
+    for (qq, vv, anchor) in ((inp.q, inp.v, 0),
+                             (permute(inp.q), permute(inp.v), int(np.nonzero(perm == 0)[0][0]))):
+        q, v = to_dev(qq, dtype), to_dev(vv, dtype)
+        r = LY.sparse_global_attention(q, q, v, w.layout, top_k=k, anchor_frame=anchor,
                                        landmarks=True, out_dtype=torch.float32)
         torch.cuda.synchronize()
         outs.append(r.out.cpu().numpy())
-    # accumulation order follows tile order, so equal within fp32 rounding, not bitwise
-    assert float(np.max(np.abs(outs[1] - permute(outs[0])))) <= 1e-3
+    err = float(np.max(np.abs(outs[1] - permute(outs[0]))))
+    say(f"  permutation max diff {err:.2e}")
+    assert err <= tol
+
+
+def test_frame_permutation_bf16():
+    # the tile order changes with the permutation, so P is rounded to bf16 against a
+    # different running max: equal within the bf16 bar, not bitwise
+    _permutation_case(synth.with_frames(synth.WORKLOADS["vggt_s32"], 4, heads=2), 10, 2e-2,
+                      torch.bfloat16)
+
+
+def test_frame_permutation_fp32():
+    w = synth.Workload(name="perm_f32", frames=4, tokens=256, stride=256, specials=0, heads=2,
+                       dtype="f32", structure="cyclic1d", bank=256, grid=(16, 16), k=3)
+    _permutation_case(w, 3, 1e-4, torch.float32)
 
 
 # ------------------------------------------------------------------ full-size workloads
@@ -270,7 +284,7 @@ def _full_size(name, n_tiles=48, seed=0):
     heads = sorted({h for h, _ in pairs})
     O, _ = oracle.sparse_attend(inp.q, Kn, Vn, ol, okl, 64, g_idx, g_cnt, 0.125,
                                 query_tiles=sorted({t for _, t in pairs}), heads=heads, **kw)
-    worst = compare_outputs(out.cpu().numpy(), O, pairs, tol=2e-2)
+    worst = compare_outputs(out.float().cpu().numpy(), O, pairs, tol=2e-2)
     say(f"[full] {name}: margin rows {nm}/{n}, max|dO| = {worst:.2e}")
 
 
