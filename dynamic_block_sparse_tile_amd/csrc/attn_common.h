@@ -1,0 +1,127 @@
+// Tile-list description shared by the attention kernels: which 64-row key block the
+// it-th step of a query tile's loop stages, and which of its rows are real keys.
+#pragma once
+
+#include "device.h"
+
+namespace s3d {
+
+struct AttnDev {
+    const void* q;
+    const void* k;
+    const void* v;
+    Lay ql, kl;
+    int Tq, Tk, Ts, nlm;
+    const int32_t* idx;
+    const int32_t* cnt;
+    int kmax;
+    const float* kbar;
+    const float* vbar;
+    float lm_bias_l2;   // landmark bias in base-2 logit units
+    float scale_l2;     // scale * log2(e)
+    void* out;
+    float* lse;
+};
+
+constexpr int KST = 72;    // bf16 K tile row stride (elements): 144 B, conflict-free b128 reads
+constexpr int FST = 68;    // fp32 K and V^T tile row stride (floats)
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+// V^T tile (bf16): 64 rows (head-dim c) x 32 words (key pairs); word w of row c lives at
+// w ^ vt_swz(c).  The XOR keeps key pairs together and spreads both the transposing
+// b32 writes and the b64 operand reads over all 32 banks.
+__device__ __forceinline__ int vt_swz(int c) { return 2 * ((c & 3) | ((c >> 1) & 12)); }
+
+enum { KIND_REG = 0, KIND_SPEC = 1, KIND_LM = 2 };
+
+struct TileDesc {
+    int kind;
+    int t;             // key tile (REG), pseudo-tile (SPEC) or landmark block (LM)
+    uint64_t mask;     // which of the 64 staged rows are real keys
+};
+
+// Leading entries of a query tile's selection list kept in LDS by the bf16 kernel.
+constexpr int IDX_CACHE = 2048;
+
+template <bool DENSE, bool LM>
+__device__ __forceinline__ TileDesc describe(const AttnDev& p, int it, int c, const int32_t* myidx,
+                                             const int32_t* s_idx, const uint32_t* s_lm) {
+    TileDesc d;
+    if (DENSE) {
+        d.kind = KIND_REG;
+        d.t = it;
+        d.mask = range_mask(0, valid_rows(p.kl, it));
+        return d;
+    }
+    if (it < p.Ts) {
+        d.kind = KIND_SPEC;
+        d.t = it;
+        d.mask = range_mask(0, min(TILE, p.kl.nsp * p.kl.S - it * TILE));
+        return d;
+    }
+    it -= p.Ts;
+    if (it < c) {
+        const int t = (s_idx && it < IDX_CACHE) ? s_idx[it] : myidx[it];
+        d.kind = KIND_REG;
+        d.t = t;
+        if (t < 0 || t >= p.Tk) {
+            d.t = 0;
+            d.mask = 0;
+        } else {
+            int lo, hi;
+            member_range(p.kl, t, lo, hi);
+            d.mask = range_mask(lo, hi);
+        }
+        return d;
+    }
+    it -= c;
+    d.kind = KIND_LM;
+    d.t = it;
+    if (LM) {
+        const uint32_t w0 = s_lm[2 * it], w1 = s_lm[2 * it + 1];
+        d.mask = (uint64_t)w0 | ((uint64_t)w1 << 32);
+    } else {
+        d.mask = 0;
+    }
+    return d;
+}
+
+// Global row (within the head) of staged row r of a REG or SPEC tile.
+__device__ __forceinline__ int src_row(const AttnDev& p, const TileDesc& d, int r) {
+    if (d.kind == KIND_SPEC) {
+        const int e = d.t * TILE + r;
+        return (e / p.kl.nsp) * p.kl.P + e % p.kl.nsp;
+    }
+    return d.t * TILE + r;
+}
+
+
+__device__ __forceinline__ void init_landmark_bitmap(const AttnDev& p, int c, const int32_t* myidx,
+                                                     uint32_t* s_lm, int tid, int nthreads) {
+    // bit t set <=> key tile t has member rows and is not selected (a landmark)
+    const int nw = 2 * p.nlm;
+    for (int i = tid; i < nw; i += nthreads) {
+        uint32_t bits = 0;
+        for (int b = 0; b < 32; ++b) {
+            const int t = i * 32 + b;
+            if (t < p.Tk) {
+                int lo, hi;
+                member_range(p.kl, t, lo, hi);
+                if (hi > lo) bits |= 1u << b;
+            }
+        }
+        s_lm[i] = bits;
+    }
+    __syncthreads();
+    for (int i = tid; i < c; i += nthreads) {
+        const int t = myidx[i];
+        if (t >= 0 && t < p.Tk) atomicAnd(&s_lm[t >> 5], ~(1u << (t & 31)));
+    }
+    __syncthreads();
+}
+
+hipError_t launch_attn_bf16(const AttnDev& d, int heads, bool dense, bool lm, bool f32out,
+                            hipStream_t st);
+
+}  // namespace s3d

@@ -20,6 +20,12 @@ from parity_helpers import (TOL, check_scores, check_selection, compare_outputs,
 
 pytestmark = pytest.mark.gpu
 
+# bf16 path: the row sum accumulates the bf16-rounded probabilities (the weights that
+# multiply V).  bf16 keeps 8 significant bits, so each is within a relative 2^-8 of the
+# exact value and the log-sum-exp is within ln(1 + 2^-8) = 3.9e-3 of the oracle's, plus
+# fp32 rounding
+LSE_TOL_BF16 = 4e-3
+
 
 def run_full_case(w, seed=0, k=None, landmarks=None, out_f32=True, pad=0.0):
     """Whole layer on the GPU, everything compared with the oracle (small workloads)."""
@@ -46,7 +52,7 @@ def run_full_case(w, seed=0, k=None, landmarks=None, out_f32=True, pad=0.0):
     H, L, _ = out.shape
     pairs = [(h, t) for h in range(H) for t in range(L // 64)]
     worst = compare_outputs(out, O, pairs, tol=tol, g_lse=res.lse.cpu().numpy(), ref_lse=lse,
-                            lse_tol=1e-3 if w.dtype == "bf16" else 1e-5)
+                            lse_tol=LSE_TOL_BF16 if w.dtype == "bf16" else 1e-5)
     qv = (np.arange(L) % w.stride) < w.tokens
     assert np.all(out[:, ~qv] == 0)
     say(f"  ok: margin rows {nm}/{n}, max|dO| = {worst:.2e}")
@@ -104,7 +110,7 @@ def test_vggt_s8_dense_sampled():
     g, gl = out.cpu().numpy(), lse.cpu().numpy()
     qv = rows[(rows % w.stride) < w.tokens]
     assert float(np.max(np.abs(g[:, qv] - O[:, qv]))) <= 2e-2
-    assert float(np.max(np.abs(gl[:, qv] - L[:, qv]))) <= 1e-3
+    assert float(np.max(np.abs(gl[:, qv] - L[:, qv]))) <= LSE_TOL_BF16
     pad = rows[(rows % w.stride) >= w.tokens]
     assert np.all(g[:, pad] == 0) and np.all(gl[:, pad] == 0)
 
@@ -127,6 +133,14 @@ def test_specials_span_tiles():
     # special pseudo-tiles run past 64 rows
     run_full_case(_custom(2, 150, 192, 70, k=2))
     run_full_case(_custom(2, 150, 192, 70, k=2), landmarks=True)
+
+
+def test_long_selection_lists():
+    # more than 128 selected tiles per query tile (the staged index list spans several
+    # passes of the workgroup) and a landmark bitmap wider than 128 words
+    w = _custom(24, 1374, 1408, 5, heads=2, k=300)
+    run_full_case(w, seed=5)
+    run_full_case(w, seed=6, landmarks=True)
 
 
 def test_single_frame_and_anchor_off():
