@@ -30,7 +30,8 @@ METRIC = "sparse global-attn effective TFLOP/s + ms/layer at S=128 frames, % bf1
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-ATTN_SRC = os.path.join(ROOT, "dynamic_block_sparse_tile_amd", "csrc", "attn.hip")
+ATTN_SRCS = [os.path.join(ROOT, "dynamic_block_sparse_tile_amd", "csrc", f)
+             for f in ("attn_bf16.hip", "attn_common.h", "device.h")]
 
 
 def log(msg):
@@ -49,6 +50,9 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-gate", action="store_true", help="skip the 90%% sparsity speedup point")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="first run a plain elementwise copy of this many MiB (fp32) twice, as a "
+                         "known-size reference for the HBM byte counters")
     return ap.parse_args()
 
 
@@ -145,6 +149,13 @@ def time_dense(torch, S, q, v, lay, reps):
     return a.elapsed_time(b) / reps
 
 
+def attn_source_sha256() -> str:
+    h = hashlib.sha256()
+    for f in ATTN_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def traffic_entry():
     """Per-launch HBM bytes of the attention kernel from committed counter runs, or None
     when the kernel source changed after the counters were taken."""
@@ -152,7 +163,7 @@ def traffic_entry():
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    sha = attn_source_sha256()
     if t.get("attn_source_sha256") != sha:
         return None
     return t
@@ -222,6 +233,16 @@ def main():
     S.library()
     torch.cuda.init()
     dev = torch.device("cuda:0")
+    if args.copy_mb > 0:
+        n = args.copy_mb * (1 << 20) // 4
+        src = torch.rand(n, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            torch.add(src, 0.0, out=dst)          # reads n*4 bytes, writes n*4 bytes
+        torch.cuda.synchronize()
+        log(f"copy reference: {args.copy_mb} MiB read + {args.copy_mb} MiB written per launch")
+        del src, dst
     w = synth.WORKLOADS[args.workload]
     log(f"workload {w.name}: S={w.frames} N={w.tokens} H={w.heads}; generating inputs")
     inp = synth.make_inputs(w, seed=args.seed)

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(128, 2) void k_attn(AttnDev p) {
     TileDesc nxt;
 
     auto fetch = [&](int it) {
-        nxt = describe<DENSE, LM>(p, it, c, myidx, nullptr, s_lm);
+        nxt = describe<DENSE, LM, false>(p, it, c, myidx, nullptr, s_lm);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             const int r = (x >> 1) * 32 + 2 * rp + (x & 1);
@@ -345,9 +345,13 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     d.out = a.out;
     d.lse = a.lse;
     const bool f32in = a.dtype == SPARSE3D_F32, f32out = a.out_dtype == SPARSE3D_F32;
-    if (!f32in) return launch_attn_bf16(d, a.heads, a.dense, lm, f32out, st);
-    if (f32out) return launch_attn_t<true, true>(d, a.heads, a.dense, lm, st);
-    return launch_attn_t<true, false>(d, a.heads, a.dense, lm, st);
+    if (!f32in && (a.dense || a.kmax <= IDX_LDS_MAX))
+        return launch_attn_bf16(d, a.heads, a.dense, lm, f32out, st);
+    // fp32 operands, or a bf16 selection list too long to stage in LDS
+    if (f32in && f32out) return launch_attn_t<true, true>(d, a.heads, a.dense, lm, st);
+    if (f32in) return launch_attn_t<true, false>(d, a.heads, a.dense, lm, st);
+    if (f32out) return launch_attn_t<false, true>(d, a.heads, a.dense, lm, st);
+    return launch_attn_t<false, false>(d, a.heads, a.dense, lm, st);
 }
 
 }  // namespace s3d

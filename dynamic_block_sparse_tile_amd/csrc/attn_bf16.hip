@@ -2,17 +2,21 @@
 // the sparse layer; Zebra3D abstract: tile-sparse attention with landmark summaries).
 //
 // Workgroup = 2 waves = one (head, query tile); wave w owns queries [32w, 32w+32).
-// Key and value tiles move HBM/L2 -> LDS by direct-to-LDS loads (global_load_lds,
-// 16 bytes per lane), so staging costs no VGPRs and no VALU; each 128-byte row of a
-// tile is stored as 8 chunks of 16 bytes in XOR-swizzled order (slot = chunk ^ row%8),
+// Key and value tiles move HBM/L2 -> LDS by direct-to-LDS buffer loads (16 bytes per
+// lane, per-lane constant offsets, the tile base in a scalar register), so staging costs
+// no VGPRs and almost no VALU; each 128-byte row of a
+// tile is stored as 8 chunks of 16 bytes in XOR-swizzled order (see swz_key),
 // which the loads realise by permuting their source chunks.  Two LDS buffers: the next
 // tile streams in while the current one computes, one barrier per tile.
 //   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, A = K rows (ds_read_b128), B = Q (VGPRs)
 //   O^T += V^T P^T   A = V^T read with ds_read_b64_tr_b16 (the transpose happens in the
 //                    LDS read), B = P^T taken straight from the S^T accumulators
-// Rows that are not keys load from a zero row and are masked to -inf by index, so pad
-// rows (which may hold NaN) never reach the arithmetic.  Landmark blocks (fp32 tile
+// Rows that are not keys load through an out-of-range buffer offset, which reads as
+// zeros, and are masked to -inf by index, so pad rows (which may hold NaN) never reach
+// the arithmetic.  Landmark blocks (fp32 tile
 // means) are converted to bf16 through registers.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "device.h"
 #include "launch.h"
@@ -26,17 +30,33 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-// Source of masked rows: direct-to-LDS loads copy whatever they read, so rows that are
-// not keys read these zeros.
-__device__ __align__(16) const unsigned char kZeroRow[128] = {};
-
 constexpr int TILE_BYTES = TILE * 128;           // one bf16 64x64 tile
 constexpr int BUF_BYTES = 2 * TILE_BYTES;        // K + V
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+// Physical 16-byte slot of logical chunk `chunk` in tile row `row`.  The XOR key uses
+// row bits 0-3 so that, with 64 LDS banks served 16 lanes (b128) or 32 lanes (b64) per
+// pass, both the K-operand reads (16 rows, one chunk each) and the transposing V reads
+// (4 rows, 4 chunks each) touch every bank at most once per pass.
+__device__ __forceinline__ int swz_key(int row) {
+    return (((row & 2) << 1) | ((row >> 2) & 3)) ^ ((row & 1) << 1);
+}
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ swz_key(row); }
 
-__device__ __forceinline__ void dma16(const void* g, lds_u8* lds_base) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
+// Word 3 of a raw buffer resource on gfx9-class parts (32-bit data format, no swizzle).
+constexpr int BUF_RSRC_WORD3 = 0x00020000;
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8; a field at its maximum does not wait).
+constexpr int WAITCNT_VM0_LGKM0 = 0x0070;        // vmcnt(0) lgkmcnt(0)
+constexpr int WAITCNT_LGKM0 = 0xC07F;            // lgkmcnt(0) only
+
+// A byte offset past every per-head buffer: buffer loads there return zeros.
+constexpr unsigned OOB_OFFSET = 0x80000000u;
+
+// 16 bytes per lane from buffer `rs` at byte offset voff + soff into LDS at
+// lds_base + 16 * lane.
+__device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t rs, lds_u8* lds_base, unsigned voff,
+                                        unsigned soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_base, 16, voff, soff, 0, 0);
 }
 
 }  // namespace
@@ -97,57 +117,63 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
         ntiles = p.Ts + c + (LM ? p.nlm : 0);
     }
     if (LM) init_landmark_bitmap(p, c, myidx, s_lm, tid, 128);
-    // the selected-tile list, staged once in LDS (the first IDX_CACHE entries) so the
-    // per-tile lookup is an LDS read instead of a dependent global load
+    // the selected-tile list, staged once in LDS so the per-tile lookup is an LDS read
+    // instead of a dependent global load (the launcher guarantees kmax <= IDX_LDS_MAX)
     int32_t* s_idx = reinterpret_cast<int32_t*>(s_lm + (LM ? 2 * p.nlm : 0));
     if (!DENSE) {
-        const int n = min(c, IDX_CACHE);
-        for (int i = tid; i < n; i += 128) s_idx[i] = myidx[i];
+        for (int i = tid; i < c; i += 128) s_idx[i] = myidx[i];
         __syncthreads();
     }
 
-    const unsigned char* kg = static_cast<const unsigned char*>(p.k) + (size_t)h * Lk * 128;
-    const unsigned char* vg = static_cast<const unsigned char*>(p.v) + (size_t)h * Lk * 128;
+    // ---- staging through buffer resources: one per head for K and for V, so a tile's
+    //      loads are a per-lane constant offset plus the tile's base in a scalar register.
+    //      Offsets at or past the end (OOB) read as zeros: that is how masked rows load.
+    const unsigned head_bytes = (unsigned)Lk * 128u;
+    const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(static_cast<const unsigned char*>(p.k)) + (size_t)h * head_bytes, 0,
+        (int)head_bytes, BUF_RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(static_cast<const unsigned char*>(p.v)) + (size_t)h * head_bytes, 0,
+        (int)head_bytes, BUF_RSRC_WORD3);
 
-    // ---- staging: wave w fills rows [32w, 32w+32) of K and of V; per instruction j the
-    //      64 lanes cover rows 32w+8j .. +8, lane l -> (row l/8, slot l%8) in LDS order
+    // wave w fills rows [32w, 32w+32) of K and of V; per instruction j the 64 lanes cover
+    // rows 32w+8j .. +8, lane l -> (row l/8, slot l%8) in LDS order
     const int srow_in = lane >> 3, sslot = lane & 7;
-    // byte offset of this lane's source chunk inside a 64-row tile, per instruction j
-    int soff[4];
+    int srow[4], soff[4];                         // row within the tile, byte offset in it
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int r = 32 * w + 8 * j + srow_in;
-        soff[j] = r * 128 + (sslot ^ (r & 7)) * 16;
+        srow[j] = 32 * w + 8 * j + srow_in;
+        soff[j] = srow[j] * 128 + swz(srow[j], sslot) * 16;
     }
     uint4 lmk[4], lmv[4];                         // landmark rows staged through registers
 
     auto issue = [&](int it, lds_u8* dst, TileDesc& d) {
-        d = describe<DENSE, LM>(p, it, c, myidx, s_idx, s_lm);
-        if (d.kind == KIND_REG && d.mask == ~0ull) {
-            // full tile: 64 consecutive rows
-            const size_t base = (size_t)d.t * TILE_BYTES;
+        d = describe<DENSE, LM, !DENSE>(p, it, c, myidx, s_idx, s_lm);
+        if (d.kind == KIND_REG) {
+            const unsigned base = (unsigned)d.t * TILE_BYTES;
+            const bool full = d.mask == ~0ull;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                dma16(kg + base + soff[j], dst + (32 * w + 8 * j) * 128);
-                dma16(vg + base + soff[j], dst + TILE_BYTES + (32 * w + 8 * j) * 128);
+                const bool ok = full || ((d.mask >> srow[j]) & 1ull);
+                const unsigned vo = ok ? (unsigned)soff[j] : OOB_OFFSET;
+                dma_buf(rs_k, dst + (32 * w + 8 * j) * 128, vo, base);
+                dma_buf(rs_v, dst + TILE_BYTES + (32 * w + 8 * j) * 128, vo, base);
             }
-        } else if (d.kind != KIND_LM) {
+        } else if (d.kind == KIND_SPEC) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 32 * w + 8 * j + srow_in;
-                const int ch = sslot ^ (r & 7);
+                const int r = srow[j];
                 const bool ok = (d.mask >> r) & 1ull;
-                const size_t off = (size_t)src_row(p, d, ok ? r : 0) * 128 + ch * 16;
-                const void* ks = ok ? (const void*)(kg + off) : (const void*)(kZeroRow + ch * 16);
-                const void* vs = ok ? (const void*)(vg + off) : (const void*)(kZeroRow + ch * 16);
-                dma16(ks, dst + (32 * w + 8 * j) * 128);
-                dma16(vs, dst + TILE_BYTES + (32 * w + 8 * j) * 128);
+                const unsigned vo = ok ? (unsigned)src_row(p, d, r) * 128u + swz(r, sslot) * 16u
+                                       : OOB_OFFSET;
+                dma_buf(rs_k, dst + (32 * w + 8 * j) * 128, vo, 0u);
+                dma_buf(rs_v, dst + TILE_BYTES + (32 * w + 8 * j) * 128, vo, 0u);
             }
         } else if (LM) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 32 * w + 8 * j + srow_in;
-                const int ch = sslot ^ (r & 7);
+                const int r = srow[j];
+                const int ch = swz(r, sslot);
                 const bool ok = (d.mask >> r) & 1ull;
                 float4 a0 = make_float4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
                 if (ok) {
@@ -168,9 +194,8 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
         if (LM && d.kind == KIND_LM) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 32 * w + 8 * j + srow_in;
-                *reinterpret_cast<uint4*>(dst + r * 128 + sslot * 16) = lmk[j];
-                *reinterpret_cast<uint4*>(dst + TILE_BYTES + r * 128 + sslot * 16) = lmv[j];
+                *reinterpret_cast<uint4*>(dst + srow[j] * 128 + sslot * 16) = lmk[j];
+                *reinterpret_cast<uint4*>(dst + TILE_BYTES + srow[j] * 128 + sslot * 16) = lmv[j];
             }
         }
     };
@@ -185,15 +210,19 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
             koff[kb][st] = r * 128 + swz(r, 2 * st + g) * 16;
         }
     // V^T through the transposing read: lane j of each 16-lane group points at
-    // V[16ks + 8half + 4g + j/4][32cb + 16*((lane/16)%2) + 4*(j%4)]; rows differ from the
-    // ks=0/half=0 row by multiples of 8, so (row & 7) and the swizzle are per-lane constants
+    // V[16ks + 8half + 4g + j/4][32cb + 16*((lane/16)%2) + 4*(j%4)]; rows for different ks
+    // differ by multiples of 16, which leave the swizzle key unchanged
     const int vrow0 = 4 * g + ((lane & 15) >> 2);
     const int vcol_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
     const int vsub = (lane & 1) * 8;
-    int voff[2];
+    int voff[2][2];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
-        voff[cb] = TILE_BYTES + vrow0 * 128 + swz(vrow0, 4 * cb + vcol_chunk) * 16 + vsub;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int r = vrow0 + 8 * hf;
+            voff[cb][hf] = TILE_BYTES + r * 128 + swz(r, 4 * cb + vcol_chunk) * 16 + vsub;
+        }
     // key index of accumulator register r of block kb: 32kb + 8(r/4) + 4g + r%4
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -215,9 +244,9 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
                 const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4i16*)(lb + voff[cb] + ks * 16 * 128));
+                    (lds_v4i16*)(lb + voff[cb][0] + ks * 16 * 128));
                 const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4i16*)(lb + voff[cb] + ks * 16 * 128 + 8 * 128));
+                    (lds_v4i16*)(lb + voff[cb][1] + ks * 16 * 128));
                 va[cb][ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             }
     };
@@ -230,11 +259,23 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
             s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1][st], qop[st], s1, 0, 0, 0);
         }
         if (cur.mask != ~0ull) {
+            if (!LM || cur.kind != KIND_LM) {
+                // contiguous valid rows [lo, hi): one unsigned compare per score
+                const unsigned lo = cur.mask ? (unsigned)__builtin_ctzll(cur.mask) : 64u;
+                const unsigned span = (unsigned)__builtin_popcountll(cur.mask);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = 8 * (r >> 2) + 4 * g + (r & 3);
-                if (!((cur.mask >> key) & 1ull)) s0[r] = -INFINITY;
-                if (!((cur.mask >> (32 + key)) & 1ull)) s1[r] = -INFINITY;
+                for (int r = 0; r < 16; ++r) {
+                    const unsigned key = 8 * (r >> 2) + 4 * g + (r & 3);
+                    if (key - lo >= span) s0[r] = -INFINITY;
+                    if (key + 32 - lo >= span) s1[r] = -INFINITY;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = 8 * (r >> 2) + 4 * g + (r & 3);
+                    if (!((cur.mask >> key) & 1ull)) s0[r] = -INFINITY;
+                    if (!((cur.mask >> (32 + key)) & 1ull)) s1[r] = -INFINITY;
+                }
             }
         }
         const float bias = (LM && cur.kind == KIND_LM) ? p.lm_bias_l2 : 0.f;
@@ -283,19 +324,29 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
         commit(s_buf, cur);
         __syncthreads();
     }
-    for (int it = 0; it < ntiles; ++it) {
-        const int b = it & 1;
+    // One step: operands of tile `it` from buffer B, then tile it+1's loads into buffer
+    // 1-B, then the math.  Unrolled by two so B is a constant and every LDS address is a
+    // per-lane register plus an immediate.
+    auto step = [&](auto bufc, int it) {
+        constexpr int B = decltype(bufc)::value;
         const bool live = cur.mask != 0;
-        if (live) fetch_operands(s_buf + b * BUF_BYTES);
-        if (it + 1 < ntiles) issue(it + 1, lbuf + (b ^ 1) * BUF_BYTES, nxt);
+        if (live) fetch_operands(s_buf + B * BUF_BYTES);
+        if (it + 1 < ntiles) issue(it + 1, lbuf + (1 - B) * BUF_BYTES, nxt);
         if (live) compute(cur);
+        __builtin_amdgcn_s_waitcnt(WAITCNT_VM0_LGKM0);   // this wave's tile-(it+1) loads landed
         if (it + 1 < ntiles) {
-            __builtin_amdgcn_s_waitcnt(0);      // this wave's tile-(it+1) loads have landed
-            commit(s_buf + (b ^ 1) * BUF_BYTES, nxt);
+            commit(s_buf + (1 - B) * BUF_BYTES, nxt);
             cur = nxt;
         }
-        __syncthreads();                        // all loads landed; all reads of buffer b done
+        if (LM) __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);   // landmark rows written to LDS
+        __builtin_amdgcn_s_barrier();           // all loads landed; all reads of buffer B done
+    };
+    int it = 0;
+    for (; it + 1 < ntiles; it += 2) {
+        step(std::integral_constant<int, 0>{}, it);
+        step(std::integral_constant<int, 1>{}, it + 1);
     }
+    if (it < ntiles) step(std::integral_constant<int, 0>{}, it);
 
     const float ltot = l + __shfl_xor(l, 32);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
@@ -328,7 +379,7 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
 template <bool F32OUT>
 static void launch_t(const AttnDev& d, int heads, bool dense, bool lm, hipStream_t st) {
     const dim3 grid((unsigned)(heads * d.Tq)), block(128);
-    const size_t shm = ((lm ? (size_t)(2 * d.nlm) : 0) + (dense ? 0 : (size_t)min(d.kmax, IDX_CACHE))) *
+    const size_t shm = ((lm ? (size_t)(2 * d.nlm) : 0) + (dense ? 0 : (size_t)d.kmax)) *
                        sizeof(uint32_t);
     if (dense) hipLaunchKernelGGL((k_attn_bf16<F32OUT, true, false>), grid, block, 0, st, d);
     else if (lm) hipLaunchKernelGGL((k_attn_bf16<F32OUT, false, true>), grid, block, shm, st, d);

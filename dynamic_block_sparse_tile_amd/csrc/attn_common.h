@@ -41,10 +41,12 @@ struct TileDesc {
     uint64_t mask;     // which of the 64 staged rows are real keys
 };
 
-// Leading entries of a query tile's selection list kept in LDS by the bf16 kernel.
-constexpr int IDX_CACHE = 2048;
+// Longest selection list the bf16 kernel stages in LDS (next to its 32 KiB of tile
+// buffers, within 64 KiB); longer lists run on the generic kernel.
+constexpr int IDX_LDS_MAX = 8000;
 
-template <bool DENSE, bool LM>
+// IDX_LDS: the list is read from its LDS copy (bf16 kernel) rather than from global memory.
+template <bool DENSE, bool LM, bool IDX_LDS>
 __device__ __forceinline__ TileDesc describe(const AttnDev& p, int it, int c, const int32_t* myidx,
                                              const int32_t* s_idx, const uint32_t* s_lm) {
     TileDesc d;
@@ -62,7 +64,7 @@ __device__ __forceinline__ TileDesc describe(const AttnDev& p, int it, int c, co
     }
     it -= p.Ts;
     if (it < c) {
-        const int t = (s_idx && it < IDX_CACHE) ? s_idx[it] : myidx[it];
+        const int t = IDX_LDS ? s_idx[it] : myidx[it];
         d.kind = KIND_REG;
         d.t = t;
         if (t < 0 || t >= p.Tk) {

@@ -143,6 +143,24 @@ def test_long_selection_lists():
     run_full_case(w, seed=6, landmarks=True)
 
 
+def test_selection_longer_than_lds_list():
+    # 8200 one-tile frames, k = 8100: the list is too long to stage in LDS next to the tile
+    # buffers, so the launcher takes the generic kernel; sampled query tiles vs the oracle
+    w = synth.Workload(name="long_list", frames=8200, tokens=64, stride=64, specials=0, heads=1,
+                       structure="cyclic1d", bank=64, grid=(8, 8), k=8100)
+    inp = synth.make_inputs(w, seed=3)
+    q, v = to_dev(inp.q, torch.bfloat16), to_dev(inp.v, torch.bfloat16)
+    res = LY.sparse_global_attention(q, q, v, w.layout, top_k=8100, anchor_frame=-1,
+                                     out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    idx, cnt = res.idx.cpu().numpy(), res.cnt.cpu().numpy()
+    assert idx.shape[2] == 8100 and np.all(cnt == 8100)
+    ol = oracle.Layout(*w.layout)
+    tiles = [0, 4100, 8199]
+    O, _ = oracle.sparse_attend(inp.q, inp.k, inp.v, ol, ol, 64, idx, cnt, 0.125, query_tiles=tiles)
+    compare_outputs(res.out.cpu().numpy(), O, [(0, t) for t in tiles], tol=2e-2)
+
+
 def test_single_frame_and_anchor_off():
     run_full_case(_custom(1, 100, 128, 3, k=1, anchor=-1))
     run_full_case(_custom(4, 64, 64, 0, k=2, anchor=-1))
