@@ -66,6 +66,8 @@ int sparse3d_sparse_attn_fwd(const void* q, const void* k, const void* v, sparse
     const int st = validate_attn(true, q, k, v, dtype, heads, head_dim, tile, qlay, klay, idx, cnt,
                                  kmax, kbar, vbar, out, out_dtype, lse);
     if (st != SPARSE3D_OK) return st;
+    const int sp = check_logit_params(scale, kbar ? landmark_bias : 0.f);
+    if (sp != SPARSE3D_OK) return sp;
     AttnArgs a{q, k, v, dtype, out_dtype, heads, to_lay(*qlay), to_lay(*klay), false, idx, cnt,
                kmax, kbar, vbar, landmark_bias, scale, out, lse};
     S3D_HIP(launch_attn(a, static_cast<hipStream_t>(stream)));
@@ -79,6 +81,8 @@ int sparse3d_dense_attn_fwd(const void* q, const void* k, const void* v, sparse3
     const int st = validate_attn(false, q, k, v, dtype, heads, head_dim, kTile, qlay, klay, nullptr,
                                  nullptr, 0, nullptr, nullptr, out, out_dtype, lse);
     if (st != SPARSE3D_OK) return st;
+    const int sp = check_logit_params(scale, 0.f);
+    if (sp != SPARSE3D_OK) return sp;
     AttnArgs a{q, k, v, dtype, out_dtype, heads, to_lay(*qlay), to_lay(*klay), true, nullptr,
                nullptr, 0, nullptr, nullptr, 0.f, scale, out, lse};
     S3D_HIP(launch_attn(a, static_cast<hipStream_t>(stream)));

@@ -2,19 +2,18 @@
 // the sparse layer; Zebra3D abstract: tile-sparse attention with landmark summaries).
 //
 // Workgroup = 2 waves = one (head, query tile); wave w owns queries [32w, 32w+32).
-// Key and value tiles move HBM/L2 -> LDS by direct-to-LDS buffer loads (16 bytes per
-// lane, per-lane constant offsets, the tile base in a scalar register), so staging costs
-// no VGPRs and almost no VALU; each 128-byte row of a
-// tile is stored as 8 chunks of 16 bytes in XOR-swizzled order (see swz_key),
-// which the loads realise by permuting their source chunks.  Two LDS buffers: the next
-// tile streams in while the current one computes, one barrier per tile.
 //   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, A = K rows (ds_read_b128), B = Q (VGPRs)
 //   O^T += V^T P^T   A = V^T read with ds_read_b64_tr_b16 (the transpose happens in the
 //                    LDS read), B = P^T taken straight from the S^T accumulators
-// Rows that are not keys load through an out-of-range buffer offset, which reads as
-// zeros, and are masked to -inf by index, so pad rows (which may hold NaN) never reach
-// the arithmetic.  Landmark blocks (fp32 tile
-// means) are converted to bf16 through registers.
+// Software pipeline: step `it` issues the QK^T products of tile it+1 on the matrix core
+// while the vector ALUs run the softmax of tile it, then accumulates P V of tile it.  K
+// therefore runs one tile ahead of V; each has two LDS buffers.  Tiles reach LDS by
+// direct-to-LDS buffer loads (16 bytes per lane; per-lane constant offsets, the tile base
+// in a scalar register), every 128-byte row stored as 8 XOR-swizzled 16-byte chunks (see
+// swz_key).  One barrier per step.  Rows that are not keys load through an out-of-range
+// offset, which reads as zeros, and are masked to -inf by index, so pad rows (which may
+// hold NaN) never reach the arithmetic.  Landmark blocks (fp32 tile means) are converted
+// to bf16 through registers.
 #include <type_traits>
 
 #include "attn_common.h"
@@ -31,7 +30,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 constexpr int TILE_BYTES = TILE * 128;           // one bf16 64x64 tile
-constexpr int BUF_BYTES = 2 * TILE_BYTES;        // K + V
 
 // Physical 16-byte slot of logical chunk `chunk` in tile row `row`.  The XOR key uses
 // row bits 0-3 so that, with 64 LDS banks served 16 lanes (b128) or 32 lanes (b64) per
@@ -76,9 +74,12 @@ constexpr float RESCALE_THRESHOLD = 8.0f;
 
 template <bool F32OUT, bool DENSE, bool LM>
 __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
-    // two buffers, each [K | V] x 64 rows x 128 B: tile it computes from buffer it%2 while
-    // tile it+1 streams into the other one
-    __shared__ __align__(16) unsigned char s_buf[2 * BUF_BYTES];
+    // K and V rings of two 8 KiB tiles each, as four separate arrays so that every access
+    // in the (two-way unrolled) loop names its buffer statically
+    __shared__ __align__(16) unsigned char s_k0[TILE_BYTES];
+    __shared__ __align__(16) unsigned char s_k1[TILE_BYTES];
+    __shared__ __align__(16) unsigned char s_v0[TILE_BYTES];
+    __shared__ __align__(16) unsigned char s_v1[TILE_BYTES];
     extern __shared__ uint32_t s_lm[];
 
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -136,8 +137,8 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
         const_cast<unsigned char*>(static_cast<const unsigned char*>(p.v)) + (size_t)h * head_bytes, 0,
         (int)head_bytes, BUF_RSRC_WORD3);
 
-    // wave w fills rows [32w, 32w+32) of K and of V; per instruction j the 64 lanes cover
-    // rows 32w+8j .. +8, lane l -> (row l/8, slot l%8) in LDS order
+    // wave w fills rows [32w, 32w+32) of a tile; per instruction j the 64 lanes cover rows
+    // 32w+8j .. +8, lane l -> (row l/8, slot l%8) in LDS order
     const int srow_in = lane >> 3, sslot = lane & 7;
     int srow[4], soff[4];                         // row within the tile, byte offset in it
 #pragma unroll
@@ -147,17 +148,21 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
     }
     uint4 lmk[4], lmv[4];                         // landmark rows staged through registers
 
-    auto issue = [&](int it, lds_u8* dst, TileDesc& d) {
-        d = describe<DENSE, LM, !DENSE>(p, it, c, myidx, s_idx, s_lm);
+    auto desc = [&](int it) { return describe<DENSE, LM, !DENSE>(p, it, c, myidx, s_idx, s_lm); };
+    // one matrix (K or V: `rs`, landmark source `lsrc`) of tile d into LDS tile `dst`
+    auto stage = [&](const __amdgpu_buffer_rsrc_t& rs, const float* lsrc, uint4 (&lmr)[4],
+                     const TileDesc& d, lds_u8* dst) {
         if (d.kind == KIND_REG) {
             const unsigned base = (unsigned)d.t * TILE_BYTES;
-            const bool full = d.mask == ~0ull;
+            if (d.mask == ~0ull) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bool ok = full || ((d.mask >> srow[j]) & 1ull);
-                const unsigned vo = ok ? (unsigned)soff[j] : OOB_OFFSET;
-                dma_buf(rs_k, dst + (32 * w + 8 * j) * 128, vo, base);
-                dma_buf(rs_v, dst + TILE_BYTES + (32 * w + 8 * j) * 128, vo, base);
+                for (int j = 0; j < 4; ++j) dma_buf(rs, dst + (32 * w + 8 * j) * 128, (unsigned)soff[j], base);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool ok = (d.mask >> srow[j]) & 1ull;
+                    dma_buf(rs, dst + (32 * w + 8 * j) * 128, ok ? (unsigned)soff[j] : OOB_OFFSET, base);
+                }
             }
         } else if (d.kind == KIND_SPEC) {
 #pragma unroll
@@ -166,49 +171,38 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
                 const bool ok = (d.mask >> r) & 1ull;
                 const unsigned vo = ok ? (unsigned)src_row(p, d, r) * 128u + swz(r, sslot) * 16u
                                        : OOB_OFFSET;
-                dma_buf(rs_k, dst + (32 * w + 8 * j) * 128, vo, 0u);
-                dma_buf(rs_v, dst + TILE_BYTES + (32 * w + 8 * j) * 128, vo, 0u);
+                dma_buf(rs, dst + (32 * w + 8 * j) * 128, vo, 0u);
             }
         } else if (LM) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = srow[j];
-                const int ch = swz(r, sslot);
                 const bool ok = (d.mask >> r) & 1ull;
-                float4 a0 = make_float4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
+                float4 a0 = make_float4(0, 0, 0, 0), a1 = a0;
                 if (ok) {
-                    const size_t o = ((size_t)h * p.Tk + d.t * TILE + r) * HD + ch * 8;
-                    a0 = *reinterpret_cast<const float4*>(p.kbar + o);
-                    a1 = *reinterpret_cast<const float4*>(p.kbar + o + 4);
-                    b0 = *reinterpret_cast<const float4*>(p.vbar + o);
-                    b1 = *reinterpret_cast<const float4*>(p.vbar + o + 4);
+                    const size_t o = ((size_t)h * p.Tk + d.t * TILE + r) * HD + swz(r, sslot) * 8;
+                    a0 = *reinterpret_cast<const float4*>(lsrc + o);
+                    a1 = *reinterpret_cast<const float4*>(lsrc + o + 4);
                 }
-                lmk[j] = make_uint4(pack_bf16x2(a0.x, a0.y), pack_bf16x2(a0.z, a0.w),
+                lmr[j] = make_uint4(pack_bf16x2(a0.x, a0.y), pack_bf16x2(a0.z, a0.w),
                                     pack_bf16x2(a1.x, a1.y), pack_bf16x2(a1.z, a1.w));
-                lmv[j] = make_uint4(pack_bf16x2(b0.x, b0.y), pack_bf16x2(b0.z, b0.w),
-                                    pack_bf16x2(b1.x, b1.y), pack_bf16x2(b1.z, b1.w));
             }
         }
     };
-    auto commit = [&](unsigned char* dst, const TileDesc& d) {
+    // landmark rows (converted in registers) go to LDS once their loads have landed
+    auto commit = [&](const uint4 (&lmr)[4], const TileDesc& d, unsigned char* dst) {
         if (LM && d.kind == KIND_LM) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                *reinterpret_cast<uint4*>(dst + srow[j] * 128 + sslot * 16) = lmk[j];
-                *reinterpret_cast<uint4*>(dst + TILE_BYTES + srow[j] * 128 + sslot * 16) = lmv[j];
-            }
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<uint4*>(dst + srow[j] * 128 + sslot * 16) = lmr[j];
         }
     };
 
-    // per-lane LDS offsets (bytes, within a buffer) of the MFMA operands
-    int koff[2][4];
+    // per-lane LDS offsets (bytes, within a tile) of the K operands for rows qc; rows
+    // qc + 32 have the same swizzle key and sit 4 KiB further on
+    int koff[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const int r = 32 * kb + qc;
-            koff[kb][st] = r * 128 + swz(r, 2 * st + g) * 16;
-        }
+    for (int st = 0; st < 4; ++st) koff[st] = qc * 128 + swz(qc, 2 * st + g) * 16;
     // V^T through the transposing read: lane j of each 16-lane group points at
     // V[16ks + 8half + 4g + j/4][32cb + 16*((lane/16)%2) + 4*(j%4)]; rows for different ks
     // differ by multiples of 16, which leave the swizzle key unchanged
@@ -221,43 +215,42 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int r = vrow0 + 8 * hf;
-            voff[cb][hf] = TILE_BYTES + r * 128 + swz(r, 4 * cb + vcol_chunk) * 16 + vsub;
+            voff[cb][hf] = r * 128 + swz(r, 4 * cb + vcol_chunk) * 16 + vsub;
         }
-    // key index of accumulator register r of block kb: 32kb + 8(r/4) + 4g + r%4
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
     float m = -INFINITY, l = 0.f;
     f32x16 o0 = {}, o1 = {};
 
-    // operands of one tile, read from LDS before the next tile's loads are issued: after
-    // that point the iteration reads no LDS, so nothing has to wait for the loads in flight
-    bf16x8 ka[2][4], va[2][4];
-    auto fetch_operands = [&](const unsigned char* kb) {
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            ka[0][st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + koff[0][st]));
-            ka[1][st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + koff[1][st]));
-        }
-        const lds_u8* lb = (const lds_u8*)kb;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4i16*)(lb + voff[cb][0] + ks * 16 * 128));
-                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4i16*)(lb + voff[cb][1] + ks * 16 * 128));
-                va[cb][ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            }
+    auto read_k = [&](const unsigned char* kt, int st, bf16x8& a0, bf16x8& a1) {
+        a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kt + koff[st]));
+        a1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kt + koff[st] + 4096));
+    };
+    auto read_v = [&](const unsigned char* vt, int ks, bf16x8& a0, bf16x8& a1) {
+        const lds_u8* lb = (const lds_u8*)vt;
+        const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lb + voff[0][0] + ks * 2048));
+        const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lb + voff[0][1] + ks * 2048));
+        const v4i16 y0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lb + voff[1][0] + ks * 2048));
+        const v4i16 y1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lb + voff[1][1] + ks * 2048));
+        a0 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+        a1 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // one 16-dim step of S^T = K Q^T for the tile in LDS at kt
+    auto qk = [&](const unsigned char* kt, f32x16& s0, f32x16& s1, int st) {
+        bf16x8 a0, a1;
+        read_k(kt, st, a0, a1);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qop[st], st ? s0 : f32x16{}, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qop[st], st ? s1 : f32x16{}, 0, 0, 0);
     };
 
-    auto compute = [&](const TileDesc& cur) {
-        f32x16 s0 = {}, s1 = {};
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0][st], qop[st], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1][st], qop[st], s1, 0, 0, 0);
-        }
+    // Softmax of tile `cur` (scores s0/s1) and its P V accumulation, with the QK^T products
+    // of the next tile (K in LDS at kn, results n0/n1) interleaved.  The products are formed
+    // unconditionally (after the last tile they read a stale buffer and are never used): a
+    // conditional product would make the compiler copy the accumulators around it.  An
+    // empty tile runs through as well; its scores are all masked, so it adds nothing.
+    auto softmax_pv = [&](const TileDesc& cur, f32x16& s0, f32x16& s1, const unsigned char* vt,
+                          const unsigned char* kn, f32x16& n0, f32x16& n1) {
+        qk(kn, n0, n1, 0);
         if (cur.mask != ~0ull) {
             if (!LM || cur.kind != KIND_LM) {
                 // contiguous valid rows [lo, hi): one unsigned compare per score
@@ -283,6 +276,7 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = max3f(mx, s0[r], s1[r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
+        qk(kn, n0, n1, 1);
         const float mt = mx == -INFINITY ? -INFINITY : fmaf(mx, p.scale_l2, bias);
         // lazy rescale: move the reference max only when some row grew past the threshold
         if (__ballot(mt > m + RESCALE_THRESHOLD)) {
@@ -298,6 +292,8 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
         for (int ks = 0; ks < 4; ++ks) {
             const f32x16& sp = (ks < 2) ? s0 : s1;
             const int j0 = 2 * (ks & 1);
+            bf16x8 va0, va1;
+            read_v(vt, ks, va0, va1);
             float pv[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -308,45 +304,68 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
                 pp[i] = bf16x2{(__bf16)pv[2 * i], (__bf16)pv[2 * i + 1]};
                 l = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, l, false);   // sum of rounded P
             }
+            if (ks < 2) qk(kn, n0, n1, 2 + ks);
             const bf16x8 pb = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
                                                       __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
                                                       0, 1, 2, 3, 4, 5, 6, 7);
-            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0][ks], pb, o0, 0, 0, 0);
-            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1][ks], pb, o1, 0, 0, 0);
+            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0, pb, o0, 0, 0, 0);
+            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1, pb, o1, 0, 0, 0);
         }
     };
 
-    TileDesc cur, nxt;
-    lds_u8* const lbuf = (lds_u8*)s_buf;
+    // ---- prologue: K(0), V(0), K(1) into LDS; S(0) = K(0) Q^T
+    TileDesc d0{}, d1{}, d2{};
+    f32x16 sa0 = {}, sa1 = {}, sb0 = {}, sb1 = {};
     if (ntiles > 0) {
-        issue(0, lbuf, cur);
-        __builtin_amdgcn_s_waitcnt(0);
-        commit(s_buf, cur);
-        __syncthreads();
-    }
-    // One step: operands of tile `it` from buffer B, then tile it+1's loads into buffer
-    // 1-B, then the math.  Unrolled by two so B is a constant and every LDS address is a
-    // per-lane register plus an immediate.
-    auto step = [&](auto bufc, int it) {
-        constexpr int B = decltype(bufc)::value;
-        const bool live = cur.mask != 0;
-        if (live) fetch_operands(s_buf + B * BUF_BYTES);
-        if (it + 1 < ntiles) issue(it + 1, lbuf + (1 - B) * BUF_BYTES, nxt);
-        if (live) compute(cur);
-        __builtin_amdgcn_s_waitcnt(WAITCNT_VM0_LGKM0);   // this wave's tile-(it+1) loads landed
-        if (it + 1 < ntiles) {
-            commit(s_buf + (1 - B) * BUF_BYTES, nxt);
-            cur = nxt;
+        d0 = desc(0);
+        stage(rs_k, p.kbar, lmk, d0, (lds_u8*)s_k0);
+        stage(rs_v, p.vbar, lmv, d0, (lds_u8*)s_v0);
+        __builtin_amdgcn_s_waitcnt(WAITCNT_VM0_LGKM0);
+        commit(lmk, d0, s_k0);
+        commit(lmv, d0, s_v0);
+        if (ntiles > 1) {
+            d1 = desc(1);
+            stage(rs_k, p.kbar, lmk, d1, (lds_u8*)s_k1);
+            __builtin_amdgcn_s_waitcnt(WAITCNT_VM0_LGKM0);
+            commit(lmk, d1, s_k1);
         }
-        if (LM) __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);   // landmark rows written to LDS
-        __builtin_amdgcn_s_barrier();           // all loads landed; all reads of buffer B done
+        __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
+        __builtin_amdgcn_s_barrier();
+        for (int st = 0; st < 4; ++st) qk(s_k0, sa0, sa1, st);
+        __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
+        __builtin_amdgcn_s_barrier();           // everyone is done reading K(0)'s buffer
+    }
+
+    // ---- step it: scores of tile it are in (s0, s1); K(it+1) is in kcur, V(it) in vcur.
+    //      Stage K(it+2) -> kfree (held K(it)) and V(it+1) -> vfree (held V(it-1)).
+    auto step = [&](int it, f32x16& s0, f32x16& s1, f32x16& n0, f32x16& n1, const TileDesc& dc,
+                    const TileDesc& dn, TileDesc& dnn, const unsigned char* kcur,
+                    unsigned char* kfree, const unsigned char* vcur, unsigned char* vfree) {
+        if (it + 2 < ntiles) {
+            dnn = desc(it + 2);
+            stage(rs_k, p.kbar, lmk, dnn, (lds_u8*)kfree);
+        }
+        if (it + 1 < ntiles) stage(rs_v, p.vbar, lmv, dn, (lds_u8*)vfree);
+        softmax_pv(dc, s0, s1, vcur, kcur, n0, n1);
+        __builtin_amdgcn_s_waitcnt(WAITCNT_VM0_LGKM0);   // this wave's loads have landed
+        if (LM) {
+            if (it + 2 < ntiles) commit(lmk, dnn, kfree);
+            if (it + 1 < ntiles) commit(lmv, dn, vfree);
+            __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
+        }
+        __builtin_amdgcn_s_barrier();           // all loads landed; all reads of freed buffers done
     };
     int it = 0;
     for (; it + 1 < ntiles; it += 2) {
-        step(std::integral_constant<int, 0>{}, it);
-        step(std::integral_constant<int, 1>{}, it + 1);
+        // even: K(it+1) in k1, V(it) in v0; free: k0, v1
+        step(it, sa0, sa1, sb0, sb1, d0, d1, d2, s_k1, s_k0, s_v0, s_v1);
+        // odd: K(it+2) in k0, V(it+1) in v1; free: k1, v0
+        step(it + 1, sb0, sb1, sa0, sa1, d1, d2, d0, s_k0, s_k1, s_v1, s_v0);
+        // the odd step wrote d(it+3) into d0; rotate to d0 = d(it+2), d1 = d(it+3)
+        d1 = d0;
+        d0 = d2;
     }
-    if (it < ntiles) step(std::integral_constant<int, 0>{}, it);
+    if (it < ntiles) step(it, sa0, sa1, sb0, sb1, d0, d1, d2, s_k1, s_k0, s_v0, s_v1);
 
     const float ltot = l + __shfl_xor(l, 32);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;

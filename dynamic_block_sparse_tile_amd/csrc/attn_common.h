@@ -64,7 +64,9 @@ __device__ __forceinline__ TileDesc describe(const AttnDev& p, int it, int c, co
     }
     it -= p.Ts;
     if (it < c) {
-        const int t = IDX_LDS ? s_idx[it] : myidx[it];
+        // the list entry is uniform across the workgroup: move it to a scalar register so
+        // the whole description (and every branch on it) stays on the scalar unit
+        const int t = __builtin_amdgcn_readfirstlane(IDX_LDS ? s_idx[it] : myidx[it]);
         d.kind = KIND_REG;
         d.t = t;
         if (t < 0 || t >= p.Tk) {
@@ -81,7 +83,8 @@ __device__ __forceinline__ TileDesc describe(const AttnDev& p, int it, int c, co
     d.kind = KIND_LM;
     d.t = it;
     if (LM) {
-        const uint32_t w0 = s_lm[2 * it], w1 = s_lm[2 * it + 1];
+        const uint32_t w0 = __builtin_amdgcn_readfirstlane(s_lm[2 * it]);
+        const uint32_t w1 = __builtin_amdgcn_readfirstlane(s_lm[2 * it + 1]);
         d.mask = (uint64_t)w0 | ((uint64_t)w1 << 32);
     } else {
         d.mask = 0;

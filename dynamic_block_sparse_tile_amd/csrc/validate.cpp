@@ -3,6 +3,7 @@
 #include "validate.h"
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 
 namespace s3d {
@@ -40,6 +41,12 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
         int _st = (expr);                  \
         if (_st != SPARSE3D_OK) return _st; \
     } while (0)
+
+int check_logit_params(float scale, float landmark_bias) {
+    if (!(std::isfinite(scale) && scale > 0.f) || !std::isfinite(landmark_bias))
+        return SPARSE3D_ERR_UNSUPPORTED;
+    return SPARSE3D_OK;
+}
 
 int validate_tile_scores(const void* q, const void* k, const void* v, int dtype, int32_t heads,
                          int32_t head_dim, int32_t tile, const sparse3d_layout* qlay,

@@ -20,6 +20,9 @@ inline size_t dtype_bytes(sparse3d_dtype d) { return d == SPARSE3D_BF16 ? 2 : 4;
 int check_layout(const sparse3d_layout* l);
 int check_dtype(int dt);
 int check_heads_dims(int32_t heads, int32_t head_dim, int32_t tile);
+// Softmax scale finite and > 0, landmark bias finite: masked logits are -inf, and only a
+// positive finite scale keeps them at -inf (exp -> 0) rather than NaN.
+int check_logit_params(float scale, float landmark_bias);
 // Byte ranges [a, a+na) and [b, b+nb) overlap (both non-empty).
 bool overlaps(const void* a, size_t na, const void* b, size_t nb);
 

@@ -119,7 +119,8 @@ int sparse3d_select_topk(const float* scores, int32_t heads, int32_t q_tiles, in
  * to attend gets out = 0 and lse = -inf.  idx entries outside [0, Tk) are skipped and
  * cnt is clamped to kmax.  out: [heads, Lq, 64] of `out_dtype` (results rounded to
  * nearest even); it must not overlap q, k or v.  Operands are bf16 (bf16 matrix cores,
- * fp32 accumulation) or fp32 (fp32 matrix cores).
+ * fp32 accumulation) or fp32 (fp32 matrix cores).  scale must be finite and > 0 and,
+ * with landmarks on, landmark_bias finite (SPARSE3D_ERR_UNSUPPORTED otherwise).
  */
 int sparse3d_sparse_attn_fwd(const void* q, const void* k, const void* v, sparse3d_dtype dtype,
                              int32_t heads, int32_t head_dim, int32_t tile,

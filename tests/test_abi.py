@@ -90,10 +90,10 @@ def test_select_validation(lib):
 
 def attn_call(lib, q=FAKE, k=FAKE + 10**9, v=FAKE + 2 * 10**9, dt=1, H=2, d=64, tile=64,
               ql=None, kl=None, idx=FAKE + 3 * 10**9, cnt=FAKE + 4 * 10**9, kmax=8, kbar=NULL,
-              vbar=NULL, out=FAKE + 5 * 10**9, odt=1, lse=NULL):
+              vbar=NULL, out=FAKE + 5 * 10**9, odt=1, lse=NULL, bias=4.1588830833596715,
+              scale=0.125):
     return lib.sparse3d_sparse_attn_fwd(q, k, v, dt, H, d, tile, ql or L(), kl or L(), idx, cnt,
-                                        kmax, kbar, vbar, 4.1588830833596715, 0.125, out, odt,
-                                        lse, NULL)
+                                        kmax, kbar, vbar, bias, scale, out, odt, lse, NULL)
 
 
 def test_attn_validation(lib):
@@ -112,6 +112,14 @@ def test_attn_validation(lib):
                                        NULL, NULL) == ERR_NULL
     assert lib.sparse3d_dense_attn_fwd(FAKE, FAKE, FAKE, 1, 2, 64, L(), L(), 0.1, FAKE + 64, 1,
                                        NULL, NULL) == ERR_ALIAS
+    # a masked logit is -inf; only a finite positive scale keeps it out of the softmax
+    for bad in (0.0, -0.125, float("inf"), float("nan")):
+        assert attn_call(lib, scale=bad) == ERR_UNSUP
+        assert lib.sparse3d_dense_attn_fwd(FAKE, FAKE, FAKE, 1, 2, 64, L(), L(), bad,
+                                           FAKE + 10**9 * 5, 1, NULL, NULL) == ERR_UNSUP
+    lm = dict(kbar=FAKE + 6 * 10**9, vbar=FAKE + 7 * 10**9)
+    assert attn_call(lib, bias=float("inf"), **lm) == ERR_UNSUP
+    assert attn_call(lib, bias=float("nan"), **lm) == ERR_UNSUP
 
 
 def test_subsample_layout_host_only(lib):
