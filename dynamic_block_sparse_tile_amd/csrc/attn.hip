@@ -30,13 +30,9 @@ __global__ __launch_bounds__(128, 2) void k_attn(AttnDev p) {
     extern __shared__ uint32_t s_lm[];   // landmark bitmap: unselected tiles with members
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qc = lane & 31, g = lane >> 5;
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int h = logical / p.Tq;
-    const int rem = logical - h * p.Tq;
-    // consecutive work items = the same in-frame query tile of successive frames: they
-    // pick overlapping key tiles, and the XCD remap keeps them on one L2
     const int tpfq = p.ql.P / TILE;
-    const int tq = (rem % p.ql.S) * tpfq + rem / p.ql.S;
+    int h, tq;
+    attn_work_item(blockIdx.x, gridDim.x, p.ql.S, tpfq, gridDim.x / p.Tq, h, tq);
     const int Lq = p.ql.S * p.ql.P, Lk = p.kl.S * p.kl.P;
     const int qrow = tq * TILE + w * 32 + qc;
     const bool qvalid = (tq % tpfq) * TILE + w * 32 + qc < p.ql.N;

@@ -46,6 +46,9 @@ constexpr int BUF_RSRC_WORD3 = 0x00020000;
 // lgkmcnt 11:8; a field at its maximum does not wait).
 constexpr int WAITCNT_VM0_LGKM0 = 0x0070;        // vmcnt(0) lgkmcnt(0)
 constexpr int WAITCNT_LGKM0 = 0xC07F;            // lgkmcnt(0) only
+// Scheduling-barrier mask: ALU, VALU, SALU, matrix, LDS and transcendental instructions may
+// move across it, vector-memory instructions may not.
+constexpr int SCHED_ALLOW_ALL_BUT_VMEM = 0x1 | 0x2 | 0x4 | 0x8 | 0x80 | 0x100 | 0x200 | 0x400;
 
 // A byte offset past every per-head buffer: buffer loads there return zeros.
 constexpr unsigned OOB_OFFSET = 0x80000000u;
@@ -84,11 +87,9 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
 
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int qc = lane & 31, g = lane >> 5;
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int h = logical / p.Tq;
-    const int rem = logical - h * p.Tq;
     const int tpfq = p.ql.P / TILE;
-    const int tq = (rem % p.ql.S) * tpfq + rem / p.ql.S;
+    int h, tq;
+    attn_work_item(blockIdx.x, gridDim.x, p.ql.S, tpfq, gridDim.x / p.Tq, h, tq);
     const int Lq = p.ql.S * p.ql.P, Lk = p.kl.S * p.kl.P;
     const int qrow = tq * TILE + w * 32 + qc;
     const bool qvalid = (tq % tpfq) * TILE + w * 32 + qc < p.ql.N;
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
     // the tile loop waits on all vector-memory traffic, the next tile's loads included
     __builtin_amdgcn_s_waitcnt(0);
 
-    int c = 0;
+    int c = 0, rot = 0;
     const int32_t* myidx = nullptr;
     int ntiles;
     if (DENSE) {
@@ -124,6 +125,16 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
     if (!DENSE) {
         for (int i = tid; i < c; i += 128) s_idx[i] = myidx[i];
         __syncthreads();
+        // Sweep the list starting at the query's own frame (wrapping round).  Workgroups
+        // start one after another in frame order, so this keeps the ones running at the same
+        // time on the same key frames, which then stay in L2 (the list order does not change
+        // the result beyond rounding).
+        {
+            const int thr = (tq / tpfq) * (p.kl.P / TILE);
+            int n = 0;
+            for (int b = 0; b < c; b += 128) n += __syncthreads_count(b + tid < c && s_idx[b + tid] < thr);
+            rot = n < c ? n : 0;
+        }
     }
 
     // ---- staging through buffer resources: one per head for K and for V, so a tile's
@@ -148,46 +159,59 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
     }
     uint4 lmk[4], lmv[4];                         // landmark rows staged through registers
 
-    auto desc = [&](int it) { return describe<DENSE, LM, !DENSE>(p, it, c, myidx, s_idx, s_lm); };
-    // one matrix (K or V: `rs`, landmark source `lsrc`) of tile d into LDS tile `dst`
-    auto stage = [&](const __amdgpu_buffer_rsrc_t& rs, const float* lsrc, uint4 (&lmr)[4],
-                     const TileDesc& d, lds_u8* dst) {
+    auto desc = [&](int it) { return describe<DENSE, LM, !DENSE>(p, it, c, myidx, s_idx, s_lm, rot); };
+    // Staging plan of one matrix of tile d: this wave's four row blocks (rows 32w + 8j .. +8)
+    // load 16 bytes per lane from byte offset voff[j] + base of the per-head buffer; rows
+    // that are not keys (and landmark tiles, which go through registers) use an offset past
+    // the end, which loads zeros.  Landmark rows are loaded here into lmr (mtx 0 = K from
+    // kbar, 1 = V from vbar) and written to LDS by commit() once they have landed.
+    auto plan = [&](int mtx, const TileDesc& d, unsigned (&voff)[4], unsigned& base, uint4 (&lmr)[4]) {
+        base = 0;
         if (d.kind == KIND_REG) {
-            const unsigned base = (unsigned)d.t * TILE_BYTES;
+            base = (unsigned)d.t * TILE_BYTES;
             if (d.mask == ~0ull) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) dma_buf(rs, dst + (32 * w + 8 * j) * 128, (unsigned)soff[j], base);
+                for (int j = 0; j < 4; ++j) voff[j] = (unsigned)soff[j];
             } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bool ok = (d.mask >> srow[j]) & 1ull;
-                    dma_buf(rs, dst + (32 * w + 8 * j) * 128, ok ? (unsigned)soff[j] : OOB_OFFSET, base);
-                }
+                for (int j = 0; j < 4; ++j) voff[j] = ((d.mask >> srow[j]) & 1ull) ? (unsigned)soff[j] : OOB_OFFSET;
             }
         } else if (d.kind == KIND_SPEC) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = srow[j];
-                const bool ok = (d.mask >> r) & 1ull;
-                const unsigned vo = ok ? (unsigned)src_row(p, d, r) * 128u + swz(r, sslot) * 16u
-                                       : OOB_OFFSET;
-                dma_buf(rs, dst + (32 * w + 8 * j) * 128, vo, 0u);
+                voff[j] = ((d.mask >> r) & 1ull) ? (unsigned)src_row(p, d, r) * 128u + swz(r, sslot) * 16u
+                                                 : OOB_OFFSET;
             }
-        } else if (LM) {
+        } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = srow[j];
-                const bool ok = (d.mask >> r) & 1ull;
-                float4 a0 = make_float4(0, 0, 0, 0), a1 = a0;
-                if (ok) {
-                    const size_t o = ((size_t)h * p.Tk + d.t * TILE + r) * HD + swz(r, sslot) * 8;
-                    a0 = *reinterpret_cast<const float4*>(lsrc + o);
-                    a1 = *reinterpret_cast<const float4*>(lsrc + o + 4);
+            for (int j = 0; j < 4; ++j) voff[j] = OOB_OFFSET;
+            if (LM) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = srow[j];
+                    float4 a0 = make_float4(0, 0, 0, 0), a1 = a0;
+                    if ((d.mask >> r) & 1ull) {
+                        const float* lsrc = mtx ? p.vbar : p.kbar;
+                        const size_t o = ((size_t)h * p.Tk + d.t * TILE + r) * HD + swz(r, sslot) * 8;
+                        a0 = *reinterpret_cast<const float4*>(lsrc + o);
+                        a1 = *reinterpret_cast<const float4*>(lsrc + o + 4);
+                    }
+                    lmr[j] = make_uint4(pack_bf16x2(a0.x, a0.y), pack_bf16x2(a0.z, a0.w),
+                                        pack_bf16x2(a1.x, a1.y), pack_bf16x2(a1.z, a1.w));
                 }
-                lmr[j] = make_uint4(pack_bf16x2(a0.x, a0.y), pack_bf16x2(a0.z, a0.w),
-                                    pack_bf16x2(a1.x, a1.y), pack_bf16x2(a1.z, a1.w));
             }
         }
+    };
+    auto dma_rows = [&](int mtx, lds_u8* dst, const unsigned (&voff)[4], unsigned base, int j) {
+        dma_buf(mtx ? rs_v : rs_k, dst + (32 * w + 8 * j) * 128, voff[j], base);
+    };
+    // the whole matrix at once (prologue)
+    auto stage = [&](int mtx, const TileDesc& d, lds_u8* dst) {
+        unsigned voff[4], base;
+        plan(mtx, d, voff, base, mtx ? lmv : lmk);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma_rows(mtx, dst, voff, base, j);
     };
     // landmark rows (converted in registers) go to LDS once their loads have landed
     auto commit = [&](const uint4 (&lmr)[4], const TileDesc& d, unsigned char* dst) {
@@ -235,12 +259,20 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
         a0 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
         a1 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    // one 16-dim step of S^T = K Q^T for the tile in LDS at kt
+    // one 16-dim step of S^T = K Q^T from K operands already in registers
+    auto qk_ops = [&](const bf16x8 (&ka)[4][2], f32x16& s0, f32x16& s1, int st) {
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st][0], qop[st], st ? s0 : f32x16{}, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st][1], qop[st], st ? s1 : f32x16{}, 0, 0, 0);
+    };
     auto qk = [&](const unsigned char* kt, f32x16& s0, f32x16& s1, int st) {
-        bf16x8 a0, a1;
-        read_k(kt, st, a0, a1);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qop[st], st ? s0 : f32x16{}, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qop[st], st ? s1 : f32x16{}, 0, 0, 0);
+        bf16x8 ka[4][2];
+        read_k(kt, st, ka[st][0], ka[st][1]);
+        qk_ops(ka, s0, s1, st);
+    };
+    // max over the two 32-lane halves (lanes l and l^32 hold the same query)
+    auto xhalf_max = [](float x) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
     };
 
     // Softmax of tile `cur` (scores s0/s1) and its P V accumulation, with the QK^T products
@@ -248,9 +280,22 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
     // unconditionally (after the last tile they read a stale buffer and are never used): a
     // conditional product would make the compiler copy the accumulators around it.  An
     // empty tile runs through as well; its scores are all masked, so it adds nothing.
+    // `issue(i)`, i = 0..7, is called at eight points spread over the first part of the step:
+    // the staging loads go out one at a time between the arithmetic, so the memory pipeline
+    // is never handed a burst that stalls the issuing wave.
     auto softmax_pv = [&](const TileDesc& cur, f32x16& s0, f32x16& s1, const unsigned char* vt,
-                          const unsigned char* kn, f32x16& n0, f32x16& n1) {
-        qk(kn, n0, n1, 0);
+                          const unsigned char* kn, f32x16& n0, f32x16& n1, auto&& issue) {
+        // every LDS operand of this step is requested up front, so the reads overlap the
+        // masking and the max instead of stalling the matrix core one by one
+        bf16x8 ka[4][2], va[4][2];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) read_k(kn, st, ka[st][0], ka[st][1]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) read_v(vt, ks, va[ks][0], va[ks][1]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(0);
+        qk_ops(ka, n0, n1, 0);
+        issue(1);
         if (cur.mask != ~0ull) {
             if (!LM || cur.kind != KIND_LM) {
                 // contiguous valid rows [lo, hi): one unsigned compare per score
@@ -275,8 +320,10 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
         float mx = max3f(s0[0], s1[0], -INFINITY);
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = max3f(mx, s0[r], s1[r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        qk(kn, n0, n1, 1);
+        issue(2);
+        mx = xhalf_max(mx);
+        qk_ops(ka, n0, n1, 1);
+        issue(3);
         const float mt = mx == -INFINITY ? -INFINITY : fmaf(mx, p.scale_l2, bias);
         // lazy rescale: move the reference max only when some row grew past the threshold
         if (__ballot(mt > m + RESCALE_THRESHOLD)) {
@@ -292,8 +339,6 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
         for (int ks = 0; ks < 4; ++ks) {
             const f32x16& sp = (ks < 2) ? s0 : s1;
             const int j0 = 2 * (ks & 1);
-            bf16x8 va0, va1;
-            read_v(vt, ks, va0, va1);
             float pv[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -304,12 +349,18 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
                 pp[i] = bf16x2{(__bf16)pv[2 * i], (__bf16)pv[2 * i + 1]};
                 l = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, l, false);   // sum of rounded P
             }
-            if (ks < 2) qk(kn, n0, n1, 2 + ks);
+            if (ks < 2) qk_ops(ka, n0, n1, 2 + ks);
+            if (ks == 0) issue(4);
+            if (ks == 1) {
+                issue(5);
+                issue(6);
+            }
+            if (ks == 2) issue(7);
             const bf16x8 pb = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
                                                       __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
                                                       0, 1, 2, 3, 4, 5, 6, 7);
-            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0, pb, o0, 0, 0, 0);
-            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1, pb, o1, 0, 0, 0);
+            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks][0], pb, o0, 0, 0, 0);
+            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks][1], pb, o1, 0, 0, 0);
         }
     };
 
@@ -318,14 +369,14 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
     f32x16 sa0 = {}, sa1 = {}, sb0 = {}, sb1 = {};
     if (ntiles > 0) {
         d0 = desc(0);
-        stage(rs_k, p.kbar, lmk, d0, (lds_u8*)s_k0);
-        stage(rs_v, p.vbar, lmv, d0, (lds_u8*)s_v0);
+        stage(0, d0, (lds_u8*)s_k0);
+        stage(1, d0, (lds_u8*)s_v0);
         __builtin_amdgcn_s_waitcnt(WAITCNT_VM0_LGKM0);
         commit(lmk, d0, s_k0);
         commit(lmv, d0, s_v0);
         if (ntiles > 1) {
             d1 = desc(1);
-            stage(rs_k, p.kbar, lmk, d1, (lds_u8*)s_k1);
+            stage(0, d1, (lds_u8*)s_k1);
             __builtin_amdgcn_s_waitcnt(WAITCNT_VM0_LGKM0);
             commit(lmk, d1, s_k1);
         }
@@ -341,16 +392,36 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
     auto step = [&](int it, f32x16& s0, f32x16& s1, f32x16& n0, f32x16& n1, const TileDesc& dc,
                     const TileDesc& dn, TileDesc& dnn, const unsigned char* kcur,
                     unsigned char* kfree, const unsigned char* vcur, unsigned char* vfree) {
-        if (it + 2 < ntiles) {
+        const bool sk = it + 2 < ntiles, sv = it + 1 < ntiles;
+        unsigned vk[4], vv[4], bk = 0, bv = 0;
+        if (sk) {
             dnn = desc(it + 2);
-            stage(rs_k, p.kbar, lmk, dnn, (lds_u8*)kfree);
+            plan(0, dnn, vk, bk, lmk);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vk[j] = OOB_OFFSET;
         }
-        if (it + 1 < ntiles) stage(rs_v, p.vbar, lmv, dn, (lds_u8*)vfree);
-        softmax_pv(dc, s0, s1, vcur, kcur, n0, n1);
+        if (sv) {
+            plan(1, dn, vv, bv, lmv);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vv[j] = OOB_OFFSET;
+        }
+        // staging load i: row block i/2 of K(it+2) (even i) or of V(it+1) (odd i), without
+        // branches; the scheduling barrier keeps each load where it is placed
+        auto issue = [&](int i) {
+            if (i & 1) dma_rows(1, (lds_u8*)vfree, vv, bv, i >> 1);
+            else dma_rows(0, (lds_u8*)kfree, vk, bk, i >> 1);
+            __builtin_amdgcn_sched_barrier(SCHED_ALLOW_ALL_BUT_VMEM);
+        };
+        softmax_pv(dc, s0, s1, vcur, kcur, n0, n1, issue);
+        // keep the whole step's arithmetic ahead of the wait below (the scheduler would
+        // otherwise hoist the wait and barrier into the middle of the softmax)
+        __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(WAITCNT_VM0_LGKM0);   // this wave's loads have landed
         if (LM) {
-            if (it + 2 < ntiles) commit(lmk, dnn, kfree);
-            if (it + 1 < ntiles) commit(lmv, dn, vfree);
+            if (sk) commit(lmk, dnn, kfree);
+            if (sv) commit(lmv, dn, vfree);
             __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
         }
         __builtin_amdgcn_s_barrier();           // all loads landed; all reads of freed buffers done

@@ -46,9 +46,10 @@ struct TileDesc {
 constexpr int IDX_LDS_MAX = 8000;
 
 // IDX_LDS: the list is read from its LDS copy (bf16 kernel) rather than from global memory.
+// The selected tiles are visited starting at list position `rot` (and wrapping round).
 template <bool DENSE, bool LM, bool IDX_LDS>
 __device__ __forceinline__ TileDesc describe(const AttnDev& p, int it, int c, const int32_t* myidx,
-                                             const int32_t* s_idx, const uint32_t* s_lm) {
+                                             const int32_t* s_idx, const uint32_t* s_lm, int rot = 0) {
     TileDesc d;
     if (DENSE) {
         d.kind = KIND_REG;
@@ -64,9 +65,10 @@ __device__ __forceinline__ TileDesc describe(const AttnDev& p, int it, int c, co
     }
     it -= p.Ts;
     if (it < c) {
+        const int pos = it + rot < c ? it + rot : it + rot - c;
         // the list entry is uniform across the workgroup: move it to a scalar register so
         // the whole description (and every branch on it) stays on the scalar unit
-        const int t = __builtin_amdgcn_readfirstlane(IDX_LDS ? s_idx[it] : myidx[it]);
+        const int t = __builtin_amdgcn_readfirstlane(IDX_LDS ? s_idx[pos] : myidx[pos]);
         d.kind = KIND_REG;
         d.t = t;
         if (t < 0 || t >= p.Tk) {

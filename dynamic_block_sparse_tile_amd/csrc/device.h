@@ -51,6 +51,33 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
     return base + slot;
 }
 
+// Work item of an attention workgroup.  Query tiles come in groups G = (head h, in-frame
+// tile j), the S query tiles (one per frame) at the same position j of one head; the tiles
+// of a group select overlapping key tiles (the same scene content seen in every frame).
+// Each XCD receives one contiguous range of workgroups (xcd_remap) and its range holds
+// whole groups, G = x, x + 8, x + 16, ... for XCD x, in increasing order.  So at any time
+// one group runs per XCD (its key tiles share that XCD's L2) and all XCDs work on
+// neighbouring groups of the same head (whose K and V then share the last-level cache),
+// instead of each XCD streaming a different head.
+__device__ __forceinline__ void attn_work_item(int bid, int nblocks, int S, int tpf, int heads,
+                                               int& h, int& tq) {
+    const int logical = xcd_remap(bid, nblocks);
+    int rank = logical / S;
+    const int s = logical - rank * S;
+    int G = rank;
+    const int ng = heads * tpf;
+    for (int x = 0; x < NXCD; ++x) {
+        const int c = (ng - x + NXCD - 1) / NXCD;   // groups with G % NXCD == x
+        if (rank < c) {
+            G = x + NXCD * rank;
+            break;
+        }
+        rank -= c;
+    }
+    h = G / tpf;
+    tq = s * tpf + (G - h * tpf);
+}
+
 // Member-row range [lo, hi) of key tile t inside its 64 rows (patch tokens only).
 __device__ __forceinline__ void member_range(const Lay& L, int t, int& lo, int& hi) {
     const int tpf = L.P / TILE;
