@@ -95,6 +95,8 @@ class Layer:
 
     def attend(self, idx, cnt, kbar, vbar):
         lm = self.w.landmarks
+        if lm and self.q.dtype != kbar.dtype:        # landmark means in the operand precision
+            kbar, vbar = self.S.sparse3d_cast(kbar, self.q.dtype), self.S.sparse3d_cast(vbar, self.q.dtype)
         return self.S.sparse3d_sparse_attn_fwd(self.q, self.K, self.V, self.lay, self.klay, idx, cnt,
                                                kbar=kbar if lm else None, vbar=vbar if lm else None)
 

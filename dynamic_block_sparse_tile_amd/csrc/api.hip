@@ -60,7 +60,7 @@ int sparse3d_sparse_attn_fwd(const void* q, const void* k, const void* v, sparse
                              int32_t heads, int32_t head_dim, int32_t tile,
                              const sparse3d_layout* qlay, const sparse3d_layout* klay,
                              const int32_t* idx, const int32_t* cnt, int32_t kmax,
-                             const float* kbar, const float* vbar, float landmark_bias,
+                             const void* kbar, const void* vbar, float landmark_bias,
                              float scale, void* out, sparse3d_dtype out_dtype, float* lse,
                              void* stream) {
     const int st = validate_attn(true, q, k, v, dtype, heads, head_dim, tile, qlay, klay, idx, cnt,
@@ -71,6 +71,14 @@ int sparse3d_sparse_attn_fwd(const void* q, const void* k, const void* v, sparse
     AttnArgs a{q, k, v, dtype, out_dtype, heads, to_lay(*qlay), to_lay(*klay), false, idx, cnt,
                kmax, kbar, vbar, landmark_bias, scale, out, lse};
     S3D_HIP(launch_attn(a, static_cast<hipStream_t>(stream)));
+    return SPARSE3D_OK;
+}
+
+int sparse3d_cast(const float* src, int64_t n, sparse3d_dtype dtype, void* dst, void* stream) {
+    const int st = validate_cast(src, n, dtype, dst);
+    if (st != SPARSE3D_OK) return st;
+    if (n == 0) return SPARSE3D_OK;
+    S3D_HIP(launch_cast(src, n, dtype, dst, static_cast<hipStream_t>(stream)));
     return SPARSE3D_OK;
 }
 

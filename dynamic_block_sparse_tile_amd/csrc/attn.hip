@@ -92,21 +92,23 @@ __global__ __launch_bounds__(128, 2) void k_attn(AttnDev p) {
             const int r = (x >> 1) * 32 + 2 * rp + (x & 1);
             const bool ok = (nxt.mask >> r) & 1ull;
             if (nxt.kind == KIND_LM) {
-                // landmark rows come from the fp32 tile means
+                // landmark rows come from the tile means (operand dtype)
                 const size_t o = ((size_t)h * p.Tk + nxt.t * TILE + r) * HD + c8 * 8;
-                float4 a0 = make_float4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
-                if (ok) {
-                    a0 = *reinterpret_cast<const float4*>(p.kbar + o);
-                    a1 = *reinterpret_cast<const float4*>(p.kbar + o + 4);
-                    b0 = *reinterpret_cast<const float4*>(p.vbar + o);
-                    b1 = *reinterpret_cast<const float4*>(p.vbar + o + 4);
-                }
                 if (!F32IN) {
-                    kr[x] = make_uint4(pack_bf16x2(a0.x, a0.y), pack_bf16x2(a0.z, a0.w),
-                                       pack_bf16x2(a1.x, a1.y), pack_bf16x2(a1.z, a1.w));
-                    vr[x] = make_uint4(pack_bf16x2(b0.x, b0.y), pack_bf16x2(b0.z, b0.w),
-                                       pack_bf16x2(b1.x, b1.y), pack_bf16x2(b1.z, b1.w));
+                    const uint16_t* km = static_cast<const uint16_t*>(p.kbar);
+                    const uint16_t* vm = static_cast<const uint16_t*>(p.vbar);
+                    kr[x] = ok ? *reinterpret_cast<const uint4*>(km + o) : make_uint4(0, 0, 0, 0);
+                    vr[x] = ok ? *reinterpret_cast<const uint4*>(vm + o) : make_uint4(0, 0, 0, 0);
                 } else {
+                    const float* km = static_cast<const float*>(p.kbar);
+                    const float* vm = static_cast<const float*>(p.vbar);
+                    float4 a0 = make_float4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
+                    if (ok) {
+                        a0 = *reinterpret_cast<const float4*>(km + o);
+                        a1 = *reinterpret_cast<const float4*>(km + o + 4);
+                        b0 = *reinterpret_cast<const float4*>(vm + o);
+                        b1 = *reinterpret_cast<const float4*>(vm + o + 4);
+                    }
                     kf[2 * x] = a0; kf[2 * x + 1] = a1;
                     vf[2 * x] = b0; vf[2 * x + 1] = b1;
                 }

@@ -147,6 +147,18 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
     const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<unsigned char*>(static_cast<const unsigned char*>(p.v)) + (size_t)h * head_bytes, 0,
         (int)head_bytes, BUF_RSRC_WORD3);
+    // landmark means (bf16 [heads, Tk, 64]): block b of 64 consecutive tile means is staged
+    // exactly like a key tile
+    __amdgpu_buffer_rsrc_t rs_lk = rs_k, rs_lv = rs_v;
+    if (LM) {
+        const unsigned mean_bytes = (unsigned)p.Tk * 128u;
+        rs_lk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<unsigned char*>(static_cast<const unsigned char*>(p.kbar)) + (size_t)h * mean_bytes, 0,
+            (int)mean_bytes, BUF_RSRC_WORD3);
+        rs_lv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<unsigned char*>(static_cast<const unsigned char*>(p.vbar)) + (size_t)h * mean_bytes, 0,
+            (int)mean_bytes, BUF_RSRC_WORD3);
+    }
 
     // wave w fills rows [32w, 32w+32) of a tile; per instruction j the 64 lanes cover rows
     // 32w+8j .. +8, lane l -> (row l/8, slot l%8) in LDS order
@@ -157,69 +169,46 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
         srow[j] = 32 * w + 8 * j + srow_in;
         soff[j] = srow[j] * 128 + swz(srow[j], sslot) * 16;
     }
-    uint4 lmk[4], lmv[4];                         // landmark rows staged through registers
 
     auto desc = [&](int it) { return describe<DENSE, LM, !DENSE>(p, it, c, myidx, s_idx, s_lm, rot); };
     // Staging plan of one matrix of tile d: this wave's four row blocks (rows 32w + 8j .. +8)
-    // load 16 bytes per lane from byte offset voff[j] + base of the per-head buffer; rows
-    // that are not keys (and landmark tiles, which go through registers) use an offset past
-    // the end, which loads zeros.  Landmark rows are loaded here into lmr (mtx 0 = K from
-    // kbar, 1 = V from vbar) and written to LDS by commit() once they have landed.
-    auto plan = [&](int mtx, const TileDesc& d, unsigned (&voff)[4], unsigned& base, uint4 (&lmr)[4]) {
-        base = 0;
-        if (d.kind == KIND_REG) {
-            base = (unsigned)d.t * TILE_BYTES;
-            if (d.mask == ~0ull) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) voff[j] = (unsigned)soff[j];
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) voff[j] = ((d.mask >> srow[j]) & 1ull) ? (unsigned)soff[j] : OOB_OFFSET;
-            }
-        } else if (d.kind == KIND_SPEC) {
+    // load 16 bytes per lane from byte offset voff[j] + base of buffer rs (mtx 0 = K or the
+    // key means, 1 = V or the value means); rows that are not keys use an offset past the
+    // end, which loads zeros.
+    auto plan = [&](int mtx, const TileDesc& dd, unsigned (&voff)[4], unsigned& base,
+                    __amdgpu_buffer_rsrc_t& rs) {
+        const TileDesc d = uniform(dd);
+        const bool spec = d.kind == KIND_SPEC;
+        // scalar choices first, outside any per-lane selection, so they stay scalar
+        base = spec ? 0u : (unsigned)d.t * TILE_BYTES;
+        rs = (LM && d.kind == KIND_LM) ? (mtx ? rs_lv : rs_lk) : (mtx ? rs_v : rs_k);
+        if (spec) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = srow[j];
-                voff[j] = ((d.mask >> r) & 1ull) ? (unsigned)src_row(p, d, r) * 128u + swz(r, sslot) * 16u
-                                                 : OOB_OFFSET;
+                const unsigned o = (unsigned)src_row(p, d, r) * 128u + swz(r, sslot) * 16u;
+                voff[j] = ((d.mask >> r) & 1ull) ? o : OOB_OFFSET;
             }
+        } else if (d.mask == ~0ull) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) voff[j] = (unsigned)soff[j];
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) voff[j] = OOB_OFFSET;
-            if (LM) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = srow[j];
-                    float4 a0 = make_float4(0, 0, 0, 0), a1 = a0;
-                    if ((d.mask >> r) & 1ull) {
-                        const float* lsrc = mtx ? p.vbar : p.kbar;
-                        const size_t o = ((size_t)h * p.Tk + d.t * TILE + r) * HD + swz(r, sslot) * 8;
-                        a0 = *reinterpret_cast<const float4*>(lsrc + o);
-                        a1 = *reinterpret_cast<const float4*>(lsrc + o + 4);
-                    }
-                    lmr[j] = make_uint4(pack_bf16x2(a0.x, a0.y), pack_bf16x2(a0.z, a0.w),
-                                        pack_bf16x2(a1.x, a1.y), pack_bf16x2(a1.z, a1.w));
-                }
-            }
+            for (int j = 0; j < 4; ++j) voff[j] = ((d.mask >> srow[j]) & 1ull) ? (unsigned)soff[j] : OOB_OFFSET;
         }
     };
-    auto dma_rows = [&](int mtx, lds_u8* dst, const unsigned (&voff)[4], unsigned base, int j) {
-        dma_buf(mtx ? rs_v : rs_k, dst + (32 * w + 8 * j) * 128, voff[j], base);
+    auto dma_rows = [&](const __amdgpu_buffer_rsrc_t& rs, lds_u8* dst, const unsigned (&voff)[4],
+                        unsigned base, int j) {
+        // the base is uniform; saying so keeps the load from becoming a loop over lanes
+        dma_buf(rs, dst + (32 * w + 8 * j) * 128, voff[j], __builtin_amdgcn_readfirstlane(base));
     };
     // the whole matrix at once (prologue)
     auto stage = [&](int mtx, const TileDesc& d, lds_u8* dst) {
         unsigned voff[4], base;
-        plan(mtx, d, voff, base, mtx ? lmv : lmk);
+        __amdgpu_buffer_rsrc_t rs;
+        plan(mtx, d, voff, base, rs);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma_rows(mtx, dst, voff, base, j);
-    };
-    // landmark rows (converted in registers) go to LDS once their loads have landed
-    auto commit = [&](const uint4 (&lmr)[4], const TileDesc& d, unsigned char* dst) {
-        if (LM && d.kind == KIND_LM) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<uint4*>(dst + srow[j] * 128 + sslot * 16) = lmr[j];
-        }
+        for (int j = 0; j < 4; ++j) dma_rows(rs, dst, voff, base, j);
     };
 
     // per-lane LDS offsets (bytes, within a tile) of the K operands for rows qc; rows
@@ -283,8 +272,9 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
     // `issue(i)`, i = 0..7, is called at eight points spread over the first part of the step:
     // the staging loads go out one at a time between the arithmetic, so the memory pipeline
     // is never handed a burst that stalls the issuing wave.
-    auto softmax_pv = [&](const TileDesc& cur, f32x16& s0, f32x16& s1, const unsigned char* vt,
+    auto softmax_pv = [&](const TileDesc& cur_in, f32x16& s0, f32x16& s1, const unsigned char* vt,
                           const unsigned char* kn, f32x16& n0, f32x16& n1, auto&& issue) {
+        const TileDesc cur = uniform(cur_in);
         // every LDS operand of this step is requested up front, so the reads overlap the
         // masking and the max instead of stalling the matrix core one by one
         bf16x8 ka[4][2], va[4][2];
@@ -308,11 +298,15 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
                     if (key + 32 - lo >= span) s1[r] = -INFINITY;
                 }
             } else {
+                // arbitrary row set (landmark block): this lane's keys 8i + 4g + (0..3) of
+                // each half, tested against a constant bit after one per-lane shift
+                const uint32_t w0 = (uint32_t)cur.mask >> (4 * g);
+                const uint32_t w1 = (uint32_t)(cur.mask >> 32) >> (4 * g);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (!((cur.mask >> key) & 1ull)) s0[r] = -INFINITY;
-                    if (!((cur.mask >> (32 + key)) & 1ull)) s1[r] = -INFINITY;
+                    const uint32_t bit = 1u << (8 * (r >> 2) + (r & 3));
+                    if (!(w0 & bit)) s0[r] = -INFINITY;
+                    if (!(w1 & bit)) s1[r] = -INFINITY;
                 }
             }
         }
@@ -371,16 +365,11 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
         d0 = desc(0);
         stage(0, d0, (lds_u8*)s_k0);
         stage(1, d0, (lds_u8*)s_v0);
-        __builtin_amdgcn_s_waitcnt(WAITCNT_VM0_LGKM0);
-        commit(lmk, d0, s_k0);
-        commit(lmv, d0, s_v0);
         if (ntiles > 1) {
             d1 = desc(1);
             stage(0, d1, (lds_u8*)s_k1);
-            __builtin_amdgcn_s_waitcnt(WAITCNT_VM0_LGKM0);
-            commit(lmk, d1, s_k1);
         }
-        __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
+        __builtin_amdgcn_s_waitcnt(WAITCNT_VM0_LGKM0);
         __builtin_amdgcn_s_barrier();
         for (int st = 0; st < 4; ++st) qk(s_k0, sa0, sa1, st);
         __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
@@ -394,15 +383,16 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
                     unsigned char* kfree, const unsigned char* vcur, unsigned char* vfree) {
         const bool sk = it + 2 < ntiles, sv = it + 1 < ntiles;
         unsigned vk[4], vv[4], bk = 0, bv = 0;
+        __amdgpu_buffer_rsrc_t rk = rs_k, rv = rs_v;
         if (sk) {
             dnn = desc(it + 2);
-            plan(0, dnn, vk, bk, lmk);
+            plan(0, dnn, vk, bk, rk);
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) vk[j] = OOB_OFFSET;
         }
         if (sv) {
-            plan(1, dn, vv, bv, lmv);
+            plan(1, dn, vv, bv, rv);
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) vv[j] = OOB_OFFSET;
@@ -410,8 +400,8 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
         // staging load i: row block i/2 of K(it+2) (even i) or of V(it+1) (odd i), without
         // branches; the scheduling barrier keeps each load where it is placed
         auto issue = [&](int i) {
-            if (i & 1) dma_rows(1, (lds_u8*)vfree, vv, bv, i >> 1);
-            else dma_rows(0, (lds_u8*)kfree, vk, bk, i >> 1);
+            if (i & 1) dma_rows(rv, (lds_u8*)vfree, vv, bv, i >> 1);
+            else dma_rows(rk, (lds_u8*)kfree, vk, bk, i >> 1);
             __builtin_amdgcn_sched_barrier(SCHED_ALLOW_ALL_BUT_VMEM);
         };
         softmax_pv(dc, s0, s1, vcur, kcur, n0, n1, issue);
@@ -419,11 +409,6 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
         // otherwise hoist the wait and barrier into the middle of the softmax)
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(WAITCNT_VM0_LGKM0);   // this wave's loads have landed
-        if (LM) {
-            if (sk) commit(lmk, dnn, kfree);
-            if (sv) commit(lmv, dn, vfree);
-            __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
-        }
         __builtin_amdgcn_s_barrier();           // all loads landed; all reads of freed buffers done
     };
     int it = 0;

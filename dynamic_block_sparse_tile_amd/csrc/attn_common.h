@@ -15,8 +15,8 @@ struct AttnDev {
     const int32_t* idx;
     const int32_t* cnt;
     int kmax;
-    const float* kbar;
-    const float* vbar;
+    const void* kbar;   // landmark means [heads, Tk, 64], operand dtype
+    const void* vbar;
     float lm_bias_l2;   // landmark bias in base-2 logit units
     float scale_l2;     // scale * log2(e)
     void* out;
@@ -40,6 +40,20 @@ struct TileDesc {
     int t;             // key tile (REG), pseudo-tile (SPEC) or landmark block (LM)
     uint64_t mask;     // which of the 64 staged rows are real keys
 };
+
+// The same description with every field forced into scalar registers.  A TileDesc that
+// has travelled through the kernel's rotating registers may sit in vector registers, where
+// a branch on it becomes divergent and a buffer resource chosen by it needs a loop over
+// lanes; the values are workgroup-uniform, so reading lane 0 is exact.
+__device__ __forceinline__ TileDesc uniform(const TileDesc& d) {
+    TileDesc u;
+    u.kind = __builtin_amdgcn_readfirstlane(d.kind);
+    u.t = __builtin_amdgcn_readfirstlane(d.t);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)d.mask);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(d.mask >> 32));
+    u.mask = (uint64_t)lo | ((uint64_t)hi << 32);
+    return u;
+}
 
 // Longest selection list the bf16 kernel stages in LDS (next to its 32 KiB of tile
 // buffers, within 64 KiB); longer lists run on the generic kernel.

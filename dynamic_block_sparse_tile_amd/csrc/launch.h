@@ -33,14 +33,16 @@ struct AttnArgs {
     const int32_t* idx;
     const int32_t* cnt;
     int kmax;
-    const float* kbar;  // landmarks on iff non-null
-    const float* vbar;
+    const void* kbar;   // landmark means in the operand dtype; landmarks on iff non-null
+    const void* vbar;
     float landmark_bias;
     float scale;
     void* out;
     float* lse;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+
+hipError_t launch_cast(const float* src, int64_t n, int dtype, void* dst, hipStream_t st);
 
 hipError_t launch_grid_subsample(const void* k, const void* v, int dtype, int heads, LayH lay,
                                  int grid_w, int window, LayH out_lay, void* k_out, void* v_out,

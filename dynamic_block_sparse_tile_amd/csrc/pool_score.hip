@@ -5,6 +5,8 @@
 // both the selection signal (query/key means -> scores) and the landmark
 // summaries (key/value means).  Both kernels are HBM-bound: the pool streams Q, K
 // (and V) once, the score kernel writes the [H, Tq, Tk] fp32 score matrix once.
+#include <algorithm>
+
 #include "device.h"
 #include "launch.h"
 
@@ -163,6 +165,20 @@ hipError_t launch_tile_scores(const float* qbar, const float* kbar, int heads, L
     const dim3 grid((Tk + 63) / 64, (Tq + 63) / 64, heads), block(256);
     hipLaunchKernelGGL(k_tile_scores, grid, block, 0, st, qbar, kbar, Tq, Tk,
                        Lay{ql.S, ql.N, ql.P, ql.nsp}, Lay{kl.S, kl.N, kl.P, kl.nsp}, scale, scores);
+    return hipGetLastError();
+}
+
+// fp32 -> bf16, round to nearest even; one value per thread, grid-stride (no alignment
+// requirement on either pointer).
+__global__ void k_cast_bf16(const float* __restrict__ src, int64_t n, __bf16* __restrict__ dst) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        dst[i] = (__bf16)src[i];
+}
+
+hipError_t launch_cast(const float* src, int64_t n, int dtype, void* dst, hipStream_t st) {
+    if (dtype == 0) return hipMemcpyAsync(dst, src, (size_t)n * 4, hipMemcpyDeviceToDevice, st);
+    const int blocks = (int)std::min<int64_t>((n + 255) / 256, 8192);
+    hipLaunchKernelGGL(k_cast_bf16, dim3(blocks), dim3(256), 0, st, src, n, static_cast<__bf16*>(dst));
     return hipGetLastError();
 }
 

@@ -103,7 +103,7 @@ int validate_select_topk(const float* scores, int32_t heads, int32_t q_tiles, in
 int validate_attn(bool sparse, const void* q, const void* k, const void* v, int dtype,
                   int32_t heads, int32_t head_dim, int32_t tile, const sparse3d_layout* qlay,
                   const sparse3d_layout* klay, const int32_t* idx, const int32_t* cnt,
-                  int32_t kmax, const float* kbar, const float* vbar, const void* out,
+                  int32_t kmax, const void* kbar, const void* vbar, const void* out,
                   int out_dtype, const float* lse) {
     if (!q || !k || !v || !out) return SPARSE3D_ERR_NULL;
     if (sparse) {
@@ -129,6 +129,22 @@ int validate_attn(bool sparse, const void* q, const void* k, const void* v, int 
         return SPARSE3D_ERR_ALIAS;
     if (overlaps(lse, lb, q, qb) || overlaps(lse, lb, k, kb) || overlaps(lse, lb, v, kb) ||
         overlaps(lse, lb, out, ob))
+        return SPARSE3D_ERR_ALIAS;
+    if (sparse && kbar) {
+        const size_t mb = size_t(heads) * lay_tiles(*klay) * head_dim * eb;   // landmark means
+        if (overlaps(out, ob, kbar, mb) || overlaps(out, ob, vbar, mb) || overlaps(lse, lb, kbar, mb) ||
+            overlaps(lse, lb, vbar, mb))
+            return SPARSE3D_ERR_ALIAS;
+    }
+    return SPARSE3D_OK;
+}
+
+int validate_cast(const float* src, int64_t n, int dtype, const void* dst) {
+    if (n < 0) return SPARSE3D_ERR_SHAPE;
+    S3D_TRY(check_dtype(dtype));
+    if (n == 0) return SPARSE3D_OK;
+    if (!src || !dst) return SPARSE3D_ERR_NULL;
+    if (overlaps(dst, size_t(n) * dtype_bytes(sparse3d_dtype(dtype)), src, size_t(n) * 4))
         return SPARSE3D_ERR_ALIAS;
     return SPARSE3D_OK;
 }

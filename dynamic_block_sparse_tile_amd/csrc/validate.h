@@ -38,8 +38,10 @@ int validate_select_topk(const float* scores, int32_t heads, int32_t q_tiles, in
 int validate_attn(bool sparse, const void* q, const void* k, const void* v, int dtype,
                   int32_t heads, int32_t head_dim, int32_t tile, const sparse3d_layout* qlay,
                   const sparse3d_layout* klay, const int32_t* idx, const int32_t* cnt,
-                  int32_t kmax, const float* kbar, const float* vbar, const void* out,
+                  int32_t kmax, const void* kbar, const void* vbar, const void* out,
                   int out_dtype, const float* lse);
+
+int validate_cast(const float* src, int64_t n, int dtype, const void* dst);
 
 int subsample_layout(const sparse3d_layout* lay, int32_t grid_h, int32_t grid_w, int32_t window,
                      int32_t tile, sparse3d_layout* out);

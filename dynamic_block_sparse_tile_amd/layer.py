@@ -96,8 +96,11 @@ def sparse_global_attention(q, k, v, qlay, klay=None, *, top_k: int, anchor_fram
     qbar, kbar, vbar, scores = S.sparse3d_tile_scores(q, k, qlay, klay, v=v if landmarks else None,
                                                       scale=scale)
     idx, cnt = S.sparse3d_select_topk(scores, top_k, tiles_per_frame(klay), anchor_frame)
+    km, vm = (kbar, vbar) if q.dtype == torch.float32 else (None, None)
+    if landmarks and q.dtype != torch.float32:          # the operand precision of the means
+        km, vm = S.sparse3d_cast(kbar, q.dtype), S.sparse3d_cast(vbar, q.dtype)
     res = S.sparse3d_sparse_attn_fwd(q, k, v, qlay, klay, idx, cnt,
-                                     kbar=kbar if landmarks else None, vbar=vbar,
+                                     kbar=km if landmarks else None, vbar=vm if landmarks else None,
                                      landmark_bias=landmark_bias, scale=scale,
                                      out_dtype=out_dtype, return_lse=return_lse)
     out, lse = res if return_lse else (res, None)

@@ -21,6 +21,7 @@ __all__ = [
     "Sparse3dError", "library", "sparse3d_abi_version", "sparse3d_status_string",
     "sparse3d_tile_scores", "sparse3d_select_topk", "sparse3d_sparse_attn_fwd",
     "sparse3d_dense_attn_fwd", "sparse3d_subsample_layout", "sparse3d_grid_subsample_kv",
+    "sparse3d_cast",
     "kmax_for", "LN64",
 ]
 
@@ -61,6 +62,7 @@ _SIGS = {
     "sparse3d_subsample_layout": ([_LP, _i32, _i32, _i32, _i32, _LP], ctypes.c_int),
     "sparse3d_grid_subsample_kv": ([_vp, _vp, ctypes.c_int, _i32, _i32, _LP, _i32, _i32, _i32,
                                     _vp, _vp, _LP, _vp], ctypes.c_int),
+    "sparse3d_cast": ([_vp, ctypes.c_int64, ctypes.c_int, _vp, _vp], ctypes.c_int),
 }
 
 
@@ -177,11 +179,18 @@ def _out_dtype(q, out_dtype):
 def sparse3d_sparse_attn_fwd(q, k, v, qlay, klay, idx, cnt, kbar=None, vbar=None,
                              landmark_bias: float = LN64, scale: Optional[float] = None,
                              out_dtype=None, return_lse: bool = False):
-    """Attention over specials + selected tiles (+ landmarks when kbar/vbar are given)."""
+    """Attention over specials + selected tiles (+ landmarks when kbar/vbar are given).
+
+    kbar/vbar are the tile means in q's dtype (for bf16, ``sparse3d_cast`` of the fp32
+    means that ``sparse3d_tile_scores`` returns)."""
     for x, n in ((q, "q"), (k, "k"), (v, "v"), (idx, "idx"), (cnt, "cnt")):
         _dev(x, n)
     if (kbar is None) != (vbar is None):
         raise ValueError("kbar and vbar go together")
+    if kbar is not None:
+        _dev(kbar, "kbar"), _dev(vbar, "vbar")
+        if kbar.dtype != q.dtype or vbar.dtype != q.dtype:
+            raise TypeError("landmark means must have the operand dtype (see sparse3d_cast)")
     H = q.shape[0]
     scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else scale
     od, odc = _out_dtype(q, out_dtype)
@@ -194,6 +203,16 @@ def sparse3d_sparse_attn_fwd(q, k, v, qlay, klay, idx, cnt, kbar=None, vbar=None
         _ptr(idx) if kmax > 0 else None, _ptr(cnt), kmax, _ptr(kbar), _ptr(vbar), landmark_bias,
         scale, _ptr(out), odc, _ptr(lse), _stream(q)))
     return (out, lse) if return_lse else out
+
+
+def sparse3d_cast(x: torch.Tensor, dtype) -> torch.Tensor:
+    """fp32 tensor -> new tensor of `dtype` (bfloat16: round to nearest even)."""
+    _dev(x, "x")
+    if x.dtype != torch.float32:
+        raise TypeError("sparse3d_cast converts from float32")
+    out = torch.empty(x.shape, device=x.device, dtype=dtype)
+    _check(library().sparse3d_cast(_ptr(x), x.numel(), _dt(out), _ptr(out), _stream(x)))
+    return out
 
 
 def sparse3d_dense_attn_fwd(q, k, v, qlay, klay=None, scale: Optional[float] = None,

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define SPARSE3D_ABI_VERSION 1
+#define SPARSE3D_ABI_VERSION 2
 
 typedef enum { SPARSE3D_F32 = 0, SPARSE3D_BF16 = 1 } sparse3d_dtype;
 
@@ -110,9 +110,12 @@ int sparse3d_select_topk(const float* scores, int32_t heads, int32_t q_tiles, in
  *
  * For a valid query row i of query tile tq, the attended set is every special key row of
  * every frame plus the member rows of the tiles idx[h,tq,0:cnt[h,tq]]; the logit of key
- * j is scale * q_i . k_j.  With landmarks on (kbar, vbar non-NULL, as written by
- * sparse3d_tile_scores), every key tile that is not selected and has member rows adds
- * one more logit scale * q_i . kbar[h,t] + landmark_bias with value vbar[h,t].
+ * j is scale * q_i . k_j.  With landmarks on (kbar, vbar non-NULL), every key tile that
+ * is not selected and has member rows adds one more logit scale * q_i . kbar[h,t] +
+ * landmark_bias with value vbar[h,t].  kbar and vbar are the key/value tile means
+ * [heads, Tk, 64] in the operand dtype: for F32 the fp32 means sparse3d_tile_scores
+ * writes, for BF16 those means rounded to bf16 (sparse3d_cast), which is the precision
+ * the matrix cores take them in.
  *   out[h,i,:] = sum_j softmax_j * value_j   (fp32 statistics and accumulation)
  *   lse[h,i]   = natural-log log-sum-exp of the logits (optional, float [heads, Lq])
  * Rows that are not valid queries get out = 0 and lse = 0; a valid query with nothing
@@ -126,7 +129,7 @@ int sparse3d_sparse_attn_fwd(const void* q, const void* k, const void* v, sparse
                              int32_t heads, int32_t head_dim, int32_t tile,
                              const sparse3d_layout* qlay, const sparse3d_layout* klay,
                              const int32_t* idx, const int32_t* cnt, int32_t kmax,
-                             const float* kbar, const float* vbar, float landmark_bias,
+                             const void* kbar, const void* vbar, float landmark_bias,
                              float scale, void* out, sparse3d_dtype out_dtype, float* lse,
                              void* stream);
 
@@ -141,6 +144,13 @@ int sparse3d_dense_attn_fwd(const void* q, const void* k, const void* v, sparse3
                             const sparse3d_layout* qlay, const sparse3d_layout* klay,
                             float scale, void* out, sparse3d_dtype out_dtype, float* lse,
                             void* stream);
+
+/*
+ * Elementwise conversion of n fp32 values to `dtype`, rounded to nearest even (F32 is a
+ * plain copy).  Used to hand the landmark means to the bf16 attention in the precision
+ * its matrix cores read.  n >= 0; dst must not overlap src.
+ */
+int sparse3d_cast(const float* src, int64_t n, sparse3d_dtype dtype, void* dst, void* stream);
 
 /*
  * Key/value layout after the AVGGT grid subsample (technical summary, section 2B.2):

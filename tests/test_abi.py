@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status(lib):
-    assert lib.sparse3d_abi_version() == 1
+    assert lib.sparse3d_abi_version() == 2
     for st in range(6):
         assert lib.sparse3d_status_string(st)
     assert lib.sparse3d_status_string(99) == b"unknown status"
@@ -120,6 +120,20 @@ def test_attn_validation(lib):
     lm = dict(kbar=FAKE + 6 * 10**9, vbar=FAKE + 7 * 10**9)
     assert attn_call(lib, bias=float("inf"), **lm) == ERR_UNSUP
     assert attn_call(lib, bias=float("nan"), **lm) == ERR_UNSUP
+    # out or lse must not overlap the landmark means ([2, 8, 64] bf16 = 2 KiB each)
+    assert attn_call(lib, kbar=FAKE + 5 * 10**9 + 1024, vbar=FAKE + 7 * 10**9) == ERR_ALIAS
+    assert attn_call(lib, lse=FAKE + 8 * 10**9, kbar=FAKE + 6 * 10**9,
+                     vbar=FAKE + 8 * 10**9 - 64) == ERR_ALIAS
+
+
+def test_cast_validation(lib):
+    cast = lib.sparse3d_cast
+    assert cast(FAKE, -1, 1, FAKE + 10**9, NULL) == ERR_SHAPE
+    assert cast(FAKE, 16, 5, FAKE + 10**9, NULL) == ERR_UNSUP
+    assert cast(NULL, 16, 1, FAKE + 10**9, NULL) == ERR_NULL
+    assert cast(FAKE, 16, 1, NULL, NULL) == ERR_NULL
+    assert cast(FAKE, 16, 1, FAKE + 32, NULL) == ERR_ALIAS              # dst inside src
+    assert cast(NULL, 0, 1, NULL, NULL) == OK                          # nothing to do, no launch
 
 
 def test_subsample_layout_host_only(lib):

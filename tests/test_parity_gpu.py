@@ -288,9 +288,9 @@ def _full_size(name, n_tiles=48, seed=0):
     k = LY.calibrate_k(LY.device_count_fn(scores, tpf, w.anchor), w.heads * Tq, ts, Tk,
                        w.target_sparsity)
     idx, cnt = S.sparse3d_select_topk(scores, k, tpf, w.anchor)
-    out = S.sparse3d_sparse_attn_fwd(q, K, V, lay, klay, idx, cnt,
-                                     kbar=kbar if w.landmarks else None,
-                                     vbar=vbar if w.landmarks else None)
+    km = S.sparse3d_cast(kbar, q.dtype) if w.landmarks else None
+    vm = S.sparse3d_cast(vbar, q.dtype) if w.landmarks else None
+    out = S.sparse3d_sparse_attn_fwd(q, K, V, lay, klay, idx, cnt, kbar=km, vbar=vm)
     torch.cuda.synchronize()
     sp = LY.measured_sparsity(int(cnt.sum()), w.heads * Tq, ts, Tk)
     say(f"[full] {name}: k={k} sparsity={sp:.4f}")
@@ -334,3 +334,32 @@ def test_full_vggt_s256_landmarks():
 
 def test_full_vggt_s256_landmarks_subsampled():
     _full_size("vggt_s256_lm_sub2", n_tiles=16)
+
+
+def _bf16_rne_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even, NaN kept NaN (from the formats'
+    definitions: drop the low 16 bits with the usual tie-to-even carry)."""
+    b = x.astype(np.float32).view(np.uint32).astype(np.uint64)
+    r = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(x)
+    r[nan] = ((b[nan] >> 16) | 0x40).astype(np.uint16)            # quiet NaN, same sign
+    return r
+
+
+@pytest.mark.parametrize("n", [0, 1, 7, 1000003])
+def test_cast_bf16_round_to_nearest_even(n):
+    say(f"[case] cast n={n}")
+    rng = np.random.default_rng(n)
+    x = (rng.standard_normal(n) * 10.0 ** rng.integers(-30, 30, n)).astype(np.float32)
+    if n >= 7:
+        # exact ties between neighbouring bf16 values (both parities), zeros, infinities, NaN
+        x[:7] = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -0.0, np.inf, -np.inf, np.nan,
+                          3.0e38], dtype=np.float32)
+    g = S.sparse3d_cast(torch.from_numpy(x).to(dev()), torch.bfloat16)
+    got = g.view(torch.int16).cpu().numpy().view(np.uint16)
+    exp = _bf16_rne_bits(x)
+    fin = ~np.isnan(x)
+    assert np.array_equal(got[fin], exp[fin])
+    assert np.all(np.isnan(g.float().cpu().numpy()[~fin]))
+    g32 = S.sparse3d_cast(torch.from_numpy(x).to(dev()), torch.float32)
+    assert np.array_equal(g32.cpu().numpy().view(np.uint32)[fin], x.view(np.uint32)[fin])
