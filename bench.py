@@ -53,7 +53,50 @@ def parse():
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first run a plain elementwise copy of this many MiB (fp32) twice, as a "
                          "known-size reference for the HBM byte counters")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn the counter files of a FETCH_SIZE run and a WRITE_SIZE "
+                         "run (rocprofv3 --pmc, both with --copy-mb) into profiles/traffic.json")
     return ap.parse_args()
+
+
+ATTN_KERNEL = "k_attn_bf16<false, false, false>"     # the sparse bf16 attention kernel
+
+
+def write_traffic(fetch_csv, write_csv, copy_mb, workload):
+    """HBM bytes per attention launch from two counter runs.  Each counter is scaled by
+    what it reads for the plain copy of known size in the same run (the largest elementwise
+    launch: copy_mb MiB read and written)."""
+    import csv
+    from collections import defaultdict
+
+    def per_dispatch(path, counter):
+        vals, names = defaultdict(float), {}
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] == counter:
+                vals[row["Dispatch_Id"]] += float(row["Counter_Value"])
+                names[row["Dispatch_Id"]] = row["Kernel_Name"]
+        attn = [v for d, v in vals.items() if ATTN_KERNEL in names[d]]
+        copy = [v for d, v in vals.items() if "elementwise" in names[d]]
+        if not attn or not copy:
+            raise SystemExit(f"{path}: no {ATTN_KERNEL} or copy dispatch with {counter}")
+        return sum(attn) / len(attn), max(copy), len(attn)
+
+    copy_bytes = copy_mb * (1 << 20)
+    out = {"workload": workload, "kernel": ATTN_KERNEL, "attn_source_sha256": attn_source_sha256(),
+           "copy_reference_bytes": copy_bytes}
+    total = 0.0
+    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        a, c, n = per_dispatch(path, counter)
+        scale = copy_bytes / (c * 1024.0)
+        out[key] = {"counter": counter, "attn_kib_per_launch": a, "launches": n, "copy_kib": c,
+                    "scale": round(scale, 4), "bytes_per_launch": round(a * 1024.0 * scale)}
+        total += a * 1024.0 * scale
+    out["bytes_per_launch"] = round(total)
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 class Layer:
@@ -223,6 +266,9 @@ def cpu_baseline(w, inp, k, budget_s, LY):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from, args.copy_mb or 1024, args.workload)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the layer shards by "
                           "head across GPUs with no communication, so per-GPU throughput is the "
