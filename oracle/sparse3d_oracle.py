@@ -35,6 +35,13 @@ What is computed, and the passages it follows
   values are thinned on the 2-D patch grid to one token per s_h x s_w window
   while every query and every special token is kept.  ``subsample_keys`` keeps
   the top-left patch of every window.
+* AVGGT technical summary, section 2B.1: the early global layers, which exchange
+  no information between views, become attention within each frame.
+  ``frame_attend`` is that operation: every valid query over the valid keys of
+  its own frame only.
+* SAF3R (abstract) finds attention patterns heterogeneous across heads; a
+  per-head budget k_h is the knob that follows it (``select_topk`` accepts one
+  k per head).
 
 Readings adopted where the pages leave a step open
 ---------------------------------------------------
@@ -150,17 +157,22 @@ def kmax_for(tk: int, k: int, tiles_per_frame: int, anchor: int) -> int:
     return min(tk, max(k, 0) + (tiles_per_frame if anchor >= 0 else 0))
 
 
-def select_topk(scores: np.ndarray, k: int, tiles_per_frame: int, anchor: int,
+def select_topk(scores: np.ndarray, k, tiles_per_frame: int, anchor: int,
                 kmax: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
-    """All rows of ``select_tiles``: idx [H, Tq, kmax] (ascending, -1 padded), cnt [H, Tq]."""
+    """All rows of ``select_tiles``: idx [H, Tq, kmax] (ascending, -1 padded), cnt [H, Tq].
+
+    ``k`` is one budget for every head, or a sequence of H budgets (head h keeps k[h]).
+    """
     H, Tq, Tk = scores.shape
+    ks = [int(k)] * H if np.ndim(k) == 0 else [int(x) for x in k]
+    assert len(ks) == H
     if kmax is None:
-        kmax = kmax_for(Tk, k, tiles_per_frame, anchor)
+        kmax = kmax_for(Tk, max(ks), tiles_per_frame, anchor)
     idx = np.full((H, Tq, kmax), -1, dtype=np.int32)
     cnt = np.zeros((H, Tq), dtype=np.int32)
     for h in range(H):
         for t in range(Tq):
-            sel = select_tiles(scores[h, t], k, tiles_per_frame, anchor)
+            sel = select_tiles(scores[h, t], ks[h], tiles_per_frame, anchor)
             cnt[h, t] = len(sel)
             idx[h, t, : len(sel)] = sel
     return idx, cnt
@@ -244,6 +256,26 @@ def dense_attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, qlay: Layout, klay
         for c in range(0, rows.size, chunk):
             r = rows[c:c + chunk]
             o, l = _softmax_rows(scale * (Q[h, r].astype(np.float64) @ Kh.T), Vh)
+            O[h, r] = o
+            lse[h, r] = l
+    return O, lse
+
+
+def frame_attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, qlay: Layout, klay: Layout,
+                 scale: float, heads: Optional[Sequence[int]] = None,
+                 frames: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Exact softmax attention of every valid query over the valid keys (specials in
+    place) of its own frame; no key of another frame takes part."""
+    assert qlay.frames == klay.frames
+    H, Lq, d = Q.shape
+    O = np.zeros((H, Lq, d))
+    lse = np.zeros((H, Lq))
+    for h in (range(H) if heads is None else heads):
+        for s in (range(qlay.frames) if frames is None else frames):
+            r = s * qlay.stride + np.arange(qlay.tokens)
+            J = s * klay.stride + np.arange(klay.tokens)
+            o, l = _softmax_rows(scale * (Q[h, r].astype(np.float64) @ K[h, J].astype(np.float64).T),
+                                 V[h, J].astype(np.float64))
             O[h, r] = o
             lse[h, r] = l
     return O, lse

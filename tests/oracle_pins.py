@@ -413,6 +413,72 @@ def pin_hand_worked(o):
             assert np.allclose(O[0, qv, 1], 1.0, rtol=0, atol=1e-12)
 
 
+# --------------------------------------------------------------------------- per-head budgets
+def pin_select_per_head(o):
+    """Head h of a per-head selection is the brute-force top-k_h of its rows (plus the
+    anchor frame), and the table is sized for the largest budget."""
+    rng = np.random.default_rng(23)
+    for trial in range(12):
+        H, Tq, Tk = int(rng.integers(2, 5)), 3, int(rng.integers(3, 10))
+        tpf = [t for t in (1, Tk) if Tk % t == 0][int(rng.integers(0, 2))]
+        anchor = int(rng.integers(-1, Tk // tpf))
+        sc = rng.integers(-3, 4, size=(H, Tq, Tk)).astype(np.float64) * 0.5
+        ks = rng.integers(0, Tk + 1, size=H)
+        idx, cnt = o.select_topk(sc, ks, tpf, anchor)
+        forced = set(range(anchor * tpf, (anchor + 1) * tpf)) if anchor >= 0 else set()
+        assert idx.shape[2] == min(Tk, int(ks.max()) + (tpf if anchor >= 0 else 0))
+        for h in range(H):
+            for t in range(Tq):
+                want = (set(_brute_topk(sc[h, t], int(ks[h])).tolist()) if ks[h] else set()) | forced
+                assert idx[h, t, :cnt[h, t]].tolist() == sorted(want), (h, t, ks, anchor)
+                assert np.all(idx[h, t, cnt[h, t]:] == -1)
+
+
+# --------------------------------------------------------------------------- frame attention
+def _sdpa_block_diagonal(Q, K, V, qlay, klay, scale):
+    """Attention through torch's routine with a mask written out from frame numbers:
+    query row r (frame r // Pq) may see key row c iff c is in the same frame and valid."""
+    qf = np.arange(Q.shape[1]) // qlay.stride
+    kf = np.arange(K.shape[1]) // klay.stride
+    kvalid = (np.arange(K.shape[1]) % klay.stride) < klay.tokens
+    allow = (qf[:, None] == kf[None, :]) & kvalid[None, :]
+    t = lambda x: torch.from_numpy(np.nan_to_num(x)).double()
+    out = torch.nn.functional.scaled_dot_product_attention(
+        t(Q), t(K), t(V), attn_mask=torch.from_numpy(allow), scale=scale)
+    logits = scale * np.einsum("hqd,hkd->hqk", np.nan_to_num(Q), np.nan_to_num(K))
+    lse = scipy.special.logsumexp(np.where(allow[None], logits, -np.inf), axis=2)
+    return out.numpy(), lse
+
+
+def pin_frame_attention(o):
+    for (S, N, P, nsp, Pk, Nk) in [(3, 60, 64, 5, 64, 60), (2, 100, 128, 2, 64, 50), (4, 10, 16, 3, 16, 10)]:
+        Q, _, _ = _rand_inputs(S, N, P, nsp, H=2, d=16, seed=N)
+        _, K, V = _rand_inputs(S, Nk, Pk, nsp, H=2, d=16, seed=N + 1)
+        qlay, klay = o.Layout(S, N, P, nsp), o.Layout(S, Nk, Pk, nsp)
+        O, lse = o.frame_attend(Q, K, V, qlay, klay, 0.25)
+        ref, rlse = _sdpa_block_diagonal(Q, K, V, qlay, klay, 0.25)
+        qv = (np.arange(S * P) % P) < N
+        assert np.allclose(O[:, qv], ref[:, qv], rtol=0, atol=1e-12)
+        assert np.allclose(lse[:, qv], rlse[:, qv], rtol=0, atol=1e-12)
+        assert np.all(O[:, ~qv] == 0) and np.all(lse[:, ~qv] == 0)
+    # one frame: frame attention is dense attention
+    Q, K, V = _rand_inputs(1, 50, 64, 4, H=2, d=8, seed=3)
+    lay = o.Layout(1, 50, 64, 4)
+    a, la = o.frame_attend(Q, K, V, lay, lay, 0.3)
+    b, lb = o.dense_attend(Q, K, V, lay, lay, 0.3)
+    assert np.allclose(a, b, rtol=0, atol=1e-12) and np.allclose(la, lb, rtol=0, atol=1e-12)
+    # another frame's keys and values never matter
+    Q, K, V = _rand_inputs(3, 40, 64, 2, H=1, d=8, seed=4)
+    lay = o.Layout(3, 40, 64, 2)
+    a, _ = o.frame_attend(Q, K, V, lay, lay, 0.3)
+    K2, V2 = K.copy(), V.copy()
+    K2[:, 64:128] += 5.0
+    V2[:, 64:128] -= 3.0
+    b, _ = o.frame_attend(Q, K2, V2, lay, lay, 0.3)
+    assert np.array_equal(a[:, :64], b[:, :64]) and np.array_equal(a[:, 128:], b[:, 128:])
+    assert not np.allclose(a[:, 64:104], b[:, 64:104])
+
+
 ALL_PINS = [
     pin_block_mean_identity, pin_tile_constant_pool, pin_symmetric_scores,
     pin_select_brute_force, pin_select_invariants,
@@ -420,4 +486,5 @@ ALL_PINS = [
     pin_frame_permutation, pin_query_tiles_independent,
     pin_landmarks_exact_on_constant_tiles, pin_landmarks_vanish_when_all_selected,
     pin_empty_key_set, pin_subsample, pin_hand_worked,
+    pin_select_per_head, pin_frame_attention,
 ]

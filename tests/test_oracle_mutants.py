@@ -32,6 +32,12 @@ MUTANTS = {
     "subsample_odd_rows": ("for y in range(0, gh, window)", "for y in range(1, gh, window)"),
     "empty_tiles_not_masked": ("sig[:, :, kcount == 0] = -np.inf", "pass"),
     "mean_over_tile_size": ("mean[h, nz] = s[nz] / count[nz, None]", "mean[h, nz] = s[nz] / Xh.shape[1]"),
+    "per_head_budget_ignored": ("select_tiles(scores[h, t], ks[h], tiles_per_frame, anchor)",
+                                "select_tiles(scores[h, t], ks[0], tiles_per_frame, anchor)"),
+    "frame_keys_from_next_frame": ("J = s * klay.stride + np.arange(klay.tokens)",
+                                   "J = ((s + 1) % klay.frames) * klay.stride + np.arange(klay.tokens)"),
+    "frame_keys_skip_specials": ("J = s * klay.stride + np.arange(klay.tokens)",
+                                 "J = s * klay.stride + np.arange(klay.specials, klay.tokens)"),
 }
 
 
