@@ -201,6 +201,20 @@ def attn_source_sha256() -> str:
     return h.hexdigest()
 
 
+def time_frame(torch, S, q, v, lay, reps):
+    """Mean time of the frame-attention call (every query over its own frame)."""
+    S.sparse3d_frame_attn_fwd(q, q, v, lay)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(st)
+    for _ in range(reps):
+        S.sparse3d_frame_attn_fwd(q, q, v, lay)
+    b.record(st)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def traffic_entry():
     """Per-launch HBM bytes of the attention kernel from committed counter runs, or None
     when the kernel source changed after the counters were taken."""
@@ -348,6 +362,11 @@ def main():
         dflops = LY.pair_flops() * w.heads * L.Tq * (w.rows // 64)
         res["dense"] = {"ms": round(dms, 3), "tflops": round(dflops / (dms * 1e-3) / 1e12, 2),
                         "speedup_layer_vs_dense": round(dms / r["ms_per_step"], 2)}
+    if not args.no_dense:
+        # frame attention (early layers, every query over its own frame) on the same inputs
+        fms = time_frame(torch, S, q, v, w.layout, 5)
+        fflops = LY.pair_flops() * w.heads * L.Tq * (w.stride // 64)
+        res["frame_attention"] = {"ms": round(fms, 4), "tflops": round(fflops / (fms * 1e-3) / 1e12, 2)}
     if not args.no_gate and not args.no_dense and w.name == "vggt_s128":
         w90 = synth.WORKLOADS["vggt_s128_90"]
         L90 = Layer(S, LY, w90, q, v)

@@ -2,6 +2,9 @@
 // (validate.cpp, no HIP), then enqueue the kernels on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "launch.h"
 #include "sparse3d.h"
 #include "validate.h"
@@ -51,7 +54,26 @@ int sparse3d_select_topk(const float* scores, int32_t heads, int32_t q_tiles, in
     const int st = validate_select_topk(scores, heads, q_tiles, k_tiles, k, tiles_per_frame,
                                         anchor_frame, idx, cnt, kmax);
     if (st != SPARSE3D_OK) return st;
-    S3D_HIP(launch_select_topk(scores, heads, q_tiles, k_tiles, k, tiles_per_frame, anchor_frame,
+    const std::vector<int32_t> ks(size_t(heads), k);
+    S3D_HIP(launch_select_topk(scores, heads, q_tiles, k_tiles, ks.data(), tiles_per_frame, anchor_frame,
+                               idx, cnt, kmax, static_cast<hipStream_t>(stream)));
+    return SPARSE3D_OK;
+}
+
+int sparse3d_select_topk_per_head(const float* scores, int32_t heads, int32_t q_tiles, int32_t k_tiles,
+                                  const int32_t* k_heads, int32_t tiles_per_frame, int32_t anchor_frame,
+                                  int32_t* idx, int32_t* cnt, int32_t kmax, void* stream) {
+    if (!k_heads) return SPARSE3D_ERR_NULL;
+    if (heads < 1) return SPARSE3D_ERR_SHAPE;
+    int32_t kbig = 0;
+    for (int32_t h = 0; h < heads; ++h) {
+        if (k_heads[h] < 0) return SPARSE3D_ERR_SHAPE;
+        kbig = std::max(kbig, k_heads[h]);
+    }
+    const int st = validate_select_topk(scores, heads, q_tiles, k_tiles, kbig, tiles_per_frame,
+                                        anchor_frame, idx, cnt, kmax);
+    if (st != SPARSE3D_OK) return st;
+    S3D_HIP(launch_select_topk(scores, heads, q_tiles, k_tiles, k_heads, tiles_per_frame, anchor_frame,
                                idx, cnt, kmax, static_cast<hipStream_t>(stream)));
     return SPARSE3D_OK;
 }
@@ -68,7 +90,7 @@ int sparse3d_sparse_attn_fwd(const void* q, const void* k, const void* v, sparse
     if (st != SPARSE3D_OK) return st;
     const int sp = check_logit_params(scale, kbar ? landmark_bias : 0.f);
     if (sp != SPARSE3D_OK) return sp;
-    AttnArgs a{q, k, v, dtype, out_dtype, heads, to_lay(*qlay), to_lay(*klay), false, idx, cnt,
+    AttnArgs a{q, k, v, dtype, out_dtype, heads, to_lay(*qlay), to_lay(*klay), false, false, idx, cnt,
                kmax, kbar, vbar, landmark_bias, scale, out, lse};
     S3D_HIP(launch_attn(a, static_cast<hipStream_t>(stream)));
     return SPARSE3D_OK;
@@ -91,7 +113,22 @@ int sparse3d_dense_attn_fwd(const void* q, const void* k, const void* v, sparse3
     if (st != SPARSE3D_OK) return st;
     const int sp = check_logit_params(scale, 0.f);
     if (sp != SPARSE3D_OK) return sp;
-    AttnArgs a{q, k, v, dtype, out_dtype, heads, to_lay(*qlay), to_lay(*klay), true, nullptr,
+    AttnArgs a{q, k, v, dtype, out_dtype, heads, to_lay(*qlay), to_lay(*klay), true, false, nullptr,
+               nullptr, 0, nullptr, nullptr, 0.f, scale, out, lse};
+    S3D_HIP(launch_attn(a, static_cast<hipStream_t>(stream)));
+    return SPARSE3D_OK;
+}
+
+int sparse3d_frame_attn_fwd(const void* q, const void* k, const void* v, sparse3d_dtype dtype,
+                            int32_t heads, int32_t head_dim, const sparse3d_layout* qlay,
+                            const sparse3d_layout* klay, float scale, void* out,
+                            sparse3d_dtype out_dtype, float* lse, void* stream) {
+    const int st = validate_attn(false, q, k, v, dtype, heads, head_dim, kTile, qlay, klay, nullptr,
+                                 nullptr, 0, nullptr, nullptr, out, out_dtype, lse);
+    if (st != SPARSE3D_OK) return st;
+    const int sp = check_logit_params(scale, 0.f);
+    if (sp != SPARSE3D_OK) return sp;
+    AttnArgs a{q, k, v, dtype, out_dtype, heads, to_lay(*qlay), to_lay(*klay), true, true, nullptr,
                nullptr, 0, nullptr, nullptr, 0.f, scale, out, lse};
     S3D_HIP(launch_attn(a, static_cast<hipStream_t>(stream)));
     return SPARSE3D_OK;

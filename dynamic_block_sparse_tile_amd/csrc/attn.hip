@@ -32,7 +32,7 @@ __global__ __launch_bounds__(128, 2) void k_attn(AttnDev p) {
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qc = lane & 31, g = lane >> 5;
     const int tpfq = p.ql.P / TILE;
     int h, tq;
-    attn_work_item(blockIdx.x, gridDim.x, p.ql.S, tpfq, gridDim.x / p.Tq, h, tq);
+    attn_work_item(blockIdx.x, gridDim.x, p.ql.S, tpfq, gridDim.x / p.Tq, h, tq, !p.frame);
     const int Lq = p.ql.S * p.ql.P, Lk = p.kl.S * p.kl.P;
     const int qrow = tq * TILE + w * 32 + qc;
     const bool qvalid = (tq % tpfq) * TILE + w * 32 + qc < p.ql.N;
@@ -61,11 +61,12 @@ __global__ __launch_bounds__(128, 2) void k_attn(AttnDev p) {
         }
     }
 
-    int c = 0;
+    int c = 0, t0 = 0;
     const int32_t* myidx = nullptr;
     int ntiles;
     if (DENSE) {
-        ntiles = p.Tk;
+        ntiles = p.frame ? p.kl.P / TILE : p.Tk;
+        t0 = p.frame ? (tq / tpfq) * (p.kl.P / TILE) : 0;
     } else {
         c = min(max(p.cnt[(size_t)h * p.Tq + tq], 0), p.kmax);
         myidx = p.idx + ((size_t)h * p.Tq + tq) * p.kmax;
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(128, 2) void k_attn(AttnDev p) {
     TileDesc nxt;
 
     auto fetch = [&](int it) {
-        nxt = describe<DENSE, LM, false>(p, it, c, myidx, nullptr, s_lm);
+        nxt = describe<DENSE, LM, false>(p, it, c, myidx, nullptr, s_lm, 0, t0);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             const int r = (x >> 1) * 32 + 2 * rp + (x & 1);
@@ -331,6 +332,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     d.Tq = a.ql.S * a.ql.P / TILE;
     d.Tk = a.kl.S * a.kl.P / TILE;
     d.Ts = a.dense ? 0 : (a.kl.nsp * a.kl.S + TILE - 1) / TILE;
+    d.frame = a.frame ? 1 : 0;
     const bool lm = !a.dense && a.kbar != nullptr;
     d.nlm = lm ? (d.Tk + TILE - 1) / TILE : 0;
     d.idx = a.idx;

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
     const int qc = lane & 31, g = lane >> 5;
     const int tpfq = p.ql.P / TILE;
     int h, tq;
-    attn_work_item(blockIdx.x, gridDim.x, p.ql.S, tpfq, gridDim.x / p.Tq, h, tq);
+    attn_work_item(blockIdx.x, gridDim.x, p.ql.S, tpfq, gridDim.x / p.Tq, h, tq, !p.frame);
     const int Lq = p.ql.S * p.ql.P, Lk = p.kl.S * p.kl.P;
     const int qrow = tq * TILE + w * 32 + qc;
     const bool qvalid = (tq % tpfq) * TILE + w * 32 + qc < p.ql.N;
@@ -108,11 +108,12 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
     // the tile loop waits on all vector-memory traffic, the next tile's loads included
     __builtin_amdgcn_s_waitcnt(0);
 
-    int c = 0, rot = 0;
+    int c = 0, rot = 0, t0 = 0;
     const int32_t* myidx = nullptr;
     int ntiles;
     if (DENSE) {
-        ntiles = p.Tk;
+        ntiles = p.frame ? p.kl.P / TILE : p.Tk;
+        t0 = p.frame ? (tq / tpfq) * (p.kl.P / TILE) : 0;
     } else {
         c = min(max(p.cnt[(size_t)h * p.Tq + tq], 0), p.kmax);
         myidx = p.idx + ((size_t)h * p.Tq + tq) * p.kmax;
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
         soff[j] = srow[j] * 128 + swz(srow[j], sslot) * 16;
     }
 
-    auto desc = [&](int it) { return describe<DENSE, LM, !DENSE>(p, it, c, myidx, s_idx, s_lm, rot); };
+    auto desc = [&](int it) { return describe<DENSE, LM, !DENSE>(p, it, c, myidx, s_idx, s_lm, rot, t0); };
     // Staging plan of one matrix of tile d: this wave's four row blocks (rows 32w + 8j .. +8)
     // load 16 bytes per lane from byte offset voff[j] + base of buffer rs (mtx 0 = K or the
     // key means, 1 = V or the value means); rows that are not keys use an offset past the

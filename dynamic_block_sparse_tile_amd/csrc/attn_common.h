@@ -17,6 +17,7 @@ struct AttnDev {
     int kmax;
     const void* kbar;   // landmark means [heads, Tk, 64], operand dtype
     const void* vbar;
+    int frame;          // dense over the query's own frame only (frame attention)
     float lm_bias_l2;   // landmark bias in base-2 logit units
     float scale_l2;     // scale * log2(e)
     void* out;
@@ -61,14 +62,17 @@ constexpr int IDX_LDS_MAX = 8000;
 
 // IDX_LDS: the list is read from its LDS copy (bf16 kernel) rather than from global memory.
 // The selected tiles are visited starting at list position `rot` (and wrapping round).
+// DENSE: the list is every key tile from t0 on (t0 = first tile of the frame in frame
+// attention, 0 otherwise).
 template <bool DENSE, bool LM, bool IDX_LDS>
 __device__ __forceinline__ TileDesc describe(const AttnDev& p, int it, int c, const int32_t* myidx,
-                                             const int32_t* s_idx, const uint32_t* s_lm, int rot = 0) {
+                                             const int32_t* s_idx, const uint32_t* s_lm, int rot = 0,
+                                             int t0 = 0) {
     TileDesc d;
     if (DENSE) {
         d.kind = KIND_REG;
-        d.t = it;
-        d.mask = range_mask(0, valid_rows(p.kl, it));
+        d.t = t0 + it;
+        d.mask = range_mask(0, valid_rows(p.kl, t0 + it));
         return d;
     }
     if (it < p.Ts) {

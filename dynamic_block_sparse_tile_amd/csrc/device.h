@@ -59,9 +59,17 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
 // one group runs per XCD (its key tiles share that XCD's L2) and all XCDs work on
 // neighbouring groups of the same head (whose K and V then share the last-level cache),
 // instead of each XCD streaming a different head.
+// (Frame attention reads only the query's own frame, so there the plain order, frame by
+// frame, is the one that shares key tiles: `grouped` = false.)
 __device__ __forceinline__ void attn_work_item(int bid, int nblocks, int S, int tpf, int heads,
-                                               int& h, int& tq) {
+                                               int& h, int& tq, bool grouped = true) {
     const int logical = xcd_remap(bid, nblocks);
+    if (!grouped) {
+        const int tqs = S * tpf;
+        h = logical / tqs;
+        tq = logical - h * tqs;
+        return;
+    }
     int rank = logical / S;
     const int s = logical - rank * S;
     int G = rank;

@@ -19,7 +19,8 @@ hipError_t launch_tile_pool(const void* x, int dtype, int heads, LayH lay, bool 
                             float* out, hipStream_t st);
 hipError_t launch_tile_scores(const float* qbar, const float* kbar, int heads, LayH ql, LayH kl,
                               float scale, float* scores, hipStream_t st);
-hipError_t launch_select_topk(const float* scores, int heads, int tq, int tk, int k, int tpf,
+// k_heads: host array of one budget per head
+hipError_t launch_select_topk(const float* scores, int heads, int tq, int tk, const int32_t* k_heads, int tpf,
                               int anchor, int32_t* idx, int32_t* cnt, int kmax, hipStream_t st);
 
 struct AttnArgs {
@@ -30,6 +31,7 @@ struct AttnArgs {
     int heads;
     LayH ql, kl;
     bool dense;
+    bool frame;         // dense over the query's own frame only (needs dense)
     const int32_t* idx;
     const int32_t* cnt;
     int kmax;

@@ -11,6 +11,8 @@
 // equal to T, plus every anchor-frame tile, and the selection is compacted in
 // ascending tile order.  Integer-only after the key transform: bit-exact and
 // deterministic for a given score row.
+#include <algorithm>
+
 #include "device.h"
 #include "launch.h"
 
@@ -61,8 +63,14 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
     return v;
 }
 
+// Budgets of up to TK_HEAD_CHUNK heads, passed by value with the launch.
+constexpr int TK_HEAD_CHUNK = 64;
+struct KBudget {
+    int32_t k[TK_HEAD_CHUNK];
+};
+
 __global__ __launch_bounds__(TK_THREADS) void k_select_topk(const float* __restrict__ scores, int Tk,
-                                                            int k, int tpf, int anchor,
+                                                            int Tq, KBudget kb, int tpf, int anchor,
                                                             int32_t* __restrict__ idx,
                                                             int32_t* __restrict__ cnt, int kmax) {
     extern __shared__ uint32_t s_keys[];           // Tk keys
@@ -74,6 +82,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_select_topk(const float* __restr
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t row = blockIdx.x;
+    const int k = kb.k[blockIdx.x / Tq];           // this row's head budget
     const float* src = scores + row * (size_t)Tk;
 
     uint32_t kmin = 0xffffffffu, kmaxk = 0u;
@@ -200,13 +209,21 @@ __global__ __launch_bounds__(TK_THREADS) void k_select_topk(const float* __restr
     if (tid == 0) cnt[row] = min(total, kmax);
 }
 
-hipError_t launch_select_topk(const float* scores, int heads, int tq, int tk, int k, int tpf,
-                              int anchor, int32_t* idx, int32_t* cnt, int kmax, hipStream_t st) {
-    const unsigned rows = (unsigned)heads * (unsigned)tq;
+hipError_t launch_select_topk(const float* scores, int heads, int tq, int tk, const int32_t* k_heads,
+                              int tpf, int anchor, int32_t* idx, int32_t* cnt, int kmax, hipStream_t st) {
     const size_t shm = (size_t)tk * sizeof(uint32_t);
-    hipLaunchKernelGGL(k_select_topk, dim3(rows), dim3(TK_THREADS), shm, st, scores, tk, k, tpf,
-                       anchor, idx, cnt, kmax);
-    return hipGetLastError();
+    for (int h0 = 0; h0 < heads; h0 += TK_HEAD_CHUNK) {
+        const int nh = std::min(TK_HEAD_CHUNK, heads - h0);
+        KBudget kb{};
+        for (int i = 0; i < nh; ++i) kb.k[i] = k_heads[h0 + i];
+        const size_t r0 = (size_t)h0 * tq;
+        hipLaunchKernelGGL(k_select_topk, dim3((unsigned)nh * (unsigned)tq), dim3(TK_THREADS), shm, st,
+                           scores + r0 * tk, tk, tq, kb, tpf, anchor, kmax > 0 ? idx + r0 * kmax : idx,
+                           cnt + r0, kmax);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace s3d

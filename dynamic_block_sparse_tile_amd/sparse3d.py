@@ -21,7 +21,7 @@ __all__ = [
     "Sparse3dError", "library", "sparse3d_abi_version", "sparse3d_status_string",
     "sparse3d_tile_scores", "sparse3d_select_topk", "sparse3d_sparse_attn_fwd",
     "sparse3d_dense_attn_fwd", "sparse3d_subsample_layout", "sparse3d_grid_subsample_kv",
-    "sparse3d_cast",
+    "sparse3d_cast", "sparse3d_select_topk_per_head", "sparse3d_frame_attn_fwd",
     "kmax_for", "LN64",
 ]
 
@@ -63,6 +63,10 @@ _SIGS = {
     "sparse3d_grid_subsample_kv": ([_vp, _vp, ctypes.c_int, _i32, _i32, _LP, _i32, _i32, _i32,
                                     _vp, _vp, _LP, _vp], ctypes.c_int),
     "sparse3d_cast": ([_vp, ctypes.c_int64, ctypes.c_int, _vp, _vp], ctypes.c_int),
+    "sparse3d_select_topk_per_head": ([_vp, _i32, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _i32, _vp],
+                                      ctypes.c_int),
+    "sparse3d_frame_attn_fwd": ([_vp, _vp, _vp, ctypes.c_int, _i32, _i32, _LP, _LP, _f32, _vp,
+                                 ctypes.c_int, _vp, _vp], ctypes.c_int),
 }
 
 
@@ -171,6 +175,24 @@ def sparse3d_select_topk(scores: torch.Tensor, k: int, tiles_per_frame: int, anc
     return idx, cnt
 
 
+def sparse3d_select_topk_per_head(scores: torch.Tensor, ks: Sequence[int], tiles_per_frame: int,
+                                  anchor_frame: int = 0, kmax: Optional[int] = None):
+    """Top-k_h key tiles per query tile of head h, united with the anchor frame."""
+    _dev(scores, "scores")
+    H, Tq, Tk = scores.shape
+    ks = [int(x) for x in ks]
+    if len(ks) != H:
+        raise ValueError(f"need one budget per head ({H}), got {len(ks)}")
+    kmax = kmax_for(Tk, max(ks), tiles_per_frame, anchor_frame) if kmax is None else kmax
+    idx = torch.empty((H, Tq, max(kmax, 0)), device=scores.device, dtype=torch.int32)
+    cnt = torch.empty((H, Tq), device=scores.device, dtype=torch.int32)
+    karr = (ctypes.c_int32 * H)(*ks)
+    _check(library().sparse3d_select_topk_per_head(
+        _ptr(scores), H, Tq, Tk, ctypes.cast(karr, ctypes.c_void_p), tiles_per_frame, anchor_frame,
+        _ptr(idx) if kmax > 0 else None, _ptr(cnt), kmax, _stream(scores)))
+    return idx, cnt
+
+
 def _out_dtype(q, out_dtype):
     od = q.dtype if out_dtype is None else out_dtype
     return od, (BF16 if od == torch.bfloat16 else F32)
@@ -228,6 +250,24 @@ def sparse3d_dense_attn_fwd(q, k, v, qlay, klay=None, scale: Optional[float] = N
     lse = torch.empty(q.shape[:2], device=q.device, dtype=torch.float32) if return_lse else None
     ql, kl = _lay(qlay), _lay(klay)
     _check(library().sparse3d_dense_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), H, q.shape[2], ctypes.byref(ql), ctypes.byref(kl),
+        scale, _ptr(out), odc, _ptr(lse), _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+def sparse3d_frame_attn_fwd(q, k, v, qlay, klay=None, scale: Optional[float] = None,
+                            out_dtype=None, return_lse: bool = False):
+    """Attention of every valid query over the valid keys of its own frame only."""
+    klay = qlay if klay is None else klay
+    for x, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(x, n)
+    H = q.shape[0]
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else scale
+    od, odc = _out_dtype(q, out_dtype)
+    out = torch.empty(q.shape, device=q.device, dtype=od)
+    lse = torch.empty(q.shape[:2], device=q.device, dtype=torch.float32) if return_lse else None
+    ql, kl = _lay(qlay), _lay(klay)
+    _check(library().sparse3d_frame_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _dt(q), H, q.shape[2], ctypes.byref(ql), ctypes.byref(kl),
         scale, _ptr(out), odc, _ptr(lse), _stream(q)))
     return (out, lse) if return_lse else out

@@ -104,6 +104,16 @@ int sparse3d_select_topk(const float* scores, int32_t heads, int32_t q_tiles, in
                          int32_t* idx, int32_t* cnt, int32_t kmax, void* stream);
 
 /*
+ * sparse3d_select_topk with one budget per head: head h keeps its k_heads[h] best tiles
+ * (SAF3R abstract: attention patterns differ across heads, so their budgets may too).
+ * k_heads is a HOST array of `heads` values >= 0 (read during the call, not kept);
+ * kmax must be >= min(Tk, max_h k_heads[h] + anchor tiles).  Everything else as above.
+ */
+int sparse3d_select_topk_per_head(const float* scores, int32_t heads, int32_t q_tiles, int32_t k_tiles,
+                                  const int32_t* k_heads, int32_t tiles_per_frame, int32_t anchor_frame,
+                                  int32_t* idx, int32_t* cnt, int32_t kmax, void* stream);
+
+/*
  * Exact softmax attention of each query tile over its selected tiles (Zebra3D abstract:
  * tile-sparse attention with landmark summaries of unselected context; EPFL figure
  * "Full vs sparse global attention": O(SNK) work).
@@ -140,6 +150,20 @@ int sparse3d_sparse_attn_fwd(const void* q, const void* k, const void* v, sparse
  * numerics as sparse3d_sparse_attn_fwd; it is the library's own dense baseline.
  */
 int sparse3d_dense_attn_fwd(const void* q, const void* k, const void* v, sparse3d_dtype dtype,
+                            int32_t heads, int32_t head_dim,
+                            const sparse3d_layout* qlay, const sparse3d_layout* klay,
+                            float scale, void* out, sparse3d_dtype out_dtype, float* lse,
+                            void* stream);
+
+/*
+ * Frame attention: every valid query attends the valid key rows (specials in place) of its
+ * OWN frame only, the per-view attention that replaces the early global layers (AVGGT
+ * technical summary, section 2B.1: those layers exchange nothing between views, so the
+ * O((NL)^2) cost drops to O(NL^2)).  qlay and klay must have the same number of frames
+ * (keys may use another layout, e.g. the subsampled one).  Same tensor conventions,
+ * outputs, numerics and errors as sparse3d_dense_attn_fwd.
+ */
+int sparse3d_frame_attn_fwd(const void* q, const void* k, const void* v, sparse3d_dtype dtype,
                             int32_t heads, int32_t head_dim,
                             const sparse3d_layout* qlay, const sparse3d_layout* klay,
                             float scale, void* out, sparse3d_dtype out_dtype, float* lse,

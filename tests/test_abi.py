@@ -126,6 +126,30 @@ def test_attn_validation(lib):
                      vbar=FAKE + 8 * 10**9 - 64) == ERR_ALIAS
 
 
+def test_per_head_select_validation(lib):
+    def call(ks, kmax=8, anchor=0, tpf=4, k_ptr=None):
+        arr = (ctypes.c_int32 * len(ks))(*ks)
+        return lib.sparse3d_select_topk_per_head(FAKE, len(ks), 8, 16, k_ptr if k_ptr is not None else
+                                                 ctypes.cast(arr, ctypes.c_void_p), tpf, anchor,
+                                                 FAKE + 10**9, FAKE + 2 * 10**9, kmax, NULL)
+    assert lib.sparse3d_select_topk_per_head(FAKE, 2, 8, 8, NULL, 4, 0, FAKE + 10**9,
+                                             FAKE + 2 * 10**9, 8, NULL) == ERR_NULL
+    assert call([2, -1]) == ERR_SHAPE                          # a negative budget
+    assert call([2, 5], kmax=8) == ERR_SHAPE                   # largest budget 5 + 4 anchor tiles > 8
+    assert call([2, 4], kmax=7) == ERR_SHAPE
+    assert call([], kmax=8) == ERR_SHAPE                       # no heads
+    assert call([1, 2], anchor=4) == ERR_SHAPE                 # only 4 frames of 4 tiles
+
+
+def test_frame_attn_validation(lib):
+    fa = lib.sparse3d_frame_attn_fwd
+    assert fa(FAKE, FAKE, NULL, 1, 2, 64, L(), L(), 0.1, FAKE + 10**9, 1, NULL, NULL) == ERR_NULL
+    assert fa(FAKE, FAKE, FAKE, 1, 2, 64, L(), L(f=3), 0.1, FAKE + 10**9, 1, NULL, NULL) == ERR_SHAPE
+    assert fa(FAKE, FAKE, FAKE, 1, 2, 32, L(), L(), 0.1, FAKE + 10**9, 1, NULL, NULL) == ERR_UNSUP
+    assert fa(FAKE, FAKE, FAKE, 1, 2, 64, L(), L(), 0.0, FAKE + 10**9, 1, NULL, NULL) == ERR_UNSUP
+    assert fa(FAKE, FAKE, FAKE, 1, 2, 64, L(), L(), 0.1, FAKE + 64, 1, NULL, NULL) == ERR_ALIAS
+
+
 def test_cast_validation(lib):
     cast = lib.sparse3d_cast
     assert cast(FAKE, -1, 1, FAKE + 10**9, NULL) == ERR_SHAPE

@@ -363,3 +363,102 @@ def test_cast_bf16_round_to_nearest_even(n):
     assert np.all(np.isnan(g.float().cpu().numpy()[~fin]))
     g32 = S.sparse3d_cast(torch.from_numpy(x).to(dev()), torch.float32)
     assert np.array_equal(g32.cpu().numpy().view(np.uint32)[fin], x.view(np.uint32)[fin])
+
+
+# --------------------------------------------------------------------------- per-head budgets
+def test_per_head_budgets_selection_and_attention():
+    w = synth.WORKLOADS["vggt_s8"]
+    say("[case] per-head budgets vggt_s8")
+    inp = synth.make_inputs(w, seed=3)
+    q, v = to_dev(inp.q, tdt(w)), to_dev(inp.v, tdt(w))
+    lay = w.layout
+    tpf = lay[2] // 64
+    ks = [0, 1, 5, 18, 40, 175, 176, 300, 3, 9, 18, 27, 36, 45, 54, 63][: w.heads]
+    _, _, _, sc = S.sparse3d_tile_scores(q, q, lay)
+    idx, cnt = S.sparse3d_select_topk_per_head(sc, ks, tpf, w.anchor)
+    torch.cuda.synchronize()
+    ref = oracle_pool_scores(inp, oracle.Layout(*lay), oracle.Layout(*lay))
+    g_sc, g_idx, g_cnt = sc.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
+    Tq = g_sc.shape[1]
+    assert g_idx.shape[2] == oracle.kmax_for(g_sc.shape[2], max(ks), tpf, w.anchor)
+    for h, kh in enumerate(ks):
+        check_selection(g_sc, g_idx, g_cnt, ref["scores"], kh, tpf, w.anchor,
+                        rows=[(h, t) for t in range(Tq)])
+    # a uniform budget through the per-head entry equals the single-budget entry
+    i1, c1 = S.sparse3d_select_topk_per_head(sc, [18] * w.heads, tpf, w.anchor)
+    i2, c2 = S.sparse3d_select_topk(sc, 18, tpf, w.anchor)
+    assert torch.equal(i1, i2) and torch.equal(c1, c2)
+    # attention under the per-head selection
+    out, lse = S.sparse3d_sparse_attn_fwd(q, q, v, lay, lay, idx, cnt, out_dtype=torch.float32,
+                                          return_lse=True)
+    ol = oracle.Layout(*lay)
+    pairs = sample_tiles(w.heads, Tq, 40, seed=5)
+    rO, rl = oracle.sparse_attend(inp.q, inp.k, inp.v, ol, ol, 64, g_idx, g_cnt, 0.125,
+                                  query_tiles=sorted({t for _, t in pairs}))
+    compare_outputs(out.cpu().numpy(), rO, pairs, tol=TOL["bf16"], g_lse=lse.cpu().numpy(),
+                    ref_lse=rl, lse_tol=LSE_TOL_BF16)
+
+
+# --------------------------------------------------------------------------- frame attention
+def _frame_case(w, seed=0, klay=None, K=None, V=None, frames=None, out_f32=True):
+    inp = synth.make_inputs(w, seed=seed)
+    dt = tdt(w)
+    lay = w.layout
+    klay = lay if klay is None else klay
+    Kn = inp.k if K is None else K
+    Vn = inp.v if V is None else V
+    q, k, v = to_dev(inp.q, dt), to_dev(Kn, dt), to_dev(Vn, dt)
+    out, lse = S.sparse3d_frame_attn_fwd(q, k, v, lay, klay, return_lse=True,
+                                         out_dtype=torch.float32 if out_f32 else None)
+    torch.cuda.synchronize()
+    ref, rl = oracle.frame_attend(inp.q, Kn, Vn, oracle.Layout(*lay), oracle.Layout(*klay), 0.125,
+                                  frames=frames)
+    return out.float().cpu().numpy(), lse.cpu().numpy(), ref, rl, lay
+
+
+def _frame_rows(lay, frames):
+    S_, N, P, _ = lay
+    fs = range(S_) if frames is None else frames
+    return np.concatenate([s * P + np.arange(P) for s in fs])
+
+
+def test_frame_attention_tiny_fp32():
+    w = synth.WORKLOADS["tiny_s2"]
+    say("[case] frame attention tiny_s2 fp32")
+    g, gl, r, rl, lay = _frame_case(w, seed=2)
+    assert float(np.max(np.abs(g - r))) <= TOL["f32"]
+    qv = (np.arange(g.shape[1]) % lay[2]) < lay[1]
+    assert np.allclose(gl[:, qv], rl[:, qv], rtol=0, atol=1e-5)
+    assert np.all(g[:, ~qv] == 0)
+
+
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_frame_attention_vggt_s8_bf16(out_f32):
+    w = synth.WORKLOADS["vggt_s8"]
+    say(f"[case] frame attention vggt_s8 bf16 out_f32={out_f32}")
+    g, gl, r, rl, lay = _frame_case(w, seed=1, out_f32=out_f32)
+    assert float(np.max(np.abs(g - r))) <= TOL["bf16"]
+    qv = (np.arange(g.shape[1]) % lay[2]) < lay[1]
+    assert np.all(np.abs(gl[:, qv] - rl[:, qv]) <= LSE_TOL_BF16)
+    assert np.all(g[:, ~qv] == 0) and np.all(gl[:, ~qv] == 0)
+
+
+def test_frame_attention_subsampled_keys():
+    w = synth.WORKLOADS["vggt_s8"]
+    say("[case] frame attention over 2x2-subsampled keys vggt_s8")
+    inp = synth.make_inputs(w, seed=4)
+    ol = oracle.Layout(*w.layout)
+    K2, V2, kl2 = oracle.subsample_keys(inp.k, inp.v, ol, w.grid, 2, 64)
+    g, gl, r, rl, lay = _frame_case(w, seed=4, klay=tuple(kl2), K=K2, V=V2)
+    assert float(np.max(np.abs(g - r))) <= TOL["bf16"]
+
+
+def test_frame_attention_full_s128_sampled_frames():
+    w = synth.WORKLOADS["vggt_s128"]
+    frames = [0, 1, 63, 127]
+    say(f"[case] frame attention vggt_s128 frames {frames}")
+    g, gl, r, rl, lay = _frame_case(w, seed=0, frames=frames, out_f32=False)
+    rows = _frame_rows(lay, frames)
+    assert float(np.max(np.abs(g[:, rows] - r[:, rows]))) <= TOL["bf16"]
+    qv = rows[(rows % lay[2]) < lay[1]]
+    assert np.all(np.abs(gl[:, qv] - rl[:, qv]) <= LSE_TOL_BF16)
