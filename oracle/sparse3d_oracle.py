@@ -35,6 +35,13 @@ What is computed, and the passages it follows
   values are thinned on the 2-D patch grid to one token per s_h x s_w window
   while every query and every special token is kept.  ``subsample_keys`` keeps
   the top-left patch of every window.
+* The same section completes the subsample with two terms: every token keeps
+  its own key (the diagonal of the attention matrix) when the subsample dropped
+  it, and the dropped columns are stood in for by a single mean key/value pair.
+  ``discarded_mean`` is that pair (means over the dropped patch rows of every
+  frame); the attention calls take both terms through ``sga``.  Reading: the
+  mean pair stands for all |D| dropped columns at once, so its logit carries
+  ln |D| (``sga_mean_bias``), exactly as a landmark carries ln 64 for its tile.
 * AVGGT technical summary, section 2B.1: the early global layers, which exchange
   no information between views, become attention within each frame.
   ``frame_attend`` is that operation: every valid query over the valid keys of
@@ -199,13 +206,16 @@ def sparse_attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, qlay: Layout, kla
                   kbar: Optional[np.ndarray] = None, vbar: Optional[np.ndarray] = None,
                   kcount: Optional[np.ndarray] = None, landmark_bias: float = LN64,
                   query_tiles: Optional[Sequence[int]] = None,
-                  heads: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+                  heads: Optional[Sequence[int]] = None,
+                  sga: Optional[dict] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Attention of each query tile over specials + its selected tiles (+ landmarks).
 
     Q: [H, Sq*Pq, d], K/V: [H, Sk*Pk, d]; idx/cnt as from ``select_topk``.
     Landmarks are on when ``kbar`` is given (then ``vbar`` and ``kcount`` too).
     Only the listed ``query_tiles`` / ``heads`` are computed; the other rows of the
-    returned O [H, Lq, d] and lse [H, Lq] are 0.
+    returned O [H, Lq, d] and lse [H, Lq] are 0.  ``sga`` adds the subsample completion
+    (own key of dropped positions from k_full/v_full, mean pair kmean/vmean + mean_bias;
+    keys: grid, window, k_full, v_full, kmean, vmean, mean_bias).
     """
     H, Lq, d = Q.shape
     Tk = klay.rows // tile
@@ -232,7 +242,10 @@ def sparse_attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, qlay: Layout, kla
                 lm = np.nonzero(~chosen & (kcount > 0))[0]
                 logits = np.concatenate([logits, scale * (q @ kbar[h, lm].T) + landmark_bias], axis=1)
                 values = np.concatenate([values, vbar[h, lm]], axis=0)
-            o, l = _softmax_rows(logits, values)
+            if sga is not None:
+                o, l = _softmax_rows_extra(logits, values, *_sga_extra(h, rows_q, q, qlay, scale, sga))
+            else:
+                o, l = _softmax_rows(logits, values)
             O[h, rows_q] = o
             lse[h, rows_q] = l
     return O, lse
@@ -241,8 +254,9 @@ def sparse_attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, qlay: Layout, kla
 def dense_attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, qlay: Layout, klay: Layout,
                  scale: float, heads: Optional[Sequence[int]] = None,
                  query_rows_subset: Optional[np.ndarray] = None,
-                 chunk: int = 2048) -> Tuple[np.ndarray, np.ndarray]:
-    """Exact softmax attention of every valid query over every valid key (specials in place)."""
+                 chunk: int = 2048, sga: Optional[dict] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Exact softmax attention of every valid query over every valid key (specials in place);
+    ``sga`` as in ``sparse_attend``."""
     H, Lq, d = Q.shape
     J = np.nonzero(key_rows_dense(klay))[0]
     rows = np.nonzero(query_rows(qlay))[0]
@@ -255,7 +269,11 @@ def dense_attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, qlay: Layout, klay
         Vh = V[h, J].astype(np.float64)
         for c in range(0, rows.size, chunk):
             r = rows[c:c + chunk]
-            o, l = _softmax_rows(scale * (Q[h, r].astype(np.float64) @ Kh.T), Vh)
+            q = Q[h, r].astype(np.float64)
+            if sga is not None:
+                o, l = _softmax_rows_extra(scale * (q @ Kh.T), Vh, *_sga_extra(h, r, q, qlay, scale, sga))
+            else:
+                o, l = _softmax_rows(scale * (q @ Kh.T), Vh)
             O[h, r] = o
             lse[h, r] = l
     return O, lse
@@ -305,6 +323,72 @@ def subsample_keys(K: np.ndarray, V: np.ndarray, lay: Layout, grid: Tuple[int, i
         K2[:, s * p2: s * p2 + n2] = K[:, s * lay.stride + pos]
         V2[:, s * p2: s * p2 + n2] = V[:, s * lay.stride + pos]
     return K2, V2, lay2
+
+
+def discarded_positions(specials: int, grid: Tuple[int, int], window: int) -> np.ndarray:
+    """In-frame positions of the patches the grid subsample drops, ascending."""
+    gh, gw = grid
+    return np.array([specials + y * gw + x for y in range(gh) for x in range(gw)
+                     if y % window or x % window], dtype=np.int64)
+
+
+def discarded_mean(K: np.ndarray, V: np.ndarray, lay: Layout, grid: Tuple[int, int],
+                   window: int) -> Tuple[np.ndarray, np.ndarray, int]:
+    """Mean key and mean value over every dropped patch row of every frame, per head:
+    (kmean [H, d], vmean [H, d], |D|).  With nothing dropped the means are 0 and |D| = 0."""
+    pos = discarded_positions(lay.specials, grid, window)
+    rows = (np.arange(lay.frames)[:, None] * lay.stride + pos[None, :]).ravel()
+    H, _, d = K.shape
+    if rows.size == 0:
+        return np.zeros((H, d)), np.zeros((H, d)), 0
+    return (K[:, rows].astype(np.float64).mean(axis=1), V[:, rows].astype(np.float64).mean(axis=1),
+            int(rows.size))
+
+
+def sga_mean_bias(count: int) -> float:
+    """Logit offset of the mean pair: it stands for all `count` dropped columns."""
+    return math.log(count)
+
+
+def _sga_extra(h: int, rows_q: np.ndarray, q: np.ndarray, qlay: Layout, scale: float, sga: dict):
+    """Per-row extra logits and values of the subsample completion: the row's own key when
+    the subsample dropped its position (-inf otherwise), and the mean pair."""
+    n, d = q.shape
+    dl = np.full(n, -np.inf)
+    dv = np.zeros((n, d))
+    if sga.get("k_full") is not None:
+        drop = np.zeros(qlay.stride, dtype=bool)
+        drop[discarded_positions(qlay.specials, sga["grid"], sga["window"])] = True
+        own = drop[rows_q % qlay.stride]
+        kf = sga["k_full"][h, rows_q].astype(np.float64)
+        dl = np.where(own, scale * np.einsum("nd,nd->n", q, np.nan_to_num(kf)), -np.inf)
+        dv = np.where(own[:, None], np.nan_to_num(sga["v_full"][h, rows_q].astype(np.float64)), 0.0)
+    ml = np.full(n, -np.inf)
+    mv = np.zeros(d)
+    if sga.get("kmean") is not None:
+        ml = scale * (q @ sga["kmean"][h]) + sga["mean_bias"]
+        mv = sga["vmean"][h]
+    return dl, dv, ml, mv
+
+
+def _softmax_rows_extra(logits, values, dl, dv, ml, mv):
+    """``_softmax_rows`` over the shared keys plus, per row, one own key (logit dl, value
+    dv) and the mean pair (logit ml, value mv); -inf logits take no part."""
+    n = dl.shape[0]
+    m = np.maximum(np.maximum(dl, ml), logits.max(axis=1) if logits.shape[1] else -np.inf)
+    out = np.zeros((n, dv.shape[1]))
+    lse = np.full(n, -np.inf)
+    live = np.isfinite(m)
+    if not np.any(live):
+        return out, lse
+    mm = m[live][:, None]
+    e = np.exp(logits[live] - mm)
+    ed = np.exp(dl[live] - m[live])
+    em = np.exp(ml[live] - m[live])
+    den = e.sum(axis=1) + ed + em
+    out[live] = (e @ values + ed[:, None] * dv[live] + em[:, None] * mv[None, :]) / den[:, None]
+    lse[live] = m[live] + np.log(den)
+    return out, lse
 
 
 # ----------------------------------------------------------------------------- the whole layer

@@ -479,6 +479,110 @@ def pin_frame_attention(o):
     assert not np.allclose(a[:, 64:104], b[:, 64:104])
 
 
+# --------------------------------------------------------------------------- subsample completion
+def _sga_setup(o, S=2, nsp=2, grid=(4, 4), window=2, tile=16, H=2, d=8, seed=0):
+    N = nsp + grid[0] * grid[1]
+    P = -(-N // tile) * tile
+    Q, K, V = _rand_inputs(S, N, P, nsp, H=H, d=d, seed=seed)
+    lay = o.Layout(S, N, P, nsp)
+    K2, V2, lay2 = o.subsample_keys(K, V, lay, grid, window, tile)
+    km, vm, n = o.discarded_mean(K, V, lay, grid, window)
+    return Q, K, V, lay, K2, V2, lay2, km, vm, n
+
+
+def _explicit_sga(Q, K, V, lay, lay2, K2, V2, key_rows2, drop_pos, km, vm, n, scale, diag, mean):
+    """Softmax over an explicitly listed key set per query row: the given subsampled key
+    rows, the row's own key if its position was dropped, and n copies of the mean pair."""
+    H, L, d = Q.shape
+    O = np.zeros((H, L, d))
+    for h in range(H):
+        for r in range(L):
+            if r % lay.stride >= lay.tokens:
+                continue
+            keys = [K2[h, c] for c in key_rows2]
+            vals = [V2[h, c] for c in key_rows2]
+            if diag and (r % lay.stride) in drop_pos:
+                keys.append(K[h, r]); vals.append(V[h, r])
+            if mean:
+                keys += [km[h]] * n; vals += [vm[h]] * n
+            kk, vv = np.array(keys), np.array(vals)
+            z = scale * (kk @ Q[h, r])
+            w = np.exp(z - z.max())
+            O[h, r] = (w @ vv) / w.sum()
+    return O
+
+
+def pin_sga_explicit_key_list(o):
+    """The completion terms equal attention over an explicit key list holding the row's own
+    key (only where the subsample dropped it) and |D| copies of the mean pair."""
+    for (grid, window, nsp) in [((4, 4), 2, 2), ((5, 3), 2, 1), ((4, 6), 3, 2)]:
+        Q, K, V, lay, K2, V2, lay2, km, vm, n = _sga_setup(o, grid=grid, window=window, nsp=nsp,
+                                                           seed=grid[1])
+        drop = set(o.discarded_positions(lay.specials, grid, window).tolist())
+        kept = set(o.subsample_positions(lay.specials, grid, window).tolist())
+        assert drop.isdisjoint(kept) and drop | kept == set(range(lay.tokens))
+        assert n == lay.frames * len(drop) and n > 0
+        scale = 0.35
+        all2 = np.nonzero((np.arange(lay2.rows) % lay2.stride) < lay2.tokens)[0]
+        for diag, mean in [(True, True), (True, False), (False, True)]:
+            sga = dict(grid=grid, window=window,
+                       k_full=K if diag else None, v_full=V if diag else None,
+                       kmean=km if mean else None, vmean=vm, mean_bias=o.sga_mean_bias(n))
+            got, _ = o.dense_attend(Q, K2, V2, lay, lay2, scale, sga=sga)
+            want = _explicit_sga(Q, K, V, lay, lay2, K2, V2, all2, drop, km, vm, n, scale, diag, mean)
+            qv = (np.arange(lay.rows) % lay.stride) < lay.tokens
+            assert np.allclose(got[:, qv], want[:, qv], rtol=0, atol=1e-12), (grid, diag, mean)
+        # the same terms on the tile-sparse call: specials + the selected tiles' members
+        tile = 16
+        T2 = lay2.rows // tile
+        mem = ((np.arange(lay2.rows) % lay2.stride >= lay2.specials) &
+               (np.arange(lay2.rows) % lay2.stride < lay2.tokens))
+        spec = np.nonzero((np.arange(lay2.rows) % lay2.stride) < lay2.specials)[0]
+        sel = np.array([T2 - 1], dtype=np.int32)
+        idx = np.broadcast_to(sel, (2, lay.rows // tile, 1)).copy()
+        cnt = np.ones((2, lay.rows // tile), dtype=np.int32)
+        sga = dict(grid=grid, window=window, k_full=K, v_full=V, kmean=km, vmean=vm,
+                   mean_bias=o.sga_mean_bias(n))
+        got, _ = o.sparse_attend(Q, K2, V2, lay, lay2, tile, idx, cnt, scale, sga=sga)
+        rows2 = np.concatenate([spec, (T2 - 1) * tile + np.nonzero(mem[(T2 - 1) * tile:T2 * tile])[0]])
+        want = _explicit_sga(Q, K, V, lay, lay2, K2, V2, rows2, drop, km, vm, n, scale, True, True)
+        qv = (np.arange(lay.rows) % lay.stride) < lay.tokens
+        assert np.allclose(got[:, qv], want[:, qv], rtol=0, atol=1e-12)
+
+
+def pin_sga_constant_dropped_is_dense(o):
+    """If every dropped key and value equals one constant pair, the mean pair with ln |D|
+    restores dense attention exactly (|D| e^{q.k} is the dropped columns' total)."""
+    Q, K, V, lay, _, _, _, _, _, _ = _sga_setup(o, grid=(6, 4), window=2, nsp=3, seed=9)
+    pos = o.discarded_positions(lay.specials, (6, 4), 2)
+    rows = (np.arange(lay.frames)[:, None] * lay.stride + pos[None, :]).ravel()
+    rng = np.random.default_rng(1)
+    for h in range(K.shape[0]):
+        K[h, rows] = rng.standard_normal(K.shape[2])
+        V[h, rows] = rng.standard_normal(V.shape[2])
+    K2, V2, lay2 = o.subsample_keys(K, V, lay, (6, 4), 2, 16)
+    km, vm, n = o.discarded_mean(K, V, lay, (6, 4), 2)
+    assert np.allclose(km, K[:, rows[0]]) and np.allclose(vm, V[:, rows[0]])
+    sga = dict(grid=(6, 4), window=2, k_full=None, v_full=None, kmean=km, vmean=vm,
+               mean_bias=o.sga_mean_bias(n))
+    got, gl = o.dense_attend(Q, K2, V2, lay, lay2, 0.4, sga=sga)
+    want, wl = o.dense_attend(Q, K, V, lay, lay, 0.4)
+    qv = (np.arange(lay.rows) % lay.stride) < lay.tokens
+    assert np.allclose(got[:, qv], want[:, qv], rtol=0, atol=1e-12)
+    assert np.allclose(gl[:, qv], wl[:, qv], rtol=0, atol=1e-12)
+
+
+def pin_sga_nothing_dropped(o):
+    """Window 1 keeps every token: no own-key term applies, |D| = 0, dense attention."""
+    Q, K, V, lay, K2, V2, lay2, km, vm, n = _sga_setup(o, grid=(4, 4), window=1, seed=5)
+    assert n == 0 and o.discarded_positions(lay.specials, (4, 4), 1).size == 0
+    sga = dict(grid=(4, 4), window=1, k_full=K, v_full=V, kmean=None, vmean=None, mean_bias=0.0)
+    got, _ = o.dense_attend(Q, K2, V2, lay, lay2, 0.3, sga=sga)
+    want, _ = o.dense_attend(Q, K, V, lay, lay, 0.3)
+    qv = (np.arange(lay.rows) % lay.stride) < lay.tokens
+    assert np.allclose(got[:, qv], want[:, qv], rtol=0, atol=1e-12)
+
+
 ALL_PINS = [
     pin_block_mean_identity, pin_tile_constant_pool, pin_symmetric_scores,
     pin_select_brute_force, pin_select_invariants,
@@ -487,4 +591,5 @@ ALL_PINS = [
     pin_landmarks_exact_on_constant_tiles, pin_landmarks_vanish_when_all_selected,
     pin_empty_key_set, pin_subsample, pin_hand_worked,
     pin_select_per_head, pin_frame_attention,
+    pin_sga_explicit_key_list, pin_sga_constant_dropped_is_dense, pin_sga_nothing_dropped,
 ]

@@ -38,6 +38,14 @@ MUTANTS = {
                                    "J = ((s + 1) % klay.frames) * klay.stride + np.arange(klay.tokens)"),
     "frame_keys_skip_specials": ("J = s * klay.stride + np.arange(klay.tokens)",
                                  "J = s * klay.stride + np.arange(klay.specials, klay.tokens)"),
+    "sga_diag_on_kept_positions": ('drop[discarded_positions(qlay.specials, sga["grid"], sga["window"])] = True',
+                                   "drop[qlay.specials:qlay.tokens] = True"),
+    "sga_mean_without_bias": ('ml = scale * (q @ sga["kmean"][h]) + sga["mean_bias"]',
+                              'ml = scale * (q @ sga["kmean"][h])'),
+    "sga_mean_over_all_patches": ("if y % window or x % window]", "if True]"),
+    "sga_bias_count_plus_one": ("return math.log(count)", "return math.log(count + 1)"),
+    "sga_diag_value_from_key": ('np.nan_to_num(sga["v_full"][h, rows_q].astype(np.float64))',
+                                'np.nan_to_num(sga["k_full"][h, rows_q].astype(np.float64))'),
 }
 
 
