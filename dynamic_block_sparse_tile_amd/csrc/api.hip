@@ -83,15 +83,17 @@ int sparse3d_sparse_attn_fwd(const void* q, const void* k, const void* v, sparse
                              const sparse3d_layout* qlay, const sparse3d_layout* klay,
                              const int32_t* idx, const int32_t* cnt, int32_t kmax,
                              const void* kbar, const void* vbar, float landmark_bias,
-                             float scale, void* out, sparse3d_dtype out_dtype, float* lse,
-                             void* stream) {
+                             float scale, const sparse3d_sga* sga, void* out, sparse3d_dtype out_dtype,
+                             float* lse, void* stream) {
     const int st = validate_attn(true, q, k, v, dtype, heads, head_dim, tile, qlay, klay, idx, cnt,
                                  kmax, kbar, vbar, out, out_dtype, lse);
     if (st != SPARSE3D_OK) return st;
     const int sp = check_logit_params(scale, kbar ? landmark_bias : 0.f);
     if (sp != SPARSE3D_OK) return sp;
+    const int sg = validate_sga(sga, dtype, heads, head_dim, qlay, klay, out, out_dtype, lse);
+    if (sg != SPARSE3D_OK) return sg;
     AttnArgs a{q, k, v, dtype, out_dtype, heads, to_lay(*qlay), to_lay(*klay), false, false, idx, cnt,
-               kmax, kbar, vbar, landmark_bias, scale, out, lse};
+               kmax, kbar, vbar, landmark_bias, scale, sga, out, lse};
     S3D_HIP(launch_attn(a, static_cast<hipStream_t>(stream)));
     return SPARSE3D_OK;
 }
@@ -106,15 +108,17 @@ int sparse3d_cast(const float* src, int64_t n, sparse3d_dtype dtype, void* dst, 
 
 int sparse3d_dense_attn_fwd(const void* q, const void* k, const void* v, sparse3d_dtype dtype,
                             int32_t heads, int32_t head_dim, const sparse3d_layout* qlay,
-                            const sparse3d_layout* klay, float scale, void* out,
-                            sparse3d_dtype out_dtype, float* lse, void* stream) {
+                            const sparse3d_layout* klay, float scale, const sparse3d_sga* sga,
+                            void* out, sparse3d_dtype out_dtype, float* lse, void* stream) {
     const int st = validate_attn(false, q, k, v, dtype, heads, head_dim, kTile, qlay, klay, nullptr,
                                  nullptr, 0, nullptr, nullptr, out, out_dtype, lse);
     if (st != SPARSE3D_OK) return st;
     const int sp = check_logit_params(scale, 0.f);
     if (sp != SPARSE3D_OK) return sp;
+    const int sg = validate_sga(sga, dtype, heads, head_dim, qlay, klay, out, out_dtype, lse);
+    if (sg != SPARSE3D_OK) return sg;
     AttnArgs a{q, k, v, dtype, out_dtype, heads, to_lay(*qlay), to_lay(*klay), true, false, nullptr,
-               nullptr, 0, nullptr, nullptr, 0.f, scale, out, lse};
+               nullptr, 0, nullptr, nullptr, 0.f, scale, sga, out, lse};
     S3D_HIP(launch_attn(a, static_cast<hipStream_t>(stream)));
     return SPARSE3D_OK;
 }
@@ -129,8 +133,20 @@ int sparse3d_frame_attn_fwd(const void* q, const void* k, const void* v, sparse3
     const int sp = check_logit_params(scale, 0.f);
     if (sp != SPARSE3D_OK) return sp;
     AttnArgs a{q, k, v, dtype, out_dtype, heads, to_lay(*qlay), to_lay(*klay), true, true, nullptr,
-               nullptr, 0, nullptr, nullptr, 0.f, scale, out, lse};
+               nullptr, 0, nullptr, nullptr, 0.f, scale, nullptr, out, lse};
     S3D_HIP(launch_attn(a, static_cast<hipStream_t>(stream)));
+    return SPARSE3D_OK;
+}
+
+int sparse3d_discarded_mean(const void* k, const void* v, sparse3d_dtype dtype, int32_t heads,
+                            int32_t head_dim, const sparse3d_layout* lay, int32_t grid_h,
+                            int32_t grid_w, int32_t window, float* kmean, float* vmean, void* stream) {
+    const int st = validate_discarded_mean(k, v, dtype, heads, head_dim, lay, grid_h, grid_w, window,
+                                           kmean, vmean);
+    if (st != SPARSE3D_OK) return st;
+    const int64_t count = int64_t(lay->frames) * dropped_per_frame(grid_h, grid_w, window);
+    S3D_HIP(launch_discarded_mean(k, v, dtype, heads, to_lay(*lay), grid_h, grid_w, window, count, kmean,
+                                  vmean, static_cast<hipStream_t>(stream)));
     return SPARSE3D_OK;
 }
 

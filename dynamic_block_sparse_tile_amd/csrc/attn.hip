@@ -284,7 +284,8 @@ __global__ __launch_bounds__(128, 2) void k_attn(AttnDev p) {
     }
 
     // ---- epilogue: combine the two key halves' row sums, normalise, write
-    const float ltot = l + __shfl_xor(l, 32);
+    float ltot = l + __shfl_xor(l, 32);
+    sga_finish<F32IN>(p, h, qrow, qvalid, g, m, ltot, o0, o1);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     const size_t obase = ((size_t)h * Lq + qrow) * HD;
 #pragma unroll
@@ -341,6 +342,14 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     d.kbar = a.kbar;
     d.vbar = a.vbar;
     d.lm_bias_l2 = a.landmark_bias * LOG2E;
+    const sparse3d_sga* sg = a.sga;
+    d.sga_kf = sg ? sg->k_full : nullptr;
+    d.sga_vf = sg ? sg->v_full : nullptr;
+    d.sga_km = sg ? sg->kmean : nullptr;
+    d.sga_vm = sg ? sg->vmean : nullptr;
+    d.sga_bias_l2 = (sg && sg->kmean) ? sg->mean_bias * LOG2E : 0.f;
+    d.sga_gw = sg ? sg->grid_w : 1;
+    d.sga_win = sg ? sg->window : 1;
     d.scale_l2 = a.scale * LOG2E;
     d.out = a.out;
     d.lse = a.lse;

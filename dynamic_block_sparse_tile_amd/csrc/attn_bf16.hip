@@ -75,7 +75,9 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 constexpr float RESCALE_THRESHOLD = 8.0f;
 
 
-template <bool F32OUT, bool DENSE, bool LM>
+// SGA: the subsample completion (own key of dropped positions, mean pair) is applied to
+// each finished row; a separate instantiation so the other variants carry none of it.
+template <bool F32OUT, bool DENSE, bool LM, bool SGA>
 __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
     // K and V rings of two 8 KiB tiles each, as four separate arrays so that every access
     // in the (two-way unrolled) loop names its buffer statically
@@ -424,7 +426,8 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
     }
     if (it < ntiles) step(it, sa0, sa1, sb0, sb1, d0, d1, d2, s_k1, s_k0, s_v0, s_v1);
 
-    const float ltot = l + __shfl_xor(l, 32);
+    float ltot = l + __shfl_xor(l, 32);
+    if (SGA) sga_finish<false>(p, h, qrow, qvalid, g, m, ltot, o0, o1);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     const size_t obase = ((size_t)h * Lq + qrow) * HD;
 #pragma unroll
@@ -452,20 +455,21 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
     }
 }
 
-template <bool F32OUT>
+template <bool F32OUT, bool SGA>
 static void launch_t(const AttnDev& d, int heads, bool dense, bool lm, hipStream_t st) {
     const dim3 grid((unsigned)(heads * d.Tq)), block(128);
     const size_t shm = ((lm ? (size_t)(2 * d.nlm) : 0) + (dense ? 0 : (size_t)d.kmax)) *
                        sizeof(uint32_t);
-    if (dense) hipLaunchKernelGGL((k_attn_bf16<F32OUT, true, false>), grid, block, 0, st, d);
-    else if (lm) hipLaunchKernelGGL((k_attn_bf16<F32OUT, false, true>), grid, block, shm, st, d);
-    else hipLaunchKernelGGL((k_attn_bf16<F32OUT, false, false>), grid, block, shm, st, d);
+    if (dense) hipLaunchKernelGGL((k_attn_bf16<F32OUT, true, false, SGA>), grid, block, 0, st, d);
+    else if (lm) hipLaunchKernelGGL((k_attn_bf16<F32OUT, false, true, SGA>), grid, block, shm, st, d);
+    else hipLaunchKernelGGL((k_attn_bf16<F32OUT, false, false, SGA>), grid, block, shm, st, d);
 }
 
 hipError_t launch_attn_bf16(const AttnDev& d, int heads, bool dense, bool lm, bool f32out,
                             hipStream_t st) {
-    if (f32out) launch_t<true>(d, heads, dense, lm, st);
-    else launch_t<false>(d, heads, dense, lm, st);
+    const bool sga = d.sga_kf || d.sga_km;
+    if (f32out) sga ? launch_t<true, true>(d, heads, dense, lm, st) : launch_t<true, false>(d, heads, dense, lm, st);
+    else sga ? launch_t<false, true>(d, heads, dense, lm, st) : launch_t<false, false>(d, heads, dense, lm, st);
     return hipGetLastError();
 }
 

@@ -20,6 +20,13 @@ struct AttnDev {
     int frame;          // dense over the query's own frame only (frame attention)
     float lm_bias_l2;   // landmark bias in base-2 logit units
     float scale_l2;     // scale * log2(e)
+    // subsample completion (own key of dropped positions; one mean pair), off when NULL
+    const void* sga_kf;
+    const void* sga_vf;
+    const float* sga_km;
+    const float* sga_vm;
+    float sga_bias_l2;
+    int sga_gw, sga_win;
     void* out;
     float* lse;
 };
@@ -144,6 +151,97 @@ __device__ __forceinline__ void init_landmark_bitmap(const AttnDev& p, int c, co
         if (t >= 0 && t < p.Tk) atomicAnd(&s_lm[t >> 5], ~(1u << (t & 31)));
     }
     __syncthreads();
+}
+
+// Subsample completion of one finished query row (AVGGT technical summary, section 2B.2):
+// fold the row's own key (when the subsample dropped its position) and the mean pair into
+// the running softmax state (m: base-2 reference, ltot: row sum relative to m, o0/o1: the
+// O^T accumulators of this lane, dims 8*(r/4) + 4g + r%4 and 32 more).  Each lane of the
+// pair (qc, g) and (qc, g^1) forms half of each 64-dim dot product.
+template <bool F32IN>
+__device__ __forceinline__ void sga_finish(const AttnDev& p, int h, int qrow, bool qvalid, int g,
+                                           float& m, float& ltot, f32x16& o0, f32x16& o1) {
+    if (!p.sga_kf && !p.sga_km) return;
+    // Pass the row indices through an empty asm so nothing below can be computed ahead
+    // of the tile loop: hoisted, it would hold registers across the whole loop.
+    asm volatile("" : "+v"(qrow), "+v"(g));
+    asm volatile("" : "+s"(h));
+    const int Lq = p.ql.S * p.ql.P;
+    const size_t rbase = ((size_t)h * Lq + qrow) * HD;
+    auto load8 = [&](const void* base, size_t off, float (&x)[8]) {   // 8 values at base[off..]
+        if (F32IN) {
+            const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+            const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off + 4);
+            x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        } else {
+            const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+            const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = __uint_as_float(w4[i] << 16);
+                x[2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
+            }
+        }
+    };
+    // own key applies to valid rows whose in-frame position is a dropped patch
+    const int j = qrow % p.ql.P;
+    const int pp = j - p.ql.nsp;
+    const bool dropped = p.sga_kf && qvalid && pp >= 0 && j < p.ql.N &&
+                         (((pp / p.sga_gw) % p.sga_win) != 0 || ((pp % p.sga_gw) % p.sga_win) != 0);
+    float dd = 0.f, dm = 0.f;
+    if (qvalid && (dropped || p.sga_km)) {
+#pragma unroll
+        for (int c = 0; c < 32; c += 8) {
+            float qv[8], kv[8];
+            load8(p.q, rbase + 32 * g + c, qv);
+            if (dropped) {
+                load8(p.sga_kf, rbase + 32 * g + c, kv);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) dd = fmaf(qv[i], kv[i], dd);
+            }
+            if (p.sga_km) {
+                const float* km = p.sga_km + (size_t)h * HD + 32 * g + c;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) dm = fmaf(qv[i], km[i], dm);
+            }
+        }
+    }
+    dd += __shfl_xor(dd, 32);
+    dm += __shfl_xor(dm, 32);
+    const float xd = dropped ? dd * p.scale_l2 : -INFINITY;
+    const float xm = (p.sga_km && qvalid) ? fmaf(dm, p.scale_l2, p.sga_bias_l2) : -INFINITY;
+    const float mnew = fmaxf(m, fmaxf(xd, xm));
+    if (mnew == -INFINITY) return;                         // nothing at all to attend
+    const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
+    const float pd = __builtin_amdgcn_exp2f(xd - mnew);    // 0 when the term is absent
+    const float pm = __builtin_amdgcn_exp2f(xm - mnew);
+    ltot = ltot * alpha + pd + pm;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        f32x16& oc = cb ? o1 : o0;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int c0 = 32 * cb + 8 * a + 4 * g;        // dims c0 .. c0+3 of this lane
+            float vd[4] = {0.f, 0.f, 0.f, 0.f}, vm[4] = {0.f, 0.f, 0.f, 0.f};
+            if (dropped) {
+                if (F32IN) {
+                    const float4 t = *reinterpret_cast<const float4*>(static_cast<const float*>(p.sga_vf) + rbase + c0);
+                    vd[0] = t.x; vd[1] = t.y; vd[2] = t.z; vd[3] = t.w;
+                } else {
+                    const uint2 t = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.sga_vf) + rbase + c0);
+                    vd[0] = __uint_as_float(t.x << 16); vd[1] = __uint_as_float(t.x & 0xffff0000u);
+                    vd[2] = __uint_as_float(t.y << 16); vd[3] = __uint_as_float(t.y & 0xffff0000u);
+                }
+            }
+            if (p.sga_km) {
+                const float4 t = *reinterpret_cast<const float4*>(p.sga_vm + (size_t)h * HD + c0);
+                vm[0] = t.x; vm[1] = t.y; vm[2] = t.z; vm[3] = t.w;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oc[4 * a + i] = oc[4 * a + i] * alpha + pd * vd[i] + pm * vm[i];
+        }
+    }
+    m = mnew;
 }
 
 hipError_t launch_attn_bf16(const AttnDev& d, int heads, bool dense, bool lm, bool f32out,

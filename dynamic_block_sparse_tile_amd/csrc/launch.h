@@ -39,12 +39,17 @@ struct AttnArgs {
     const void* vbar;
     float landmark_bias;
     float scale;
+    const sparse3d_sga* sga;   // subsample completion, or NULL
     void* out;
     float* lse;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 
 hipError_t launch_cast(const float* src, int64_t n, int dtype, void* dst, hipStream_t st);
+
+hipError_t launch_discarded_mean(const void* k, const void* v, int dtype, int heads, LayH lay,
+                                 int grid_h, int grid_w, int window, int64_t count, float* kmean,
+                                 float* vmean, hipStream_t st);
 
 hipError_t launch_grid_subsample(const void* k, const void* v, int dtype, int heads, LayH lay,
                                  int grid_w, int window, LayH out_lay, void* k_out, void* v_out,

@@ -139,6 +139,52 @@ int validate_attn(bool sparse, const void* q, const void* k, const void* v, int 
     return SPARSE3D_OK;
 }
 
+int64_t dropped_per_frame(int32_t grid_h, int32_t grid_w, int32_t window) {
+    const int64_t kh = (grid_h + window - 1) / window, kw = (grid_w + window - 1) / window;
+    return int64_t(grid_h) * grid_w - kh * kw;
+}
+
+int validate_sga(const sparse3d_sga* sga, int dtype, int32_t heads, int32_t head_dim,
+                 const sparse3d_layout* qlay, const sparse3d_layout* klay, const void* out,
+                 int out_dtype, const float* lse) {
+    if (!sga) return SPARSE3D_OK;
+    if ((sga->k_full == nullptr) != (sga->v_full == nullptr)) return SPARSE3D_ERR_NULL;
+    if ((sga->kmean == nullptr) != (sga->vmean == nullptr)) return SPARSE3D_ERR_NULL;
+    // klay must be exactly the subsample of qlay
+    sparse3d_layout want;
+    S3D_TRY(subsample_layout(qlay, sga->grid_h, sga->grid_w, sga->window, kTile, &want));
+    if (klay->frames != want.frames || klay->tokens != want.tokens || klay->stride != want.stride ||
+        klay->specials != want.specials)
+        return SPARSE3D_ERR_SHAPE;
+    if (sga->kmean && !std::isfinite(sga->mean_bias)) return SPARSE3D_ERR_UNSUPPORTED;
+    const size_t eb = dtype_bytes(sparse3d_dtype(dtype));
+    const size_t fb = size_t(heads) * lay_rows(*qlay) * head_dim * eb;       // k_full / v_full
+    const size_t mb = size_t(heads) * head_dim * 4;                          // kmean / vmean
+    const size_t ob = size_t(heads) * lay_rows(*qlay) * head_dim * dtype_bytes(sparse3d_dtype(out_dtype));
+    const size_t lb = size_t(heads) * lay_rows(*qlay) * 4;
+    const void* ins[4] = {sga->k_full, sga->v_full, sga->kmean, sga->vmean};
+    const size_t inb[4] = {fb, fb, mb, mb};
+    for (int i = 0; i < 4; ++i)
+        if (overlaps(out, ob, ins[i], inb[i]) || overlaps(lse, lb, ins[i], inb[i])) return SPARSE3D_ERR_ALIAS;
+    return SPARSE3D_OK;
+}
+
+int validate_discarded_mean(const void* k, const void* v, int dtype, int32_t heads, int32_t head_dim,
+                            const sparse3d_layout* lay, int32_t grid_h, int32_t grid_w,
+                            int32_t window, const float* kmean, const float* vmean) {
+    if (!k || !v || !kmean || !vmean) return SPARSE3D_ERR_NULL;
+    S3D_TRY(check_dtype(dtype));
+    S3D_TRY(check_heads_dims(heads, head_dim, kTile));
+    sparse3d_layout sub;
+    S3D_TRY(subsample_layout(lay, grid_h, grid_w, window, kTile, &sub));
+    const size_t ib = size_t(heads) * lay_rows(*lay) * head_dim * dtype_bytes(sparse3d_dtype(dtype));
+    const size_t mb = size_t(heads) * head_dim * 4;
+    if (overlaps(kmean, mb, k, ib) || overlaps(kmean, mb, v, ib) || overlaps(vmean, mb, k, ib) ||
+        overlaps(vmean, mb, v, ib) || overlaps(kmean, mb, vmean, mb))
+        return SPARSE3D_ERR_ALIAS;
+    return SPARSE3D_OK;
+}
+
 int validate_cast(const float* src, int64_t n, int dtype, const void* dst) {
     if (n < 0) return SPARSE3D_ERR_SHAPE;
     S3D_TRY(check_dtype(dtype));

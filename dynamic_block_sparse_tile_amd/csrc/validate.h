@@ -43,6 +43,17 @@ int validate_attn(bool sparse, const void* q, const void* k, const void* v, int 
 
 int validate_cast(const float* src, int64_t n, int dtype, const void* dst);
 
+// The subsample completion of an attention call (sga may be NULL: nothing to check).
+int validate_sga(const sparse3d_sga* sga, int dtype, int32_t heads, int32_t head_dim,
+                 const sparse3d_layout* qlay, const sparse3d_layout* klay, const void* out,
+                 int out_dtype, const float* lse);
+
+int validate_discarded_mean(const void* k, const void* v, int dtype, int32_t heads, int32_t head_dim,
+                            const sparse3d_layout* lay, int32_t grid_h, int32_t grid_w,
+                            int32_t window, const float* kmean, const float* vmean);
+// Dropped patch rows per frame of the subsample (grid_h, grid_w, window).
+int64_t dropped_per_frame(int32_t grid_h, int32_t grid_w, int32_t window);
+
 int subsample_layout(const sparse3d_layout* lay, int32_t grid_h, int32_t grid_w, int32_t window,
                      int32_t tile, sparse3d_layout* out);
 

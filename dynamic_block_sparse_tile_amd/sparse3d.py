@@ -22,6 +22,7 @@ __all__ = [
     "sparse3d_tile_scores", "sparse3d_select_topk", "sparse3d_sparse_attn_fwd",
     "sparse3d_dense_attn_fwd", "sparse3d_subsample_layout", "sparse3d_grid_subsample_kv",
     "sparse3d_cast", "sparse3d_select_topk_per_head", "sparse3d_frame_attn_fwd",
+    "sparse3d_discarded_mean", "Sga",
     "kmax_for", "LN64",
 ]
 
@@ -44,8 +45,15 @@ class _Layout(ctypes.Structure):
                 ("stride", ctypes.c_int32), ("specials", ctypes.c_int32)]
 
 
+class _Sga(ctypes.Structure):
+    _fields_ = [("k_full", ctypes.c_void_p), ("v_full", ctypes.c_void_p),
+                ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("kmean", ctypes.c_void_p), ("vmean", ctypes.c_void_p), ("mean_bias", ctypes.c_float)]
+
+
 _i32, _f32, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 _LP = ctypes.POINTER(_Layout)
+_SP = ctypes.POINTER(_Sga)
 
 _SIGS = {
     "sparse3d_abi_version": ([], ctypes.c_int),
@@ -55,10 +63,12 @@ _SIGS = {
     "sparse3d_select_topk": ([_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp],
                              ctypes.c_int),
     "sparse3d_sparse_attn_fwd": ([_vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32, _LP, _LP, _vp,
-                                  _vp, _i32, _vp, _vp, _f32, _f32, _vp, ctypes.c_int, _vp, _vp],
+                                  _vp, _i32, _vp, _vp, _f32, _f32, _SP, _vp, ctypes.c_int, _vp, _vp],
                                  ctypes.c_int),
-    "sparse3d_dense_attn_fwd": ([_vp, _vp, _vp, ctypes.c_int, _i32, _i32, _LP, _LP, _f32, _vp,
+    "sparse3d_dense_attn_fwd": ([_vp, _vp, _vp, ctypes.c_int, _i32, _i32, _LP, _LP, _f32, _SP, _vp,
                                  ctypes.c_int, _vp, _vp], ctypes.c_int),
+    "sparse3d_discarded_mean": ([_vp, _vp, ctypes.c_int, _i32, _i32, _LP, _i32, _i32, _i32, _vp, _vp,
+                                 _vp], ctypes.c_int),
     "sparse3d_subsample_layout": ([_LP, _i32, _i32, _i32, _i32, _LP], ctypes.c_int),
     "sparse3d_grid_subsample_kv": ([_vp, _vp, ctypes.c_int, _i32, _i32, _LP, _i32, _i32, _i32,
                                     _vp, _vp, _LP, _vp], ctypes.c_int),
@@ -120,6 +130,36 @@ def _stream(x: torch.Tensor) -> int:
 
 def _ptr(x: Optional[torch.Tensor]) -> Optional[int]:
     return None if x is None else x.data_ptr()
+
+
+class Sga:
+    """Subsample completion for the attention calls: the own key of dropped positions
+    (k_full/v_full: K and V before the subsample) and/or one mean pair (kmean/vmean from
+    ``sparse3d_discarded_mean``, logit offset mean_bias = ln |D|)."""
+
+    def __init__(self, grid, window, k_full=None, v_full=None, kmean=None, vmean=None,
+                 mean_bias: float = 0.0):
+        self.grid, self.window = tuple(grid), int(window)
+        self.k_full, self.v_full, self.kmean, self.vmean = k_full, v_full, kmean, vmean
+        self.mean_bias = float(mean_bias)
+
+    def _c(self, q):
+        for x, n in ((self.k_full, "k_full"), (self.v_full, "v_full")):
+            if x is not None:
+                _dev(x, n)
+                if x.dtype != q.dtype:
+                    raise TypeError(f"{n} must have the operand dtype")
+        for x, n in ((self.kmean, "kmean"), (self.vmean, "vmean")):
+            if x is not None:
+                _dev(x, n)
+                if x.dtype != torch.float32:
+                    raise TypeError(f"{n} must be float32")
+        return _Sga(_ptr(self.k_full), _ptr(self.v_full), self.grid[0], self.grid[1], self.window,
+                    _ptr(self.kmean), _ptr(self.vmean), self.mean_bias)
+
+
+def _sga_ref(sga, q):
+    return None if sga is None else ctypes.byref(sga._c(q))
 
 
 def sparse3d_abi_version() -> int:
@@ -200,7 +240,7 @@ def _out_dtype(q, out_dtype):
 
 def sparse3d_sparse_attn_fwd(q, k, v, qlay, klay, idx, cnt, kbar=None, vbar=None,
                              landmark_bias: float = LN64, scale: Optional[float] = None,
-                             out_dtype=None, return_lse: bool = False):
+                             out_dtype=None, return_lse: bool = False, sga: Optional[Sga] = None):
     """Attention over specials + selected tiles (+ landmarks when kbar/vbar are given).
 
     kbar/vbar are the tile means in q's dtype (for bf16, ``sparse3d_cast`` of the fp32
@@ -223,7 +263,7 @@ def sparse3d_sparse_attn_fwd(q, k, v, qlay, klay, idx, cnt, kbar=None, vbar=None
     _check(library().sparse3d_sparse_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _dt(q), H, q.shape[2], TILE, ctypes.byref(ql), ctypes.byref(kl),
         _ptr(idx) if kmax > 0 else None, _ptr(cnt), kmax, _ptr(kbar), _ptr(vbar), landmark_bias,
-        scale, _ptr(out), odc, _ptr(lse), _stream(q)))
+        scale, _sga_ref(sga, q), _ptr(out), odc, _ptr(lse), _stream(q)))
     return (out, lse) if return_lse else out
 
 
@@ -238,7 +278,7 @@ def sparse3d_cast(x: torch.Tensor, dtype) -> torch.Tensor:
 
 
 def sparse3d_dense_attn_fwd(q, k, v, qlay, klay=None, scale: Optional[float] = None,
-                            out_dtype=None, return_lse: bool = False):
+                            out_dtype=None, return_lse: bool = False, sga: Optional[Sga] = None):
     """Dense global attention over every valid key (the library's own baseline)."""
     klay = qlay if klay is None else klay
     for x, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -251,7 +291,7 @@ def sparse3d_dense_attn_fwd(q, k, v, qlay, klay=None, scale: Optional[float] = N
     ql, kl = _lay(qlay), _lay(klay)
     _check(library().sparse3d_dense_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _dt(q), H, q.shape[2], ctypes.byref(ql), ctypes.byref(kl),
-        scale, _ptr(out), odc, _ptr(lse), _stream(q)))
+        scale, _sga_ref(sga, q), _ptr(out), odc, _ptr(lse), _stream(q)))
     return (out, lse) if return_lse else out
 
 
@@ -271,6 +311,22 @@ def sparse3d_frame_attn_fwd(q, k, v, qlay, klay=None, scale: Optional[float] = N
         _ptr(q), _ptr(k), _ptr(v), _dt(q), H, q.shape[2], ctypes.byref(ql), ctypes.byref(kl),
         scale, _ptr(out), odc, _ptr(lse), _stream(q)))
     return (out, lse) if return_lse else out
+
+
+def sparse3d_discarded_mean(k, v, lay, grid: Tuple[int, int], window: int):
+    """Mean key and value of the patch rows the grid subsample drops (all frames, per head):
+    (kmean [H, 64] fp32, vmean [H, 64] fp32, |D|)."""
+    _dev(k, "k"), _dev(v, "v")
+    H = k.shape[0]
+    kmean = torch.empty((H, HEAD_DIM), device=k.device, dtype=torch.float32)
+    vmean = torch.empty_like(kmean)
+    il = _lay(lay)
+    _check(library().sparse3d_discarded_mean(_ptr(k), _ptr(v), _dt(k), H, k.shape[2], ctypes.byref(il),
+                                             grid[0], grid[1], window, _ptr(kmean), _ptr(vmean),
+                                             _stream(k)))
+    gh, gw = grid
+    kept = -(-gh // window) * -(-gw // window)
+    return kmean, vmean, int(lay[0]) * (gh * gw - kept)
 
 
 def sparse3d_subsample_layout(lay, grid_h: int, grid_w: int, window: int, tile: int = TILE):

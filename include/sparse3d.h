@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define SPARSE3D_ABI_VERSION 2
+#define SPARSE3D_ABI_VERSION 3
 
 typedef enum { SPARSE3D_F32 = 0, SPARSE3D_BF16 = 1 } sparse3d_dtype;
 
@@ -53,6 +53,29 @@ typedef enum {
 
 /* One token sequence: `frames` views of `tokens` valid rows each (the first `specials`
  * of them camera/register tokens), every frame padded to `stride` rows. */
+/*
+ * Completion of the AVGGT key/value subsample (technical summary, section 2B.2): each
+ * query keeps its own key when the subsample dropped its position (the diagonal), and
+ * the dropped columns are stood in for by one mean key/value pair.  Passed to the
+ * attention calls when klay is the layout sparse3d_grid_subsample_kv produced from qlay
+ * with (grid_h, grid_w, window); NULL there means neither term.
+ *   - own key: k_full/v_full are K and V BEFORE the subsample, in layout qlay and the
+ *     operand dtype.  A valid query row i whose in-frame position is a dropped patch gets
+ *     one more logit scale * q_i . k_full[i] with value v_full[i].  NULL = no such term.
+ *   - mean pair: kmean/vmean [heads, 64] fp32 (sparse3d_discarded_mean).  Every valid
+ *     query gets one more logit scale * q_i . kmean[h] + mean_bias with value vmean[h];
+ *     mean_bias = ln |D| (|D| = dropped rows of all frames) makes the one pair stand for
+ *     all dropped columns.  NULL = no such term.
+ */
+typedef struct {
+    const void* k_full;
+    const void* v_full;
+    int32_t grid_h, grid_w, window;
+    const float* kmean;
+    const float* vmean;
+    float mean_bias;
+} sparse3d_sga;
+
 typedef struct {
     int32_t frames;
     int32_t tokens;
@@ -140,8 +163,8 @@ int sparse3d_sparse_attn_fwd(const void* q, const void* k, const void* v, sparse
                              const sparse3d_layout* qlay, const sparse3d_layout* klay,
                              const int32_t* idx, const int32_t* cnt, int32_t kmax,
                              const void* kbar, const void* vbar, float landmark_bias,
-                             float scale, void* out, sparse3d_dtype out_dtype, float* lse,
-                             void* stream);
+                             float scale, const sparse3d_sga* sga, void* out, sparse3d_dtype out_dtype,
+                             float* lse, void* stream);
 
 /*
  * Dense global attention, the quadratic operation the sparse call replaces (SAF3R
@@ -152,8 +175,19 @@ int sparse3d_sparse_attn_fwd(const void* q, const void* k, const void* v, sparse
 int sparse3d_dense_attn_fwd(const void* q, const void* k, const void* v, sparse3d_dtype dtype,
                             int32_t heads, int32_t head_dim,
                             const sparse3d_layout* qlay, const sparse3d_layout* klay,
-                            float scale, void* out, sparse3d_dtype out_dtype, float* lse,
-                            void* stream);
+                            float scale, const sparse3d_sga* sga, void* out, sparse3d_dtype out_dtype,
+                            float* lse, void* stream);
+
+/*
+ * The mean key and mean value of every patch row the grid subsample (grid_h, grid_w,
+ * window) drops, over all frames, per head (the pair that stands in for the dropped
+ * columns, AVGGT technical summary, section 2B.2): kmean/vmean [heads, 64] fp32,
+ * accumulated in fp32 in a fixed order (deterministic).  Zero when nothing is dropped.
+ * Requires lay->tokens == lay->specials + grid_h*grid_w.
+ */
+int sparse3d_discarded_mean(const void* k, const void* v, sparse3d_dtype dtype, int32_t heads,
+                            int32_t head_dim, const sparse3d_layout* lay, int32_t grid_h,
+                            int32_t grid_w, int32_t window, float* kmean, float* vmean, void* stream);
 
 /*
  * Frame attention: every valid query attends the valid key rows (specials in place) of its

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status(lib):
-    assert lib.sparse3d_abi_version() == 2
+    assert lib.sparse3d_abi_version() == 3
     for st in range(6):
         assert lib.sparse3d_status_string(st)
     assert lib.sparse3d_status_string(99) == b"unknown status"
@@ -91,9 +91,9 @@ def test_select_validation(lib):
 def attn_call(lib, q=FAKE, k=FAKE + 10**9, v=FAKE + 2 * 10**9, dt=1, H=2, d=64, tile=64,
               ql=None, kl=None, idx=FAKE + 3 * 10**9, cnt=FAKE + 4 * 10**9, kmax=8, kbar=NULL,
               vbar=NULL, out=FAKE + 5 * 10**9, odt=1, lse=NULL, bias=4.1588830833596715,
-              scale=0.125):
+              scale=0.125, sga=NULL):
     return lib.sparse3d_sparse_attn_fwd(q, k, v, dt, H, d, tile, ql or L(), kl or L(), idx, cnt,
-                                        kmax, kbar, vbar, bias, scale, out, odt, lse, NULL)
+                                        kmax, kbar, vbar, bias, scale, sga, out, odt, lse, NULL)
 
 
 def test_attn_validation(lib):
@@ -108,14 +108,14 @@ def test_attn_validation(lib):
     assert attn_call(lib, kl=L(f=3)) == ERR_SHAPE
     assert attn_call(lib, out=FAKE + 64) == ERR_ALIAS                   # out overlaps q
     assert attn_call(lib, lse=FAKE + 5 * 10**9 + 128) == ERR_ALIAS      # lse overlaps out
-    assert lib.sparse3d_dense_attn_fwd(FAKE, FAKE, NULL, 1, 2, 64, L(), L(), 0.1, FAKE + 10**9, 1,
+    assert lib.sparse3d_dense_attn_fwd(FAKE, FAKE, NULL, 1, 2, 64, L(), L(), 0.1, NULL, FAKE + 10**9, 1,
                                        NULL, NULL) == ERR_NULL
-    assert lib.sparse3d_dense_attn_fwd(FAKE, FAKE, FAKE, 1, 2, 64, L(), L(), 0.1, FAKE + 64, 1,
+    assert lib.sparse3d_dense_attn_fwd(FAKE, FAKE, FAKE, 1, 2, 64, L(), L(), 0.1, NULL, FAKE + 64, 1,
                                        NULL, NULL) == ERR_ALIAS
     # a masked logit is -inf; only a finite positive scale keeps it out of the softmax
     for bad in (0.0, -0.125, float("inf"), float("nan")):
         assert attn_call(lib, scale=bad) == ERR_UNSUP
-        assert lib.sparse3d_dense_attn_fwd(FAKE, FAKE, FAKE, 1, 2, 64, L(), L(), bad,
+        assert lib.sparse3d_dense_attn_fwd(FAKE, FAKE, FAKE, 1, 2, 64, L(), L(), bad, NULL,
                                            FAKE + 10**9 * 5, 1, NULL, NULL) == ERR_UNSUP
     lm = dict(kbar=FAKE + 6 * 10**9, vbar=FAKE + 7 * 10**9)
     assert attn_call(lib, bias=float("inf"), **lm) == ERR_UNSUP
@@ -148,6 +148,42 @@ def test_frame_attn_validation(lib):
     assert fa(FAKE, FAKE, FAKE, 1, 2, 32, L(), L(), 0.1, FAKE + 10**9, 1, NULL, NULL) == ERR_UNSUP
     assert fa(FAKE, FAKE, FAKE, 1, 2, 64, L(), L(), 0.0, FAKE + 10**9, 1, NULL, NULL) == ERR_UNSUP
     assert fa(FAKE, FAKE, FAKE, 1, 2, 64, L(), L(), 0.1, FAKE + 64, 1, NULL, NULL) == ERR_ALIAS
+
+
+def _sga(k_full=NULL, v_full=NULL, grid=(4, 4), window=2, kmean=NULL, vmean=NULL, bias=3.0):
+    return ctypes.byref(S._Sga(k_full, v_full, grid[0], grid[1], window, kmean, vmean, bias))
+
+
+def test_sga_validation(lib):
+    # queries: 2 frames x (2 specials + 4x4 patches) in stride 64; keys: the 2x2 subsample
+    ql = L(f=2, n=18, p=64, s=2)
+    kl_ok = L(f=2, n=6, p=64, s=2)
+    call = lambda sga, kl=None, out=FAKE + 5 * 10**9: attn_call(lib, ql=ql, kl=kl or kl_ok, sga=sga,
+                                                                 kmax=2, out=out)
+    assert call(_sga(k_full=FAKE + 6 * 10**9)) == ERR_NULL                  # own key without values
+    assert call(_sga(kmean=FAKE + 7 * 10**9)) == ERR_NULL                   # mean key without value
+    assert call(_sga(), kl=L(f=2, n=7, p=64, s=2)) == ERR_SHAPE             # keys are not that subsample
+    assert call(_sga(grid=(3, 5))) == ERR_SHAPE                             # grid does not tile the frame
+    assert call(_sga(window=0)) == ERR_SHAPE
+    assert call(_sga(kmean=FAKE + 7 * 10**9, vmean=FAKE + 8 * 10**9, bias=float("nan"))) == ERR_UNSUP
+    assert call(_sga(kmean=FAKE + 5 * 10**9 + 256, vmean=FAKE + 8 * 10**9)) == ERR_ALIAS   # inside out
+    assert call(_sga(k_full=FAKE + 6 * 10**9, v_full=FAKE + 5 * 10**9 + 64)) == ERR_ALIAS
+    dense = lambda sga: lib.sparse3d_dense_attn_fwd(FAKE, FAKE + 10**9, FAKE + 2 * 10**9, 1, 2, 64, ql,
+                                                    L(f=2, n=5, p=64, s=2), 0.1, sga, FAKE + 5 * 10**9,
+                                                    1, NULL, NULL)
+    assert dense(_sga()) == ERR_SHAPE
+
+
+def test_discarded_mean_validation(lib):
+    dm = lambda k=FAKE, km=FAKE + 10**9, vm=FAKE + 2 * 10**9, grid=(4, 4), window=2, lay=None: \
+        lib.sparse3d_discarded_mean(k, FAKE + 3 * 10**9, 1, 2, 64, lay or L(f=2, n=18, p=64, s=2),
+                                    grid[0], grid[1], window, km, vm, NULL)
+    assert dm(k=NULL) == ERR_NULL
+    assert dm(km=NULL) == ERR_NULL
+    assert dm(grid=(4, 5)) == ERR_SHAPE
+    assert dm(window=0) == ERR_SHAPE
+    assert dm(km=FAKE + 64) == ERR_ALIAS                                    # means inside k
+    assert dm(vm=FAKE + 10**9 + 128) == ERR_ALIAS                           # the two means overlap
 
 
 def test_cast_validation(lib):

@@ -462,3 +462,83 @@ def test_frame_attention_full_s128_sampled_frames():
     assert float(np.max(np.abs(g[:, rows] - r[:, rows]))) <= TOL["bf16"]
     qv = rows[(rows % lay[2]) < lay[1]]
     assert np.all(np.abs(gl[:, qv] - rl[:, qv]) <= LSE_TOL_BF16)
+
+
+# --------------------------------------------------------------------------- subsample completion
+def _sga_inputs(w, seed, window=2):
+    inp = synth.make_inputs(w, seed=seed)
+    dt = tdt(w)
+    q, v = to_dev(inp.q, dt), to_dev(inp.v, dt)
+    lay = w.layout
+    K2, V2, klay = S.sparse3d_grid_subsample_kv(q, v, lay, w.grid, window)
+    ol = oracle.Layout(*lay)
+    rK2, rV2, rkl = oracle.subsample_keys(inp.k, inp.v, ol, w.grid, window, 64)
+    assert tuple(rkl) == tuple(klay)
+    km, vm, n = oracle.discarded_mean(inp.k, inp.v, ol, w.grid, window)
+    return inp, q, v, K2, V2, klay, ol, rK2, rV2, (km, vm, n)
+
+
+@pytest.mark.parametrize("name", ["tiny_s2", "vggt_s8"])
+def test_discarded_mean(name):
+    w = synth.WORKLOADS[name]
+    say(f"[case] discarded mean {name}")
+    inp, q, v, *_ , (km, vm, n) = _sga_inputs(w, seed=6)
+    gk, gv, gn = S.sparse3d_discarded_mean(q, v, w.layout, w.grid, 2)
+    assert gn == n
+    assert np.allclose(gk.cpu().numpy(), km, rtol=0, atol=1e-5)
+    assert np.allclose(gv.cpu().numpy(), vm, rtol=0, atol=1e-5)
+    g2, _, _ = S.sparse3d_discarded_mean(q, v, w.layout, w.grid, 2)
+    assert torch.equal(gk, g2)                                  # fixed summation order
+    z, _, zn = S.sparse3d_discarded_mean(q, v, w.layout, w.grid, 1)
+    assert zn == 0 and torch.count_nonzero(z) == 0             # nothing dropped
+
+
+@pytest.mark.parametrize("name,diag,mean", [("tiny_s2", True, True), ("vggt_s8", True, True),
+                                            ("vggt_s8", True, False), ("vggt_s8", False, True)])
+def test_subsample_completion_dense(name, diag, mean):
+    w = synth.WORKLOADS[name]
+    say(f"[case] subsample completion, dense over kept keys: {name} diag={diag} mean={mean}")
+    inp, q, v, K2, V2, klay, ol, rK2, rV2, (km, vm, n) = _sga_inputs(w, seed=7)
+    gk, gv, _ = S.sparse3d_discarded_mean(q, v, w.layout, w.grid, 2)
+    bias = oracle.sga_mean_bias(n)
+    sga = S.Sga(w.grid, 2, k_full=q if diag else None, v_full=v if diag else None,
+                kmean=gk if mean else None, vmean=gv if mean else None, mean_bias=bias)
+    out, lse = S.sparse3d_dense_attn_fwd(q, K2, V2, w.layout, klay, out_dtype=torch.float32,
+                                         return_lse=True, sga=sga)
+    rsga = dict(grid=w.grid, window=2, k_full=inp.k if diag else None, v_full=inp.v if diag else None,
+                kmean=km if mean else None, vmean=vm, mean_bias=bias)
+    rO, rl = oracle.dense_attend(inp.q, rK2, rV2, ol, oracle.Layout(*klay), 0.125, sga=rsga)
+    g, gl = out.cpu().numpy(), lse.cpu().numpy()
+    qv = oracle.query_rows(ol)
+    tol = TOL["f32"] if w.dtype == "f32" else TOL["bf16"]
+    ltol = 1e-5 if w.dtype == "f32" else LSE_TOL_BF16
+    assert float(np.max(np.abs(g[:, qv] - rO[:, qv]))) <= tol
+    assert np.all(np.abs(gl[:, qv] - rl[:, qv]) <= ltol)
+    assert np.all(g[:, ~qv] == 0)
+
+
+def test_subsample_completion_sparse_with_landmarks():
+    w = synth.WORKLOADS["vggt_s8"]
+    say("[case] subsample completion on the tile-sparse call with landmarks, vggt_s8")
+    inp, q, v, K2, V2, klay, ol, rK2, rV2, (km, vm, n) = _sga_inputs(w, seed=8)
+    okl = oracle.Layout(*klay)
+    _, kbar, vbar, sc = S.sparse3d_tile_scores(q, K2, w.layout, klay, v=V2)
+    tpf = klay[2] // 64
+    idx, cnt = S.sparse3d_select_topk(sc, 6, tpf, 0)
+    gk, gv, _ = S.sparse3d_discarded_mean(q, v, w.layout, w.grid, 2)
+    bias = oracle.sga_mean_bias(n)
+    sga = S.Sga(w.grid, 2, k_full=q, v_full=v, kmean=gk, vmean=gv, mean_bias=bias)
+    out, lse = S.sparse3d_sparse_attn_fwd(q, K2, V2, w.layout, klay, idx, cnt,
+                                          kbar=S.sparse3d_cast(kbar, q.dtype),
+                                          vbar=S.sparse3d_cast(vbar, q.dtype),
+                                          out_dtype=torch.float32, return_lse=True, sga=sga)
+    rkbar, kc = oracle.tile_pool(rK2, okl, 64, "key")
+    rvbar, _ = oracle.tile_pool(rV2, okl, 64, "key")
+    rsga = dict(grid=w.grid, window=2, k_full=inp.k, v_full=inp.v, kmean=km, vmean=vm, mean_bias=bias)
+    g_idx, g_cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    rO, rl = oracle.sparse_attend(inp.q, rK2, rV2, ol, okl, 64, g_idx, g_cnt, 0.125, kbar=rkbar,
+                                  vbar=rvbar, kcount=kc, sga=rsga)
+    g, gl = out.cpu().numpy(), lse.cpu().numpy()
+    qv = oracle.query_rows(ol)
+    assert float(np.max(np.abs(g[:, qv] - rO[:, qv]))) <= TOL["bf16"]
+    assert np.all(np.abs(gl[:, qv] - rl[:, qv]) <= LSE_TOL_BF16)
