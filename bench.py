@@ -215,6 +215,33 @@ def time_frame(torch, S, q, v, lay, reps):
     return a.elapsed_time(b) / reps
 
 
+def time_sga(torch, S, LY, q, v, w, reps=3):
+    """AVGGT subsampled global attention on the same inputs: 2x2 key/value subsample, the
+    dropped patches' mean pair, then every query over all kept keys + its own key (where
+    dropped) + the mean pair.  Times the mean and the attention call."""
+    K2, V2, klay = S.sparse3d_grid_subsample_kv(q, v, w.layout, w.grid, 2)
+    km, vm, n = S.sparse3d_discarded_mean(q, v, w.layout, w.grid, 2)
+    sga = S.Sga(w.grid, 2, k_full=q, v_full=v, kmean=km, vmean=vm, mean_bias=math.log(n))
+    S.sparse3d_dense_attn_fwd(q, K2, V2, w.layout, klay, sga=sga)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(st)
+    for _ in range(reps):
+        S.sparse3d_discarded_mean(q, v, w.layout, w.grid, 2)
+    ev[1].record(st)
+    for _ in range(reps):
+        S.sparse3d_dense_attn_fwd(q, K2, V2, w.layout, klay, sga=sga)
+    ev[2].record(st)
+    torch.cuda.synchronize()
+    mean_ms = ev[0].elapsed_time(ev[1]) / reps
+    attn_ms = ev[1].elapsed_time(ev[2]) / reps
+    flops = LY.pair_flops() * w.heads * (w.rows // 64) * (klay[0] * klay[2] // 64)
+    return {"window": 2, "kept_keys_per_frame": klay[1], "dropped_rows": n,
+            "discarded_mean_ms": round(mean_ms, 4), "attn_ms": round(attn_ms, 4),
+            "attn_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 2)}
+
+
 def traffic_entry():
     """Per-launch HBM bytes of the attention kernel from committed counter runs, or None
     when the kernel source changed after the counters were taken."""
@@ -367,6 +394,8 @@ def main():
         fms = time_frame(torch, S, q, v, w.layout, 5)
         fflops = LY.pair_flops() * w.heads * L.Tq * (w.stride // 64)
         res["frame_attention"] = {"ms": round(fms, 4), "tflops": round(fflops / (fms * 1e-3) / 1e12, 2)}
+        if w.landmarks is False and w.kv_window == 1:
+            res["subsampled_global_attention"] = time_sga(torch, S, LY, q, v, w)
     if not args.no_gate and not args.no_dense and w.name == "vggt_s128":
         w90 = synth.WORKLOADS["vggt_s128_90"]
         L90 = Layer(S, LY, w90, q, v)
