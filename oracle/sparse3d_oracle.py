@@ -42,6 +42,13 @@ What is computed, and the passages it follows
   frame); the attention calls take both terms through ``sga``.  Reading: the
   mean pair stands for all |D| dropped columns at once, so its logit carries
   ln |D| (``sga_mean_bias``), exactly as a landmark carries ln 64 for its tile.
+* Zebra3D (abstract) also trains after conversion, and the EPFL page trains
+  with sparse attention; both need the gradient of the sparse layer.
+  ``sparse_attend_bwd`` is the exact gradient of ``sparse_attend``'s output with
+  the selection held fixed (top-k is piecewise constant, so no gradient flows
+  through the scores): with P the softmax weights of a row, dP = dO V^T,
+  D = rowsum(dO * O), dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q,
+  dV = P^T dO, summed over every query that attends a key.
 * AVGGT technical summary, section 2B.1: the early global layers, which exchange
   no information between views, become attention within each frame.
   ``frame_attend`` is that operation: every valid query over the valid keys of
@@ -249,6 +256,60 @@ def sparse_attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, qlay: Layout, kla
             O[h, rows_q] = o
             lse[h, rows_q] = l
     return O, lse
+
+
+def sparse_attend_bwd(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray, qlay: Layout,
+                      klay: Layout, tile: int, idx: np.ndarray, cnt: np.ndarray,
+                      scale: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of ``sparse_attend`` (no landmarks) w.r.t. Q, K, V for the output cotangent
+    dO, selection fixed: (dQ [H, Lq, d], dK [H, Lk, d], dV [H, Lk, d], D [H, Lq]) in fp64,
+    D = rowsum(dO * O).  Rows that are not valid queries contribute nothing and get
+    dQ = 0, D = 0; key rows nobody attends (pad, unselected tiles) get dK = dV = 0."""
+    H, Lq, d = Q.shape
+    Tk = klay.rows // tile
+    qv = query_rows(qlay)
+    mem = member_rows(klay).reshape(Tk, tile)
+    spec = np.nonzero(special_rows(klay))[0]
+    dQ = np.zeros((H, Lq, d))
+    dK = np.zeros((H, K.shape[1], d))
+    dV = np.zeros((H, K.shape[1], d))
+    D = np.zeros((H, Lq))
+    for h in range(H):
+        for tq in range(qlay.rows // tile):
+            rows_q = tq * tile + np.nonzero(qv[tq * tile:(tq + 1) * tile])[0]
+            if rows_q.size == 0:
+                continue
+            sel = idx[h, tq, : cnt[h, tq]]
+            J = np.concatenate([spec] + [t * tile + np.nonzero(mem[t])[0] for t in sel]).astype(np.int64)
+            if J.size == 0:
+                continue
+            q = Q[h, rows_q].astype(np.float64)
+            kk = K[h, J].astype(np.float64)
+            vv = V[h, J].astype(np.float64)
+            g = dO[h, rows_q].astype(np.float64)
+            s = scale * (q @ kk.T)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            o = p @ vv
+            dp = g @ vv.T
+            Di = np.sum(g * o, axis=1)
+            ds = p * (dp - Di[:, None])
+            dQ[h, rows_q] = scale * (ds @ kk)
+            np.add.at(dK[h], J, scale * (ds.T @ q))
+            np.add.at(dV[h], J, p.T @ g)
+            D[h, rows_q] = Di
+    return dQ, dK, dV, D
+
+
+def selection_transpose(idx: np.ndarray, cnt: np.ndarray, k_tiles: int) -> list:
+    """For each head and key tile, the ascending list of query tiles that selected it."""
+    H, Tq, _ = idx.shape
+    out = [[[] for _ in range(k_tiles)] for _ in range(H)]
+    for h in range(H):
+        for tq in range(Tq):
+            for t in idx[h, tq, : cnt[h, tq]]:
+                out[h][int(t)].append(tq)
+    return out
 
 
 def dense_attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, qlay: Layout, klay: Layout,

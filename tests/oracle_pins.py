@@ -583,6 +583,94 @@ def pin_sga_nothing_dropped(o):
     assert np.allclose(got[:, qv], want[:, qv], rtol=0, atol=1e-12)
 
 
+# --------------------------------------------------------------------------- backward
+def _bwd_case(o, S=2, N=60, P=64, nsp=5, tile=16, k=2, seed=0, H=2, d=8):
+    Q, K, V = _rand_inputs(S, N, P, nsp, H=H, d=d, seed=seed)
+    lay = o.Layout(S, N, P, nsp)
+    idx, cnt, _, _ = _selection(o, Q, K, lay, tile, k, 0, 0.3)
+    rng = np.random.default_rng(seed + 1)
+    dO = rng.standard_normal(Q.shape)
+    return Q, K, V, dO, lay, idx, cnt
+
+
+def _explicit_mask(lay, tile, idx, cnt, h):
+    """[Lq, Lk] boolean: valid query i may attend key j (special, or member of a tile its
+    query tile selected), written out from positions."""
+    L = lay.rows
+    j = np.arange(L) % lay.stride
+    qvalid = j < lay.tokens
+    special = j < lay.specials
+    member = (j >= lay.specials) & (j < lay.tokens)
+    M = np.zeros((L, L), dtype=bool)
+    for i in np.nonzero(qvalid)[0]:
+        tq = i // tile
+        allowed = special.copy()
+        for t in idx[h, tq, :cnt[h, tq]]:
+            allowed[t * tile:(t + 1) * tile] |= member[t * tile:(t + 1) * tile]
+        M[i] = allowed
+    return M
+
+
+def pin_backward_autograd(o):
+    """The gradient equals torch autograd (fp64, CPU) of masked attention whose mask is
+    written out from the selection."""
+    for (S, N, P, nsp, tile, k) in [(2, 60, 64, 5, 16, 2), (3, 40, 48, 0, 16, 3), (2, 30, 32, 6, 8, 1)]:
+        Q, K, V, dO, lay, idx, cnt = _bwd_case(o, S, N, P, nsp, tile, k, seed=N)
+        dQ, dK, dV, D = o.sparse_attend_bwd(Q, K, V, dO, lay, lay, tile, idx, cnt, 0.3)
+        qv = (np.arange(lay.rows) % lay.stride) < lay.tokens
+        for h in range(Q.shape[0]):
+            M = torch.from_numpy(_explicit_mask(lay, tile, idx, cnt, h))
+            qt = torch.tensor(np.nan_to_num(Q[h]), requires_grad=True)
+            kt = torch.tensor(np.nan_to_num(K[h]), requires_grad=True)
+            vt = torch.tensor(np.nan_to_num(V[h]), requires_grad=True)
+            logits = (0.3 * qt @ kt.T).masked_fill(~M, float("-inf"))
+            rows = torch.from_numpy(qv)
+            pr = torch.softmax(logits[rows], dim=1)
+            out = pr @ vt
+            (out * torch.from_numpy(dO[h][qv])).sum().backward()
+            assert np.allclose(dQ[h], qt.grad.numpy(), rtol=0, atol=1e-10)
+            assert np.allclose(dK[h], kt.grad.numpy(), rtol=0, atol=1e-10)
+            assert np.allclose(dV[h], vt.grad.numpy(), rtol=0, atol=1e-10)
+            O, _ = o.sparse_attend(Q, K, V, lay, lay, tile, idx, cnt, 0.3)
+            assert np.allclose(D[h, qv], np.sum(dO[h, qv] * O[h, qv], axis=1), rtol=0, atol=1e-12)
+            assert np.all(dQ[h, ~qv] == 0) and np.all(D[h, ~qv] == 0)
+
+
+def pin_backward_finite_difference(o):
+    """Central differences of sum(dO * O) through the forward oracle."""
+    S, N, P, nsp, tile = 2, 7, 8, 2, 4
+    Q, K, V = _rand_inputs(S, N, P, nsp, H=1, d=3, seed=2, pad=0.0)
+    lay = o.Layout(S, N, P, nsp)
+    idx, cnt, _, _ = _selection(o, Q, K, lay, tile, 1, 0, 0.5)
+    dO = np.random.default_rng(3).standard_normal(Q.shape)
+    dQ, dK, dV, _ = o.sparse_attend_bwd(Q, K, V, dO, lay, lay, tile, idx, cnt, 0.5)
+    f = lambda Q_, K_, V_: float(np.sum(dO * o.sparse_attend(Q_, K_, V_, lay, lay, tile, idx, cnt, 0.5)[0]))
+    eps = 1e-6
+    for X, G, which in ((Q, dQ, 0), (K, dK, 1), (V, dV, 2)):
+        for r in range(X.shape[1]):
+            for c in range(X.shape[2]):
+                args = [Q.copy(), K.copy(), V.copy()]
+                args[which][0, r, c] += eps
+                up = f(*args)
+                args[which][0, r, c] -= 2 * eps
+                dn = f(*args)
+                assert abs((up - dn) / (2 * eps) - G[0, r, c]) < 1e-6, (which, r, c)
+
+
+def pin_selection_transpose(o):
+    rng = np.random.default_rng(31)
+    for _ in range(10):
+        H, Tq, Tk = 2, int(rng.integers(1, 12)), int(rng.integers(1, 12))
+        sc = rng.standard_normal((H, Tq, Tk))
+        k = int(rng.integers(0, Tk + 1))
+        idx, cnt = o.select_topk(sc, k, 1, -1)
+        T = o.selection_transpose(idx, cnt, Tk)
+        for h in range(H):
+            for t in range(Tk):
+                want = [tq for tq in range(Tq) if t in set(idx[h, tq, :cnt[h, tq]].tolist())]
+                assert T[h][t] == want
+
+
 ALL_PINS = [
     pin_block_mean_identity, pin_tile_constant_pool, pin_symmetric_scores,
     pin_select_brute_force, pin_select_invariants,
@@ -592,4 +680,5 @@ ALL_PINS = [
     pin_empty_key_set, pin_subsample, pin_hand_worked,
     pin_select_per_head, pin_frame_attention,
     pin_sga_explicit_key_list, pin_sga_constant_dropped_is_dense, pin_sga_nothing_dropped,
+    pin_backward_autograd, pin_backward_finite_difference, pin_selection_transpose,
 ]

@@ -44,6 +44,12 @@ MUTANTS = {
                               'ml = scale * (q @ sga["kmean"][h])'),
     "sga_mean_over_all_patches": ("if y % window or x % window]", "if True]"),
     "sga_bias_count_plus_one": ("return math.log(count)", "return math.log(count + 1)"),
+    "bwd_without_rowsum": ("ds = p * (dp - Di[:, None])", "ds = p * dp"),
+    "bwd_dk_unscaled": ("np.add.at(dK[h], J, scale * (ds.T @ q))", "np.add.at(dK[h], J, ds.T @ q)"),
+    "bwd_dv_from_ds": ("np.add.at(dV[h], J, p.T @ g)", "np.add.at(dV[h], J, ds.T @ g)"),
+    "bwd_dq_transposed_keys": ("dQ[h, rows_q] = scale * (ds @ kk)", "dQ[h, rows_q] = scale * (ds @ vv)"),
+    "transpose_drops_first": ("            for t in idx[h, tq, : cnt[h, tq]]:\n                out[h][int(t)].append(tq)",
+                              "            for t in idx[h, tq, 1: cnt[h, tq]]:\n                out[h][int(t)].append(tq)"),
     "sga_diag_value_from_key": ('np.nan_to_num(sga["v_full"][h, rows_q].astype(np.float64))',
                                 'np.nan_to_num(sga["k_full"][h, rows_q].astype(np.float64))'),
 }
