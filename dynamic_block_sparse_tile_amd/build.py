@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsparse3d.so")
 
-SOURCES = ["validate.cpp", "api.hip", "pool_score.hip", "topk.hip", "attn.hip", "attn_bf16.hip", "subsample.hip"]
+SOURCES = ["validate.cpp", "api.hip", "pool_score.hip", "topk.hip", "attn.hip", "attn_bf16.hip", "attn_bwd.hip",
+           "subsample.hip"]
 
 ARCH = os.environ.get("SPARSE3D_ARCH", "gfx950")
 # Packed fp32 VALU ops are disabled in device code (the compiler would otherwise form

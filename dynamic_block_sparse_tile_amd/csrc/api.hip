@@ -150,6 +150,31 @@ int sparse3d_discarded_mean(const void* k, const void* v, sparse3d_dtype dtype, 
     return SPARSE3D_OK;
 }
 
+int sparse3d_selection_transpose(const int32_t* idx, const int32_t* cnt, int32_t heads, int32_t q_tiles,
+                                 int32_t k_tiles, int32_t kmax, int32_t* t_end, int32_t* t_list,
+                                 void* stream) {
+    const int st = validate_selection_transpose(idx, cnt, heads, q_tiles, k_tiles, kmax, t_end, t_list);
+    if (st != SPARSE3D_OK) return st;
+    S3D_HIP(launch_selection_transpose(idx, cnt, heads, q_tiles, k_tiles, kmax, t_end, t_list,
+                                       static_cast<hipStream_t>(stream)));
+    return SPARSE3D_OK;
+}
+
+int sparse3d_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                             const float* lse, sparse3d_dtype dtype, int32_t heads, int32_t head_dim,
+                             int32_t tile, const sparse3d_layout* qlay, const sparse3d_layout* klay,
+                             const int32_t* idx, const int32_t* cnt, int32_t kmax, const int32_t* t_end,
+                             const int32_t* t_list, float scale, float* dq, float* dk, float* dv,
+                             float* delta, void* stream) {
+    const int st = validate_attn_bwd(q, k, v, out, dout, lse, dtype, heads, head_dim, tile, qlay, klay, idx,
+                                     cnt, kmax, t_end, t_list, scale, dq, dk, dv, delta);
+    if (st != SPARSE3D_OK) return st;
+    BwdArgs a{q, k, v, out, dout, lse, heads, to_lay(*qlay), to_lay(*klay), idx, cnt, kmax, t_end, t_list,
+              scale, dq, dk, dv, delta};
+    S3D_HIP(launch_attn_bwd(a, static_cast<hipStream_t>(stream)));
+    return SPARSE3D_OK;
+}
+
 int sparse3d_subsample_layout(const sparse3d_layout* lay, int32_t grid_h, int32_t grid_w,
                               int32_t window, int32_t tile, sparse3d_layout* out_lay) {
     return subsample_layout(lay, grid_h, grid_w, window, tile, out_lay);

@@ -19,48 +19,11 @@
 #include "attn_common.h"
 #include "device.h"
 #include "launch.h"
+#include "tile_lds.h"
 
 namespace s3d {
 
-namespace {
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
-
-constexpr int TILE_BYTES = TILE * 128;           // one bf16 64x64 tile
-
-// Physical 16-byte slot of logical chunk `chunk` in tile row `row`.  The XOR key uses
-// row bits 0-3 so that, with 64 LDS banks served 16 lanes (b128) or 32 lanes (b64) per
-// pass, both the K-operand reads (16 rows, one chunk each) and the transposing V reads
-// (4 rows, 4 chunks each) touch every bank at most once per pass.
-__device__ __forceinline__ int swz_key(int row) {
-    return (((row & 2) << 1) | ((row >> 2) & 3)) ^ ((row & 1) << 1);
-}
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ swz_key(row); }
-
-// Word 3 of a raw buffer resource on gfx9-class parts (32-bit data format, no swizzle).
-constexpr int BUF_RSRC_WORD3 = 0x00020000;
-// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
-// lgkmcnt 11:8; a field at its maximum does not wait).
-constexpr int WAITCNT_VM0_LGKM0 = 0x0070;        // vmcnt(0) lgkmcnt(0)
-constexpr int WAITCNT_LGKM0 = 0xC07F;            // lgkmcnt(0) only
-// Scheduling-barrier mask: ALU, VALU, SALU, matrix, LDS and transcendental instructions may
-// move across it, vector-memory instructions may not.
-constexpr int SCHED_ALLOW_ALL_BUT_VMEM = 0x1 | 0x2 | 0x4 | 0x8 | 0x80 | 0x100 | 0x200 | 0x400;
-
-// A byte offset past every per-head buffer: buffer loads there return zeros.
-constexpr unsigned OOB_OFFSET = 0x80000000u;
-
-// 16 bytes per lane from buffer `rs` at byte offset voff + soff into LDS at
-// lds_base + 16 * lane.
-__device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t rs, lds_u8* lds_base, unsigned voff,
-                                        unsigned soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_base, 16, voff, soff, 0, 0);
-}
-
-}  // namespace
+using namespace tl;
 
 // max of three floats without the NaN-quieting canonicalisation the compiler adds around
 // fmaxf (scores come from the matrix core or are -inf, never signalling NaNs)

@@ -45,6 +45,31 @@ struct AttnArgs {
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 
+// Backward of the sparse attention (bf16 operands; fp32 gradients)
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* out;
+    const void* dout;
+    const float* lse;
+    int heads;
+    LayH ql, kl;
+    const int32_t* idx;
+    const int32_t* cnt;
+    int kmax;
+    const int32_t* t_end;
+    const int32_t* t_list;
+    float scale;
+    float* dq;
+    float* dk;
+    float* dv;
+    float* delta;
+};
+hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t st);
+hipError_t launch_selection_transpose(const int32_t* idx, const int32_t* cnt, int heads, int tq, int tk,
+                                      int kmax, int32_t* t_end, int32_t* t_list, hipStream_t st);
+
 hipError_t launch_cast(const float* src, int64_t n, int dtype, void* dst, hipStream_t st);
 
 hipError_t launch_discarded_mean(const void* k, const void* v, int dtype, int heads, LayH lay,

@@ -185,6 +185,56 @@ int validate_discarded_mean(const void* k, const void* v, int dtype, int32_t hea
     return SPARSE3D_OK;
 }
 
+namespace {
+// any two of n byte ranges overlap
+bool any_overlap(const void* const* p, const size_t* n, int count) {
+    for (int i = 0; i < count; ++i)
+        for (int j = i + 1; j < count; ++j)
+            if (overlaps(p[i], n[i], p[j], n[j])) return true;
+    return false;
+}
+}  // namespace
+
+int validate_selection_transpose(const int32_t* idx, const int32_t* cnt, int32_t heads, int32_t q_tiles,
+                                 int32_t k_tiles, int32_t kmax, const int32_t* t_end, const int32_t* t_list) {
+    if (!cnt || !t_end) return SPARSE3D_ERR_NULL;
+    if (kmax > 0 && (!idx || !t_list)) return SPARSE3D_ERR_NULL;
+    if (heads < 1 || q_tiles < 1 || k_tiles < 1 || kmax < 0) return SPARSE3D_ERR_SHAPE;
+    if (q_tiles > kMaxTransposeQ || k_tiles > kMaxTopkTiles) return SPARSE3D_ERR_UNSUPPORTED;
+    const size_t ib = size_t(heads) * q_tiles * kmax * 4, cb = size_t(heads) * q_tiles * 4;
+    const size_t eb = size_t(heads) * k_tiles * 4;
+    const void* p[4] = {idx, cnt, t_end, t_list};
+    const size_t n[4] = {ib, cb, eb, ib};
+    if (any_overlap(p, n, 4)) return SPARSE3D_ERR_ALIAS;
+    return SPARSE3D_OK;
+}
+
+int validate_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                      const float* lse, int dtype, int32_t heads, int32_t head_dim, int32_t tile,
+                      const sparse3d_layout* qlay, const sparse3d_layout* klay, const int32_t* idx,
+                      const int32_t* cnt, int32_t kmax, const int32_t* t_end, const int32_t* t_list,
+                      float scale, const float* dq, const float* dk, const float* dv, const float* delta) {
+    if (!out || !dout || !lse || !t_end || !dq || !dk || !dv || !delta) return SPARSE3D_ERR_NULL;
+    if (kmax > 0 && !t_list) return SPARSE3D_ERR_NULL;
+    S3D_TRY(validate_attn(true, q, k, v, dtype, heads, head_dim, tile, qlay, klay, idx, cnt, kmax,
+                          nullptr, nullptr, dq, SPARSE3D_F32, nullptr));
+    if (dtype != SPARSE3D_BF16) return SPARSE3D_ERR_UNSUPPORTED;
+    if (kmax > kMaxBwdList || lay_tiles(*qlay) > kMaxTransposeQ) return SPARSE3D_ERR_UNSUPPORTED;
+    S3D_TRY(check_logit_params(scale, 0.f));
+    const size_t qb = size_t(heads) * lay_rows(*qlay) * head_dim;     // elements
+    const size_t kb = size_t(heads) * lay_rows(*klay) * head_dim;
+    const size_t lb = size_t(heads) * lay_rows(*qlay) * 4;
+    const size_t ib = size_t(heads) * lay_tiles(*qlay) * kmax * 4;
+    const size_t cb = size_t(heads) * lay_tiles(*qlay) * 4, eb = size_t(heads) * lay_tiles(*klay) * 4;
+    const void* p[14] = {q, k, v, out, dout, lse, idx, cnt, t_end, t_list, dq, dk, dv, delta};
+    const size_t n[14] = {qb * 2, kb * 2, kb * 2, qb * 2, qb * 2, lb, ib, cb, eb, ib, qb * 4, kb * 4, kb * 4, lb};
+    // outputs (the last four) against everything else and each other; q may equal k (self-attention)
+    for (int i = 10; i < 14; ++i)
+        for (int j = 0; j < 14; ++j)
+            if (j != i && overlaps(p[i], n[i], p[j], n[j])) return SPARSE3D_ERR_ALIAS;
+    return SPARSE3D_OK;
+}
+
 int validate_cast(const float* src, int64_t n, int dtype, const void* dst) {
     if (n < 0) return SPARSE3D_ERR_SHAPE;
     S3D_TRY(check_dtype(dtype));

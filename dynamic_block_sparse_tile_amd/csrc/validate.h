@@ -51,6 +51,20 @@ int validate_sga(const sparse3d_sga* sga, int dtype, int32_t heads, int32_t head
 int validate_discarded_mean(const void* k, const void* v, int dtype, int32_t heads, int32_t head_dim,
                             const sparse3d_layout* lay, int32_t grid_h, int32_t grid_w,
                             int32_t window, const float* kmean, const float* vmean);
+int validate_selection_transpose(const int32_t* idx, const int32_t* cnt, int32_t heads, int32_t q_tiles,
+                                 int32_t k_tiles, int32_t kmax, const int32_t* t_end, const int32_t* t_list);
+
+int validate_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                      const float* lse, int dtype, int32_t heads, int32_t head_dim, int32_t tile,
+                      const sparse3d_layout* qlay, const sparse3d_layout* klay, const int32_t* idx,
+                      const int32_t* cnt, int32_t kmax, const int32_t* t_end, const int32_t* t_list,
+                      float scale, const float* dq, const float* dk, const float* dv, const float* delta);
+
+// Longest tile list the backward's dQ kernel stages in LDS.
+constexpr int kMaxBwdList = 8000;
+// Most query tiles the selection transpose sorts per key tile (LDS bitonic sort).
+constexpr int kMaxTransposeQ = 16384;
+
 // Dropped patch rows per frame of the subsample (grid_h, grid_w, window).
 int64_t dropped_per_frame(int32_t grid_h, int32_t grid_w, int32_t window);
 

@@ -22,7 +22,7 @@ __all__ = [
     "sparse3d_tile_scores", "sparse3d_select_topk", "sparse3d_sparse_attn_fwd",
     "sparse3d_dense_attn_fwd", "sparse3d_subsample_layout", "sparse3d_grid_subsample_kv",
     "sparse3d_cast", "sparse3d_select_topk_per_head", "sparse3d_frame_attn_fwd",
-    "sparse3d_discarded_mean", "Sga",
+    "sparse3d_discarded_mean", "Sga", "sparse3d_selection_transpose", "sparse3d_sparse_attn_bwd",
     "kmax_for", "LN64",
 ]
 
@@ -69,6 +69,9 @@ _SIGS = {
                                  ctypes.c_int, _vp, _vp], ctypes.c_int),
     "sparse3d_discarded_mean": ([_vp, _vp, ctypes.c_int, _i32, _i32, _LP, _i32, _i32, _i32, _vp, _vp,
                                  _vp], ctypes.c_int),
+    "sparse3d_selection_transpose": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
+    "sparse3d_sparse_attn_bwd": ([_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32, _LP, _LP,
+                                  _vp, _vp, _i32, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "sparse3d_subsample_layout": ([_LP, _i32, _i32, _i32, _i32, _LP], ctypes.c_int),
     "sparse3d_grid_subsample_kv": ([_vp, _vp, ctypes.c_int, _i32, _i32, _LP, _i32, _i32, _i32,
                                     _vp, _vp, _LP, _vp], ctypes.c_int),
@@ -327,6 +330,43 @@ def sparse3d_discarded_mean(k, v, lay, grid: Tuple[int, int], window: int):
     gh, gw = grid
     kept = -(-gh // window) * -(-gw // window)
     return kmean, vmean, int(lay[0]) * (gh * gw - kept)
+
+
+def sparse3d_selection_transpose(idx: torch.Tensor, cnt: torch.Tensor, k_tiles: int):
+    """For each head and key tile, the ascending query tiles that selected it (CSR with end
+    offsets).  Returns (t_end int32 [H, k_tiles], t_list int32 [H, q_tiles * kmax])."""
+    _dev(idx, "idx"), _dev(cnt, "cnt")
+    H, Tq, kmax = idx.shape
+    t_end = torch.empty((H, k_tiles), device=idx.device, dtype=torch.int32)
+    t_list = torch.empty((H, Tq * max(kmax, 0)), device=idx.device, dtype=torch.int32)
+    _check(library().sparse3d_selection_transpose(_ptr(idx) if kmax > 0 else None, _ptr(cnt), H, Tq,
+                                                  k_tiles, kmax, _ptr(t_end),
+                                                  _ptr(t_list) if kmax > 0 else None, _stream(idx)))
+    return t_end, t_list
+
+
+def sparse3d_sparse_attn_bwd(q, k, v, out, dout, lse, qlay, klay, idx, cnt, t_end, t_list,
+                             scale: Optional[float] = None):
+    """Gradients of the sparse attention (no landmarks), selection fixed.
+    Returns (dq, dk, dv, delta), fp32."""
+    for x, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout"), (lse, "lse"),
+                 (idx, "idx"), (cnt, "cnt"), (t_end, "t_end"), (t_list, "t_list")):
+        _dev(x, n)
+    H = q.shape[0]
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else scale
+    f = dict(device=q.device, dtype=torch.float32)
+    dq = torch.empty(q.shape, **f)
+    dk = torch.empty(k.shape, **f)
+    dv = torch.empty(v.shape, **f)
+    delta = torch.empty(q.shape[:2], **f)
+    ql, kl = _lay(qlay), _lay(klay)
+    kmax = idx.shape[2]
+    _check(library().sparse3d_sparse_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _dt(q), H, q.shape[2], TILE,
+        ctypes.byref(ql), ctypes.byref(kl), _ptr(idx) if kmax > 0 else None, _ptr(cnt), kmax,
+        _ptr(t_end), _ptr(t_list) if kmax > 0 else None, scale, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta),
+        _stream(q)))
+    return dq, dk, dv, delta
 
 
 def sparse3d_subsample_layout(lay, grid_h: int, grid_w: int, window: int, tile: int = TILE):

@@ -179,6 +179,40 @@ int sparse3d_dense_attn_fwd(const void* q, const void* k, const void* v, sparse3
                             float* lse, void* stream);
 
 /*
+ * The selection transposed, for the backward pass: for each head h and key tile t, the
+ * query tiles whose list (idx/cnt as written by sparse3d_select_topk) holds t, ascending.
+ * CSR with end offsets: the list of (h, t) is t_list[h, b .. e) with e = t_end[h, t] and
+ * b = t_end[h, t-1] (0 for t = 0).  t_end: int32 [heads, k_tiles]; t_list: int32
+ * [heads, q_tiles * kmax] (the first sum-of-counts entries of each head are written).
+ * q_tiles <= 16384.  Deterministic (each list is sorted).
+ */
+int sparse3d_selection_transpose(const int32_t* idx, const int32_t* cnt, int32_t heads, int32_t q_tiles,
+                                 int32_t k_tiles, int32_t kmax, int32_t* t_end, int32_t* t_list,
+                                 void* stream);
+
+/*
+ * Backward of sparse3d_sparse_attn_fwd without landmarks, for training through the sparse
+ * layer (Zebra3D abstract: post-conversion training; EPFL "(Full) Attention is More Than
+ * You Need": sparse training).  The selection is held fixed (top-k is piecewise constant,
+ * no gradient flows into the scores).  Inputs: q, k, v, the forward's out and the output
+ * cotangent dout (all bf16, layouts as in the forward), the forward's lse, the selection
+ * idx/cnt and its transpose t_end/t_list (sparse3d_selection_transpose).  With P the
+ * softmax weights and D = rowsum(dout * out):
+ *   dS = P * (dout V^T - D),  dq = scale dS K,  dk = scale dS^T Q,  dv = P^T dout
+ * (special keys are attended by every query, member keys by the query tiles that selected
+ * their tile).  Outputs, fp32 and fully overwritten: dq [heads, Lq, 64] (0 on rows that
+ * are not valid queries), dk and dv [heads, Lk, 64] (0 on pad rows and on keys nobody
+ * attends), delta [heads, Lq] = D (0 on invalid rows).  bf16 operands only
+ * (SPARSE3D_ERR_UNSUPPORTED for F32), kmax <= 8000, Tq <= 16384.  Deterministic.
+ */
+int sparse3d_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                             const float* lse, sparse3d_dtype dtype, int32_t heads, int32_t head_dim,
+                             int32_t tile, const sparse3d_layout* qlay, const sparse3d_layout* klay,
+                             const int32_t* idx, const int32_t* cnt, int32_t kmax, const int32_t* t_end,
+                             const int32_t* t_list, float scale, float* dq, float* dk, float* dv,
+                             float* delta, void* stream);
+
+/*
  * The mean key and mean value of every patch row the grid subsample (grid_h, grid_w,
  * window) drops, over all frames, per head (the pair that stands in for the dropped
  * columns, AVGGT technical summary, section 2B.2): kmean/vmean [heads, 64] fp32,

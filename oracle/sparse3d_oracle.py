@@ -260,11 +260,15 @@ def sparse_attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, qlay: Layout, kla
 
 def sparse_attend_bwd(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray, qlay: Layout,
                       klay: Layout, tile: int, idx: np.ndarray, cnt: np.ndarray,
-                      scale: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+                      scale: float, query_tiles: Optional[Sequence[int]] = None,
+                      heads: Optional[Sequence[int]] = None
+                      ) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
     """Gradients of ``sparse_attend`` (no landmarks) w.r.t. Q, K, V for the output cotangent
     dO, selection fixed: (dQ [H, Lq, d], dK [H, Lk, d], dV [H, Lk, d], D [H, Lq]) in fp64,
     D = rowsum(dO * O).  Rows that are not valid queries contribute nothing and get
-    dQ = 0, D = 0; key rows nobody attends (pad, unselected tiles) get dK = dV = 0."""
+    dQ = 0, D = 0; key rows nobody attends (pad, unselected tiles) get dK = dV = 0.
+    With ``query_tiles`` / ``heads`` only those query tiles contribute (dK/dV of a key tile
+    are then complete when the list holds every query tile that selected it)."""
     H, Lq, d = Q.shape
     Tk = klay.rows // tile
     qv = query_rows(qlay)
@@ -274,8 +278,8 @@ def sparse_attend_bwd(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarra
     dK = np.zeros((H, K.shape[1], d))
     dV = np.zeros((H, K.shape[1], d))
     D = np.zeros((H, Lq))
-    for h in range(H):
-        for tq in range(qlay.rows // tile):
+    for h in (range(H) if heads is None else heads):
+        for tq in (range(qlay.rows // tile) if query_tiles is None else query_tiles):
             rows_q = tq * tile + np.nonzero(qv[tq * tile:(tq + 1) * tile])[0]
             if rows_q.size == 0:
                 continue

@@ -186,6 +186,37 @@ def test_discarded_mean_validation(lib):
     assert dm(vm=FAKE + 10**9 + 128) == ERR_ALIAS                           # the two means overlap
 
 
+def test_transpose_validation(lib):
+    tr = lambda idx=FAKE, cnt=FAKE + 10**9, H=2, tq=8, tk=8, kmax=4, te=FAKE + 2 * 10**9, tl=FAKE + 3 * 10**9: \
+        lib.sparse3d_selection_transpose(idx, cnt, H, tq, tk, kmax, te, tl, NULL)
+    assert tr(cnt=NULL) == ERR_NULL
+    assert tr(te=NULL) == ERR_NULL
+    assert tr(tl=NULL) == ERR_NULL
+    assert tr(kmax=-1) == ERR_SHAPE
+    assert tr(H=0) == ERR_SHAPE
+    assert tr(tq=16385) == ERR_UNSUP
+    assert tr(tl=FAKE + 64) == ERR_ALIAS                                  # list inside idx
+
+
+def test_backward_validation(lib):
+    ql = L()
+    def bwd(q=FAKE, out=FAKE + 3 * 10**9, dout=FAKE + 4 * 10**9, lse=FAKE + 5 * 10**9, dt=1, kmax=8,
+            dq=FAKE + 9 * 10**9, dk=FAKE + 10 * 10**9, dv=FAKE + 11 * 10**9, delta=FAKE + 12 * 10**9,
+            scale=0.125, d=64):
+        return lib.sparse3d_sparse_attn_bwd(q, FAKE + 10**9, FAKE + 2 * 10**9, out, dout, lse, dt, 2, d, 64,
+                                            ql, ql, FAKE + 6 * 10**9, FAKE + 7 * 10**9, kmax,
+                                            FAKE + 8 * 10**9, FAKE + 13 * 10**9, scale, dq, dk, dv, delta, NULL)
+    assert bwd(out=NULL) == ERR_NULL
+    assert bwd(lse=NULL) == ERR_NULL
+    assert bwd(delta=NULL) == ERR_NULL
+    assert bwd(dt=0) == ERR_UNSUP                                          # fp32 operands
+    assert bwd(d=32) == ERR_UNSUP
+    assert bwd(scale=0.0) == ERR_UNSUP
+    assert bwd(dq=FAKE + 64) == ERR_ALIAS                                  # dq inside q
+    assert bwd(dk=FAKE + 9 * 10**9 + 64) == ERR_ALIAS                     # dk inside dq
+    assert bwd(delta=FAKE + 5 * 10**9 + 4) == ERR_ALIAS                   # delta inside lse
+
+
 def test_cast_validation(lib):
     cast = lib.sparse3d_cast
     assert cast(FAKE, -1, 1, FAKE + 10**9, NULL) == ERR_SHAPE

@@ -542,3 +542,107 @@ def test_subsample_completion_sparse_with_landmarks():
     qv = oracle.query_rows(ol)
     assert float(np.max(np.abs(g[:, qv] - rO[:, qv]))) <= TOL["bf16"]
     assert np.all(np.abs(gl[:, qv] - rl[:, qv]) <= LSE_TOL_BF16)
+
+
+# --------------------------------------------------------------------------- backward
+def _grad_close(g, ref, what, rel=2e-2):
+    lim = rel * max(1.0, float(np.max(np.abs(ref))))
+    err = float(np.max(np.abs(g.astype(np.float64) - ref)))
+    assert err <= lim, (what, err, lim)
+    return err
+
+
+def _bwd_setup(w, seed, k=None):
+    inp = synth.make_inputs(w, seed=seed)
+    q, v = to_dev(inp.q, torch.bfloat16), to_dev(inp.v, torch.bfloat16)
+    lay = w.layout
+    tpf = lay[2] // 64
+    _, _, _, sc = S.sparse3d_tile_scores(q, q, lay)
+    idx, cnt = S.sparse3d_select_topk(sc, w.k if k is None else k, tpf, w.anchor)
+    out, lse = S.sparse3d_sparse_attn_fwd(q, q, v, lay, lay, idx, cnt, return_lse=True)
+    rng = np.random.default_rng(seed + 100)
+    dO = synth.round_bf16(rng.standard_normal(inp.q.shape).astype(np.float32))
+    dout = to_dev(dO, torch.bfloat16)
+    t_end, t_list = S.sparse3d_selection_transpose(idx, cnt, sc.shape[2])
+    dq, dk, dv, delta = S.sparse3d_sparse_attn_bwd(q, q, v, out, dout, lse, lay, lay, idx, cnt, t_end, t_list)
+    torch.cuda.synchronize()
+    return inp, dO, idx.cpu().numpy(), cnt.cpu().numpy(), t_end, t_list, (dq, dk, dv, delta), out, sc.shape[2]
+
+
+def test_selection_transpose():
+    w = synth.WORKLOADS["vggt_s8"]
+    say("[case] selection transpose vggt_s8")
+    inp, dO, g_idx, g_cnt, t_end, t_list, *_ , Tk = _bwd_setup(w, seed=11)
+    ref = oracle.selection_transpose(g_idx, g_cnt, Tk)
+    te, tl = t_end.cpu().numpy(), t_list.cpu().numpy()
+    for h in range(g_idx.shape[0]):
+        b = 0
+        for t in range(Tk):
+            e = int(te[h, t])
+            assert tl[h, b:e].tolist() == ref[h][t], (h, t)
+            b = e
+
+
+@pytest.mark.parametrize("seed,k", [(12, None), (13, 40), (14, 0)])
+def test_backward_vggt_s8(seed, k):
+    w = synth.WORKLOADS["vggt_s8"]
+    say(f"[case] backward vggt_s8 seed={seed} k={k}")
+    inp, dO, g_idx, g_cnt, t_end, t_list, (dq, dk, dv, delta), out, Tk = _bwd_setup(w, seed, k)
+    ol = oracle.Layout(*w.layout)
+    rdq, rdk, rdv, rD = oracle.sparse_attend_bwd(inp.q, inp.k, inp.v, dO, ol, ol, 64, g_idx, g_cnt, 0.125)
+    _grad_close(dq.cpu().numpy(), rdq, "dq")
+    _grad_close(dk.cpu().numpy(), rdk, "dk")
+    _grad_close(dv.cpu().numpy(), rdv, "dv")
+    _grad_close(delta.cpu().numpy(), rD, "delta")
+    qv = oracle.query_rows(ol)
+    assert np.all(dq.cpu().numpy()[:, ~qv] == 0)
+    pad = ~oracle.query_rows(ol)
+    assert np.all(dk.cpu().numpy()[:, pad] == 0) and np.all(dv.cpu().numpy()[:, pad] == 0)
+
+
+def test_backward_nan_pad_and_determinism():
+    w = synth.WORKLOADS["vggt_s8"]
+    say("[case] backward with NaN pad rows, twice")
+    inp = synth.make_inputs(w, seed=15, pad_value=np.nan)
+    q, v = to_dev(inp.q, torch.bfloat16), to_dev(inp.v, torch.bfloat16)
+    lay = w.layout
+    _, _, _, sc = S.sparse3d_tile_scores(q, q, lay)
+    idx, cnt = S.sparse3d_select_topk(sc, 18, lay[2] // 64, 0)
+    out, lse = S.sparse3d_sparse_attn_fwd(q, q, v, lay, lay, idx, cnt, return_lse=True)
+    dO = np.random.default_rng(16).standard_normal(inp.q.shape).astype(np.float32)
+    dO[:, ~oracle.query_rows(oracle.Layout(*lay))] = np.nan           # the cotangent's pad may hold NaN too
+    dout = to_dev(dO, torch.bfloat16)
+    t_end, t_list = S.sparse3d_selection_transpose(idx, cnt, sc.shape[2])
+    r1 = S.sparse3d_sparse_attn_bwd(q, q, v, out, dout, lse, lay, lay, idx, cnt, t_end, t_list)
+    r2 = S.sparse3d_sparse_attn_bwd(q, q, v, out, dout, lse, lay, lay, idx, cnt, t_end, t_list)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+        assert not torch.isnan(a).any()
+
+
+def test_backward_full_s128_sampled():
+    w = synth.WORKLOADS["vggt_s128"]
+    say("[case] backward vggt_s128 (k=138), sampled query and key tiles")
+    inp, dO, g_idx, g_cnt, t_end, t_list, (dq, dk, dv, delta), out, Tk = _bwd_setup(w, seed=0, k=138)
+    ol = oracle.Layout(*w.layout)
+    H, Tq = g_idx.shape[0], g_idx.shape[1]
+    pairs = sample_tiles(H, Tq, 6, seed=3)
+    for (h, t) in pairs:                                             # dQ of sampled query tiles
+        rdq, _, _, rD = oracle.sparse_attend_bwd(inp.q, inp.k, inp.v, dO, ol, ol, 64, g_idx, g_cnt, 0.125,
+                                                 query_tiles=[t], heads=[h])
+        r = slice(t * 64, (t + 1) * 64)
+        _grad_close(dq[h, r].cpu().numpy(), rdq[h, r], ("dq", h, t))
+        _grad_close(delta[h, r].cpu().numpy(), rD[h, r], ("delta", h, t))
+    te = t_end.cpu().numpy()
+    tl = t_list.cpu().numpy()
+    tpf = w.layout[2] // 64
+    key_pairs = [(h, t) for (h, t) in sample_tiles(H, Tk, 4, seed=4) if t >= tpf]   # not the anchor frame
+    for (h, t) in key_pairs:                                         # dK, dV of sampled key tiles
+        b = 0 if t == 0 else int(te[h, t - 1])
+        qt = tl[h, b:int(te[h, t])].tolist()
+        _, rdk, rdv, _ = oracle.sparse_attend_bwd(inp.q, inp.k, inp.v, dO, ol, ol, 64, g_idx, g_cnt, 0.125,
+                                                  query_tiles=qt, heads=[h])
+        j = np.arange(t * 64, (t + 1) * 64)
+        mem = j[oracle.member_rows(ol)[j]]
+        _grad_close(dk[h, mem].cpu().numpy(), rdk[h, mem], ("dk", h, t))
+        _grad_close(dv[h, mem].cpu().numpy(), rdv[h, mem], ("dv", h, t))
