@@ -33,6 +33,37 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
     return r;
 }
 
+// max over the 32 scores of a lane (two 16-element accumulators), as two asm blocks of
+// eight dependent v_max3_f32 each: one block per chain keeps the compiler from padding
+// every step of the chain with wait states, as it does between separate asm statements
+__device__ __forceinline__ float max32f(const f32x16& a, const f32x16& b) {
+    float m;
+    asm("v_max3_f32 %0, %1, %2, %3\n\t"
+        "v_max3_f32 %0, %0, %4, %5\n\t"
+        "v_max3_f32 %0, %0, %6, %7\n\t"
+        "v_max3_f32 %0, %0, %8, %9\n\t"
+        "v_max3_f32 %0, %0, %10, %11\n\t"
+        "v_max3_f32 %0, %0, %12, %13\n\t"
+        "v_max3_f32 %0, %0, %14, %15\n\t"
+        "v_max3_f32 %0, %0, %16, %17"
+        : "=&v"(m)
+        : "v"(a[0]), "v"(b[0]), "v"(a[1]), "v"(b[1]), "v"(a[2]), "v"(b[2]), "v"(a[3]), "v"(b[3]),
+          "v"(a[4]), "v"(b[4]), "v"(a[5]), "v"(b[5]), "v"(a[6]), "v"(b[6]), "v"(a[7]), "v"(b[7]),
+          "v"(-INFINITY));
+    asm("v_max3_f32 %0, %0, %1, %2\n\t"
+        "v_max3_f32 %0, %0, %3, %4\n\t"
+        "v_max3_f32 %0, %0, %5, %6\n\t"
+        "v_max3_f32 %0, %0, %7, %8\n\t"
+        "v_max3_f32 %0, %0, %9, %10\n\t"
+        "v_max3_f32 %0, %0, %11, %12\n\t"
+        "v_max3_f32 %0, %0, %13, %14\n\t"
+        "v_max3_f32 %0, %0, %15, %16"
+        : "+v"(m)
+        : "v"(a[8]), "v"(b[8]), "v"(a[9]), "v"(b[9]), "v"(a[10]), "v"(b[10]), "v"(a[11]), "v"(b[11]),
+          "v"(a[12]), "v"(b[12]), "v"(a[13]), "v"(b[13]), "v"(a[14]), "v"(b[14]), "v"(a[15]), "v"(b[15]));
+    return m;
+}
+
 // Rescale the running output only when some row max grew by more than this (base-2
 // units); otherwise probabilities are taken against the stale max and stay <= 2^8.
 constexpr float RESCALE_THRESHOLD = 8.0f;
@@ -89,7 +120,7 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
     // instead of a dependent global load (the launcher guarantees kmax <= IDX_LDS_MAX)
     int32_t* s_idx = reinterpret_cast<int32_t*>(s_lm + (LM ? 2 * p.nlm : 0));
     if (!DENSE) {
-        for (int i = tid; i < c; i += 128) s_idx[i] = myidx[i];
+        for (int i = tid; i < c; i += 128) s_idx[i] = pack_tile_entry(p, myidx[i]);
         __syncthreads();
         // Sweep the list starting at the query's own frame (wrapping round).  Workgroups
         // start one after another in frame order, so this keeps the ones running at the same
@@ -98,7 +129,8 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
         {
             const int thr = (tq / tpfq) * (p.kl.P / TILE);
             int n = 0;
-            for (int b = 0; b < c; b += 128) n += __syncthreads_count(b + tid < c && s_idx[b + tid] < thr);
+            for (int b = 0; b < c; b += 128)
+                n += __syncthreads_count(b + tid < c && (s_idx[b + tid] & 0xFFFF) < thr);
             rot = n < c ? n : 0;
         }
     }
@@ -277,9 +309,7 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
             }
         }
         const float bias = (LM && cur.kind == KIND_LM) ? p.lm_bias_l2 : 0.f;
-        float mx = max3f(s0[0], s1[0], -INFINITY);
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = max3f(mx, s0[r], s1[r]);
+        float mx = max32f(s0, s1);
         issue(2);
         mx = xhalf_max(mx);
         qk_ops(ka, n0, n1, 1);

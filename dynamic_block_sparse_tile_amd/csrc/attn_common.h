@@ -63,6 +63,15 @@ __device__ __forceinline__ TileDesc uniform(const TileDesc& d) {
     return u;
 }
 
+// A list entry with its member-row range precomputed: tile | lo << 16 | hi << 23, or -1
+// for an entry outside [0, Tk) (skipped).  Needs Tk < 65536 (the library allows 12288).
+__device__ __forceinline__ int32_t pack_tile_entry(const AttnDev& p, int32_t t) {
+    if (t < 0 || t >= p.Tk) return -1;
+    int lo, hi;
+    member_range(p.kl, t, lo, hi);
+    return t | (lo << 16) | (hi << 23);
+}
+
 // Longest selection list the bf16 kernel stages in LDS (next to its 32 KiB of tile
 // buffers, within 64 KiB); longer lists run on the generic kernel.
 constexpr int IDX_LDS_MAX = 8000;
@@ -91,10 +100,17 @@ __device__ __forceinline__ TileDesc describe(const AttnDev& p, int it, int c, co
     it -= p.Ts;
     if (it < c) {
         const int pos = it + rot < c ? it + rot : it + rot - c;
-        // the list entry is uniform across the workgroup: move it to a scalar register so
-        // the whole description (and every branch on it) stays on the scalar unit
-        const int t = __builtin_amdgcn_readfirstlane(IDX_LDS ? s_idx[pos] : myidx[pos]);
         d.kind = KIND_REG;
+        if (IDX_LDS) {
+            // the LDS copy holds pack_tile_entry() words, decoded when the list was staged;
+            // the entry is uniform across the workgroup, so it goes to a scalar register and
+            // the whole description (and every branch on it) stays on the scalar unit
+            const int word = __builtin_amdgcn_readfirstlane(s_idx[pos]);
+            d.t = word < 0 ? 0 : (word & 0xFFFF);
+            d.mask = word < 0 ? 0ull : range_mask((word >> 16) & 127, (word >> 23) & 127);
+            return d;
+        }
+        const int t = __builtin_amdgcn_readfirstlane(myidx[pos]);
         d.t = t;
         if (t < 0 || t >= p.Tk) {
             d.t = 0;
