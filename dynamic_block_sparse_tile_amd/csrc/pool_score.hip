@@ -71,77 +71,87 @@ __global__ __launch_bounds__(256) void k_tile_pool(const void* __restrict__ x, i
     }
 }
 
-// scores[h, tq, tk] = scale * qbar[h,tq] . kbar[h,tk] (-inf if either tile is empty).
-// 64x64 output block per workgroup of 256 threads, 4x4 outputs per thread; both
-// operand blocks are staged transposed in LDS so each inner step is two float4 reads.
-// The dot product is one fp32 FMA chain over d = 0..63, a fixed order.
-constexpr int SC_LD = 68;
-
-__global__ __launch_bounds__(256) void k_tile_scores(const float* __restrict__ qbar,
-                                                     const float* __restrict__ kbar, int Tq, int Tk,
-                                                     Lay ql, Lay kl, float scale,
-                                                     float* __restrict__ scores) {
-    __shared__ __align__(16) float qs[HD * SC_LD];
-    __shared__ __align__(16) float ks[HD * SC_LD];
+// Tile scores: a 128 x 128 block of scores per workgroup of 256 threads, 8 x 8 per thread
+// in fp32 FMAs (four 16-byte LDS reads per 64 FMAs), the 64 dims of the pooled means
+// staged in two transposed halves of 32.  sigma = scale * qbar . kbar, -inf where either
+// tile has no rows; the block's stores are whole 32-byte row segments.
+constexpr int SC2_T = 128;              // queries x keys per workgroup
+constexpr int SC2_LD = SC2_T + 4;       // padded row of the transposed halves
+__global__ __launch_bounds__(256) void k_tile_scores8(const float* __restrict__ qbar,
+                                                      const float* __restrict__ kbar, int Tq, int Tk,
+                                                      Lay ql, Lay kl, float scale,
+                                                      float* __restrict__ scores) {
+    __shared__ __align__(16) float qs[32 * SC2_LD];
+    __shared__ __align__(16) float ks[32 * SC2_LD];
     const int tid = threadIdx.x;
-    const int tk0 = blockIdx.x * 64, tq0 = blockIdx.y * 64, h = blockIdx.z;
+    const int tk0 = blockIdx.x * SC2_T, tq0 = blockIdx.y * SC2_T, h = blockIdx.z;
     const float* qb = qbar + (size_t)h * Tq * HD;
     const float* kb = kbar + (size_t)h * Tk * HD;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = tid / 16 + 16 * i, d4 = tid % 16;
-        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-        if (tq0 + r < Tq) a = *reinterpret_cast<const float4*>(qb + (size_t)(tq0 + r) * HD + d4 * 4);
-        if (tk0 + r < Tk) b = *reinterpret_cast<const float4*>(kb + (size_t)(tk0 + r) * HD + d4 * 4);
-        qs[(d4 * 4 + 0) * SC_LD + r] = a.x;
-        qs[(d4 * 4 + 1) * SC_LD + r] = a.y;
-        qs[(d4 * 4 + 2) * SC_LD + r] = a.z;
-        qs[(d4 * 4 + 3) * SC_LD + r] = a.w;
-        ks[(d4 * 4 + 0) * SC_LD + r] = b.x;
-        ks[(d4 * 4 + 1) * SC_LD + r] = b.y;
-        ks[(d4 * 4 + 2) * SC_LD + r] = b.z;
-        ks[(d4 * 4 + 3) * SC_LD + r] = b.w;
-    }
-    __syncthreads();
     const int ty = tid / 16, tx = tid % 16;
-    float acc[4][4];
+    float acc[8][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-#pragma unroll 8
-    for (int d = 0; d < HD; ++d) {
-        const float4 a = *reinterpret_cast<const float4*>(qs + d * SC_LD + ty * 4);
-        const float4 b = *reinterpret_cast<const float4*>(ks + d * SC_LD + tx * 4);
-        const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+    for (int half = 0; half < 2; ++half) {
+        if (half) __syncthreads();
+        // 128 rows x 32 dims of each side: 8 float4 per row, 1024 float4 per side
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int it = 0; it < 4; ++it) {
+            const int e = tid + 256 * it;
+            const int r = e / 8, d4 = e % 8;
+            float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+            if (tq0 + r < Tq) a = *reinterpret_cast<const float4*>(qb + (size_t)(tq0 + r) * HD + 32 * half + 4 * d4);
+            if (tk0 + r < Tk) b = *reinterpret_cast<const float4*>(kb + (size_t)(tk0 + r) * HD + 32 * half + 4 * d4);
+            qs[(4 * d4 + 0) * SC2_LD + r] = a.x;
+            qs[(4 * d4 + 1) * SC2_LD + r] = a.y;
+            qs[(4 * d4 + 2) * SC2_LD + r] = a.z;
+            qs[(4 * d4 + 3) * SC2_LD + r] = a.w;
+            ks[(4 * d4 + 0) * SC2_LD + r] = b.x;
+            ks[(4 * d4 + 1) * SC2_LD + r] = b.y;
+            ks[(4 * d4 + 2) * SC2_LD + r] = b.z;
+            ks[(4 * d4 + 3) * SC2_LD + r] = b.w;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int d = 0; d < 32; ++d) {
+            const float4 a0 = *reinterpret_cast<const float4*>(qs + d * SC2_LD + ty * 8);
+            const float4 a1 = *reinterpret_cast<const float4*>(qs + d * SC2_LD + ty * 8 + 4);
+            const float4 b0 = *reinterpret_cast<const float4*>(ks + d * SC2_LD + tx * 8);
+            const float4 b1 = *reinterpret_cast<const float4*>(ks + d * SC2_LD + tx * 8 + 4);
+            const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+        }
     }
-    int kl_lo[4], kl_hi[4];
-    bool kempty[4];
+    bool kempty[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int c = tk0 + tx * 4 + j;
-        member_range(kl, c < Tk ? c : 0, kl_lo[j], kl_hi[j]);
-        kempty[j] = kl_hi[j] <= kl_lo[j];
+    for (int j = 0; j < 8; ++j) {
+        const int c = tk0 + tx * 8 + j;
+        int lo, hi;
+        member_range(kl, c < Tk ? c : 0, lo, hi);
+        kempty[j] = hi <= lo;
     }
+    const int c0 = tk0 + tx * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = tq0 + ty * 4 + i;
+    for (int i = 0; i < 8; ++i) {
+        const int r = tq0 + ty * 8 + i;
         if (r >= Tq) continue;
         const bool qempty = valid_rows(ql, r) == 0;
-        float o[4];
+        float o[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = (qempty || kempty[j]) ? -INFINITY : acc[i][j] * scale;
-        float* dst = scores + ((size_t)h * Tq + r) * Tk + tk0 + tx * 4;
-        if ((Tk & 3) == 0 && tk0 + tx * 4 + 3 < Tk) {
+        for (int j = 0; j < 8; ++j) o[j] = (qempty || kempty[j]) ? -INFINITY : acc[i][j] * scale;
+        float* dst = scores + ((size_t)h * Tq + r) * Tk + c0;
+        if ((Tk & 3) == 0 && c0 + 7 < Tk) {
             *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (tk0 + tx * 4 + j < Tk) dst[j] = o[j];
+            for (int j = 0; j < 8; ++j)
+                if (c0 + j < Tk) dst[j] = o[j];
         }
     }
 }
@@ -162,9 +172,9 @@ hipError_t launch_tile_pool(const void* x, int dtype, int heads, LayH lay, bool 
 hipError_t launch_tile_scores(const float* qbar, const float* kbar, int heads, LayH ql, LayH kl,
                               float scale, float* scores, hipStream_t st) {
     const int Tq = ql.S * ql.P / TILE, Tk = kl.S * kl.P / TILE;
-    const dim3 grid((Tk + 63) / 64, (Tq + 63) / 64, heads), block(256);
-    hipLaunchKernelGGL(k_tile_scores, grid, block, 0, st, qbar, kbar, Tq, Tk,
-                       Lay{ql.S, ql.N, ql.P, ql.nsp}, Lay{kl.S, kl.N, kl.P, kl.nsp}, scale, scores);
+    const Lay lq{ql.S, ql.N, ql.P, ql.nsp}, lk{kl.S, kl.N, kl.P, kl.nsp};
+    const dim3 grid((Tk + SC2_T - 1) / SC2_T, (Tq + SC2_T - 1) / SC2_T, heads), block(256);
+    hipLaunchKernelGGL(k_tile_scores8, grid, block, 0, st, qbar, kbar, Tq, Tk, lq, lk, scale, scores);
     return hipGetLastError();
 }
 

@@ -35,6 +35,11 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(S._SIGS), "binding signatures must cover the header exactly"
 
 
+def test_library_resolves_every_symbol_at_load():
+    # RTLD_NOW: an undefined symbol in the built library fails here, on the CPU
+    ctypes.CDLL(S._LIBPATH, mode=os.RTLD_NOW)
+
+
 def test_version_and_status(lib):
     assert lib.sparse3d_abi_version() == 3
     for st in range(6):
