@@ -284,6 +284,39 @@ def traffic_entry():
     return t
 
 
+def rocminfo_peak():
+    """Matrix peak recomputed from the agent's compute-unit count and maximum clock as rocminfo
+    reports them (4096 bf16 FLOP per clock per CU), or None where rocminfo is unavailable."""
+    import subprocess
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for block in txt.split("Agent ")[1:]:
+        if "gfx950" not in block:
+            continue
+        cu = clk = None
+        for line in block.splitlines():
+            key, _, val = line.strip().partition(":")
+            if key == "Compute Unit":
+                cu = int(val.split()[0])
+            elif key == "Max Clock Freq. (MHz)":
+                clk = int(val.split()[0])
+        if cu and clk:
+            return {"cus": cu, "max_clock_mhz": clk, "peak_tflops": round(cu * clk * 1e6 * 4096 / 1e12, 1)}
+    return None
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, inp, k, budget_s, LY):
     """The fp64 oracle on a bounded sample of the same workload, scaled to TFLOP/s."""
     import oracle
@@ -327,7 +360,7 @@ def cpu_baseline(w, inp, k, budget_s, LY):
     flops_sample = LY.selected_flops(cnt_sum, done, ts)
     flops_layer = flops_sample * (H * Tq / done)
     return dict(value=flops_layer / t_layer / 1e12, unit="TFLOP/s", cores=int(min(threads, cores)),
-                kind="oracle",
+                kind="oracle", cpu_model=cpu_model(),
                 sample=(f"head 0: full pool+score ({t_ps:.1f}s), select+attend on {done} of {Tq} "
                         f"query tiles ({t_att:.1f}s); layer time extrapolated x{H} heads, "
                         f"x{Tq / done:.1f} tiles = {t_layer:.0f}s"),
@@ -398,6 +431,8 @@ def main():
         "kernels_ms": {"grid_subsample": round(r["sub_ms"], 4), "tile_scores": round(r["scores_ms"], 4),
                        "select_topk": round(r["select_ms"], 4), "sparse_attn": round(r["attn_ms"], 4)},
         "selected_flops": flops,
+        "valid_pair_flops": LY.valid_pair_flops(r["idx"].cpu().numpy(), r["cnt"].cpu().numpy(),
+                                                w.layout, L.klay),
     }
     Lq = w.rows
     bytes_in = 2 * w.heads * Lq * 64 * (2 if w.dtype == "bf16" else 4)
@@ -412,6 +447,10 @@ def main():
     res["roofline"] = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                        "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                        "traffic": (tr["bytes_per_launch"] if tr and tr.get("workload") == w.name else None)}
+    dev_peak = rocminfo_peak()
+    if dev_peak:
+        dev_peak["attn_frac"] = round(attn_tflops / dev_peak["peak_tflops"], 4)
+        res["peak_rocminfo"] = dev_peak
     if not args.no_dense:
         log("timing the dense kernel")
         dms = time_dense(torch, S, q, v, w.layout, args.dense_reps)

@@ -74,6 +74,26 @@ def selected_flops(total_cnt: int, rows: int, ts: int, landmarks: int = 0,
     return (rows * ts + total_cnt) * pair_flops(tile, head_dim) + landmarks * tile * 4 * head_dim
 
 
+def valid_pair_flops(idx, cnt, qlay, klay, tile: int = TILE, head_dim: int = 64) -> int:
+    """FLOPs of the attended pairs counted over real rows only: valid query rows (in-frame
+    position below N) times member keys (patch tokens of a selected tile, special tokens of
+    the special pseudo-tiles), 4*d per (query, key).  ``idx``/``cnt`` are host arrays
+    [heads, Tq, kmax] / [heads, Tq]."""
+    import numpy as np
+    S, N, P, nsp = klay
+    tpf = P // tile
+    j0 = (np.arange(S * tpf) % tpf) * tile
+    members = np.clip(np.minimum(tile, N - j0) - np.maximum(0, nsp - j0), 0, None)
+    qS, qN, qP, _ = qlay
+    qj0 = (np.arange(qS * (qP // tile)) % (qP // tile)) * tile
+    vq = np.clip(np.minimum(tile, qN - qj0), 0, None)
+    kmax = idx.shape[2]
+    live = np.arange(kmax)[None, None, :] < cnt[:, :, None]
+    safe = np.where(live, idx, 0)
+    keys = (members[safe] * live).sum(axis=2) + nsp * S          # members per row, specials included
+    return int((keys * vq[None, :]).sum()) * 4 * head_dim
+
+
 @dataclass
 class LayerResult:
     out: torch.Tensor

@@ -37,3 +37,33 @@ def test_flops():
     assert LY.pair_flops() == 4 * 64 ** 3 == 1048576
     assert LY.selected_flops(total_cnt=5, rows=2, ts=1) == 7 * 1048576
     assert LY.selected_flops(total_cnt=0, rows=1, ts=0, landmarks=10) == 10 * 64 * 4 * 64
+
+
+def test_valid_pair_flops_brute_force():
+    # two frames of N=150 tokens (3 specials) padded to P=192: three 64-row tiles per frame
+    S, N, P, nsp = 2, 150, 192, 3
+    lay = (S, N, P, nsp)
+    rng = np.random.default_rng(5)
+    Tq = Tk = S * P // 64
+    kmax = 4
+    idx = np.full((2, Tq, kmax), -1, np.int32)
+    cnt = np.zeros((2, Tq), np.int32)
+    for h in range(2):
+        for t in range(Tq):
+            c = int(rng.integers(0, kmax + 1))
+            idx[h, t, :c] = np.sort(rng.choice(Tk, c, replace=False))
+            cnt[h, t] = c
+    total = 0
+    for h in range(2):
+        for tq in range(Tq):
+            for r in range(64):
+                pos = (tq % 3) * 64 + r                      # in-frame position of the query row
+                if pos >= N:
+                    continue
+                keys = S * nsp                                 # every frame's special tokens
+                for t in idx[h, tq, :cnt[h, tq]]:
+                    for kr in range(64):
+                        kpos = (t % 3) * 64 + kr
+                        keys += nsp <= kpos < N                # patch tokens of the tile only
+                total += keys
+    assert LY.valid_pair_flops(idx, cnt, lay, lay) == total * 4 * 64
