@@ -448,11 +448,245 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
     }
 }
 
+// Variant for three waves per SIMD (no landmarks, no subsample completion): at most 168
+// VGPRs per wave and 24 KiB of tile buffers per workgroup, so six workgroups share a CU.
+// Step `it` forms S(it) = K(it) Q^T at its start (no S double buffer), then the softmax and
+// P V of tile it.  K has one buffer: once every wave has read K(it) (first barrier of the
+// step) the loads of K(it+1) go out.  V has two: V(it+1) loads from the start of step it
+// into the buffer V(it-1) left.  Operands are read from LDS as they are needed.
+template <bool F32OUT, bool DENSE>
+__global__ __launch_bounds__(128, 3) void k_attn_bf16_o3(AttnDev p) {
+    __shared__ __align__(16) unsigned char s_k[TILE_BYTES];
+    __shared__ __align__(16) unsigned char s_v0[TILE_BYTES];
+    __shared__ __align__(16) unsigned char s_v1[TILE_BYTES];
+    extern __shared__ uint32_t s_dyn[];
+
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int qc = lane & 31, g = lane >> 5;
+    const int tpfq = p.ql.P / TILE;
+    int h, tq;
+    attn_work_item(blockIdx.x, gridDim.x, p.ql.S, tpfq, gridDim.x / p.Tq, h, tq, !p.frame);
+    const int Lq = p.ql.S * p.ql.P, Lk = p.kl.S * p.kl.P;
+    const int qrow = tq * TILE + w * 32 + qc;
+    const bool qvalid = (tq % tpfq) * TILE + w * 32 + qc < p.ql.N;
+
+    bf16x8 qop[4];
+    {
+        const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((size_t)h * Lq + qrow) * HD;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint4 u = qvalid ? *reinterpret_cast<const uint4*>(qp + 16 * s + 8 * g)
+                                   : make_uint4(0, 0, 0, 0);
+            qop[s] = __builtin_bit_cast(bf16x8, u);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+
+    int c = 0, rot = 0, t0 = 0;
+    const int32_t* myidx = nullptr;
+    int ntiles;
+    if (DENSE) {
+        ntiles = p.frame ? p.kl.P / TILE : p.Tk;
+        t0 = p.frame ? (tq / tpfq) * (p.kl.P / TILE) : 0;
+    } else {
+        c = min(max(p.cnt[(size_t)h * p.Tq + tq], 0), p.kmax);
+        myidx = p.idx + ((size_t)h * p.Tq + tq) * p.kmax;
+        ntiles = p.Ts + c;
+    }
+    int32_t* s_idx = reinterpret_cast<int32_t*>(s_dyn);
+    if (!DENSE) {
+        for (int i = tid; i < c; i += 128) s_idx[i] = pack_tile_entry(p, myidx[i]);
+        __syncthreads();
+        const int thr = (tq / tpfq) * (p.kl.P / TILE);
+        int n = 0;
+        for (int b = 0; b < c; b += 128)
+            n += __syncthreads_count(b + tid < c && (s_idx[b + tid] & 0xFFFF) < thr);
+        rot = n < c ? n : 0;
+    }
+
+    const unsigned head_bytes = (unsigned)Lk * 128u;
+    const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(static_cast<const unsigned char*>(p.k)) + (size_t)h * head_bytes, 0,
+        (int)head_bytes, BUF_RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(static_cast<const unsigned char*>(p.v)) + (size_t)h * head_bytes, 0,
+        (int)head_bytes, BUF_RSRC_WORD3);
+
+    const int srow_in = lane >> 3, sslot = lane & 7;
+    int srow[4], soff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        srow[j] = 32 * w + 8 * j + srow_in;
+        soff[j] = srow[j] * 128 + swz(srow[j], sslot) * 16;
+    }
+    auto desc = [&](int it) { return describe<DENSE, false, !DENSE>(p, it, c, myidx, s_idx, nullptr, rot, t0); };
+    auto plan = [&](const TileDesc& dd, unsigned (&voff)[4], unsigned& base) {
+        const TileDesc d = uniform(dd);
+        const bool spec = d.kind == KIND_SPEC;
+        base = spec ? 0u : (unsigned)d.t * TILE_BYTES;
+        if (spec) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = srow[j];
+                const unsigned o = (unsigned)src_row(p, d, r) * 128u + swz(r, sslot) * 16u;
+                voff[j] = ((d.mask >> r) & 1ull) ? o : OOB_OFFSET;
+            }
+        } else if (d.mask == ~0ull) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) voff[j] = (unsigned)soff[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) voff[j] = ((d.mask >> srow[j]) & 1ull) ? (unsigned)soff[j] : OOB_OFFSET;
+        }
+    };
+    auto dma4 = [&](const __amdgpu_buffer_rsrc_t& rs, lds_u8* dst, const unsigned (&voff)[4], unsigned base) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            dma_buf(rs, dst + (32 * w + 8 * j) * 128, voff[j], __builtin_amdgcn_readfirstlane(base));
+    };
+
+    TileOffsets to;
+    to.init(lane);
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float m = -INFINITY, l = 0.f;
+    f32x16 o0 = {}, o1 = {};
+
+    auto step = [&](int it, TileDesc& dcur, const unsigned char* vcur, unsigned char* vnext) {
+        const TileDesc cur = uniform(dcur);
+        const bool more = it + 1 < ntiles;
+        TileDesc dn{};
+        unsigned vk[4], vv[4], bk = 0, bv = 0;
+        if (more) {
+            dn = desc(it + 1);
+            plan(dn, vk, bk);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vv[j] = vk[j];
+            bv = bk;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vk[j] = vv[j] = OOB_OFFSET;
+        }
+        dma4(rs_v, (lds_u8*)vnext, vv, bv);                 // V(it+1)
+        f32x16 s0, s1;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            bf16x8 a0, a1;
+            read_rows(s_k, to, st, a0, a1);
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qop[st], st ? s0 : f32x16{}, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qop[st], st ? s1 : f32x16{}, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
+        __builtin_amdgcn_s_barrier();                       // every wave has read K(it)
+        dma4(rs_k, (lds_u8*)s_k, vk, bk);                   // K(it+1)
+        __builtin_amdgcn_sched_barrier(0);
+        if (cur.mask != ~0ull) {
+            const unsigned lo = cur.mask ? (unsigned)__builtin_ctzll(cur.mask) : 64u;
+            const unsigned span = (unsigned)__builtin_popcountll(cur.mask);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const unsigned key = 8 * (r >> 2) + 4 * g + (r & 3);
+                if (key - lo >= span) s0[r] = -INFINITY;
+                if (key + 32 - lo >= span) s1[r] = -INFINITY;
+            }
+        }
+        float mx = max32f(s0, s1);
+        {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        }
+        const float mt = mx == -INFINITY ? -INFINITY : mx * p.scale_l2;
+        if (__ballot(mt > m + RESCALE_THRESHOLD)) {
+            const float mnew = fmaxf(m, mt);
+            const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+            l *= alpha;
+            o0 *= alpha;
+            o1 *= alpha;
+            m = mnew;
+        }
+        const float off = -(m == -INFINITY ? 0.f : m);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const f32x16& sp = (ks < 2) ? s0 : s1;
+            const int j0 = 2 * (ks & 1);
+            bf16x8 va0, va1;
+            read_tr(vcur, to, ks, va0, va1);
+            float pv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sp[4 * j0 + i], p.scale_l2, off));
+            bf16x2 pp[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pp[i] = bf16x2{(__bf16)pv[2 * i], (__bf16)pv[2 * i + 1]};
+                l = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, l, false);
+            }
+            const bf16x8 pb = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+                                                      __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
+                                                      0, 1, 2, 3, 4, 5, 6, 7);
+            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0, pb, o0, 0, 0, 0);
+            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1, pb, o1, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(WAITCNT_VM0_LGKM0);      // K(it+1), V(it+1) landed; V(it) read
+        __builtin_amdgcn_s_barrier();
+        dcur = dn;
+    };
+
+    TileDesc d{};
+    if (ntiles > 0) {
+        d = desc(0);
+        unsigned v0[4], b0;
+        plan(d, v0, b0);
+        dma4(rs_k, (lds_u8*)s_k, v0, b0);
+        dma4(rs_v, (lds_u8*)s_v0, v0, b0);
+        __builtin_amdgcn_s_waitcnt(WAITCNT_VM0_LGKM0);
+        __builtin_amdgcn_s_barrier();
+    }
+    int it = 0;
+    for (; it + 1 < ntiles; it += 2) {
+        step(it, d, s_v0, s_v1);
+        step(it + 1, d, s_v1, s_v0);
+    }
+    if (it < ntiles) step(it, d, s_v0, s_v1);
+
+    const float ltot = l + __shfl_xor(l, 32);
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    const size_t obase = ((size_t)h * Lq + qrow) * HD;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const f32x16& oc = cb ? o1 : o0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c0 = 32 * cb + 8 * j + 4 * g;
+            float v4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v4[i] = qvalid ? oc[4 * j + i] * inv : 0.f;
+            if (F32OUT) {
+                *reinterpret_cast<float4*>(static_cast<float*>(p.out) + obase + c0) =
+                    make_float4(v4[0], v4[1], v4[2], v4[3]);
+            } else {
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + obase + c0) =
+                    make_uint2(pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3]));
+            }
+        }
+    }
+    if (p.lse && g == 0) {
+        float v = 0.f;
+        if (qvalid) v = ltot > 0.f ? (m + log2f(ltot)) * LN2 : -INFINITY;
+        p.lse[(size_t)h * Lq + qrow] = v;
+    }
+}
+
 template <bool F32OUT, bool SGA>
 static void launch_t(const AttnDev& d, int heads, bool dense, bool lm, hipStream_t st) {
     const dim3 grid((unsigned)(heads * d.Tq)), block(128);
     const size_t shm = ((lm ? (size_t)(2 * d.nlm) : 0) + (dense ? 0 : (size_t)d.kmax)) *
                        sizeof(uint32_t);
+    if (!lm && !SGA) {
+        if (dense) hipLaunchKernelGGL((k_attn_bf16_o3<F32OUT, true>), grid, block, 0, st, d);
+        else hipLaunchKernelGGL((k_attn_bf16_o3<F32OUT, false>), grid, block, shm, st, d);
+        return;
+    }
     if (dense) hipLaunchKernelGGL((k_attn_bf16<F32OUT, true, false, SGA>), grid, block, 0, st, d);
     else if (lm) hipLaunchKernelGGL((k_attn_bf16<F32OUT, false, true, SGA>), grid, block, shm, st, d);
     else hipLaunchKernelGGL((k_attn_bf16<F32OUT, false, false, SGA>), grid, block, shm, st, d);
