@@ -12,8 +12,14 @@
 // in a scalar register), every 128-byte row stored as 8 XOR-swizzled 16-byte chunks (see
 // swz_key).  One barrier per step.  Rows that are not keys load through an out-of-range
 // offset, which reads as zeros, and are masked to -inf by index, so pad rows (which may
-// hold NaN) never reach the arithmetic.  Landmark blocks (fp32 tile means) are converted
-// to bf16 through registers.
+// hold NaN) never reach the arithmetic.  Landmark blocks (tile means in the operand
+// precision) are staged like key tiles.
+//
+// Two kernels share this machinery.  k_attn_bf16 (two waves per SIMD, ~240 VGPRs, 32 KiB
+// of tile buffers) carries the landmark and subsample-completion variants.
+// k_attn_bf16_o3 (three waves per SIMD, <= 168 VGPRs, 24 KiB) runs the plain sparse,
+// dense and frame attention: the third wave hides more of the latency that two cannot,
+// and the sparse path skips the per-tile row max (see its softmax).
 #include <type_traits>
 
 #include "attn_common.h"
@@ -67,6 +73,9 @@ __device__ __forceinline__ float max32f(const f32x16& a, const f32x16& b) {
 // Rescale the running output only when some row max grew by more than this (base-2
 // units); otherwise probabilities are taken against the stale max and stay <= 2^8.
 constexpr float RESCALE_THRESHOLD = 8.0f;
+// Largest sum of one half tile's probabilities (16 per lane) taken without moving the
+// reference max (three-wave kernel).
+constexpr float PROB_SUM_LIMIT = 65536.0f;
 
 
 // SGA: the subsample completion (own key of dropped positions, mean pair) is applied to
@@ -590,41 +599,103 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16_o3(AttnDev p) {
                 if (key + 32 - lo >= span) s1[r] = -INFINITY;
             }
         }
-        float mx = max32f(s0, s1);
-        {
-            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-            mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-        }
-        const float mt = mx == -INFINITY ? -INFINITY : mx * p.scale_l2;
-        if (__ballot(mt > m + RESCALE_THRESHOLD)) {
-            const float mnew = fmaxf(m, mt);
-            const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-            l *= alpha;
-            o0 *= alpha;
-            o1 *= alpha;
-            m = mnew;
-        }
-        const float off = -(m == -INFINITY ? 0.f : m);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const f32x16& sp = (ks < 2) ? s0 : s1;
-            const int j0 = 2 * (ks & 1);
-            bf16x8 va0, va1;
-            read_tr(vcur, to, ks, va0, va1);
-            float pv[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sp[4 * j0 + i], p.scale_l2, off));
-            bf16x2 pp[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pp[i] = bf16x2{(__bf16)pv[2 * i], (__bf16)pv[2 * i + 1]};
-                l = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, l, false);
+        if constexpr (DENSE) {
+            // every workgroup sweeps the keys in the same order, so the probabilities are
+            // taken against the tile's row max (lazy rescale, as in the two-wave kernel)
+            float mx = max32f(s0, s1);
+            {
+                const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
             }
-            const bf16x8 pb = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
-                                                      __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
-                                                      0, 1, 2, 3, 4, 5, 6, 7);
-            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0, pb, o0, 0, 0, 0);
-            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1, pb, o1, 0, 0, 0);
+            const float mt = mx == -INFINITY ? -INFINITY : mx * p.scale_l2;
+            if (__ballot(mt > m + RESCALE_THRESHOLD)) {
+                const float mnew = fmaxf(m, mt);
+                const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+                l *= alpha;
+                o0 *= alpha;
+                o1 *= alpha;
+                m = mnew;
+            }
+            const float off = -(m == -INFINITY ? 0.f : m);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const f32x16& sp = (ks < 2) ? s0 : s1;
+                const int j0 = 2 * (ks & 1);
+                bf16x8 va0, va1;
+                read_tr(vcur, to, ks, va0, va1);
+                float pv[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sp[4 * j0 + i], p.scale_l2, off));
+                bf16x2 pp[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pp[i] = bf16x2{(__bf16)pv[2 * i], (__bf16)pv[2 * i + 1]};
+                    l = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, l, false);
+                }
+                const bf16x8 pb = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+                                                          __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
+                                                          0, 1, 2, 3, 4, 5, 6, 7);
+                o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0, pb, o0, 0, 0, 0);
+                o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1, pb, o1, 0, 0, 0);
+            }
+        } else {
+            // Probabilities are taken against the running reference m without first forming
+            // the tile's row max.  Each half tile (32 keys) checks afterwards that its rounded
+            // probabilities sum to at most 2^16 (then none exceeds 2^16: nothing overflowed,
+            // and the accumulators keep ample range); only a half that fails, or any half while a
+            // row has no reference yet, forms the max of its scores, moves the reference
+            // (rescaling O and l) and recomputes.  Rounding is relative, so the reference only
+            // has to keep the probabilities in range, not equal the running max.
+            const bool fresh = __ballot(m == -INFINITY) != 0;
+    #pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const f32x16& sp = hf ? s1 : s0;
+                bf16x8 pb[2];
+                float lh;
+                auto probs = [&]() {
+                    const float off = m == -INFINITY ? 0.f : -m;
+                    lh = 0.f;
+    #pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        float pv[8];
+    #pragma unroll
+                        for (int i = 0; i < 8; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sp[8 * kk + i], p.scale_l2, off));
+                        bf16x2 pp[4];
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            pp[i] = bf16x2{(__bf16)pv[2 * i], (__bf16)pv[2 * i + 1]};
+                            lh = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, lh, false);
+                        }
+                        pb[kk] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+                                                         __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
+                                                         0, 1, 2, 3, 4, 5, 6, 7);
+                    }
+                };
+                probs();
+                if (fresh || __ballot(!(lh <= PROB_SUM_LIMIT))) {
+                    float mx = sp[0];
+    #pragma unroll
+                    for (int i = 1; i < 15; i += 2) mx = max3f(mx, sp[i], sp[i + 1]);
+                    mx = fmaxf(mx, sp[15]);
+                    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                    mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+                    const float mnew = fmaxf(m, mx == -INFINITY ? -INFINITY : mx * p.scale_l2);
+                    const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
+                    l *= alpha;
+                    o0 *= alpha;
+                    o1 *= alpha;
+                    m = mnew;
+                    probs();
+                }
+                l += lh;
+    #pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    bf16x8 va0, va1;
+                    read_tr(vcur, to, 2 * hf + kk, va0, va1);
+                    o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0, pb[kk], o0, 0, 0, 0);
+                    o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1, pb[kk], o1, 0, 0, 0);
+                }
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(WAITCNT_VM0_LGKM0);      // K(it+1), V(it+1) landed; V(it) read

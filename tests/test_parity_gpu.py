@@ -175,11 +175,14 @@ def test_k_all_tiles_equals_dense():
     dense = S.sparse3d_dense_attn_fwd(q, q, v, w.layout, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.all(res.cnt == Tk)
-    # same keys, different tile order and pseudo-tiles: equal within accumulation rounding
-    assert float((res.out - dense).abs().max()) <= 5e-3
     ol = oracle.Layout(*w.layout)
     O, _ = oracle.dense_attend(inp.q, inp.k, inp.v, ol, ol, 0.125)
     assert float(np.max(np.abs(res.out.cpu().numpy() - O))) <= 2e-2
+    assert float(np.max(np.abs(dense.cpu().numpy() - O))) <= 2e-2
+    # same keys, different tile order and pseudo-tiles, and the probabilities rounded to
+    # bf16 against different references (the sparse kernel's running reference, the dense
+    # kernel's tile max): the two agree to about one bf16 rounding of the weights
+    assert float((res.out - dense).abs().max()) <= 1e-2
 
 
 def test_empty_key_set():
