@@ -39,6 +39,14 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
     return r;
 }
 
+// x in the lanes whose bit is set in `lanes` (a wave-uniform mask in scalar registers),
+// -inf in the others: one v_cndmask with the mask as its condition operand
+__device__ __forceinline__ float keep_lanes(float x, uint64_t lanes) {
+    float r;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(-INFINITY), "v"(x), "s"(lanes));
+    return r;
+}
+
 // max over the 32 scores of a lane (two 16-element accumulators), as two asm blocks of
 // eight dependent v_max3_f32 each: one block per chain keeps the compiler from padding
 // every step of the chain with wait states, as it does between separate asm statements
@@ -590,13 +598,22 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16_o3(AttnDev p) {
         dma4(rs_k, (lds_u8*)s_k, vk, bk);                   // K(it+1)
         __builtin_amdgcn_sched_barrier(0);
         if (cur.mask != ~0ull) {
-            const unsigned lo = cur.mask ? (unsigned)__builtin_ctzll(cur.mask) : 64u;
-            const unsigned span = (unsigned)__builtin_popcountll(cur.mask);
+            // slot r of a lane in half-wave g holds key 8 (r / 4) + 4 g + r % 4 (+32 in s1): its
+            // lane mask takes one row bit for lanes 0-31 and another for lanes 32-63, formed
+            // on the scalar unit from the uniform row mask.  The scores come from the matrix
+            // core; the compiler does not see the reads inside the asm, so a few idle
+            // cycles keep them clear of the products' write-back
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_nop 7\n\ts_nop 7");
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const unsigned key = 8 * (r >> 2) + 4 * g + (r & 3);
-                if (key - lo >= span) s0[r] = -INFINITY;
-                if (key + 32 - lo >= span) s1[r] = -INFINITY;
+                const int cr = 8 * (r >> 2) + (r & 3);
+                const uint64_t k0 = (((cur.mask >> cr) & 1ull) ? 0x00000000FFFFFFFFull : 0ull) |
+                                    (((cur.mask >> (cr + 4)) & 1ull) ? 0xFFFFFFFF00000000ull : 0ull);
+                const uint64_t k1 = (((cur.mask >> (cr + 32)) & 1ull) ? 0x00000000FFFFFFFFull : 0ull) |
+                                    (((cur.mask >> (cr + 36)) & 1ull) ? 0xFFFFFFFF00000000ull : 0ull);
+                s0[r] = keep_lanes(s0[r], k0);
+                s1[r] = keep_lanes(s1[r], k1);
             }
         }
         if constexpr (DENSE) {
@@ -619,6 +636,7 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16_o3(AttnDev p) {
             const float off = -(m == -INFINITY ? 0.f : m);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
+                if ((uint32_t)(cur.mask >> (32 * (ks >> 1))) == 0u) continue;   // no key in this half
                 const f32x16& sp = (ks < 2) ? s0 : s1;
                 const int j0 = 2 * (ks & 1);
                 bf16x8 va0, va1;
@@ -649,6 +667,7 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16_o3(AttnDev p) {
             const bool fresh = __ballot(m == -INFINITY) != 0;
     #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
+                if ((uint32_t)(cur.mask >> (32 * hf)) == 0u) continue;   // no key in this half
                 const f32x16& sp = hf ? s1 : s0;
                 bf16x8 pb[2];
                 float lh;
