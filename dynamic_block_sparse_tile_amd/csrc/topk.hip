@@ -209,6 +209,126 @@ __global__ __launch_bounds__(TK_THREADS) void k_select_topk(const float* __restr
     if (tid == 0) cnt[row] = min(total, kmax);
 }
 
+// The same selection with one wave per score row (rows of at most 64 * E tiles): the keys
+// stay in registers (tile i * 64 + lane in slot i) and every count is a ballot and a scalar
+// popcount, so a row needs no LDS histogram and no barrier.  The k-th largest key T is
+// bracketed by bisection of the key interval, keeping count(key >= lo) >= k >
+// count(key > hi); once at most 64 keys remain inside the bracket they are gathered, one
+// per lane, and ordered by a bitonic network across the lanes, which yields T directly.
+// Selection and compaction then run over the slots in tile order with ballot prefix
+// counts, exactly as in the workgroup kernel (keys above T, the lowest-index ties, the
+// anchor frame).
+constexpr int TKW_WAVES = 4;            // rows per workgroup
+template <int E>
+__global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float* __restrict__ scores, int Tk,
+                                                                     int Tq, int rows, KBudget kb, int tpf,
+                                                                     int anchor, int32_t* __restrict__ idx,
+                                                                     int32_t* __restrict__ cnt, int kmax) {
+    __shared__ uint32_t s_cand[TKW_WAVES][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = blockIdx.x * TKW_WAVES + wave;
+    if (row >= rows) return;                        // whole wave leaves together
+    const int k = kb.k[row / Tq];
+    const float* src = scores + (size_t)row * Tk;
+    uint32_t key[E];
+    float f[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) f[i] = src[min(i * 64 + lane, Tk - 1)];   // all loads in flight at once
+#pragma unroll
+    for (int i = 0; i < E; ++i) key[i] = i * 64 + lane < Tk ? order_key(f[i]) : 0u;   // pad slots rank lowest
+    auto count_ge = [&](uint32_t t) {
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < E; ++i) c += __popcll(__ballot(key[i] >= t));
+        return c;
+    };
+    // mode: 0 = nothing from top-k, 1 = every tile, 2 = threshold T with ties
+    const int mode = k <= 0 ? 0 : (k >= Tk ? 1 : 2);
+    uint32_t T = 0;
+    int greater = 0;
+    if (mode == 2) {
+        uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+            if (i * 64 + lane < Tk) {
+                lo = min(lo, key[i]);
+                hi = max(hi, key[i]);
+            }
+        }
+        lo = wave_min(lo);
+        hi = wave_max(hi);
+        int c_lo = Tk, c_hi = 0;                    // count(key >= lo), count(key > hi)
+        while (lo != hi) {
+            if (c_lo - c_hi <= 64) {
+                // gather the keys inside [lo, hi] and rank them across the lanes
+                int base = 0;
+#pragma unroll
+                for (int i = 0; i < E; ++i) {
+                    const bool in = i * 64 + lane < Tk && key[i] >= lo && key[i] <= hi;
+                    const uint64_t m = __ballot(in);
+                    const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    if (in) s_cand[wave][pos] = key[i];
+                    base += __popcll(m);
+                }
+                __builtin_amdgcn_wave_barrier();
+                uint32_t v = lane < base ? s_cand[wave][lane] : 0u;
+#pragma unroll
+                for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+                    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                        const uint32_t o = (uint32_t)__shfl_xor((int)v, stride);
+                        const bool desc = (lane & size) == 0, lower = (lane & stride) == 0;
+                        v = (lower == desc) ? max(v, o) : min(v, o);
+                    }
+                }
+                lo = (uint32_t)__shfl((int)v, k - c_hi - 1);   // rank k - c_hi among the candidates
+                hi = lo;
+                break;
+            }
+            const uint32_t mid = lo + (uint32_t)(((uint64_t)hi - lo + 1) >> 1);
+            const int c = count_ge(mid);
+            if (c >= k) {
+                lo = mid;
+                c_lo = c;
+            } else {
+                hi = mid - 1;
+                c_hi = c;
+            }
+        }
+        T = lo;
+#pragma unroll
+        for (int i = 0; i < E; ++i) greater += __popcll(__ballot(i * 64 + lane < Tk && key[i] > T));
+    }
+    int ties_before = 0;                            // keys == T in earlier slots
+    const int need_eq = mode == 2 ? k - greater : 0;   // ties to take, lowest index first
+    const int a0 = anchor >= 0 ? anchor * tpf : 0, a1 = anchor >= 0 ? a0 + tpf : 0;
+    int32_t* out = idx + (size_t)row * kmax;
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+        const int t = i * 64 + lane;
+        const bool valid = t < Tk;
+        bool sel = valid && t >= a0 && t < a1;
+        if (mode == 1) sel = valid;
+        else if (mode == 2) {
+            const uint64_t eqm = __ballot(valid && key[i] == T);
+            const int eq_rank = ties_before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eqm >> 32),
+                                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)eqm, 0u));
+            ties_before += __popcll(eqm);
+            if (valid && key[i] > T) sel = true;
+            else if (valid && key[i] == T && eq_rank < need_eq) sel = true;
+        }
+        const uint64_t sm = __ballot(sel);
+        const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(sm >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)sm, 0u));
+        if (sel && pos < kmax) out[pos] = t;
+        base += __popcll(sm);
+    }
+    for (int q = base + lane; q < kmax; q += 64) out[q] = -1;
+    if (lane == 0) cnt[row] = min(base, kmax);
+}
+
 hipError_t launch_select_topk(const float* scores, int heads, int tq, int tk, const int32_t* k_heads,
                               int tpf, int anchor, int32_t* idx, int32_t* cnt, int kmax, hipStream_t st) {
     const size_t shm = (size_t)tk * sizeof(uint32_t);
@@ -217,9 +337,21 @@ hipError_t launch_select_topk(const float* scores, int heads, int tq, int tk, co
         KBudget kb{};
         for (int i = 0; i < nh; ++i) kb.k[i] = k_heads[h0 + i];
         const size_t r0 = (size_t)h0 * tq;
-        hipLaunchKernelGGL(k_select_topk, dim3((unsigned)nh * (unsigned)tq), dim3(TK_THREADS), shm, st,
-                           scores + r0 * tk, tk, tq, kb, tpf, anchor, kmax > 0 ? idx + r0 * kmax : idx,
-                           cnt + r0, kmax);
+        const int rows = nh * tq;
+        int32_t* ix = kmax > 0 ? idx + r0 * kmax : idx;
+        const dim3 wgrid((unsigned)((rows + TKW_WAVES - 1) / TKW_WAVES)), wblock(64 * TKW_WAVES);
+        if (tk <= 64 * 16)
+            hipLaunchKernelGGL(k_select_topk_wave<16>, wgrid, wblock, 0, st, scores + r0 * tk, tk, tq, rows, kb,
+                               tpf, anchor, ix, cnt + r0, kmax);
+        else if (tk <= 64 * 48)
+            hipLaunchKernelGGL(k_select_topk_wave<48>, wgrid, wblock, 0, st, scores + r0 * tk, tk, tq, rows, kb,
+                               tpf, anchor, ix, cnt + r0, kmax);
+        else if (tk <= 64 * 96)
+            hipLaunchKernelGGL(k_select_topk_wave<96>, wgrid, wblock, 0, st, scores + r0 * tk, tk, tq, rows, kb,
+                               tpf, anchor, ix, cnt + r0, kmax);
+        else
+            hipLaunchKernelGGL(k_select_topk, dim3((unsigned)rows), dim3(TK_THREADS), shm, st,
+                               scores + r0 * tk, tk, tq, kb, tpf, anchor, ix, cnt + r0, kmax);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
