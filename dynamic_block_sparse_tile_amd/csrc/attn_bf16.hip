@@ -5,21 +5,18 @@
 //   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, A = K rows (ds_read_b128), B = Q (VGPRs)
 //   O^T += V^T P^T   A = V^T read with ds_read_b64_tr_b16 (the transpose happens in the
 //                    LDS read), B = P^T taken straight from the S^T accumulators
-// Software pipeline: step `it` issues the QK^T products of tile it+1 on the matrix core
-// while the vector ALUs run the softmax of tile it, then accumulates P V of tile it.  K
-// therefore runs one tile ahead of V; each has two LDS buffers.  Tiles reach LDS by
-// direct-to-LDS buffer loads (16 bytes per lane; per-lane constant offsets, the tile base
-// in a scalar register), every 128-byte row stored as 8 XOR-swizzled 16-byte chunks (see
-// swz_key).  One barrier per step.  Rows that are not keys load through an out-of-range
-// offset, which reads as zeros, and are masked to -inf by index, so pad rows (which may
-// hold NaN) never reach the arithmetic.  Landmark blocks (tile means in the operand
-// precision) are staged like key tiles.
-//
-// Two kernels share this machinery.  k_attn_bf16 (two waves per SIMD, ~240 VGPRs, 32 KiB
-// of tile buffers) carries the landmark and subsample-completion variants.
-// k_attn_bf16_o3 (three waves per SIMD, <= 168 VGPRs, 24 KiB) runs the plain sparse,
-// dense and frame attention: the third wave hides more of the latency that two cannot,
-// and the sparse path skips the per-tile row max (see its softmax).
+// Three waves share each SIMD: at most 168 VGPRs per wave and 24 KiB of tile buffers per
+// workgroup, so six workgroups fit a CU.  Step `it` forms S(it) = K(it) Q^T at its start,
+// then the softmax and P V of tile it; the third wave hides the latency that a single
+// wave's chain (LDS read, matrix core, softmax, matrix core) exposes.  K has one buffer:
+// once every wave has read K(it) (first barrier of the step) the loads of K(it+1) go out.
+// V has two: V(it+1) loads from the start of step it into the buffer V(it-1) left.  Tiles
+// reach LDS by direct-to-LDS buffer loads (16 bytes per lane; per-lane constant offsets,
+// the tile base in a scalar register), every 128-byte row stored as 8 XOR-swizzled 16-byte
+// chunks (see swz_key).  Rows that are not keys load through an out-of-range offset, which
+// reads as zeros, and are masked to -inf by index, so pad rows (which may hold NaN) never
+// reach the arithmetic.  Landmark blocks (tile means in the operand precision) are staged
+// like key tiles.
 #include <type_traits>
 
 #include "attn_common.h"
@@ -78,401 +75,19 @@ __device__ __forceinline__ float max32f(const f32x16& a, const f32x16& b) {
     return m;
 }
 
-// Rescale the running output only when some row max grew by more than this (base-2
-// units); otherwise probabilities are taken against the stale max and stay <= 2^8.
+// Dense and frame attention: rescale the running output only when some row max grew by
+// more than this (base-2 units); otherwise probabilities are taken against the stale max
+// and stay <= 2^8.
 constexpr float RESCALE_THRESHOLD = 8.0f;
-// Largest sum of one half tile's probabilities (16 per lane) taken without moving the
-// reference max (three-wave kernel).
+// Sparse attention: largest sum of one half tile's probabilities (16 per lane) taken
+// without moving the reference max.
 constexpr float PROB_SUM_LIMIT = 65536.0f;
 
 
 // SGA: the subsample completion (own key of dropped positions, mean pair) is applied to
 // each finished row; a separate instantiation so the other variants carry none of it.
 template <bool F32OUT, bool DENSE, bool LM, bool SGA>
-__global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnDev p) {
-    // K and V rings of two 8 KiB tiles each, as four separate arrays so that every access
-    // in the (two-way unrolled) loop names its buffer statically
-    __shared__ __align__(16) unsigned char s_k0[TILE_BYTES];
-    __shared__ __align__(16) unsigned char s_k1[TILE_BYTES];
-    __shared__ __align__(16) unsigned char s_v0[TILE_BYTES];
-    __shared__ __align__(16) unsigned char s_v1[TILE_BYTES];
-    extern __shared__ uint32_t s_lm[];
-
-    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int qc = lane & 31, g = lane >> 5;
-    const int tpfq = p.ql.P / TILE;
-    int h, tq;
-    attn_work_item(blockIdx.x, gridDim.x, p.ql.S, tpfq, gridDim.x / p.Tq, h, tq, !p.frame);
-    const int Lq = p.ql.S * p.ql.P, Lk = p.kl.S * p.kl.P;
-    const int qrow = tq * TILE + w * 32 + qc;
-    const bool qvalid = (tq % tpfq) * TILE + w * 32 + qc < p.ql.N;
-
-    bf16x8 qop[4];
-    {
-        const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((size_t)h * Lq + qrow) * HD;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const uint4 u = qvalid ? *reinterpret_cast<const uint4*>(qp + 16 * s + 8 * g)
-                                   : make_uint4(0, 0, 0, 0);
-            qop[s] = __builtin_bit_cast(bf16x8, u);
-        }
-    }
-    // settle the Q loads here, on every path: otherwise the first matrix-core use inside
-    // the tile loop waits on all vector-memory traffic, the next tile's loads included
-    __builtin_amdgcn_s_waitcnt(0);
-
-    int c = 0, rot = 0, t0 = 0;
-    const int32_t* myidx = nullptr;
-    int ntiles;
-    if (DENSE) {
-        ntiles = p.frame ? p.kl.P / TILE : p.Tk;
-        t0 = p.frame ? (tq / tpfq) * (p.kl.P / TILE) : 0;
-    } else {
-        c = min(max(p.cnt[(size_t)h * p.Tq + tq], 0), p.kmax);
-        myidx = p.idx + ((size_t)h * p.Tq + tq) * p.kmax;
-        ntiles = p.Ts + c + (LM ? p.nlm : 0);
-    }
-    if (LM) init_landmark_bitmap(p, c, myidx, s_lm, tid, 128);
-    // the selected-tile list, staged once in LDS so the per-tile lookup is an LDS read
-    // instead of a dependent global load (the launcher guarantees kmax <= IDX_LDS_MAX)
-    int32_t* s_idx = reinterpret_cast<int32_t*>(s_lm + (LM ? 2 * p.nlm : 0));
-    if (!DENSE) {
-        for (int i = tid; i < c; i += 128) s_idx[i] = pack_tile_entry(p, myidx[i]);
-        __syncthreads();
-        // Sweep the list starting at the query's own frame (wrapping round).  Workgroups
-        // start one after another in frame order, so this keeps the ones running at the same
-        // time on the same key frames, which then stay in L2 (the list order does not change
-        // the result beyond rounding).
-        {
-            const int thr = (tq / tpfq) * (p.kl.P / TILE);
-            int n = 0;
-            for (int b = 0; b < c; b += 128)
-                n += __syncthreads_count(b + tid < c && (s_idx[b + tid] & 0xFFFF) < thr);
-            rot = n < c ? n : 0;
-        }
-    }
-
-    // ---- staging through buffer resources: one per head for K and for V, so a tile's
-    //      loads are a per-lane constant offset plus the tile's base in a scalar register.
-    //      Offsets at or past the end (OOB) read as zeros: that is how masked rows load.
-    const unsigned head_bytes = (unsigned)Lk * 128u;
-    const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<unsigned char*>(static_cast<const unsigned char*>(p.k)) + (size_t)h * head_bytes, 0,
-        (int)head_bytes, BUF_RSRC_WORD3);
-    const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<unsigned char*>(static_cast<const unsigned char*>(p.v)) + (size_t)h * head_bytes, 0,
-        (int)head_bytes, BUF_RSRC_WORD3);
-    // landmark means (bf16 [heads, Tk, 64]): block b of 64 consecutive tile means is staged
-    // exactly like a key tile
-    __amdgpu_buffer_rsrc_t rs_lk = rs_k, rs_lv = rs_v;
-    if (LM) {
-        const unsigned mean_bytes = (unsigned)p.Tk * 128u;
-        rs_lk = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<unsigned char*>(static_cast<const unsigned char*>(p.kbar)) + (size_t)h * mean_bytes, 0,
-            (int)mean_bytes, BUF_RSRC_WORD3);
-        rs_lv = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<unsigned char*>(static_cast<const unsigned char*>(p.vbar)) + (size_t)h * mean_bytes, 0,
-            (int)mean_bytes, BUF_RSRC_WORD3);
-    }
-
-    // wave w fills rows [32w, 32w+32) of a tile; per instruction j the 64 lanes cover rows
-    // 32w+8j .. +8, lane l -> (row l/8, slot l%8) in LDS order
-    const int srow_in = lane >> 3, sslot = lane & 7;
-    int srow[4], soff[4];                         // row within the tile, byte offset in it
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        srow[j] = 32 * w + 8 * j + srow_in;
-        soff[j] = srow[j] * 128 + swz(srow[j], sslot) * 16;
-    }
-
-    auto desc = [&](int it) { return describe<DENSE, LM, !DENSE>(p, it, c, myidx, s_idx, s_lm, rot, t0); };
-    // Staging plan of one matrix of tile d: this wave's four row blocks (rows 32w + 8j .. +8)
-    // load 16 bytes per lane from byte offset voff[j] + base of buffer rs (mtx 0 = K or the
-    // key means, 1 = V or the value means); rows that are not keys use an offset past the
-    // end, which loads zeros.
-    auto plan = [&](int mtx, const TileDesc& dd, unsigned (&voff)[4], unsigned& base,
-                    __amdgpu_buffer_rsrc_t& rs) {
-        const TileDesc d = uniform(dd);
-        const bool spec = d.kind == KIND_SPEC;
-        // scalar choices first, outside any per-lane selection, so they stay scalar
-        base = spec ? 0u : (unsigned)d.t * TILE_BYTES;
-        rs = (LM && d.kind == KIND_LM) ? (mtx ? rs_lv : rs_lk) : (mtx ? rs_v : rs_k);
-        if (spec) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = srow[j];
-                const unsigned o = (unsigned)src_row(p, d, r) * 128u + swz(r, sslot) * 16u;
-                voff[j] = ((d.mask >> r) & 1ull) ? o : OOB_OFFSET;
-            }
-        } else if (d.mask == ~0ull) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) voff[j] = (unsigned)soff[j];
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) voff[j] = ((d.mask >> srow[j]) & 1ull) ? (unsigned)soff[j] : OOB_OFFSET;
-        }
-    };
-    auto dma_rows = [&](const __amdgpu_buffer_rsrc_t& rs, lds_u8* dst, const unsigned (&voff)[4],
-                        unsigned base, int j) {
-        // the base is uniform; saying so keeps the load from becoming a loop over lanes
-        dma_buf(rs, dst + (32 * w + 8 * j) * 128, voff[j], __builtin_amdgcn_readfirstlane(base));
-    };
-    // the whole matrix at once (prologue)
-    auto stage = [&](int mtx, const TileDesc& d, lds_u8* dst) {
-        unsigned voff[4], base;
-        __amdgpu_buffer_rsrc_t rs;
-        plan(mtx, d, voff, base, rs);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dma_rows(rs, dst, voff, base, j);
-    };
-
-    // per-lane LDS offsets (bytes, within a tile) of the K operands for rows qc; rows
-    // qc + 32 have the same swizzle key and sit 4 KiB further on
-    int koff[4];
-#pragma unroll
-    for (int st = 0; st < 4; ++st) koff[st] = qc * 128 + swz(qc, 2 * st + g) * 16;
-    // V^T through the transposing read: lane j of each 16-lane group points at
-    // V[16ks + 8half + 4g + j/4][32cb + 16*((lane/16)%2) + 4*(j%4)]; rows for different ks
-    // differ by multiples of 16, which leave the swizzle key unchanged
-    const int vrow0 = 4 * g + ((lane & 15) >> 2);
-    const int vcol_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    const int vsub = (lane & 1) * 8;
-    int voff[2][2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const int r = vrow0 + 8 * hf;
-            voff[cb][hf] = r * 128 + swz(r, 4 * cb + vcol_chunk) * 16 + vsub;
-        }
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-
-    float m = -INFINITY, l = 0.f;
-    f32x16 o0 = {}, o1 = {};
-
-    auto read_k = [&](const unsigned char* kt, int st, bf16x8& a0, bf16x8& a1) {
-        a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kt + koff[st]));
-        a1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kt + koff[st] + 4096));
-    };
-    auto read_v = [&](const unsigned char* vt, int ks, bf16x8& a0, bf16x8& a1) {
-        const lds_u8* lb = (const lds_u8*)vt;
-        const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lb + voff[0][0] + ks * 2048));
-        const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lb + voff[0][1] + ks * 2048));
-        const v4i16 y0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lb + voff[1][0] + ks * 2048));
-        const v4i16 y1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lb + voff[1][1] + ks * 2048));
-        a0 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-        a1 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    // one 16-dim step of S^T = K Q^T from K operands already in registers
-    auto qk_ops = [&](const bf16x8 (&ka)[4][2], f32x16& s0, f32x16& s1, int st) {
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st][0], qop[st], st ? s0 : f32x16{}, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st][1], qop[st], st ? s1 : f32x16{}, 0, 0, 0);
-    };
-    auto qk = [&](const unsigned char* kt, f32x16& s0, f32x16& s1, int st) {
-        bf16x8 ka[4][2];
-        read_k(kt, st, ka[st][0], ka[st][1]);
-        qk_ops(ka, s0, s1, st);
-    };
-    // max over the two 32-lane halves (lanes l and l^32 hold the same query)
-    auto xhalf_max = [](float x) {
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-    };
-
-    // Softmax of tile `cur` (scores s0/s1) and its P V accumulation, with the QK^T products
-    // of the next tile (K in LDS at kn, results n0/n1) interleaved.  The products are formed
-    // unconditionally (after the last tile they read a stale buffer and are never used): a
-    // conditional product would make the compiler copy the accumulators around it.  An
-    // empty tile runs through as well; its scores are all masked, so it adds nothing.
-    // `issue(i)`, i = 0..7, is called at eight points spread over the first part of the step:
-    // the staging loads go out one at a time between the arithmetic, so the memory pipeline
-    // is never handed a burst that stalls the issuing wave.
-    auto softmax_pv = [&](const TileDesc& cur_in, f32x16& s0, f32x16& s1, const unsigned char* vt,
-                          const unsigned char* kn, f32x16& n0, f32x16& n1, auto&& issue) {
-        const TileDesc cur = uniform(cur_in);
-        // every LDS operand of this step is requested up front, so the reads overlap the
-        // masking and the max instead of stalling the matrix core one by one
-        bf16x8 ka[4][2], va[4][2];
-#pragma unroll
-        for (int st = 0; st < 4; ++st) read_k(kn, st, ka[st][0], ka[st][1]);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) read_v(vt, ks, va[ks][0], va[ks][1]);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(0);
-        qk_ops(ka, n0, n1, 0);
-        issue(1);
-        if (cur.mask != ~0ull) {
-            if (!LM || cur.kind != KIND_LM) {
-                // contiguous valid rows [lo, hi): one unsigned compare per score
-                const unsigned lo = cur.mask ? (unsigned)__builtin_ctzll(cur.mask) : 64u;
-                const unsigned span = (unsigned)__builtin_popcountll(cur.mask);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const unsigned key = 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (key - lo >= span) s0[r] = -INFINITY;
-                    if (key + 32 - lo >= span) s1[r] = -INFINITY;
-                }
-            } else {
-                // arbitrary row set (landmark block): this lane's keys 8i + 4g + (0..3) of
-                // each half, tested against a constant bit after one per-lane shift
-                const uint32_t w0 = (uint32_t)cur.mask >> (4 * g);
-                const uint32_t w1 = (uint32_t)(cur.mask >> 32) >> (4 * g);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const uint32_t bit = 1u << (8 * (r >> 2) + (r & 3));
-                    if (!(w0 & bit)) s0[r] = -INFINITY;
-                    if (!(w1 & bit)) s1[r] = -INFINITY;
-                }
-            }
-        }
-        const float bias = (LM && cur.kind == KIND_LM) ? p.lm_bias_l2 : 0.f;
-        float mx = max32f(s0, s1);
-        issue(2);
-        mx = xhalf_max(mx);
-        qk_ops(ka, n0, n1, 1);
-        issue(3);
-        const float mt = mx == -INFINITY ? -INFINITY : fmaf(mx, p.scale_l2, bias);
-        // lazy rescale: move the reference max only when some row grew past the threshold
-        if (__ballot(mt > m + RESCALE_THRESHOLD)) {
-            const float mnew = fmaxf(m, mt);
-            const float alpha = __builtin_amdgcn_exp2f(m - mnew);   // 0 when m was -inf
-            l *= alpha;
-            o0 *= alpha;
-            o1 *= alpha;
-            m = mnew;
-        }
-        const float off = bias - (m == -INFINITY ? 0.f : m);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const f32x16& sp = (ks < 2) ? s0 : s1;
-            const int j0 = 2 * (ks & 1);
-            float pv[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                pv[i] = __builtin_amdgcn_exp2f(fmaf(sp[4 * j0 + i], p.scale_l2, off));
-            bf16x2 pp[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pp[i] = bf16x2{(__bf16)pv[2 * i], (__bf16)pv[2 * i + 1]};
-                l = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, l, false);   // sum of rounded P
-            }
-            if (ks < 2) qk_ops(ka, n0, n1, 2 + ks);
-            if (ks == 0) issue(4);
-            if (ks == 1) {
-                issue(5);
-                issue(6);
-            }
-            if (ks == 2) issue(7);
-            const bf16x8 pb = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
-                                                      __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
-                                                      0, 1, 2, 3, 4, 5, 6, 7);
-            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks][0], pb, o0, 0, 0, 0);
-            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks][1], pb, o1, 0, 0, 0);
-        }
-    };
-
-    // ---- prologue: K(0), V(0), K(1) into LDS; S(0) = K(0) Q^T
-    TileDesc d0{}, d1{}, d2{};
-    f32x16 sa0 = {}, sa1 = {}, sb0 = {}, sb1 = {};
-    if (ntiles > 0) {
-        d0 = desc(0);
-        stage(0, d0, (lds_u8*)s_k0);
-        stage(1, d0, (lds_u8*)s_v0);
-        if (ntiles > 1) {
-            d1 = desc(1);
-            stage(0, d1, (lds_u8*)s_k1);
-        }
-        __builtin_amdgcn_s_waitcnt(WAITCNT_VM0_LGKM0);
-        __builtin_amdgcn_s_barrier();
-        for (int st = 0; st < 4; ++st) qk(s_k0, sa0, sa1, st);
-        __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
-        __builtin_amdgcn_s_barrier();           // everyone is done reading K(0)'s buffer
-    }
-
-    // ---- step it: scores of tile it are in (s0, s1); K(it+1) is in kcur, V(it) in vcur.
-    //      Stage K(it+2) -> kfree (held K(it)) and V(it+1) -> vfree (held V(it-1)).
-    auto step = [&](int it, f32x16& s0, f32x16& s1, f32x16& n0, f32x16& n1, const TileDesc& dc,
-                    const TileDesc& dn, TileDesc& dnn, const unsigned char* kcur,
-                    unsigned char* kfree, const unsigned char* vcur, unsigned char* vfree) {
-        const bool sk = it + 2 < ntiles, sv = it + 1 < ntiles;
-        unsigned vk[4], vv[4], bk = 0, bv = 0;
-        __amdgpu_buffer_rsrc_t rk = rs_k, rv = rs_v;
-        if (sk) {
-            dnn = desc(it + 2);
-            plan(0, dnn, vk, bk, rk);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) vk[j] = OOB_OFFSET;
-        }
-        if (sv) {
-            plan(1, dn, vv, bv, rv);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) vv[j] = OOB_OFFSET;
-        }
-        // staging load i: row block i/2 of K(it+2) (even i) or of V(it+1) (odd i), without
-        // branches; the scheduling barrier keeps each load where it is placed
-        auto issue = [&](int i) {
-            if (i & 1) dma_rows(rv, (lds_u8*)vfree, vv, bv, i >> 1);
-            else dma_rows(rk, (lds_u8*)kfree, vk, bk, i >> 1);
-            __builtin_amdgcn_sched_barrier(SCHED_ALLOW_ALL_BUT_VMEM);
-        };
-        softmax_pv(dc, s0, s1, vcur, kcur, n0, n1, issue);
-        // keep the whole step's arithmetic ahead of the wait below (the scheduler would
-        // otherwise hoist the wait and barrier into the middle of the softmax)
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(WAITCNT_VM0_LGKM0);   // this wave's loads have landed
-        __builtin_amdgcn_s_barrier();           // all loads landed; all reads of freed buffers done
-    };
-    int it = 0;
-    for (; it + 1 < ntiles; it += 2) {
-        // even: K(it+1) in k1, V(it) in v0; free: k0, v1
-        step(it, sa0, sa1, sb0, sb1, d0, d1, d2, s_k1, s_k0, s_v0, s_v1);
-        // odd: K(it+2) in k0, V(it+1) in v1; free: k1, v0
-        step(it + 1, sb0, sb1, sa0, sa1, d1, d2, d0, s_k0, s_k1, s_v1, s_v0);
-        // the odd step wrote d(it+3) into d0; rotate to d0 = d(it+2), d1 = d(it+3)
-        d1 = d0;
-        d0 = d2;
-    }
-    if (it < ntiles) step(it, sa0, sa1, sb0, sb1, d0, d1, d2, s_k1, s_k0, s_v0, s_v1);
-
-    float ltot = l + __shfl_xor(l, 32);
-    if (SGA) sga_finish<false>(p, h, qrow, qvalid, g, m, ltot, o0, o1);
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    const size_t obase = ((size_t)h * Lq + qrow) * HD;
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-        const f32x16& oc = cb ? o1 : o0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c0 = 32 * cb + 8 * j + 4 * g;
-            float v4[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v4[i] = qvalid ? oc[4 * j + i] * inv : 0.f;
-            if (F32OUT) {
-                *reinterpret_cast<float4*>(static_cast<float*>(p.out) + obase + c0) =
-                    make_float4(v4[0], v4[1], v4[2], v4[3]);
-            } else {
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + obase + c0) =
-                    make_uint2(pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3]));
-            }
-        }
-    }
-    if (p.lse && g == 0) {
-        float v = 0.f;
-        if (qvalid) v = ltot > 0.f ? (m + log2f(ltot)) * LN2 : -INFINITY;
-        p.lse[(size_t)h * Lq + qrow] = v;
-    }
-}
-
-// Variant for three waves per SIMD (no landmarks, no subsample completion): at most 168
-// VGPRs per wave and 24 KiB of tile buffers per workgroup, so six workgroups share a CU.
-// Step `it` forms S(it) = K(it) Q^T at its start (no S double buffer), then the softmax and
-// P V of tile it.  K has one buffer: once every wave has read K(it) (first barrier of the
-// step) the loads of K(it+1) go out.  V has two: V(it+1) loads from the start of step it
-// into the buffer V(it-1) left.  Operands are read from LDS as they are needed.
-template <bool F32OUT, bool DENSE>
-__global__ __launch_bounds__(128, 3) void k_attn_bf16_o3(AttnDev p) {
+__global__ __launch_bounds__(128, 3) void k_attn_bf16(AttnDev p) {
     __shared__ __align__(16) unsigned char s_k[TILE_BYTES];
     __shared__ __align__(16) unsigned char s_v0[TILE_BYTES];
     __shared__ __align__(16) unsigned char s_v1[TILE_BYTES];
@@ -508,9 +123,11 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16_o3(AttnDev p) {
     } else {
         c = min(max(p.cnt[(size_t)h * p.Tq + tq], 0), p.kmax);
         myidx = p.idx + ((size_t)h * p.Tq + tq) * p.kmax;
-        ntiles = p.Ts + c;
+        ntiles = p.Ts + c + (LM ? p.nlm : 0);
     }
-    int32_t* s_idx = reinterpret_cast<int32_t*>(s_dyn);
+    uint32_t* s_lm = s_dyn;                          // landmark bitmap (2 nlm words), then the list
+    if (LM) init_landmark_bitmap(p, c, myidx, s_lm, tid, 128);
+    int32_t* s_idx = reinterpret_cast<int32_t*>(s_dyn + (LM ? 2 * p.nlm : 0));
     if (!DENSE) {
         for (int i = tid; i < c; i += 128) s_idx[i] = pack_tile_entry(p, myidx[i]);
         __syncthreads();
@@ -528,6 +145,18 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16_o3(AttnDev p) {
     const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<unsigned char*>(static_cast<const unsigned char*>(p.v)) + (size_t)h * head_bytes, 0,
         (int)head_bytes, BUF_RSRC_WORD3);
+    // landmark means (operand dtype, [heads, Tk, 64]): block b of 64 consecutive tile means
+    // is staged like a key tile
+    __amdgpu_buffer_rsrc_t rs_lk = rs_k, rs_lv = rs_v;
+    if (LM) {
+        const unsigned mean_bytes = (unsigned)p.Tk * 128u;
+        rs_lk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<unsigned char*>(static_cast<const unsigned char*>(p.kbar)) + (size_t)h * mean_bytes, 0,
+            (int)mean_bytes, BUF_RSRC_WORD3);
+        rs_lv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<unsigned char*>(static_cast<const unsigned char*>(p.vbar)) + (size_t)h * mean_bytes, 0,
+            (int)mean_bytes, BUF_RSRC_WORD3);
+    }
 
     const int srow_in = lane >> 3, sslot = lane & 7;
     int srow[4], soff[4];
@@ -536,7 +165,7 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16_o3(AttnDev p) {
         srow[j] = 32 * w + 8 * j + srow_in;
         soff[j] = srow[j] * 128 + swz(srow[j], sslot) * 16;
     }
-    auto desc = [&](int it) { return describe<DENSE, false, !DENSE>(p, it, c, myidx, s_idx, nullptr, rot, t0); };
+    auto desc = [&](int it) { return describe<DENSE, LM, !DENSE>(p, it, c, myidx, s_idx, s_lm, rot, t0); };
     auto plan = [&](const TileDesc& dd, unsigned (&voff)[4], unsigned& base) {
         const TileDesc d = uniform(dd);
         const bool spec = d.kind == KIND_SPEC;
@@ -573,17 +202,19 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16_o3(AttnDev p) {
         const bool more = it + 1 < ntiles;
         TileDesc dn{};
         unsigned vk[4], vv[4], bk = 0, bv = 0;
+        bool nlmk = false;                                  // tile it+1 is a landmark block
         if (more) {
             dn = desc(it + 1);
             plan(dn, vk, bk);
 #pragma unroll
             for (int j = 0; j < 4; ++j) vv[j] = vk[j];
             bv = bk;
+            nlmk = LM && uniform(dn).kind == KIND_LM;
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) vk[j] = vv[j] = OOB_OFFSET;
         }
-        dma4(rs_v, (lds_u8*)vnext, vv, bv);                 // V(it+1)
+        dma4(nlmk ? rs_lv : rs_v, (lds_u8*)vnext, vv, bv);  // V(it+1)
         f32x16 s0, s1;
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
@@ -595,7 +226,7 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16_o3(AttnDev p) {
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
         __builtin_amdgcn_s_barrier();                       // every wave has read K(it)
-        dma4(rs_k, (lds_u8*)s_k, vk, bk);                   // K(it+1)
+        dma4(nlmk ? rs_lk : rs_k, (lds_u8*)s_k, vk, bk);    // K(it+1)
         __builtin_amdgcn_sched_barrier(0);
         if (cur.mask != ~0ull) {
             // slot r of a lane in half-wave g holds key 8 (r / 4) + 4 g + r % 4 (+32 in s1): its
@@ -618,7 +249,7 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16_o3(AttnDev p) {
         }
         if constexpr (DENSE) {
             // every workgroup sweeps the keys in the same order, so the probabilities are
-            // taken against the tile's row max (lazy rescale, as in the two-wave kernel)
+            // taken against the tile's row max (lazy rescale)
             float mx = max32f(s0, s1);
             {
                 const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
@@ -665,6 +296,7 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16_o3(AttnDev p) {
             // (rescaling O and l) and recomputes.  Rounding is relative, so the reference only
             // has to keep the probabilities in range, not equal the running max.
             const bool fresh = __ballot(m == -INFINITY) != 0;
+            const float bias = (LM && cur.kind == KIND_LM) ? p.lm_bias_l2 : 0.f;   // landmark logit bias
     #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 if ((uint32_t)(cur.mask >> (32 * hf)) == 0u) continue;   // no key in this half
@@ -672,7 +304,7 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16_o3(AttnDev p) {
                 bf16x8 pb[2];
                 float lh;
                 auto probs = [&]() {
-                    const float off = m == -INFINITY ? 0.f : -m;
+                    const float off = bias - (m == -INFINITY ? 0.f : m);
                     lh = 0.f;
     #pragma unroll
                     for (int kk = 0; kk < 2; ++kk) {
@@ -698,7 +330,7 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16_o3(AttnDev p) {
                     mx = fmaxf(mx, sp[15]);
                     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
                     mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-                    const float mnew = fmaxf(m, mx == -INFINITY ? -INFINITY : mx * p.scale_l2);
+                    const float mnew = fmaxf(m, mx == -INFINITY ? -INFINITY : fmaf(mx, p.scale_l2, bias));
                     const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
                     l *= alpha;
                     o0 *= alpha;
@@ -727,8 +359,9 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16_o3(AttnDev p) {
         d = desc(0);
         unsigned v0[4], b0;
         plan(d, v0, b0);
-        dma4(rs_k, (lds_u8*)s_k, v0, b0);
-        dma4(rs_v, (lds_u8*)s_v0, v0, b0);
+        const bool lmk = LM && uniform(d).kind == KIND_LM;
+        dma4(lmk ? rs_lk : rs_k, (lds_u8*)s_k, v0, b0);
+        dma4(lmk ? rs_lv : rs_v, (lds_u8*)s_v0, v0, b0);
         __builtin_amdgcn_s_waitcnt(WAITCNT_VM0_LGKM0);
         __builtin_amdgcn_s_barrier();
     }
@@ -739,7 +372,8 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16_o3(AttnDev p) {
     }
     if (it < ntiles) step(it, d, s_v0, s_v1);
 
-    const float ltot = l + __shfl_xor(l, 32);
+    float ltot = l + __shfl_xor(l, 32);
+    if (SGA) sga_finish<false>(p, h, qrow, qvalid, g, m, ltot, o0, o1);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     const size_t obase = ((size_t)h * Lq + qrow) * HD;
 #pragma unroll
@@ -772,11 +406,6 @@ static void launch_t(const AttnDev& d, int heads, bool dense, bool lm, hipStream
     const dim3 grid((unsigned)(heads * d.Tq)), block(128);
     const size_t shm = ((lm ? (size_t)(2 * d.nlm) : 0) + (dense ? 0 : (size_t)d.kmax)) *
                        sizeof(uint32_t);
-    if (!lm && !SGA) {
-        if (dense) hipLaunchKernelGGL((k_attn_bf16_o3<F32OUT, true>), grid, block, 0, st, d);
-        else hipLaunchKernelGGL((k_attn_bf16_o3<F32OUT, false>), grid, block, shm, st, d);
-        return;
-    }
     if (dense) hipLaunchKernelGGL((k_attn_bf16<F32OUT, true, false, SGA>), grid, block, 0, st, d);
     else if (lm) hipLaunchKernelGGL((k_attn_bf16<F32OUT, false, true, SGA>), grid, block, shm, st, d);
     else hipLaunchKernelGGL((k_attn_bf16<F32OUT, false, false, SGA>), grid, block, shm, st, d);

@@ -72,7 +72,7 @@ __device__ __forceinline__ int32_t pack_tile_entry(const AttnDev& p, int32_t t) 
     return t | (lo << 16) | (hi << 23);
 }
 
-// Longest selection list the bf16 kernel stages in LDS (next to its 32 KiB of tile
+// Longest selection list the bf16 kernel stages in LDS (next to its 24 KiB of tile
 // buffers, within 64 KiB); longer lists run on the generic kernel.
 constexpr int IDX_LDS_MAX = 8000;
 
