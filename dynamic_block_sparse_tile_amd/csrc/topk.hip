@@ -86,11 +86,22 @@ __global__ __launch_bounds__(TK_THREADS) void k_select_topk(const float* __restr
     const float* src = scores + row * (size_t)Tk;
 
     uint32_t kmin = 0xffffffffu, kmaxk = 0u;
-    for (int i = tid; i < Tk; i += TK_THREADS) {
-        const uint32_t key = order_key(src[i]);
-        s_keys[i] = key;
-        kmin = min(kmin, key);
-        kmaxk = max(kmaxk, key);
+    // eight loads in flight per thread before any is used
+    constexpr int LB = 8;
+    for (int i0 = 0; i0 < Tk; i0 += LB * TK_THREADS) {
+        float f[LB];
+#pragma unroll
+        for (int u = 0; u < LB; ++u) f[u] = src[min(i0 + u * TK_THREADS + tid, Tk - 1)];
+#pragma unroll
+        for (int u = 0; u < LB; ++u) {
+            const int i = i0 + u * TK_THREADS + tid;
+            if (i < Tk) {
+                const uint32_t key = order_key(f[u]);
+                s_keys[i] = key;
+                kmin = min(kmin, key);
+                kmaxk = max(kmaxk, key);
+            }
+        }
     }
     kmin = wave_min(kmin);
     kmaxk = wave_max(kmaxk);
@@ -340,14 +351,13 @@ hipError_t launch_select_topk(const float* scores, int heads, int tq, int tk, co
         const int rows = nh * tq;
         int32_t* ix = kmax > 0 ? idx + r0 * kmax : idx;
         const dim3 wgrid((unsigned)((rows + TKW_WAVES - 1) / TKW_WAVES)), wblock(64 * TKW_WAVES);
+        // one wave per row while the keys fit 48 registers per lane; longer rows (fewer per
+        // launch, and each would hold too many registers) use a workgroup per row
         if (tk <= 64 * 16)
             hipLaunchKernelGGL(k_select_topk_wave<16>, wgrid, wblock, 0, st, scores + r0 * tk, tk, tq, rows, kb,
                                tpf, anchor, ix, cnt + r0, kmax);
         else if (tk <= 64 * 48)
             hipLaunchKernelGGL(k_select_topk_wave<48>, wgrid, wblock, 0, st, scores + r0 * tk, tk, tq, rows, kb,
-                               tpf, anchor, ix, cnt + r0, kmax);
-        else if (tk <= 64 * 96)
-            hipLaunchKernelGGL(k_select_topk_wave<96>, wgrid, wblock, 0, st, scores + r0 * tk, tk, tq, rows, kb,
                                tpf, anchor, ix, cnt + r0, kmax);
         else
             hipLaunchKernelGGL(k_select_topk, dim3((unsigned)rows), dim3(TK_THREADS), shm, st,
