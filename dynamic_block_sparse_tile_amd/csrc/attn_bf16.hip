@@ -129,8 +129,13 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16(AttnDev p) {
     if (LM) init_landmark_bitmap(p, c, myidx, s_lm, tid, 128);
     int32_t* s_idx = reinterpret_cast<int32_t*>(s_dyn + (LM ? 2 * p.nlm : 0));
     if (!DENSE) {
+        // the selected-tile list, staged once in LDS so that each step's lookup is an LDS read
+        // (the launcher guarantees kmax <= IDX_LDS_MAX)
         for (int i = tid; i < c; i += 128) s_idx[i] = pack_tile_entry(p, myidx[i]);
         __syncthreads();
+        // Sweep the list starting at the query's own frame (wrapping round): its tiles hold the
+        // highest scores, so the softmax reference settles on the first steps (the list order
+        // changes the result only by rounding).
         const int thr = (tq / tpfq) * (p.kl.P / TILE);
         int n = 0;
         for (int b = 0; b < c; b += 128)
@@ -297,22 +302,27 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16(AttnDev p) {
             // has to keep the probabilities in range, not equal the running max.
             const bool fresh = __ballot(m == -INFINITY) != 0;
             const float bias = (LM && cur.kind == KIND_LM) ? p.lm_bias_l2 : 0.f;   // landmark logit bias
-    #pragma unroll
+#pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 if ((uint32_t)(cur.mask >> (32 * hf)) == 0u) continue;   // no key in this half
+                // this half's V operands, requested before the exponentials so that the LDS
+                // reads overlap them
+                bf16x8 va[2][2];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) read_tr(vcur, to, 2 * hf + kk, va[kk][0], va[kk][1]);
                 const f32x16& sp = hf ? s1 : s0;
                 bf16x8 pb[2];
                 float lh;
                 auto probs = [&]() {
                     const float off = bias - (m == -INFINITY ? 0.f : m);
                     lh = 0.f;
-    #pragma unroll
+#pragma unroll
                     for (int kk = 0; kk < 2; ++kk) {
                         float pv[8];
-    #pragma unroll
+#pragma unroll
                         for (int i = 0; i < 8; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sp[8 * kk + i], p.scale_l2, off));
                         bf16x2 pp[4];
-    #pragma unroll
+#pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             pp[i] = bf16x2{(__bf16)pv[2 * i], (__bf16)pv[2 * i + 1]};
                             lh = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, lh, false);
@@ -325,7 +335,7 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16(AttnDev p) {
                 probs();
                 if (fresh || __ballot(!(lh <= PROB_SUM_LIMIT))) {
                     float mx = sp[0];
-    #pragma unroll
+#pragma unroll
                     for (int i = 1; i < 15; i += 2) mx = max3f(mx, sp[i], sp[i + 1]);
                     mx = fmaxf(mx, sp[15]);
                     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
@@ -339,12 +349,10 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16(AttnDev p) {
                     probs();
                 }
                 l += lh;
-    #pragma unroll
+#pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    bf16x8 va0, va1;
-                    read_tr(vcur, to, 2 * hf + kk, va0, va1);
-                    o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0, pb[kk], o0, 0, 0, 0);
-                    o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1, pb[kk], o1, 0, 0, 0);
+                    o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk][0], pb[kk], o0, 0, 0, 0);
+                    o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk][1], pb[kk], o1, 0, 0, 0);
                 }
             }
         }
