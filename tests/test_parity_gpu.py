@@ -135,6 +135,33 @@ def test_specials_span_tiles():
     run_full_case(_custom(2, 150, 192, 70, k=2), landmarks=True)
 
 
+def test_rising_logits_move_the_reference():
+    # Every frame's tokens scaled by 2^frame (exact in bf16): scores grow by factors of up to
+    # 2^(2*3) across frames, spanning ~100 base-2 units, so the sparse kernel's running
+    # reference must move many times within a row (its slow path) and every rescale of O
+    # and l is exercised; outputs and lse still match the oracle.
+    w = _custom(4, 256, 256, 5, k=6)
+    inp = synth.make_inputs(w, seed=3)
+    S_, P = w.frames, w.stride
+    scale = np.repeat(2.0 ** np.arange(S_), P).astype(np.float32)[None, :, None]
+    q_np = (inp.q * scale).astype(np.float32)
+    assert np.array_equal(torch.from_numpy(q_np).to(torch.bfloat16).float().numpy(), q_np)   # exact
+    q, v = to_dev(q_np, torch.bfloat16), to_dev(inp.v, torch.bfloat16)
+    res = LY.sparse_global_attention(q, q, v, w.layout, top_k=w.k, anchor_frame=w.anchor,
+                                     out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    ol = oracle.Layout(*w.layout)
+    g_idx, g_cnt = res.idx.cpu().numpy(), res.cnt.cpu().numpy()
+    O, lse = oracle.sparse_attend(q_np, q_np, inp.v, ol, ol, 64, g_idx, g_cnt, 0.125)
+    out = res.out.cpu().numpy()
+    H, L, _ = out.shape
+    pairs = [(h, t) for h in range(H) for t in range(L // 64)]
+    # lse reaches several hundred here; its fp32 accumulation error stays far below 1e-2
+    worst = compare_outputs(out, O, pairs, tol=TOL["bf16"], g_lse=res.lse.cpu().numpy(), ref_lse=lse,
+                            lse_tol=1e-2)
+    say(f"  ok: max|dO| = {worst:.2e}")
+
+
 def test_long_selection_lists():
     # more than 128 selected tiles per query tile (the staged index list spans several
     # passes of the workgroup) and a landmark bitmap wider than 128 words
