@@ -29,6 +29,11 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The float whose order_key() is k (+0.0 for the folded zero).
+__device__ __forceinline__ float key_float(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 // Block-wide exclusive prefix sum over thread order; also returns the total.
 __device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int& total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -223,8 +228,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_select_topk(const float* __restr
 // The same selection with one wave per score row (rows of at most 64 * E tiles): the keys
 // stay in registers (tile i * 64 + lane in slot i) and every count is a ballot and a scalar
 // popcount, so a row needs no LDS histogram and no barrier.  The k-th largest key T is
-// bracketed by bisection of the key interval, keeping count(key >= lo) >= k >
-// count(key > hi); once at most 64 keys remain inside the bracket they are gathered, one
+// bracketed by bisection, keeping count(key >= lo) >= k > count(key > hi); once at most 64 keys remain inside the bracket they are gathered, one
 // per lane, and ordered by a bitonic network across the lanes, which yields T directly.
 // Selection and compaction then run over the slots in tile order with ballot prefix
 // counts, exactly as in the workgroup kernel (keys above T, the lowest-index ties, the
@@ -269,6 +273,11 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
         lo = wave_min(lo);
         hi = wave_max(hi);
         int c_lo = Tk, c_hi = 0;                    // count(key >= lo), count(key > hi)
+        // The probe halves the bracket in value (the midpoint of the two floats) while that
+        // keeps shrinking the candidate count by at least a quarter, else in key order: on
+        // score rows the value midpoint needs about half the passes of key bisection, and
+        // the alternation bounds rows whose values span many binades.
+        bool by_key = false;
         while (lo != hi) {
             if (c_lo - c_hi <= 64) {
                 // gather the keys inside [lo, hi] and rank them across the lanes
@@ -297,7 +306,13 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
                 hi = lo;
                 break;
             }
-            const uint32_t mid = lo + (uint32_t)(((uint64_t)hi - lo + 1) >> 1);
+            uint32_t mid = lo + (uint32_t)(((uint64_t)hi - lo + 1) >> 1);
+            if (!by_key) {
+                const float fl = key_float(lo), fh = key_float(hi);
+                if (__builtin_isfinite(fl) && __builtin_isfinite(fh))
+                    mid = min(max(order_key(0.5f * fl + 0.5f * fh), lo + 1), hi);
+            }
+            const int before = c_lo - c_hi;
             const int c = count_ge(mid);
             if (c >= k) {
                 lo = mid;
@@ -306,6 +321,7 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
                 hi = mid - 1;
                 c_hi = c;
             }
+            by_key = !by_key && 4 * (c_lo - c_hi) > 3 * before;
         }
         T = lo;
 #pragma unroll
@@ -355,6 +371,12 @@ hipError_t launch_select_topk(const float* scores, int heads, int tq, int tk, co
         // launch, and each would hold too many registers) use a workgroup per row
         if (tk <= 64 * 16)
             hipLaunchKernelGGL(k_select_topk_wave<16>, wgrid, wblock, 0, st, scores + r0 * tk, tk, tq, rows, kb,
+                               tpf, anchor, ix, cnt + r0, kmax);
+        else if (tk <= 64 * 32)
+            hipLaunchKernelGGL(k_select_topk_wave<32>, wgrid, wblock, 0, st, scores + r0 * tk, tk, tq, rows, kb,
+                               tpf, anchor, ix, cnt + r0, kmax);
+        else if (tk <= 64 * 44)
+            hipLaunchKernelGGL(k_select_topk_wave<44>, wgrid, wblock, 0, st, scores + r0 * tk, tk, tq, rows, kb,
                                tpf, anchor, ix, cnt + r0, kmax);
         else if (tk <= 64 * 48)
             hipLaunchKernelGGL(k_select_topk_wave<48>, wgrid, wblock, 0, st, scores + r0 * tk, tk, tq, rows, kb,

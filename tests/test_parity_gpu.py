@@ -162,6 +162,39 @@ def test_rising_logits_move_the_reference():
     say(f"  ok: max|dO| = {worst:.2e}")
 
 
+def test_select_topk_hard_rows():
+    # Score rows built to stress the k-th-largest search: heavy ties, values spread over
+    # many binades (with overflow to +inf), masked (-inf) entries, constant rows and signed
+    # zeros, at lengths that take each wave width and the workgroup kernel.  Compared with
+    # the oracle's rule applied to the same fp32 scores.
+    rng = np.random.default_rng(21)
+    for Tk in (100, 1000, 2000, 2816, 3000, 5000):
+        tpf = 22 if Tk % 22 == 0 else 20
+        rows = [rng.standard_normal(Tk),
+                rng.integers(-3, 3, Tk).astype(np.float64),
+                np.exp(rng.normal(0.0, 20.0, Tk)),
+                rng.standard_normal(Tk) * 10.0 ** rng.integers(-30, 30, Tk),
+                np.where(rng.random(Tk) < 0.5, -np.inf, rng.standard_normal(Tk)),
+                np.full(Tk, -np.inf),
+                np.full(Tk, 2.5)]
+        r = rng.standard_normal(Tk)
+        r[::7] = 0.0
+        r[::11] = -0.0
+        rows.append(r)
+        with np.errstate(over="ignore"):
+            sc = np.stack(rows).astype(np.float32)[None]
+        g = to_dev(sc, torch.float32)
+        say(f"[case] select hard rows Tk={Tk}")
+        for k in (1, 5, 138, Tk - 1, Tk, Tk + 3):
+            for anchor in (-1, 0):
+                idx, cnt = S.sparse3d_select_topk(g, k, tpf, anchor)
+                gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+                for t in range(sc.shape[1]):
+                    ref = oracle.select_tiles(sc[0, t].astype(np.float64), k, tpf, anchor)
+                    assert gc[0, t] == len(ref) and np.array_equal(gi[0, t, :gc[0, t]], ref), (Tk, k, anchor, t)
+                    assert np.all(gi[0, t, gc[0, t]:] == -1)
+
+
 def test_long_selection_lists():
     # more than 128 selected tiles per query tile (the staged index list spans several
     # passes of the workgroup) and a landmark bitmap wider than 128 words
