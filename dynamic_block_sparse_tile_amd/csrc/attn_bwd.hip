@@ -236,7 +236,11 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dq(BwdDev p) {
 
 // ------------------------------------------------------------------------------ dK, dV
 // Work items: H * Ts special pseudo-tiles first (attended by every query tile, the longest
-// items), then H * Tk frame tiles.
+// items), then H * Tk frame tiles, taken in launch order: workgroup i runs on XCD i % 8, so
+// the long special items spread evenly over the XCDs and all XCDs work through the same
+// head's key tiles at a time (their query tiles then share the last-level cache).  Giving
+// each XCD a contiguous range of items instead put every special item on one XCD, which
+// then carried about 40 % more work than the others.
 __global__ __launch_bounds__(128, 2) void k_attn_bwd_dkv(BwdDev p) {
     __shared__ __align__(16) unsigned char s_q[2][TILE_BYTES];
     __shared__ __align__(16) unsigned char s_do[2][TILE_BYTES];
@@ -246,7 +250,7 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dkv(BwdDev p) {
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int kc = lane & 31, g = lane >> 5;
     const int heads = gridDim.x / (p.Ts + p.Tk);
-    const int item = xcd_remap(blockIdx.x, gridDim.x);
+    const int item = blockIdx.x;
     const int nspec = heads * p.Ts;
     int h;
     Block kb;
