@@ -101,6 +101,11 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16(AttnDev p) {
     const int Lq = p.ql.S * p.ql.P, Lk = p.kl.S * p.kl.P;
     const int qrow = tq * TILE + w * 32 + qc;
     const bool qvalid = (tq % tpfq) * TILE + w * 32 + qc < p.ql.N;
+    // In the sparse paths a wave whose 32 rows are all padding (the second half of a frame's
+    // last tile) still stages its half of every tile and meets every barrier, but skips the
+    // products.  (Dense and frame attention keep every wave busy: there the workgroups sweep
+    // the keys in lockstep and share them through L2, and one finishing early was slower.)
+    const bool wq = DENSE || __ballot(qvalid) != 0ull;
 
     bf16x8 qop[4];
     {
@@ -221,138 +226,142 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16(AttnDev p) {
         }
         dma4(nlmk ? rs_lv : rs_v, (lds_u8*)vnext, vv, bv);  // V(it+1)
         f32x16 s0, s1;
+        if (wq) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            bf16x8 a0, a1;
-            read_rows(s_k, to, st, a0, a1);
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qop[st], st ? s0 : f32x16{}, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qop[st], st ? s1 : f32x16{}, 0, 0, 0);
+            for (int st = 0; st < 4; ++st) {
+                bf16x8 a0, a1;
+                read_rows(s_k, to, st, a0, a1);
+                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qop[st], st ? s0 : f32x16{}, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qop[st], st ? s1 : f32x16{}, 0, 0, 0);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
         __builtin_amdgcn_s_barrier();                       // every wave has read K(it)
         dma4(nlmk ? rs_lk : rs_k, (lds_u8*)s_k, vk, bk);    // K(it+1)
         __builtin_amdgcn_sched_barrier(0);
-        if (cur.mask != ~0ull) {
-            // slot r of a lane in half-wave g holds key 8 (r / 4) + 4 g + r % 4 (+32 in s1): its
-            // lane mask takes one row bit for lanes 0-31 and another for lanes 32-63, formed
-            // on the scalar unit from the uniform row mask.  The scores come from the matrix
-            // core; the compiler does not see the reads inside the asm, so a few idle
-            // cycles keep them clear of the products' write-back
-            __builtin_amdgcn_sched_barrier(0);
-            asm volatile("s_nop 7\n\ts_nop 7");
+        if (wq) {
+            if (cur.mask != ~0ull) {
+                // slot r of a lane in half-wave g holds key 8 (r / 4) + 4 g + r % 4 (+32 in s1): its
+                // lane mask takes one row bit for lanes 0-31 and another for lanes 32-63, formed
+                // on the scalar unit from the uniform row mask.  The scores come from the matrix
+                // core; the compiler does not see the reads inside the asm, so a few idle
+                // cycles keep them clear of the products' write-back
+                __builtin_amdgcn_sched_barrier(0);
+                asm volatile("s_nop 7\n\ts_nop 7");
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int cr = 8 * (r >> 2) + (r & 3);
-                const uint64_t k0 = (((cur.mask >> cr) & 1ull) ? 0x00000000FFFFFFFFull : 0ull) |
-                                    (((cur.mask >> (cr + 4)) & 1ull) ? 0xFFFFFFFF00000000ull : 0ull);
-                const uint64_t k1 = (((cur.mask >> (cr + 32)) & 1ull) ? 0x00000000FFFFFFFFull : 0ull) |
-                                    (((cur.mask >> (cr + 36)) & 1ull) ? 0xFFFFFFFF00000000ull : 0ull);
-                s0[r] = keep_lanes(s0[r], k0);
-                s1[r] = keep_lanes(s1[r], k1);
-            }
-        }
-        if constexpr (DENSE) {
-            // every workgroup sweeps the keys in the same order, so the probabilities are
-            // taken against the tile's row max (lazy rescale)
-            float mx = max32f(s0, s1);
-            {
-                const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-                mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-            }
-            const float mt = mx == -INFINITY ? -INFINITY : mx * p.scale_l2;
-            if (__ballot(mt > m + RESCALE_THRESHOLD)) {
-                const float mnew = fmaxf(m, mt);
-                const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-                l *= alpha;
-                o0 *= alpha;
-                o1 *= alpha;
-                m = mnew;
-            }
-            const float off = -(m == -INFINITY ? 0.f : m);
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                if ((uint32_t)(cur.mask >> (32 * (ks >> 1))) == 0u) continue;   // no key in this half
-                const f32x16& sp = (ks < 2) ? s0 : s1;
-                const int j0 = 2 * (ks & 1);
-                bf16x8 va0, va1;
-                read_tr(vcur, to, ks, va0, va1);
-                float pv[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sp[4 * j0 + i], p.scale_l2, off));
-                bf16x2 pp[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pp[i] = bf16x2{(__bf16)pv[2 * i], (__bf16)pv[2 * i + 1]};
-                    l = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, l, false);
+                for (int r = 0; r < 16; ++r) {
+                    const int cr = 8 * (r >> 2) + (r & 3);
+                    const uint64_t k0 = (((cur.mask >> cr) & 1ull) ? 0x00000000FFFFFFFFull : 0ull) |
+                                        (((cur.mask >> (cr + 4)) & 1ull) ? 0xFFFFFFFF00000000ull : 0ull);
+                    const uint64_t k1 = (((cur.mask >> (cr + 32)) & 1ull) ? 0x00000000FFFFFFFFull : 0ull) |
+                                        (((cur.mask >> (cr + 36)) & 1ull) ? 0xFFFFFFFF00000000ull : 0ull);
+                    s0[r] = keep_lanes(s0[r], k0);
+                    s1[r] = keep_lanes(s1[r], k1);
                 }
-                const bf16x8 pb = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
-                                                          __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
-                                                          0, 1, 2, 3, 4, 5, 6, 7);
-                o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0, pb, o0, 0, 0, 0);
-                o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1, pb, o1, 0, 0, 0);
             }
-        } else {
-            // Probabilities are taken against the running reference m without first forming
-            // the tile's row max.  Each half tile (32 keys) checks afterwards that its rounded
-            // probabilities sum to at most 2^16 (then none exceeds 2^16: nothing overflowed,
-            // and the accumulators keep ample range); only a half that fails, or any half while a
-            // row has no reference yet, forms the max of its scores, moves the reference
-            // (rescaling O and l) and recomputes.  Rounding is relative, so the reference only
-            // has to keep the probabilities in range, not equal the running max.
-            const bool fresh = __ballot(m == -INFINITY) != 0;
-            const float bias = (LM && cur.kind == KIND_LM) ? p.lm_bias_l2 : 0.f;   // landmark logit bias
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                if ((uint32_t)(cur.mask >> (32 * hf)) == 0u) continue;   // no key in this half
-                // this half's V operands, requested before the exponentials so that the LDS
-                // reads overlap them
-                bf16x8 va[2][2];
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) read_tr(vcur, to, 2 * hf + kk, va[kk][0], va[kk][1]);
-                const f32x16& sp = hf ? s1 : s0;
-                bf16x8 pb[2];
-                float lh;
-                auto probs = [&]() {
-                    const float off = bias - (m == -INFINITY ? 0.f : m);
-                    lh = 0.f;
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        float pv[8];
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sp[8 * kk + i], p.scale_l2, off));
-                        bf16x2 pp[4];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            pp[i] = bf16x2{(__bf16)pv[2 * i], (__bf16)pv[2 * i + 1]};
-                            lh = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, lh, false);
-                        }
-                        pb[kk] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
-                                                         __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
-                                                         0, 1, 2, 3, 4, 5, 6, 7);
-                    }
-                };
-                probs();
-                if (fresh || __ballot(!(lh <= PROB_SUM_LIMIT))) {
-                    float mx = sp[0];
-#pragma unroll
-                    for (int i = 1; i < 15; i += 2) mx = max3f(mx, sp[i], sp[i + 1]);
-                    mx = fmaxf(mx, sp[15]);
+            if constexpr (DENSE) {
+                // every workgroup sweeps the keys in the same order, so the probabilities are
+                // taken against the tile's row max (lazy rescale)
+                float mx = max32f(s0, s1);
+                {
                     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
                     mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-                    const float mnew = fmaxf(m, mx == -INFINITY ? -INFINITY : fmaf(mx, p.scale_l2, bias));
-                    const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
+                }
+                const float mt = mx == -INFINITY ? -INFINITY : mx * p.scale_l2;
+                if (__ballot(mt > m + RESCALE_THRESHOLD)) {
+                    const float mnew = fmaxf(m, mt);
+                    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
                     l *= alpha;
                     o0 *= alpha;
                     o1 *= alpha;
                     m = mnew;
-                    probs();
                 }
-                l += lh;
+                const float off = -(m == -INFINITY ? 0.f : m);
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk][0], pb[kk], o0, 0, 0, 0);
-                    o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk][1], pb[kk], o1, 0, 0, 0);
+                for (int ks = 0; ks < 4; ++ks) {
+                    if ((uint32_t)(cur.mask >> (32 * (ks >> 1))) == 0u) continue;   // no key in this half
+                    const f32x16& sp = (ks < 2) ? s0 : s1;
+                    const int j0 = 2 * (ks & 1);
+                    bf16x8 va0, va1;
+                    read_tr(vcur, to, ks, va0, va1);
+                    float pv[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sp[4 * j0 + i], p.scale_l2, off));
+                    bf16x2 pp[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        pp[i] = bf16x2{(__bf16)pv[2 * i], (__bf16)pv[2 * i + 1]};
+                        l = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, l, false);
+                    }
+                    const bf16x8 pb = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+                                                              __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
+                                                              0, 1, 2, 3, 4, 5, 6, 7);
+                    o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0, pb, o0, 0, 0, 0);
+                    o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1, pb, o1, 0, 0, 0);
+                }
+            } else {
+                // Probabilities are taken against the running reference m without first forming
+                // the tile's row max.  Each half tile (32 keys) checks afterwards that its rounded
+                // probabilities sum to at most 2^16 (then none exceeds 2^16: nothing overflowed,
+                // and the accumulators keep ample range); only a half that fails, or any half while a
+                // row has no reference yet, forms the max of its scores, moves the reference
+                // (rescaling O and l) and recomputes.  Rounding is relative, so the reference only
+                // has to keep the probabilities in range, not equal the running max.
+                const bool fresh = __ballot(m == -INFINITY) != 0;
+                const float bias = (LM && cur.kind == KIND_LM) ? p.lm_bias_l2 : 0.f;   // landmark logit bias
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    if ((uint32_t)(cur.mask >> (32 * hf)) == 0u) continue;   // no key in this half
+                    // this half's V operands, requested before the exponentials so that the LDS
+                    // reads overlap them
+                    bf16x8 va[2][2];
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) read_tr(vcur, to, 2 * hf + kk, va[kk][0], va[kk][1]);
+                    const f32x16& sp = hf ? s1 : s0;
+                    bf16x8 pb[2];
+                    float lh;
+                    auto probs = [&]() {
+                        const float off = bias - (m == -INFINITY ? 0.f : m);
+                        lh = 0.f;
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk) {
+                            float pv[8];
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sp[8 * kk + i], p.scale_l2, off));
+                            bf16x2 pp[4];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                pp[i] = bf16x2{(__bf16)pv[2 * i], (__bf16)pv[2 * i + 1]};
+                                lh = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, lh, false);
+                            }
+                            pb[kk] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+                                                             __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
+                                                             0, 1, 2, 3, 4, 5, 6, 7);
+                        }
+                    };
+                    probs();
+                    if (fresh || __ballot(!(lh <= PROB_SUM_LIMIT))) {
+                        float mx = sp[0];
+#pragma unroll
+                        for (int i = 1; i < 15; i += 2) mx = max3f(mx, sp[i], sp[i + 1]);
+                        mx = fmaxf(mx, sp[15]);
+                        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                        mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+                        const float mnew = fmaxf(m, mx == -INFINITY ? -INFINITY : fmaf(mx, p.scale_l2, bias));
+                        const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
+                        l *= alpha;
+                        o0 *= alpha;
+                        o1 *= alpha;
+                        m = mnew;
+                        probs();
+                    }
+                    l += lh;
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk][0], pb[kk], o0, 0, 0, 0);
+                        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk][1], pb[kk], o1, 0, 0, 0);
+                    }
                 }
             }
         }
