@@ -148,6 +148,9 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dq(BwdDev p) {
         dpart = dot_bf16x8(dop[s], load_b(p.o, qbase + 16 * s + 8 * g, qvalid), dpart);
     }
     const float D = dpart + __shfl_xor(dpart, 32);       // rowsum(dO * O), both halves
+    // a wave whose 32 query rows are all padding stages and meets the barriers but skips
+    // the products
+    const bool wq = __ballot(qvalid) != 0ull;
     const float lse = qvalid ? p.lse[(size_t)h * Lq + qrow] : INFINITY;
     // base-2 offset of P = exp(s - lse); a row with nothing attended (lse = -inf) or not a
     // query gets P = 0
@@ -183,37 +186,39 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dq(BwdDev p) {
         if (it + 1 < ntiles) nxt = stage(it + 1, b ^ 1);
         const unsigned char* kt = s_k[b];
         const unsigned char* vt = s_v[b];
-        f32x16 s0 = {}, s1 = {}, p0 = {}, p1 = {};
+        if (wq) {
+            f32x16 s0 = {}, s1 = {}, p0 = {}, p1 = {};
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            bf16x8 a0, a1, v0, v1;
-            read_rows(kt, off, st, a0, a1);
-            read_rows(vt, off, st, v0, v1);
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qop[st], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qop[st], s1, 0, 0, 0);
-            p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, dop[st], p0, 0, 0, 0);
-            p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, dop[st], p1, 0, 0, 0);
-        }
-        // dS^T = P^T (dP^T - D); key rows outside the block's mask take no part
-        // this lane's keys 8i + 4g + (0..3) of each half, tested against constant bits
-        const uint32_t w0 = __builtin_amdgcn_readfirstlane((uint32_t)cur.mask) >> (4 * g);
-        const uint32_t w1 = __builtin_amdgcn_readfirstlane((uint32_t)(cur.mask >> 32)) >> (4 * g);
-        f32x16 d0, d1;
+            for (int st = 0; st < 4; ++st) {
+                bf16x8 a0, a1, v0, v1;
+                read_rows(kt, off, st, a0, a1);
+                read_rows(vt, off, st, v0, v1);
+                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qop[st], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qop[st], s1, 0, 0, 0);
+                p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, dop[st], p0, 0, 0, 0);
+                p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, dop[st], p1, 0, 0, 0);
+            }
+            // dS^T = P^T (dP^T - D); key rows outside the block's mask take no part
+            // this lane's keys 8i + 4g + (0..3) of each half, tested against constant bits
+            const uint32_t w0 = __builtin_amdgcn_readfirstlane((uint32_t)cur.mask) >> (4 * g);
+            const uint32_t w1 = __builtin_amdgcn_readfirstlane((uint32_t)(cur.mask >> 32)) >> (4 * g);
+            f32x16 d0, d1;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const uint32_t bit = 1u << (8 * (r >> 2) + (r & 3));
-            const float pa = (w0 & bit) ? __builtin_amdgcn_exp2f(fmaf(s0[r], p.scale_l2, -lse_l2)) : 0.f;
-            const float pb = (w1 & bit) ? __builtin_amdgcn_exp2f(fmaf(s1[r], p.scale_l2, -lse_l2)) : 0.f;
-            d0[r] = pa * (p0[r] - D);
-            d1[r] = pb * (p1[r] - D);
-        }
+            for (int r = 0; r < 16; ++r) {
+                const uint32_t bit = 1u << (8 * (r >> 2) + (r & 3));
+                const float pa = (w0 & bit) ? __builtin_amdgcn_exp2f(fmaf(s0[r], p.scale_l2, -lse_l2)) : 0.f;
+                const float pb = (w1 & bit) ? __builtin_amdgcn_exp2f(fmaf(s1[r], p.scale_l2, -lse_l2)) : 0.f;
+                d0[r] = pa * (p0[r] - D);
+                d1[r] = pb * (p1[r] - D);
+            }
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            bf16x8 a0, a1;
-            read_tr(kt, off, ks, a0, a1);
-            const bf16x8 bs = acc_to_b(d0, d1, ks, [](float x, int, int) { return x; });
-            dq0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bs, dq0, 0, 0, 0);
-            dq1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bs, dq1, 0, 0, 0);
+            for (int ks = 0; ks < 4; ++ks) {
+                bf16x8 a0, a1;
+                read_tr(kt, off, ks, a0, a1);
+                const bf16x8 bs = acc_to_b(d0, d1, ks, [](float x, int, int) { return x; });
+                dq0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bs, dq0, 0, 0, 0);
+                dq1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bs, dq1, 0, 0, 0);
+            }
         }
         cur = nxt;
         __builtin_amdgcn_s_waitcnt(0x0070);
@@ -272,6 +277,9 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dkv(BwdDev p) {
     const int kr = 32 * w + kc;                                  // key row within the block
     const bool kvalid = (kb.mask >> kr) & 1ull;
     const int krow = block_row(p.kl, kb, kr);                    // row within the head
+    // a wave with no key row in this block stages and meets the barriers but skips the
+    // products (its accumulators stay zero)
+    const bool wk = __ballot(kvalid) != 0ull;
     const size_t kbase = ((size_t)h * Lk + krow) * HD;
 
     bf16x8 kop[4], vop[4];
@@ -343,50 +351,52 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dkv(BwdDev p) {
         }
         const unsigned char* qt = s_q[b];
         const unsigned char* dt = s_do[b];
-        // S = Q K^T and dP = dO V^T, lane = key column, rows = queries
-        f32x16 s0 = {}, s1 = {}, p0 = {}, p1 = {};
+        if (wk) {
+            // S = Q K^T and dP = dO V^T, lane = key column, rows = queries
+            f32x16 s0 = {}, s1 = {}, p0 = {}, p1 = {};
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            bf16x8 a0, a1, o0, o1;
-            read_rows(qt, off, st, a0, a1);
-            read_rows(dt, off, st, o0, o1);
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, kop[st], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, kop[st], s1, 0, 0, 0);
-            p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o0, vop[st], p0, 0, 0, 0);
-            p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o1, vop[st], p1, 0, 0, 0);
-        }
-        // P and dS per query row (8 (r/4) + 4 g + r % 4, +32)
-        f32x16 pp0, pp1, d0, d1;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const int q4 = 8 * a + 4 * g;
-            const float4 la = *reinterpret_cast<const float4*>(&s_lse[b][q4]);
-            const float4 lb = *reinterpret_cast<const float4*>(&s_lse[b][q4 + 32]);
-            const float4 da = *reinterpret_cast<const float4*>(&s_d[b][q4]);
-            const float4 db = *reinterpret_cast<const float4*>(&s_d[b][q4 + 32]);
-            const float lav[4] = {la.x, la.y, la.z, la.w}, lbv[4] = {lb.x, lb.y, lb.z, lb.w};
-            const float dav[4] = {da.x, da.y, da.z, da.w}, dbv[4] = {db.x, db.y, db.z, db.w};
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const int r = 4 * a + i4;
-                pp0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], p.scale_l2, -lav[i4]));
-                pp1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], p.scale_l2, -lbv[i4]));
-                d0[r] = pp0[r] * (p0[r] - dav[i4]);
-                d1[r] = pp1[r] * (p1[r] - dbv[i4]);
+            for (int st = 0; st < 4; ++st) {
+                bf16x8 a0, a1, o0, o1;
+                read_rows(qt, off, st, a0, a1);
+                read_rows(dt, off, st, o0, o1);
+                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, kop[st], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, kop[st], s1, 0, 0, 0);
+                p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o0, vop[st], p0, 0, 0, 0);
+                p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o1, vop[st], p1, 0, 0, 0);
             }
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS (k = queries)
+            // P and dS per query row (8 (r/4) + 4 g + r % 4, +32)
+            f32x16 pp0, pp1, d0, d1;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            bf16x8 a0, a1, c0, c1;
-            read_tr(dt, off, ks, a0, a1);
-            read_tr(qt, off, ks, c0, c1);
-            const bf16x8 bp = acc_to_b(pp0, pp1, ks, [](float x, int, int) { return x; });
-            const bf16x8 bd = acc_to_b(d0, d1, ks, [](float x, int, int) { return x; });
-            dv0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bp, dv0, 0, 0, 0);
-            dv1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bp, dv1, 0, 0, 0);
-            dk0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c0, bd, dk0, 0, 0, 0);
-            dk1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c1, bd, dk1, 0, 0, 0);
+            for (int a = 0; a < 4; ++a) {
+                const int q4 = 8 * a + 4 * g;
+                const float4 la = *reinterpret_cast<const float4*>(&s_lse[b][q4]);
+                const float4 lb = *reinterpret_cast<const float4*>(&s_lse[b][q4 + 32]);
+                const float4 da = *reinterpret_cast<const float4*>(&s_d[b][q4]);
+                const float4 db = *reinterpret_cast<const float4*>(&s_d[b][q4 + 32]);
+                const float lav[4] = {la.x, la.y, la.z, la.w}, lbv[4] = {lb.x, lb.y, lb.z, lb.w};
+                const float dav[4] = {da.x, da.y, da.z, da.w}, dbv[4] = {db.x, db.y, db.z, db.w};
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const int r = 4 * a + i4;
+                    pp0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], p.scale_l2, -lav[i4]));
+                    pp1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], p.scale_l2, -lbv[i4]));
+                    d0[r] = pp0[r] * (p0[r] - dav[i4]);
+                    d1[r] = pp1[r] * (p1[r] - dbv[i4]);
+                }
+            }
+            // dV^T += dO^T P and dK^T += Q^T dS (k = queries)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                bf16x8 a0, a1, c0, c1;
+                read_tr(dt, off, ks, a0, a1);
+                read_tr(qt, off, ks, c0, c1);
+                const bf16x8 bp = acc_to_b(pp0, pp1, ks, [](float x, int, int) { return x; });
+                const bf16x8 bd = acc_to_b(d0, d1, ks, [](float x, int, int) { return x; });
+                dv0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bp, dv0, 0, 0, 0);
+                dv1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bp, dv1, 0, 0, 0);
+                dk0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c0, bd, dk0, 0, 0, 0);
+                dk1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c1, bd, dk1, 0, 0, 0);
+            }
         }
         __builtin_amdgcn_s_waitcnt(0x0070);
         if (i + 1 < nq) (tid < 64 ? s_lse[b ^ 1] : s_d[b ^ 1])[tid & 63] = rowval;
