@@ -78,8 +78,8 @@ __global__ __launch_bounds__(256) void k_tile_pool(const void* __restrict__ x, i
 // and the product takes all four cross terms, exact products accumulated in fp32: the
 // scores agree with the fp32 dot product to about 1e-6 relative, while the kernel, bound by
 // writing the score matrix, runs several times faster than fp32 FMAs on the vector ALU.
-// A lane holds one score column and 16 rows of each accumulator, so every store instruction
-// writes two 128-byte row segments.
+// The product is formed transposed (keys as accumulator rows), so a lane holds four runs
+// of four consecutive scores of one query row and writes each with one 16-byte store.
 constexpr int SC_T = 128;               // queries x keys per workgroup
 __device__ __forceinline__ void split_bf16x8(const float* x, bf16x8& hi, bf16x8& lo) {
     uint32_t hw[4], lw[4];
@@ -161,31 +161,46 @@ __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restric
     const bool any_empty = (s_empty[0][0] | s_empty[0][1] | s_empty[1][0] | s_empty[1][1]) != 0ull;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-        const uint32_t qw = (uint32_t)(qe >> (32 * rb)) >> (4 * g);
+        // lane: query row r (its column of sigma^T); keys 8 (i / 4) + 4 g + i % 4 of the block
+        const int r = r0 + 32 * rb + col;
+        const bool qempty = (qe >> (32 * rb + col)) & 1ull;
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
+            // sigma^T = kbar qbar^T: keys are the accumulator rows, so four consecutive keys
+            // of the lane's query row are one 16-byte store
             f32x16 acc = {};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {           // small terms first
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[rb][ks], bl[cb][ks], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[rb][ks], bh[cb][ks], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[rb][ks], bl[cb][ks], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bl[cb][ks], al[rb][ks], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[cb][ks], al[rb][ks], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bl[cb][ks], ah[rb][ks], acc, 0, 0, 0);
             }
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[rb][ks], bh[cb][ks], acc, 0, 0, 0);
-            // lane: column c; rows 8 (i / 4) + 4 g + i % 4 of the 32-row block
-            const int c = c0 + 32 * cb + col;
-            if (c >= Tk) continue;                      // (would wrap into the next row)
-            const bool kempty = (ke >> (32 * cb + col)) & 1ull;
-            const unsigned voff = ((unsigned)(r0 + 32 * rb + 4 * g) * (unsigned)Tk + (unsigned)c) * 4u;
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[cb][ks], ah[rb][ks], acc, 0, 0, 0);
+            const uint32_t kw = (uint32_t)(ke >> (32 * cb)) >> (4 * g);
+            const int cbase = c0 + 32 * cb + 4 * g;
+            const unsigned voff = ((unsigned)r * (unsigned)Tk + (unsigned)cbase) * 4u;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int dr = 8 * (i >> 2) + (i & 3);
-                float v = acc[i] * scale;
-                if (any_empty && (kempty || ((qw >> dr) & 1u))) v = -INFINITY;
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, (int)voff,
-                                                      __builtin_amdgcn_readfirstlane(dr * Tk * 4), 0);
+            for (int a = 0; a < 4; ++a) {
+                float v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[j] = acc[4 * a + j] * scale;
+                    if (any_empty && (qempty || ((kw >> (8 * a + j)) & 1u))) v[j] = -INFINITY;
+                }
+                if (cbase + 8 * a + 3 < Tk) {
+                    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                    const u32x4 pk = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                      __float_as_uint(v[3])};
+                    __builtin_amdgcn_raw_buffer_store_b128(pk, rs, (int)voff, 32 * a, 0);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)            // a ragged last column block
+                        if (cbase + 8 * a + j < Tk)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[j]), rs, (int)voff,
+                                                                  32 * a + 4 * j, 0);
+                }
             }
         }
     }
