@@ -228,8 +228,9 @@ __global__ __launch_bounds__(TK_THREADS) void k_select_topk(const float* __restr
 // The same selection with one wave per score row (rows of at most 64 * E tiles): the keys
 // stay in registers (tile i * 64 + lane in slot i) and every count is a ballot and a scalar
 // popcount, so a row needs no LDS histogram and no barrier.  The k-th largest key T is
-// bracketed by bisection, keeping count(key >= lo) >= k > count(key > hi); once at most 64 keys remain inside the bracket they are gathered, one
-// per lane, and ordered by a bitonic network across the lanes, which yields T directly.
+// bracketed by bisection, keeping count(key >= lo) >= k > count(key > hi); once at most 64
+// keys remain inside the bracket they are gathered, one per lane, and ordered by a bitonic
+// network across the lanes, which yields T directly.
 // Selection and compaction then run over the slots in tile order with ballot prefix
 // counts, exactly as in the workgroup kernel (keys above T, the lowest-index ties, the
 // anchor frame).
