@@ -104,7 +104,10 @@ const char* sparse3d_status_string(int status);
  * element type `dtype`.  qbar: float [heads, Tq, 64]; kbar, vbar: float [heads, Tk, 64];
  * scores: float [heads, Tq, Tk], with Tq = qlay.frames*qlay.stride/tile and
  * Tk = klay.frames*klay.stride/tile.  Sums accumulate in fp32 in a fixed order, so
- * repeated calls are bit-identical.  v and vbar must be both NULL or both non-NULL.
+ * repeated calls are bit-identical.  The score products run on the bf16 matrix cores with
+ * each fp32 mean split into two bf16 terms and all four cross products accumulated in
+ * fp32, within about 1e-6 (relative) of the fp32 dot product.  v and vbar must be both
+ * NULL or both non-NULL.
  */
 int sparse3d_tile_scores(const void* q, const void* k, const void* v, sparse3d_dtype dtype,
                          int32_t heads, int32_t head_dim, int32_t tile,
