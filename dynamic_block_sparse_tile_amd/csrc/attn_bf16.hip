@@ -44,6 +44,11 @@ __device__ __forceinline__ float keep_lanes(float x, uint64_t lanes) {
     return r;
 }
 
+// all ones if bit b of w is set, else zero
+__device__ __forceinline__ uint32_t bit_to_word(uint32_t w, int b) {
+    return (uint32_t)((int32_t)(w << (31 - b)) >> 31);
+}
+
 // max over the 32 scores of a lane (two 16-element accumulators), as two asm blocks of
 // eight dependent v_max3_f32 each: one block per chain keeps the compiler from padding
 // every step of the chain with wait states, as it does between separate asm statements
@@ -249,13 +254,13 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16(AttnDev p) {
                 // cycles keep them clear of the products' write-back
                 __builtin_amdgcn_sched_barrier(0);
                 asm volatile("s_nop 7\n\ts_nop 7");
+                const uint32_t mlo = (uint32_t)cur.mask, mhi = (uint32_t)(cur.mask >> 32);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int cr = 8 * (r >> 2) + (r & 3);
-                    const uint64_t k0 = (((cur.mask >> cr) & 1ull) ? 0x00000000FFFFFFFFull : 0ull) |
-                                        (((cur.mask >> (cr + 4)) & 1ull) ? 0xFFFFFFFF00000000ull : 0ull);
-                    const uint64_t k1 = (((cur.mask >> (cr + 32)) & 1ull) ? 0x00000000FFFFFFFFull : 0ull) |
-                                        (((cur.mask >> (cr + 36)) & 1ull) ? 0xFFFFFFFF00000000ull : 0ull);
+                    // each 32-bit half of a lane mask is one row bit sign-extended (s_bfe_i32)
+                    const uint64_t k0 = (uint64_t)bit_to_word(mlo, cr) | ((uint64_t)bit_to_word(mlo, cr + 4) << 32);
+                    const uint64_t k1 = (uint64_t)bit_to_word(mhi, cr) | ((uint64_t)bit_to_word(mhi, cr + 4) << 32);
                     s0[r] = keep_lanes(s0[r], k0);
                     s1[r] = keep_lanes(s1[r], k1);
                 }
