@@ -481,12 +481,20 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_tr_scan(int32_t* t_end, int Tk
     }
 }
 
-// sort each key tile's list ascending (bitonic in LDS; lists hold at most Tq entries)
+// Order each key tile's list ascending.  The entries are distinct query tiles (a selection
+// row names a tile once), so the list is a set: mark its members in an LDS bitmap of Tq bits
+// and write them back in bit order, each thread a contiguous run of words at the offset a
+// block scan of the word popcounts gives.  A list whose marks do not add up to its length
+// (a row that repeats a tile, or an index outside [0, Tq)) is sorted by a bitonic network.
 constexpr int SORT_THREADS = 256;
+constexpr int TR_WORDS_MAX = 512;                     // bitmap words: Tq <= 16384
 __global__ __launch_bounds__(SORT_THREADS) void k_tr_sort(const int32_t* __restrict__ t_end,
                                                           int32_t* __restrict__ t_list, int Tq, int kmax,
                                                           int Tk, int cap) {
     extern __shared__ int32_t s_v[];                  // cap entries (a power of two >= Tq)
+    __shared__ uint32_t s_bits[TR_WORDS_MAX];
+    __shared__ int s_part[SORT_THREADS];
+    const int tid = threadIdx.x;
     const int h = blockIdx.x / Tk, t = blockIdx.x % Tk;
     const int32_t* te = t_end + (size_t)h * Tk;
     const int b = t == 0 ? 0 : te[t - 1];
@@ -494,13 +502,45 @@ __global__ __launch_bounds__(SORT_THREADS) void k_tr_sort(const int32_t* __restr
     const int n = min(te[t] - b, cap);
     if (n <= 1) return;
     int32_t* seg = t_list + (size_t)h * Tq * kmax + b;
+    const int nw = (Tq + 31) >> 5;
+    for (int i = tid; i < nw; i += SORT_THREADS) s_bits[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n; i += SORT_THREADS) {
+        const int v = seg[i];
+        if (v >= 0 && v < Tq) atomicOr(&s_bits[v >> 5], 1u << (v & 31));
+    }
+    __syncthreads();
+    const int per = (nw + SORT_THREADS - 1) / SORT_THREADS;
+    const int w0 = min(tid * per, nw), w1 = min(w0 + per, nw);
+    int local = 0;
+    for (int w = w0; w < w1; ++w) local += __popc(s_bits[w]);
+    s_part[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < SORT_THREADS; off <<= 1) {   // inclusive Hillis-Steele scan
+        const int v = tid >= off ? s_part[tid - off] : 0;
+        __syncthreads();
+        s_part[tid] += v;
+        __syncthreads();
+    }
+    const int total = s_part[SORT_THREADS - 1];
+    if (total == n) {
+        int pos = s_part[tid] - local;
+        for (int w = w0; w < w1; ++w) {
+            uint32_t m = s_bits[w];
+            while (m) {
+                seg[pos++] = 32 * w + __builtin_ctz(m);
+                m &= m - 1u;
+            }
+        }
+        return;
+    }
     int np = 1;
     while (np < n) np <<= 1;
-    for (int i = threadIdx.x; i < np; i += SORT_THREADS) s_v[i] = i < n ? seg[i] : 0x7fffffff;
+    for (int i = tid; i < np; i += SORT_THREADS) s_v[i] = i < n ? seg[i] : 0x7fffffff;
     __syncthreads();
     for (int k = 2; k <= np; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < np; i += SORT_THREADS) {
+            for (int i = tid; i < np; i += SORT_THREADS) {
                 const int l = i ^ j;
                 if (l > i) {
                     const bool up = (i & k) == 0;
@@ -514,7 +554,7 @@ __global__ __launch_bounds__(SORT_THREADS) void k_tr_sort(const int32_t* __restr
             __syncthreads();
         }
     }
-    for (int i = threadIdx.x; i < n; i += SORT_THREADS) seg[i] = s_v[i];
+    for (int i = tid; i < n; i += SORT_THREADS) seg[i] = s_v[i];
 }
 
 hipError_t launch_selection_transpose(const int32_t* idx, const int32_t* cnt, int heads, int tq, int tk,
