@@ -91,8 +91,11 @@ constexpr float PROB_SUM_LIMIT = 65536.0f;
 
 // SGA: the subsample completion (own key of dropped positions, mean pair) is applied to
 // each finished row; a separate instantiation so the other variants carry none of it.
-template <bool F32OUT, bool DENSE, bool LM, bool SGA>
-__global__ __launch_bounds__(128, 3) void k_attn_bf16(AttnDev p) {
+// QT = 2 (dense and frame attention only): a workgroup of four waves takes two query tiles
+// that sweep the same key tiles, so every staged tile serves 128 queries.
+template <bool F32OUT, bool DENSE, bool LM, bool SGA, int QT = 1>
+__global__ __launch_bounds__(128 * QT, 3) void k_attn_bf16(AttnDev p) {
+    static_assert(QT == 1 || (QT == 2 && DENSE), "two query tiles per workgroup need a shared key sweep");
     __shared__ __align__(16) unsigned char s_k[TILE_BYTES];
     __shared__ __align__(16) unsigned char s_v0[TILE_BYTES];
     __shared__ __align__(16) unsigned char s_v1[TILE_BYTES];
@@ -102,10 +105,20 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16(AttnDev p) {
     const int qc = lane & 31, g = lane >> 5;
     const int tpfq = p.ql.P / TILE;
     int h, tq;
-    attn_work_item(blockIdx.x, gridDim.x, p.ql.S, tpfq, gridDim.x / p.Tq, h, tq, !p.frame);
+    if (QT == 1) {
+        attn_work_item(blockIdx.x, gridDim.x, p.ql.S, tpfq, gridDim.x / p.Tq, h, tq, !p.frame);
+    } else {
+        // pairs of query tiles in plain order (the launcher takes QT = 2 only when Tq and the
+        // tiles per frame are even, so a pair never straddles a frame)
+        const int pairs = p.Tq / 2;
+        h = blockIdx.x / pairs;
+        tq = 2 * (blockIdx.x - h * pairs);
+    }
+    const int wt = QT == 1 ? 0 : (w >> 1);         // this wave's query tile within the workgroup
+    const int wh = QT == 1 ? w : (w & 1);          // and its 32-row half
     const int Lq = p.ql.S * p.ql.P, Lk = p.kl.S * p.kl.P;
-    const int qrow = tq * TILE + w * 32 + qc;
-    const bool qvalid = (tq % tpfq) * TILE + w * 32 + qc < p.ql.N;
+    const int qrow = (tq + wt) * TILE + wh * 32 + qc;
+    const bool qvalid = ((tq + wt) % tpfq) * TILE + wh * 32 + qc < p.ql.N;
     // In the sparse paths a wave whose 32 rows are all padding (the second half of a frame's
     // last tile) still stages its half of every tile and meets every barrier, but skips the
     // products.  (Dense and frame attention keep every wave busy: there the workgroups sweep
@@ -174,36 +187,38 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16(AttnDev p) {
     }
 
     const int srow_in = lane >> 3, sslot = lane & 7;
-    int srow[4], soff[4];
+    // each wave stages 32 / QT rows of every tile (8 rows per 16-byte-per-lane load)
+    constexpr int NJ = 4 / QT;
+    int srow[NJ], soff[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        srow[j] = 32 * w + 8 * j + srow_in;
+    for (int j = 0; j < NJ; ++j) {
+        srow[j] = (32 / QT) * w + 8 * j + srow_in;
         soff[j] = srow[j] * 128 + swz(srow[j], sslot) * 16;
     }
     auto desc = [&](int it) { return describe<DENSE, LM, !DENSE>(p, it, c, myidx, s_idx, s_lm, rot, t0); };
-    auto plan = [&](const TileDesc& dd, unsigned (&voff)[4], unsigned& base) {
+    auto plan = [&](const TileDesc& dd, unsigned (&voff)[NJ], unsigned& base) {
         const TileDesc d = uniform(dd);
         const bool spec = d.kind == KIND_SPEC;
         base = spec ? 0u : (unsigned)d.t * TILE_BYTES;
         if (spec) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 const int r = srow[j];
                 const unsigned o = (unsigned)src_row(p, d, r) * 128u + swz(r, sslot) * 16u;
                 voff[j] = ((d.mask >> r) & 1ull) ? o : OOB_OFFSET;
             }
         } else if (d.mask == ~0ull) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) voff[j] = (unsigned)soff[j];
+            for (int j = 0; j < NJ; ++j) voff[j] = (unsigned)soff[j];
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) voff[j] = ((d.mask >> srow[j]) & 1ull) ? (unsigned)soff[j] : OOB_OFFSET;
+            for (int j = 0; j < NJ; ++j) voff[j] = ((d.mask >> srow[j]) & 1ull) ? (unsigned)soff[j] : OOB_OFFSET;
         }
     };
-    auto dma4 = [&](const __amdgpu_buffer_rsrc_t& rs, lds_u8* dst, const unsigned (&voff)[4], unsigned base) {
+    auto dma4 = [&](const __amdgpu_buffer_rsrc_t& rs, lds_u8* dst, const unsigned (&voff)[NJ], unsigned base) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            dma_buf(rs, dst + (32 * w + 8 * j) * 128, voff[j], __builtin_amdgcn_readfirstlane(base));
+        for (int j = 0; j < NJ; ++j)
+            dma_buf(rs, dst + ((32 / QT) * w + 8 * j) * 128, voff[j], __builtin_amdgcn_readfirstlane(base));
     };
 
     TileOffsets to;
@@ -216,18 +231,18 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16(AttnDev p) {
         const TileDesc cur = uniform(dcur);
         const bool more = it + 1 < ntiles;
         TileDesc dn{};
-        unsigned vk[4], vv[4], bk = 0, bv = 0;
+        unsigned vk[NJ], vv[NJ], bk = 0, bv = 0;
         bool nlmk = false;                                  // tile it+1 is a landmark block
         if (more) {
             dn = desc(it + 1);
             plan(dn, vk, bk);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) vv[j] = vk[j];
+            for (int j = 0; j < NJ; ++j) vv[j] = vk[j];
             bv = bk;
             nlmk = LM && uniform(dn).kind == KIND_LM;
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) vk[j] = vv[j] = OOB_OFFSET;
+            for (int j = 0; j < NJ; ++j) vk[j] = vv[j] = OOB_OFFSET;
         }
         dma4(nlmk ? rs_lv : rs_v, (lds_u8*)vnext, vv, bv);  // V(it+1)
         f32x16 s0, s1;
@@ -379,7 +394,7 @@ __global__ __launch_bounds__(128, 3) void k_attn_bf16(AttnDev p) {
     TileDesc d{};
     if (ntiles > 0) {
         d = desc(0);
-        unsigned v0[4], b0;
+        unsigned v0[NJ], b0;
         plan(d, v0, b0);
         const bool lmk = LM && uniform(d).kind == KIND_LM;
         dma4(lmk ? rs_lk : rs_k, (lds_u8*)s_k, v0, b0);
@@ -428,7 +443,11 @@ static void launch_t(const AttnDev& d, int heads, bool dense, bool lm, hipStream
     const dim3 grid((unsigned)(heads * d.Tq)), block(128);
     const size_t shm = ((lm ? (size_t)(2 * d.nlm) : 0) + (dense ? 0 : (size_t)d.kmax)) *
                        sizeof(uint32_t);
-    if (dense) hipLaunchKernelGGL((k_attn_bf16<F32OUT, true, false, SGA>), grid, block, 0, st, d);
+    const int tpfq = d.ql.P / TILE;
+    if (dense && d.Tq % 2 == 0 && tpfq % 2 == 0)
+        hipLaunchKernelGGL((k_attn_bf16<F32OUT, true, false, SGA, 2>), dim3((unsigned)(heads * d.Tq / 2)),
+                           dim3(256), 0, st, d);
+    else if (dense) hipLaunchKernelGGL((k_attn_bf16<F32OUT, true, false, SGA>), grid, block, 0, st, d);
     else if (lm) hipLaunchKernelGGL((k_attn_bf16<F32OUT, false, true, SGA>), grid, block, shm, st, d);
     else hipLaunchKernelGGL((k_attn_bf16<F32OUT, false, false, SGA>), grid, block, shm, st, d);
 }
