@@ -59,7 +59,7 @@ def parse():
     return ap.parse_args()
 
 
-ATTN_KERNEL = "k_attn_bf16<false, false, false, false>"     # the sparse bf16 attention kernel
+ATTN_KERNEL = "k_attn_bf16<false, false, false, false, 1>"     # the sparse bf16 attention kernel
 
 
 def write_traffic(fetch_csv, write_csv, copy_mb, workload):
