@@ -245,6 +245,26 @@ def test_k_all_tiles_equals_dense():
     assert float((res.out - dense).abs().max()) <= 1e-2
 
 
+def test_dense_and_frame_with_odd_tiles_per_frame():
+    # 3 tiles per frame, 4 frames: the dense call pairs query tiles across frame boundaries
+    # (two per workgroup), the frame call takes one query tile per workgroup
+    w = _custom(4, 150, 192, 5, heads=2)
+    inp = synth.make_inputs(w, seed=17)
+    q, v = to_dev(inp.q, torch.bfloat16), to_dev(inp.v, torch.bfloat16)
+    ol = oracle.Layout(*w.layout)
+    d, dl = S.sparse3d_dense_attn_fwd(q, q, v, w.layout, out_dtype=torch.float32, return_lse=True)
+    f, fl = S.sparse3d_frame_attn_fwd(q, q, v, w.layout, w.layout, out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    O, L = oracle.dense_attend(inp.q, inp.k, inp.v, ol, ol, 0.125)
+    Of, Lf = oracle.frame_attend(inp.q, inp.k, inp.v, ol, ol, 0.125)
+    qv = (np.arange(O.shape[1]) % w.stride) < w.tokens
+    for g, gl, r, rl in ((d, dl, O, L), (f, fl, Of, Lf)):
+        g, gl = g.cpu().numpy(), gl.cpu().numpy()
+        assert float(np.max(np.abs(g - r))) <= TOL["bf16"]
+        assert float(np.max(np.abs(gl[:, qv] - rl[:, qv]))) <= LSE_TOL_BF16
+        assert np.all(g[:, ~qv] == 0)
+
+
 def test_empty_key_set():
     w = _custom(2, 128, 128, 0, dtype="f32", k=0, anchor=-1)
     inp = synth.make_inputs(w, seed=1)
