@@ -1,7 +1,8 @@
 // bf16 attention over a query tile's key-tile list, tuned for gfx950 (the hot kernel of
 // the sparse layer; Zebra3D abstract: tile-sparse attention with landmark summaries).
 //
-// Workgroup = 2 waves = one (head, query tile); wave w owns queries [32w, 32w+32).
+// Workgroup = 2 waves = one (head, query tile); wave w owns queries [32w, 32w+32).  (Dense
+// and frame attention: 4 waves = two query tiles that share every staged key tile.)
 //   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, A = K rows (ds_read_b128), B = Q (VGPRs)
 //   O^T += V^T P^T   A = V^T read with ds_read_b64_tr_b16 (the transpose happens in the
 //                    LDS read), B = P^T taken straight from the S^T accumulators
