@@ -262,6 +262,7 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
     const int mode = k <= 0 ? 0 : (k >= Tk ? 1 : 2);
     uint32_t T = 0;
     int greater = 0;
+    bool take_ge = false;                           // exactly k keys are >= T: no tie to break
     if (mode == 2) {
         uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
@@ -305,6 +306,7 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
                 }
                 lo = (uint32_t)__shfl((int)v, k - c_hi - 1);   // rank k - c_hi among the candidates
                 hi = lo;
+                take_ge = c_hi + __popcll(__ballot(v >= lo)) == k;   // pad lanes hold 0 < lo
                 break;
             }
             uint32_t mid = lo + (uint32_t)(((uint64_t)hi - lo + 1) >> 1);
@@ -323,10 +325,13 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
                 c_hi = c;
             }
             by_key = !by_key && 4 * (c_lo - c_hi) > 3 * before;
+            if (lo == hi) take_ge = c_lo == k;      // converged: c_lo = count(key >= T)
         }
         T = lo;
+        if (!take_ge) {
 #pragma unroll
-        for (int i = 0; i < E; ++i) greater += __popcll(__ballot(i * 64 + lane < Tk && key[i] > T));
+            for (int i = 0; i < E; ++i) greater += __popcll(__ballot(i * 64 + lane < Tk && key[i] > T));
+        }
     }
     int ties_before = 0;                            // keys == T in earlier slots
     const int need_eq = mode == 2 ? k - greater : 0;   // ties to take, lowest index first
@@ -339,7 +344,9 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
         const bool valid = t < Tk;
         bool sel = valid && t >= a0 && t < a1;
         if (mode == 1) sel = valid;
-        else if (mode == 2) {
+        else if (mode == 2 && take_ge) {
+            sel = sel || (valid && key[i] >= T);
+        } else if (mode == 2) {
             const uint64_t eqm = __ballot(valid && key[i] == T);
             const int eq_rank = ties_before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eqm >> 32),
                                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)eqm, 0u));
