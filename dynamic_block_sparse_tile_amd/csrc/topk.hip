@@ -235,7 +235,8 @@ __global__ __launch_bounds__(TK_THREADS) void k_select_topk(const float* __restr
 // counts, exactly as in the workgroup kernel (keys above T, the lowest-index ties, the
 // anchor frame).
 constexpr int TKW_WAVES = 4;            // rows per workgroup
-template <int E>
+// FULL: the row fills every slot (Tk = 64 E), so no slot needs a range check.
+template <int E, bool FULL>
 __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float* __restrict__ scores, int Tk,
                                                                      int Tq, int rows, KBudget kb, int tpf,
                                                                      int anchor, int32_t* __restrict__ idx,
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
 #pragma unroll
     for (int i = 0; i < E; ++i) f[i] = src[min(i * 64 + lane, Tk - 1)];   // all loads in flight at once
 #pragma unroll
-    for (int i = 0; i < E; ++i) key[i] = i * 64 + lane < Tk ? order_key(f[i]) : 0u;   // pad slots rank lowest
+    for (int i = 0; i < E; ++i) key[i] = FULL || i * 64 + lane < Tk ? order_key(f[i]) : 0u;   // pad slots rank lowest
     auto count_ge = [&](uint32_t t) {
         int c = 0;
 #pragma unroll
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
         uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
         for (int i = 0; i < E; ++i) {
-            if (i * 64 + lane < Tk) {
+            if (FULL || i * 64 + lane < Tk) {
                 lo = min(lo, key[i]);
                 hi = max(hi, key[i]);
             }
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
                 int base = 0;
 #pragma unroll
                 for (int i = 0; i < E; ++i) {
-                    const bool in = i * 64 + lane < Tk && key[i] >= lo && key[i] <= hi;
+                    const bool in = (FULL || i * 64 + lane < Tk) && key[i] >= lo && key[i] <= hi;
                     const uint64_t m = __ballot(in);
                     const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -330,7 +331,7 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
         T = lo;
         if (!take_ge) {
 #pragma unroll
-            for (int i = 0; i < E; ++i) greater += __popcll(__ballot(i * 64 + lane < Tk && key[i] > T));
+            for (int i = 0; i < E; ++i) greater += __popcll(__ballot((FULL || i * 64 + lane < Tk) && key[i] > T));
         }
     }
     int ties_before = 0;                            // keys == T in earlier slots
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
 #pragma unroll
     for (int i = 0; i < E; ++i) {
         const int t = i * 64 + lane;
-        const bool valid = t < Tk;
+        const bool valid = FULL || t < Tk;
         bool sel = valid && t >= a0 && t < a1;
         if (mode == 1) sel = valid;
         else if (mode == 2 && take_ge) {
@@ -364,6 +365,17 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
     if (lane == 0) cnt[row] = min(base, kmax);
 }
 
+template <int E>
+static void launch_wave(bool full, dim3 grid, dim3 block, hipStream_t st, const float* scores, int tk, int tq,
+                        int rows, const KBudget& kb, int tpf, int anchor, int32_t* ix, int32_t* cn, int kmax) {
+    if (full)
+        hipLaunchKernelGGL((k_select_topk_wave<E, true>), grid, block, 0, st, scores, tk, tq, rows, kb, tpf, anchor, ix,
+                           cn, kmax);
+    else
+        hipLaunchKernelGGL((k_select_topk_wave<E, false>), grid, block, 0, st, scores, tk, tq, rows, kb, tpf, anchor, ix,
+                           cn, kmax);
+}
+
 hipError_t launch_select_topk(const float* scores, int heads, int tq, int tk, const int32_t* k_heads,
                               int tpf, int anchor, int32_t* idx, int32_t* cnt, int kmax, hipStream_t st) {
     const size_t shm = (size_t)tk * sizeof(uint32_t);
@@ -378,17 +390,17 @@ hipError_t launch_select_topk(const float* scores, int heads, int tq, int tk, co
         // one wave per row while the keys fit 48 registers per lane; longer rows (fewer per
         // launch, and each would hold too many registers) use a workgroup per row
         if (tk <= 64 * 16)
-            hipLaunchKernelGGL(k_select_topk_wave<16>, wgrid, wblock, 0, st, scores + r0 * tk, tk, tq, rows, kb,
-                               tpf, anchor, ix, cnt + r0, kmax);
+            launch_wave<16>(tk == 64 * 16, wgrid, wblock, st, scores + r0 * tk, tk, tq, rows, kb, tpf, anchor, ix,
+                           cnt + r0, kmax);
         else if (tk <= 64 * 32)
-            hipLaunchKernelGGL(k_select_topk_wave<32>, wgrid, wblock, 0, st, scores + r0 * tk, tk, tq, rows, kb,
-                               tpf, anchor, ix, cnt + r0, kmax);
+            launch_wave<32>(tk == 64 * 32, wgrid, wblock, st, scores + r0 * tk, tk, tq, rows, kb, tpf, anchor, ix,
+                           cnt + r0, kmax);
         else if (tk <= 64 * 44)
-            hipLaunchKernelGGL(k_select_topk_wave<44>, wgrid, wblock, 0, st, scores + r0 * tk, tk, tq, rows, kb,
-                               tpf, anchor, ix, cnt + r0, kmax);
+            launch_wave<44>(tk == 64 * 44, wgrid, wblock, st, scores + r0 * tk, tk, tq, rows, kb, tpf, anchor, ix,
+                           cnt + r0, kmax);
         else if (tk <= 64 * 48)
-            hipLaunchKernelGGL(k_select_topk_wave<48>, wgrid, wblock, 0, st, scores + r0 * tk, tk, tq, rows, kb,
-                               tpf, anchor, ix, cnt + r0, kmax);
+            launch_wave<48>(tk == 64 * 48, wgrid, wblock, st, scores + r0 * tk, tk, tq, rows, kb, tpf, anchor, ix,
+                           cnt + r0, kmax);
         else
             hipLaunchKernelGGL(k_select_topk, dim3((unsigned)rows), dim3(TK_THREADS), shm, st,
                                scores + r0 * tk, tk, tq, kb, tpf, anchor, ix, cnt + r0, kmax);

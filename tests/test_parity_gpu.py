@@ -168,8 +168,8 @@ def test_select_topk_hard_rows():
     # zeros, at lengths that take each wave width and the workgroup kernel.  Compared with
     # the oracle's rule applied to the same fp32 scores.
     rng = np.random.default_rng(21)
-    for Tk in (100, 1000, 2000, 2816, 3000, 5000):
-        tpf = 22 if Tk % 22 == 0 else 20
+    for Tk in (100, 1000, 1024, 2000, 2048, 2816, 3000, 3072, 5000):   # 1024, 2048, 2816, 3072: full rows
+        tpf = 22 if Tk % 22 == 0 else (20 if Tk % 20 == 0 else 16)
         rows = [rng.standard_normal(Tk),
                 rng.integers(-3, 3, Tk).astype(np.float64),
                 np.exp(rng.normal(0.0, 20.0, Tk)),
