@@ -233,7 +233,8 @@ __global__ __launch_bounds__(TK_THREADS) void k_select_topk(const float* __restr
 // network across the lanes, which yields T directly.
 // Selection and compaction then run over the slots in tile order with ballot prefix
 // counts, exactly as in the workgroup kernel (keys above T, the lowest-index ties, the
-// anchor frame).
+// anchor frame); when exactly k keys are >= T (the bracket counts tell) there is no tie to
+// rank and every key >= T is taken.
 constexpr int TKW_WAVES = 4;            // rows per workgroup
 // FULL: the row fills every slot (Tk = 64 E), so no slot needs a range check.
 template <int E, bool FULL>
