@@ -152,12 +152,14 @@ __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restric
     __syncthreads();
     const uint64_t qe = s_empty[0][w >> 1];            // this wave's 64 query rows
     const uint64_t ke = s_empty[1][w & 1];             // this wave's 64 key columns
-    // stores through a buffer resource over the head's [Tq, Tk] slice: the row offset is a
-    // scalar, and rows past Tq (last block row) fall outside the resource and are dropped
-    // (the library's tile-count limits keep the slice far below 2^32 bytes)
-    const unsigned slice = (unsigned)Tq * (unsigned)Tk * 4u;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(scores + (size_t)h * Tq * Tk, 0,
-                                                                        (int)slice, 0x00020000);
+    // stores through a buffer resource over this wave's 64 query rows of the head's [Tq, Tk]
+    // slice, based at its first row in 64-bit arithmetic: rows past Tq (last block row) fall
+    // outside the resource and are dropped, and the offsets inside it stay below
+    // 64 * Tk * 4 bytes (the host caps Tk at 2^23, so they fit 32 bits at any Tq)
+    const long long rows_here = (long long)Tq - r0 < 0 ? 0 : ((long long)Tq - r0 < 64 ? (long long)Tq - r0 : 64);
+    const unsigned slice = (unsigned)(rows_here * Tk * 4);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        scores + ((size_t)h * Tq + (size_t)r0) * (size_t)Tk, 0, (int)slice, 0x00020000);
     const bool any_empty = (s_empty[0][0] | s_empty[0][1] | s_empty[1][0] | s_empty[1][1]) != 0ull;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restric
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[cb][ks], ah[rb][ks], acc, 0, 0, 0);
             const uint32_t kw = (uint32_t)(ke >> (32 * cb)) >> (4 * g);
             const int cbase = c0 + 32 * cb + 4 * g;
-            const unsigned voff = ((unsigned)r * (unsigned)Tk + (unsigned)cbase) * 4u;
+            const unsigned voff = ((unsigned)(r - r0) * (unsigned)Tk + (unsigned)cbase) * 4u;
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 float v[4];

@@ -59,6 +59,9 @@ int validate_tile_scores(const void* q, const void* k, const void* v, int dtype,
     S3D_TRY(check_layout(qlay));
     S3D_TRY(check_layout(klay));
     if (qlay->frames != klay->frames) return SPARSE3D_ERR_SHAPE;
+    // the score kernel takes 128 query tiles per grid row (at most 65535 rows) and addresses
+    // 64 score rows per wave with 32-bit offsets (64 * Tk * 4 bytes)
+    if (lay_tiles(*qlay) > kMaxScoreQTiles || lay_tiles(*klay) > kMaxScoreKTiles) return SPARSE3D_ERR_UNSUPPORTED;
     const size_t eb = dtype_bytes(sparse3d_dtype(dtype));
     const size_t qb = size_t(heads) * lay_rows(*qlay) * head_dim * eb;
     const size_t kb = size_t(heads) * lay_rows(*klay) * head_dim * eb;
@@ -119,6 +122,9 @@ int validate_attn(bool sparse, const void* q, const void* k, const void* v, int 
     S3D_TRY(check_layout(klay));
     if (qlay->frames != klay->frames) return SPARSE3D_ERR_SHAPE;
     if (sparse && lay_tiles(*klay) > kMaxTopkTiles) return SPARSE3D_ERR_UNSUPPORTED;
+    // the bf16 kernels address one head of K/V (and, in the backward, Q) through a buffer
+    // resource with 32-bit offsets, masked rows at an offset of 2^31 past its start
+    if (lay_rows(*qlay) > kMaxAttnRows || lay_rows(*klay) > kMaxAttnRows) return SPARSE3D_ERR_UNSUPPORTED;
     if (int64_t(heads) * lay_tiles(*qlay) > (int64_t(1) << 31) - 1) return SPARSE3D_ERR_UNSUPPORTED;
     const size_t eb = dtype_bytes(sparse3d_dtype(dtype));
     const size_t qb = size_t(heads) * lay_rows(*qlay) * head_dim * eb;

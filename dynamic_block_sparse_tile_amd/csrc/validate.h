@@ -12,6 +12,13 @@ namespace s3d {
 constexpr int kTile = 64;
 constexpr int kHeadDim = 64;
 constexpr int kMaxTopkTiles = 12288;   // row keys live in LDS (48 KiB)
+// Rows per head of any attention operand: one head of bf16 rows (128 bytes each) must stay
+// below the 2^31-byte offset at which the kernels place masked rows.
+constexpr int64_t kMaxAttnRows = int64_t(1) << 24;
+// Tile scores: query tiles up to 65535 grid rows of 128, key tiles so that 64 score rows
+// (64 * Tk * 4 bytes) stay within 2^31.
+constexpr int64_t kMaxScoreQTiles = int64_t(65535) * 128;
+constexpr int64_t kMaxScoreKTiles = int64_t(1) << 23;
 
 inline int64_t lay_rows(const sparse3d_layout& l) { return int64_t(l.frames) * l.stride; }
 inline int64_t lay_tiles(const sparse3d_layout& l) { return lay_rows(l) / kTile; }

@@ -127,6 +127,47 @@ def _dev(x: torch.Tensor, name: str) -> torch.Tensor:
     return x
 
 
+def _rows(lay) -> int:
+    return int(lay[0]) * int(lay[2])
+
+
+def _expect(x: Optional[torch.Tensor], name: str, shape: Sequence[int], dtypes) -> None:
+    """Shape and dtype of one argument against what the layouts and sizes imply; runs
+    before anything touches the device, so a mismatched tensor never reaches a kernel."""
+    if x is None:
+        return
+    want = tuple(int(d) for d in shape)
+    if tuple(x.shape) != want:
+        raise ValueError(f"{name} has shape {tuple(x.shape)}, expected {want}")
+    if x.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {x.dtype}, expected one of {[str(d) for d in dtypes]}")
+
+
+_OPERAND = (torch.bfloat16, torch.float32)
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+
+
+def _operands(q, k, v, qlay, klay, heads=None):
+    """q: [H, qlay rows, 64] in bf16 or fp32; k (and v): [H, klay rows, 64] in q's dtype."""
+    if q.dim() != 3:
+        raise ValueError(f"q must be [heads, rows, {HEAD_DIM}], got shape {tuple(q.shape)}")
+    H = q.shape[0] if heads is None else heads
+    _expect(q, "q", (H, _rows(qlay), HEAD_DIM), _OPERAND)
+    _expect(k, "k", (H, _rows(klay), HEAD_DIM), (q.dtype,))
+    _expect(v, "v", (H, _rows(klay), HEAD_DIM), (q.dtype,))
+    devs = {x.device for x in (q, k, v) if x is not None}
+    if len(devs) > 1:
+        raise ValueError("q, k and v must be on one device")
+    return H
+
+
+def _same_device(ref: torch.Tensor, *xs) -> None:
+    for x in xs:
+        if x is not None and x.device != ref.device:
+            raise ValueError("every tensor of a call must be on one device")
+
+
 def _stream(x: torch.Tensor) -> int:
     return torch.cuda.current_stream(x.device).cuda_stream
 
@@ -147,16 +188,16 @@ class Sga:
         self.mean_bias = float(mean_bias)
 
     def _c(self, q):
+        H = q.shape[0]
         for x, n in ((self.k_full, "k_full"), (self.v_full, "v_full")):
-            if x is not None:
-                _dev(x, n)
-                if x.dtype != q.dtype:
-                    raise TypeError(f"{n} must have the operand dtype")
+            _expect(x, n, q.shape, (q.dtype,))
         for x, n in ((self.kmean, "kmean"), (self.vmean, "vmean")):
+            _expect(x, n, (H, HEAD_DIM), _F32)
+        _same_device(q, self.k_full, self.v_full, self.kmean, self.vmean)
+        for x, n in ((self.k_full, "k_full"), (self.v_full, "v_full"), (self.kmean, "kmean"),
+                     (self.vmean, "vmean")):
             if x is not None:
                 _dev(x, n)
-                if x.dtype != torch.float32:
-                    raise TypeError(f"{n} must be float32")
         return _Sga(_ptr(self.k_full), _ptr(self.v_full), self.grid[0], self.grid[1], self.window,
                     _ptr(self.kmean), _ptr(self.vmean), self.mean_bias)
 
@@ -181,10 +222,10 @@ def sparse3d_tile_scores(q: torch.Tensor, k: torch.Tensor, qlay, klay=None,
                          v: Optional[torch.Tensor] = None, scale: Optional[float] = None):
     """Pooled tile summaries and tile scores.  Returns (qbar, kbar, vbar|None, scores)."""
     klay = qlay if klay is None else klay
+    H = _operands(q, k, v, qlay, klay)
     _dev(q, "q"), _dev(k, "k")
     if v is not None:
         _dev(v, "v")
-    H = q.shape[0]
     scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else scale
     Tq, Tk = _tiles(qlay), _tiles(klay)
     f = dict(device=q.device, dtype=torch.float32)
@@ -207,6 +248,9 @@ def kmax_for(k_tiles: int, k: int, tiles_per_frame: int, anchor_frame: int) -> i
 def sparse3d_select_topk(scores: torch.Tensor, k: int, tiles_per_frame: int, anchor_frame: int = 0,
                          kmax: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Top-k key tiles per query tile united with the anchor frame.  Returns (idx, cnt)."""
+    if scores.dim() != 3:
+        raise ValueError(f"scores must be [heads, q_tiles, k_tiles], got shape {tuple(scores.shape)}")
+    _expect(scores, "scores", scores.shape, _F32)
     _dev(scores, "scores")
     H, Tq, Tk = scores.shape
     kmax = kmax_for(Tk, k, tiles_per_frame, anchor_frame) if kmax is None else kmax
@@ -221,6 +265,9 @@ def sparse3d_select_topk(scores: torch.Tensor, k: int, tiles_per_frame: int, anc
 def sparse3d_select_topk_per_head(scores: torch.Tensor, ks: Sequence[int], tiles_per_frame: int,
                                   anchor_frame: int = 0, kmax: Optional[int] = None):
     """Top-k_h key tiles per query tile of head h, united with the anchor frame."""
+    if scores.dim() != 3:
+        raise ValueError(f"scores must be [heads, q_tiles, k_tiles], got shape {tuple(scores.shape)}")
+    _expect(scores, "scores", scores.shape, _F32)
     _dev(scores, "scores")
     H, Tq, Tk = scores.shape
     ks = [int(x) for x in ks]
@@ -238,6 +285,8 @@ def sparse3d_select_topk_per_head(scores: torch.Tensor, ks: Sequence[int], tiles
 
 def _out_dtype(q, out_dtype):
     od = q.dtype if out_dtype is None else out_dtype
+    if od not in _OPERAND:
+        raise TypeError(f"out_dtype must be bfloat16 or float32, not {od}")
     return od, (BF16 if od == torch.bfloat16 else F32)
 
 
@@ -248,15 +297,24 @@ def sparse3d_sparse_attn_fwd(q, k, v, qlay, klay, idx, cnt, kbar=None, vbar=None
 
     kbar/vbar are the tile means in q's dtype (for bf16, ``sparse3d_cast`` of the fp32
     means that ``sparse3d_tile_scores`` returns)."""
-    for x, n in ((q, "q"), (k, "k"), (v, "v"), (idx, "idx"), (cnt, "cnt")):
-        _dev(x, n)
+    H = _operands(q, k, v, qlay, klay)
+    _out_dtype(q, out_dtype)
+    if idx.dim() != 3:
+        raise ValueError(f"idx must be [heads, q_tiles, kmax], got shape {tuple(idx.shape)}")
+    Tq, Tk = _tiles(qlay), _tiles(klay)
+    _expect(idx, "idx", (H, Tq, idx.shape[2]), _I32)
+    _expect(cnt, "cnt", (H, Tq), _I32)
     if (kbar is None) != (vbar is None):
         raise ValueError("kbar and vbar go together")
+    # landmark means in the operand dtype (for bf16: sparse3d_cast of the fp32 means)
+    _expect(kbar, "kbar", (H, Tk, HEAD_DIM), (q.dtype,))
+    _expect(vbar, "vbar", (H, Tk, HEAD_DIM), (q.dtype,))
+    _same_device(q, idx, cnt, kbar, vbar)
+    sga_c = _sga_ref(sga, q)
+    for x, n in ((q, "q"), (k, "k"), (v, "v"), (idx, "idx"), (cnt, "cnt")):
+        _dev(x, n)
     if kbar is not None:
         _dev(kbar, "kbar"), _dev(vbar, "vbar")
-        if kbar.dtype != q.dtype or vbar.dtype != q.dtype:
-            raise TypeError("landmark means must have the operand dtype (see sparse3d_cast)")
-    H = q.shape[0]
     scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else scale
     od, odc = _out_dtype(q, out_dtype)
     out = torch.empty(q.shape, device=q.device, dtype=od)
@@ -266,15 +324,17 @@ def sparse3d_sparse_attn_fwd(q, k, v, qlay, klay, idx, cnt, kbar=None, vbar=None
     _check(library().sparse3d_sparse_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _dt(q), H, q.shape[2], TILE, ctypes.byref(ql), ctypes.byref(kl),
         _ptr(idx) if kmax > 0 else None, _ptr(cnt), kmax, _ptr(kbar), _ptr(vbar), landmark_bias,
-        scale, _sga_ref(sga, q), _ptr(out), odc, _ptr(lse), _stream(q)))
+        scale, sga_c, _ptr(out), odc, _ptr(lse), _stream(q)))
     return (out, lse) if return_lse else out
 
 
 def sparse3d_cast(x: torch.Tensor, dtype) -> torch.Tensor:
     """fp32 tensor -> new tensor of `dtype` (bfloat16: round to nearest even)."""
-    _dev(x, "x")
     if x.dtype != torch.float32:
         raise TypeError("sparse3d_cast converts from float32")
+    if dtype not in _OPERAND:
+        raise TypeError(f"sparse3d_cast converts to bfloat16 or float32, not {dtype}")
+    _dev(x, "x")
     out = torch.empty(x.shape, device=x.device, dtype=dtype)
     _check(library().sparse3d_cast(_ptr(x), x.numel(), _dt(out), _ptr(out), _stream(x)))
     return out
@@ -284,9 +344,11 @@ def sparse3d_dense_attn_fwd(q, k, v, qlay, klay=None, scale: Optional[float] = N
                             out_dtype=None, return_lse: bool = False, sga: Optional[Sga] = None):
     """Dense global attention over every valid key (the library's own baseline)."""
     klay = qlay if klay is None else klay
+    H = _operands(q, k, v, qlay, klay)
+    _out_dtype(q, out_dtype)
+    sga_c = _sga_ref(sga, q)
     for x, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(x, n)
-    H = q.shape[0]
     scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else scale
     od, odc = _out_dtype(q, out_dtype)
     out = torch.empty(q.shape, device=q.device, dtype=od)
@@ -294,7 +356,7 @@ def sparse3d_dense_attn_fwd(q, k, v, qlay, klay=None, scale: Optional[float] = N
     ql, kl = _lay(qlay), _lay(klay)
     _check(library().sparse3d_dense_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _dt(q), H, q.shape[2], ctypes.byref(ql), ctypes.byref(kl),
-        scale, _sga_ref(sga, q), _ptr(out), odc, _ptr(lse), _stream(q)))
+        scale, sga_c, _ptr(out), odc, _ptr(lse), _stream(q)))
     return (out, lse) if return_lse else out
 
 
@@ -302,9 +364,10 @@ def sparse3d_frame_attn_fwd(q, k, v, qlay, klay=None, scale: Optional[float] = N
                             out_dtype=None, return_lse: bool = False):
     """Attention of every valid query over the valid keys of its own frame only."""
     klay = qlay if klay is None else klay
+    H = _operands(q, k, v, qlay, klay)
+    _out_dtype(q, out_dtype)
     for x, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(x, n)
-    H = q.shape[0]
     scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else scale
     od, odc = _out_dtype(q, out_dtype)
     out = torch.empty(q.shape, device=q.device, dtype=od)
@@ -319,8 +382,8 @@ def sparse3d_frame_attn_fwd(q, k, v, qlay, klay=None, scale: Optional[float] = N
 def sparse3d_discarded_mean(k, v, lay, grid: Tuple[int, int], window: int):
     """Mean key and value of the patch rows the grid subsample drops (all frames, per head):
     (kmean [H, 64] fp32, vmean [H, 64] fp32, |D|)."""
+    H = _operands(k, k, v, lay, lay)
     _dev(k, "k"), _dev(v, "v")
-    H = k.shape[0]
     kmean = torch.empty((H, HEAD_DIM), device=k.device, dtype=torch.float32)
     vmean = torch.empty_like(kmean)
     il = _lay(lay)
@@ -335,8 +398,13 @@ def sparse3d_discarded_mean(k, v, lay, grid: Tuple[int, int], window: int):
 def sparse3d_selection_transpose(idx: torch.Tensor, cnt: torch.Tensor, k_tiles: int):
     """For each head and key tile, the ascending query tiles that selected it (CSR with end
     offsets).  Returns (t_end int32 [H, k_tiles], t_list int32 [H, q_tiles * kmax])."""
-    _dev(idx, "idx"), _dev(cnt, "cnt")
+    if idx.dim() != 3:
+        raise ValueError(f"idx must be [heads, q_tiles, kmax], got shape {tuple(idx.shape)}")
     H, Tq, kmax = idx.shape
+    _expect(idx, "idx", idx.shape, _I32)
+    _expect(cnt, "cnt", (H, Tq), _I32)
+    _same_device(idx, cnt)
+    _dev(idx, "idx"), _dev(cnt, "cnt")
     t_end = torch.empty((H, k_tiles), device=idx.device, dtype=torch.int32)
     t_list = torch.empty((H, Tq * max(kmax, 0)), device=idx.device, dtype=torch.int32)
     _check(library().sparse3d_selection_transpose(_ptr(idx) if kmax > 0 else None, _ptr(cnt), H, Tq,
@@ -349,10 +417,21 @@ def sparse3d_sparse_attn_bwd(q, k, v, out, dout, lse, qlay, klay, idx, cnt, t_en
                              scale: Optional[float] = None):
     """Gradients of the sparse attention (no landmarks), selection fixed.
     Returns (dq, dk, dv, delta), fp32."""
+    H = _operands(q, k, v, qlay, klay)
+    if idx.dim() != 3:
+        raise ValueError(f"idx must be [heads, q_tiles, kmax], got shape {tuple(idx.shape)}")
+    Tq, Tk = _tiles(qlay), _tiles(klay)
+    _expect(idx, "idx", (H, Tq, idx.shape[2]), _I32)
+    _expect(cnt, "cnt", (H, Tq), _I32)
+    _expect(out, "out", q.shape, (q.dtype,))
+    _expect(dout, "dout", q.shape, (q.dtype,))
+    _expect(lse, "lse", q.shape[:2], _F32)
+    _expect(t_end, "t_end", (H, Tk), _I32)
+    _expect(t_list, "t_list", (H, Tq * idx.shape[2]), _I32)
+    _same_device(q, out, dout, lse, idx, cnt, t_end, t_list)
     for x, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout"), (lse, "lse"),
                  (idx, "idx"), (cnt, "cnt"), (t_end, "t_end"), (t_list, "t_list")):
         _dev(x, n)
-    H = q.shape[0]
     scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else scale
     f = dict(device=q.device, dtype=torch.float32)
     dq = torch.empty(q.shape, **f)
@@ -379,8 +458,8 @@ def sparse3d_subsample_layout(lay, grid_h: int, grid_w: int, window: int, tile: 
 
 def sparse3d_grid_subsample_kv(k, v, lay, grid: Tuple[int, int], window: int):
     """Thin keys/values on the patch grid.  Returns (k_sub, v_sub, layout_sub)."""
+    H = _operands(k, k, v, lay, lay)
     _dev(k, "k"), _dev(v, "v")
-    H = k.shape[0]
     out_lay = sparse3d_subsample_layout(lay, grid[0], grid[1], window)
     rows = out_lay[0] * out_lay[2]
     k2 = torch.empty((H, rows, k.shape[2]), device=k.device, dtype=k.dtype)

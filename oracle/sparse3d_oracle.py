@@ -192,6 +192,34 @@ def select_topk(scores: np.ndarray, k, tiles_per_frame: int, anchor: int,
     return idx, cnt
 
 
+def select_mask(scores: np.ndarray, k, tiles_per_frame: int, anchor: int) -> np.ndarray:
+    """``select_tiles`` of every row at once, as a boolean [H, Tq, Tk] membership mask.
+
+    The same rule written by threshold: with T the k-th largest score of the row, a tile
+    is among the k best iff its score exceeds T, or equals T and fewer than k tiles lie
+    above T plus the equal ones of lower index; the anchor frame's tiles are added.  Meant
+    for large score matrices (one partial sort per head instead of one full sort per row).
+    ``k`` is one budget or one per head.
+    """
+    H, Tq, Tk = scores.shape
+    ks = [int(k)] * H if np.ndim(k) == 0 else [int(x) for x in k]
+    out = np.zeros((H, Tq, Tk), dtype=bool)
+    for h in range(H):
+        kh = min(max(ks[h], 0), Tk)
+        row = scores[h].astype(np.float64)
+        if kh == Tk:
+            out[h] = True
+        elif kh > 0:
+            T = np.partition(row, Tk - kh, axis=1)[:, Tk - kh]          # the k-th largest value
+            above = row > T[:, None]
+            tie = row == T[:, None]
+            room = kh - above.sum(axis=1)                               # how many ties to take
+            out[h] = above | (tie & (np.cumsum(tie, axis=1) <= room[:, None]))
+        if anchor >= 0:
+            out[h, :, anchor * tiles_per_frame:(anchor + 1) * tiles_per_frame] = True
+    return out
+
+
 # ----------------------------------------------------------------------------- step 4: attend
 def _softmax_rows(logits: np.ndarray, values: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     """Exact softmax-weighted average of ``values`` per row of ``logits``; also log-sum-exp.
@@ -261,14 +289,29 @@ def sparse_attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, qlay: Layout, kla
 def sparse_attend_bwd(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray, qlay: Layout,
                       klay: Layout, tile: int, idx: np.ndarray, cnt: np.ndarray,
                       scale: float, query_tiles: Optional[Sequence[int]] = None,
-                      heads: Optional[Sequence[int]] = None
-                      ) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
-    """Gradients of ``sparse_attend`` (no landmarks) w.r.t. Q, K, V for the output cotangent
-    dO, selection fixed: (dQ [H, Lq, d], dK [H, Lk, d], dV [H, Lk, d], D [H, Lq]) in fp64,
+                      heads: Optional[Sequence[int]] = None, *,
+                      kbar: Optional[np.ndarray] = None, vbar: Optional[np.ndarray] = None,
+                      kcount: Optional[np.ndarray] = None, landmark_bias: float = LN64,
+                      means: bool = False, magnitudes: bool = False):
+    """Gradients of ``sparse_attend`` w.r.t. Q, K, V for the output cotangent dO, selection
+    fixed: (dQ [H, Lq, d], dK [H, Lk, d], dV [H, Lk, d], D [H, Lq]) in fp64,
     D = rowsum(dO * O).  Rows that are not valid queries contribute nothing and get
     dQ = 0, D = 0; key rows nobody attends (pad, unselected tiles) get dK = dV = 0.
     With ``query_tiles`` / ``heads`` only those query tiles contribute (dK/dV of a key tile
-    are then complete when the list holds every query tile that selected it)."""
+    are then complete when the list holds every query tile that selected it).
+
+    Landmarks (``kbar``/``vbar``/``kcount`` as in ``sparse_attend``): every unselected
+    non-empty tile t is one more key of the row, kbar[t] with logit bias ``landmark_bias``
+    and value vbar[t].  Its gradients dkbar[t] = scale sum_i dS_it q_i and
+    dvbar[t] = sum_i P_it dO_i flow through the mean pool (kbar[t] is the mean of K over
+    the member rows M(t)) into every member row: dK[r] += dkbar[t] / |M(t)|, likewise dV.
+    ``means``: also return dkbar, dvbar [H, Tk, d] (zero without landmarks).
+
+    ``magnitudes``: also return a dict of absolute-value sums that bound how rounding of the
+    softmax weights and of dS propagates (same shapes as the gradients):
+      M_ij = P_ij (|dP_ij - D_i| + A_D_i),  A_D_i = sum_c |dO_ic| (|O_ic| + sum_j P_ij |V_jc|),
+      dQ: scale sum_j M_ij |K_j|;  dK: scale sum_i M_ij |Q_i|;  dV: sum_i P_ij |dO_i|;  D: A_D
+    (landmark columns chained to member rows like the gradients)."""
     H, Lq, d = Q.shape
     Tk = klay.rows // tile
     qv = query_rows(qlay)
@@ -278,6 +321,11 @@ def sparse_attend_bwd(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarra
     dK = np.zeros((H, K.shape[1], d))
     dV = np.zeros((H, K.shape[1], d))
     D = np.zeros((H, Lq))
+    dkb = np.zeros((H, Tk, d))
+    dvb = np.zeros((H, Tk, d))
+    if magnitudes:
+        mag = {n: np.zeros_like(x) for n, x in (("dQ", dQ), ("dK", dK), ("dV", dV), ("D", D))}
+        mkb, mvb = np.zeros((H, Tk, d)), np.zeros((H, Tk, d))
     for h in (range(H) if heads is None else heads):
         for tq in (range(qlay.rows // tile) if query_tiles is None else query_tiles):
             rows_q = tq * tile + np.nonzero(qv[tq * tile:(tq + 1) * tile])[0]
@@ -285,13 +333,22 @@ def sparse_attend_bwd(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarra
                 continue
             sel = idx[h, tq, : cnt[h, tq]]
             J = np.concatenate([spec] + [t * tile + np.nonzero(mem[t])[0] for t in sel]).astype(np.int64)
-            if J.size == 0:
-                continue
-            q = Q[h, rows_q].astype(np.float64)
             kk = K[h, J].astype(np.float64)
             vv = V[h, J].astype(np.float64)
+            bias = np.zeros(J.size)
+            lm = np.empty(0, dtype=np.int64)
+            if kbar is not None:
+                chosen = np.zeros(Tk, dtype=bool)
+                chosen[sel] = True
+                lm = np.nonzero(~chosen & (kcount > 0))[0]
+                kk = np.concatenate([kk, kbar[h, lm]])
+                vv = np.concatenate([vv, vbar[h, lm]])
+                bias = np.concatenate([bias, np.full(lm.size, landmark_bias)])
+            if kk.shape[0] == 0:
+                continue
+            q = Q[h, rows_q].astype(np.float64)
             g = dO[h, rows_q].astype(np.float64)
-            s = scale * (q @ kk.T)
+            s = scale * (q @ kk.T) + bias
             p = np.exp(s - s.max(axis=1, keepdims=True))
             p /= p.sum(axis=1, keepdims=True)
             o = p @ vv
@@ -299,10 +356,38 @@ def sparse_attend_bwd(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarra
             Di = np.sum(g * o, axis=1)
             ds = p * (dp - Di[:, None])
             dQ[h, rows_q] = scale * (ds @ kk)
-            np.add.at(dK[h], J, scale * (ds.T @ q))
-            np.add.at(dV[h], J, p.T @ g)
+            gk, gv = scale * (ds.T @ q), p.T @ g          # per attended key, then per landmark
+            np.add.at(dK[h], J, gk[:J.size])
+            np.add.at(dV[h], J, gv[:J.size])
+            dkb[h, lm] += gk[J.size:]
+            dvb[h, lm] += gv[J.size:]
             D[h, rows_q] = Di
-    return dQ, dK, dV, D
+            if magnitudes:
+                AD = np.sum(np.abs(g) * (np.abs(o) + p @ np.abs(vv)), axis=1)
+                M = p * (np.abs(dp - Di[:, None]) + AD[:, None])
+                mag["dQ"][h, rows_q] = scale * (M @ np.abs(kk))
+                ak, av = scale * (M.T @ np.abs(q)), p.T @ np.abs(g)
+                np.add.at(mag["dK"][h], J, ak[:J.size])
+                np.add.at(mag["dV"][h], J, av[:J.size])
+                mkb[h, lm] += ak[J.size:]
+                mvb[h, lm] += av[J.size:]
+                mag["D"][h, rows_q] = AD
+    if kbar is not None:
+        # the mean pool: each member row of tile t receives 1/|M(t)| of the mean's gradient
+        rows_t = [t * tile + np.nonzero(mem[t])[0] for t in range(Tk)]
+        for t in range(Tk):
+            if kcount[t] > 0:
+                dK[:, rows_t[t]] += dkb[:, t, None, :] / kcount[t]
+                dV[:, rows_t[t]] += dvb[:, t, None, :] / kcount[t]
+                if magnitudes:
+                    mag["dK"][:, rows_t[t]] += mkb[:, t, None, :] / kcount[t]
+                    mag["dV"][:, rows_t[t]] += mvb[:, t, None, :] / kcount[t]
+    res = (dQ, dK, dV, D)
+    if means:
+        res = res + (dkb, dvb)
+    if magnitudes:
+        res = res + (mag,)
+    return res
 
 
 def selection_transpose(idx: np.ndarray, cnt: np.ndarray, k_tiles: int) -> list:

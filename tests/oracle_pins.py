@@ -657,6 +657,131 @@ def pin_backward_finite_difference(o):
                 assert abs((up - dn) / (2 * eps) - G[0, r, c]) < 1e-6, (which, r, c)
 
 
+def _landmark_bwd_case(o, S, N, P, nsp, tile, k, seed):
+    Q, K, V, dO, lay, idx, cnt = _bwd_case(o, S, N, P, nsp, tile, k, seed=seed)
+    kbar, kc = o.tile_pool(K, lay, tile, "key")
+    vbar, _ = o.tile_pool(V, lay, tile, "key")
+    return Q, K, V, dO, lay, idx, cnt, kbar, vbar, kc
+
+
+def pin_backward_landmarks_autograd(o):
+    """With landmarks, the gradient equals torch autograd (fp64, CPU) of an explicit
+    computation: every query row attends its masked keys plus one pseudo-key per unselected
+    tile that has members, whose key and value are the means of the tile's member rows
+    taken inside the graph (so the gradient reaches K and V through the mean) and whose
+    logit carries the bias; dkbar/dvbar equal the gradients of those means."""
+    for (S, N, P, nsp, tile, k, bias) in [(2, 60, 64, 5, 16, 2, math.log(64.0)), (3, 40, 48, 0, 16, 1, 0.7),
+                                          (2, 30, 32, 6, 8, 2, 2.0)]:
+        Q, K, V, dO, lay, idx, cnt, kbar, vbar, kc = _landmark_bwd_case(o, S, N, P, nsp, tile, k, seed=N + 1)
+        dQ, dK, dV, D, dkb, dvb = o.sparse_attend_bwd(Q, K, V, dO, lay, lay, tile, idx, cnt, 0.3, kbar=kbar,
+                                                      vbar=vbar, kcount=kc, landmark_bias=bias, means=True)
+        L = lay.rows
+        j = np.arange(L) % lay.stride
+        qv = j < lay.tokens
+        member = (j >= lay.specials) & (j < lay.tokens)
+        Tk = L // tile
+        for h in range(Q.shape[0]):
+            M = torch.from_numpy(_explicit_mask(lay, tile, idx, cnt, h))
+            qt = torch.tensor(np.nan_to_num(Q[h]), requires_grad=True)
+            kt = torch.tensor(np.nan_to_num(K[h]), requires_grad=True)
+            vt = torch.tensor(np.nan_to_num(V[h]), requires_grad=True)
+            kms, vms = [], []
+            for t in range(Tk):
+                rows = [r for r in range(t * tile, (t + 1) * tile) if member[r]]
+                kms.append(kt[rows].mean(0) if rows else torch.zeros(kt.shape[1], dtype=kt.dtype))
+                vms.append(vt[rows].mean(0) if rows else torch.zeros(vt.shape[1], dtype=vt.dtype))
+            km, vm = torch.stack(kms), torch.stack(vms)
+            km.retain_grad()
+            vm.retain_grad()
+            # landmark mask [L, Tk]: query row i gets tile t iff its query tile did not select t
+            # and t has members
+            LMm = np.zeros((L, Tk), dtype=bool)
+            has = np.array([member[t * tile:(t + 1) * tile].any() for t in range(Tk)])
+            for i in np.nonzero(qv)[0]:
+                sel = set(idx[h, i // tile, :cnt[h, i // tile]].tolist())
+                LMm[i] = has & np.array([t not in sel for t in range(Tk)])
+            logits = torch.cat([(0.3 * qt @ kt.T).masked_fill(~M, float("-inf")),
+                                (0.3 * qt @ km.T + bias).masked_fill(~torch.from_numpy(LMm), float("-inf"))], 1)
+            rows = torch.from_numpy(qv)
+            pr = torch.softmax(logits[rows], dim=1)
+            out = pr @ torch.cat([vt, vm])
+            (out * torch.from_numpy(dO[h][qv])).sum().backward()
+            assert np.allclose(dQ[h], qt.grad.numpy(), rtol=0, atol=1e-10)
+            assert np.allclose(dK[h], kt.grad.numpy(), rtol=0, atol=1e-10)
+            assert np.allclose(dV[h], vt.grad.numpy(), rtol=0, atol=1e-10)
+            assert np.allclose(dkb[h], km.grad.numpy(), rtol=0, atol=1e-10)
+            assert np.allclose(dvb[h], vm.grad.numpy(), rtol=0, atol=1e-10)
+            O, _ = o.sparse_attend(Q, K, V, lay, lay, tile, idx, cnt, 0.3, kbar=kbar, vbar=vbar, kcount=kc,
+                                   landmark_bias=bias)
+            assert np.allclose(D[h, qv], np.sum(dO[h, qv] * O[h, qv], axis=1), rtol=0, atol=1e-12)
+
+
+def pin_backward_landmarks_finite_difference(o):
+    """Central differences of sum(dO * O) through the forward oracle with landmarks, the
+    means recomputed from the perturbed K and V by the pool (selection held fixed)."""
+    S, N, P, nsp, tile = 2, 7, 8, 2, 4
+    Q, K, V = _rand_inputs(S, N, P, nsp, H=1, d=3, seed=4, pad=0.0)
+    lay = o.Layout(S, N, P, nsp)
+    idx, cnt, _, _ = _selection(o, Q, K, lay, tile, 1, -1, 0.5)
+    dO = np.random.default_rng(5).standard_normal(Q.shape)
+
+    def f(Q_, K_, V_):
+        kb, kc = o.tile_pool(K_, lay, tile, "key")
+        vb, _ = o.tile_pool(V_, lay, tile, "key")
+        return float(np.sum(dO * o.sparse_attend(Q_, K_, V_, lay, lay, tile, idx, cnt, 0.5, kbar=kb, vbar=vb,
+                                                 kcount=kc)[0]))
+    kb, kc = o.tile_pool(K, lay, tile, "key")
+    vb, _ = o.tile_pool(V, lay, tile, "key")
+    dQ, dK, dV, _ = o.sparse_attend_bwd(Q, K, V, dO, lay, lay, tile, idx, cnt, 0.5, kbar=kb, vbar=vb, kcount=kc)
+    assert np.any(cnt[0] < S * P // tile)                      # some tiles are landmarks
+    eps = 1e-6
+    for X, G, which in ((Q, dQ, 0), (K, dK, 1), (V, dV, 2)):
+        for r in range(X.shape[1]):
+            for c in range(X.shape[2]):
+                args = [Q.copy(), K.copy(), V.copy()]
+                args[which][0, r, c] += eps
+                up = f(*args)
+                args[which][0, r, c] -= 2 * eps
+                dn = f(*args)
+                assert abs((up - dn) / (2 * eps) - G[0, r, c]) < 1e-6, (which, r, c)
+
+
+def pin_backward_magnitudes_bound_the_gradients(o):
+    """The absolute-value sums returned with ``magnitudes`` bound the gradients by the
+    triangle inequality (|dS_ij| = P_ij |dP_ij - D_i| <= M_ij, |D_i| <= A_D_i), with and
+    without landmarks; every gradient entry that is nonzero has a nonzero magnitude."""
+    for lm in (False, True):
+        Q, K, V, dO, lay, idx, cnt, kbar, vbar, kc = _landmark_bwd_case(o, 2, 60, 64, 5, 16, 2, seed=9)
+        kw = dict(kbar=kbar, vbar=vbar, kcount=kc) if lm else {}
+        *g, mag = o.sparse_attend_bwd(Q, K, V, dO, lay, lay, 16, idx, cnt, 0.3, magnitudes=True, **kw)
+        for x, n in zip(g, ("dQ", "dK", "dV", "D")):
+            assert np.all(np.abs(x) <= mag[n] * (1 + 1e-12) + 1e-300), n
+            assert np.all(mag[n][x != 0] > 0), n
+
+
+def pin_select_mask_equals_per_row_rule(o):
+    """The whole-matrix selection mask equals ``select_tiles`` row by row, on rows full of
+    ties (integer scores), signed zeros, -inf entries and constant rows, for budgets from 0
+    past Tk, per head, with and without the anchor."""
+    rng = np.random.default_rng(41)
+    for trial in range(12):
+        H, Tq, tpf = 2, int(rng.integers(1, 9)), int(rng.integers(1, 5))
+        Tk = tpf * int(rng.integers(1, 6))
+        sc = rng.integers(-3, 3, (H, Tq, Tk)).astype(np.float64)
+        sc[:, ::3] = rng.standard_normal((H, sc[:, ::3].shape[1], Tk))
+        sc[sc == 0] = np.where(rng.random(np.count_nonzero(sc == 0)) < 0.5, -0.0, 0.0)
+        sc[rng.random(sc.shape) < 0.1] = -np.inf
+        if Tq > 1:
+            sc[:, 1] = 2.5
+        ks = [int(x) for x in rng.integers(0, Tk + 3, H)]
+        for anchor in (-1, 0, Tk // tpf - 1):
+            m = o.select_mask(sc, ks, tpf, anchor)
+            for h in range(H):
+                for t in range(Tq):
+                    want = o.select_tiles(sc[h, t], ks[h], tpf, anchor)
+                    assert np.array_equal(np.nonzero(m[h, t])[0], want), (trial, h, t, anchor)
+
+
 def pin_selection_transpose(o):
     rng = np.random.default_rng(31)
     for _ in range(10):
@@ -681,4 +806,6 @@ ALL_PINS = [
     pin_select_per_head, pin_frame_attention,
     pin_sga_explicit_key_list, pin_sga_constant_dropped_is_dense, pin_sga_nothing_dropped,
     pin_backward_autograd, pin_backward_finite_difference, pin_selection_transpose,
+    pin_backward_landmarks_autograd, pin_backward_landmarks_finite_difference,
+    pin_backward_magnitudes_bound_the_gradients, pin_select_mask_equals_per_row_rule,
 ]

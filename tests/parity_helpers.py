@@ -39,8 +39,11 @@ def margin_rows(ref_scores: np.ndarray, k: int) -> np.ndarray:
     H, Tq, Tk = ref_scores.shape
     if k <= 0 or k >= Tk:
         return np.ones((H, Tq), dtype=bool)
-    srt = -np.sort(-ref_scores, axis=2)
-    a, b = srt[:, :, k - 1], srt[:, :, k]
+    a = np.empty((H, Tq))
+    b = np.empty((H, Tq))
+    for h in range(H):                  # the k-th and (k+1)-th largest by a partial sort
+        part = np.partition(ref_scores[h], (Tk - k - 1, Tk - k), axis=1)
+        a[h], b[h] = part[:, Tk - k], part[:, Tk - k - 1]
     with np.errstate(invalid="ignore"):
         den = np.maximum(np.abs(a), np.abs(b))
         rel = np.where(np.isfinite(a) & np.isfinite(b),
@@ -68,6 +71,41 @@ def check_selection(g_scores, g_idx, g_cnt, ref_scores, k, tpf, anchor, rows=Non
             ref = oracle.select_tiles(ref_scores[h, t], k, tpf, anchor)
             assert np.array_equal(got, ref), ("margin row differs", h, t, got, ref)
     return n_margin, len(pairs)
+
+
+def selection_mask(g_idx, g_cnt, Tk):
+    """[H, Tq, Tk] membership of the GPU's lists, after checking their form: ascending,
+    in range, -1 after the count."""
+    H, Tq, kmax = g_idx.shape
+    assert np.all((g_cnt >= 0) & (g_cnt <= kmax))
+    live = np.arange(kmax)[None, None, :] < g_cnt[:, :, None]
+    assert np.all(g_idx[~live] == -1)
+    assert np.all((g_idx[live] >= 0) & (g_idx[live] < Tk))
+    if kmax > 1:
+        both = live[:, :, 1:]
+        assert np.all(np.diff(g_idx, axis=2)[both] > 0)          # strictly ascending
+    m = np.zeros((H, Tq, Tk), dtype=bool)
+    h, t, e = np.nonzero(live)
+    m[h, t, g_idx[h, t, e]] = True
+    return m
+
+
+def check_selection_all_rows(g_scores, g_idx, g_cnt, ref_scores, k, tpf, anchor):
+    """``check_selection`` on every (head, query tile) row of a large case, through the
+    oracle's whole-matrix form of the selection rule.  Returns (margin rows, rows)."""
+    H, Tq, Tk = g_scores.shape
+    got = selection_mask(g_idx, g_cnt, Tk)
+    n_margin = 0
+    for h in range(H):
+        own = oracle.select_mask(g_scores[h:h + 1].astype(np.float64), k, tpf, anchor)[0]
+        bad = np.nonzero(np.any(got[h] != own, axis=1))[0]
+        assert bad.size == 0, ("GPU selection differs from the rule on its own scores", h, bad[:8])
+        ok = margin_rows(ref_scores[h:h + 1], k)[0]
+        ref = oracle.select_mask(ref_scores[h:h + 1], k, tpf, anchor)[0]
+        bad = np.nonzero(ok & np.any(got[h] != ref, axis=1))[0]
+        assert bad.size == 0, ("margin row differs from the oracle's selection", h, bad[:8])
+        n_margin += int(ok.sum())
+    return n_margin, H * Tq
 
 
 def check_scores(g_qbar, g_kbar, g_scores, ref, atol_bar=2e-5, rtol_sc=2e-5):

@@ -255,3 +255,94 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(2, 256, 64)
     with pytest.raises(ValueError):
         S.sparse3d_tile_scores(x, x, (2, 256, 256, 0))
+
+
+def test_size_caps_of_the_kernels(lib):
+    # score matrix: 64 score rows per wave are addressed with 32-bit offsets, so key tiles
+    # are capped at 2^23; query tiles at 65535 grid rows of 128
+    big_k = L(f=131072, n=64, p=8192)                     # 2^24 key tiles
+    assert scores_call(lib, ql=L(f=131072, n=64, p=64), kl=big_k) == ERR_UNSUP
+    assert scores_call(lib, ql=L(f=131072, n=64, p=4096), kl=L(f=131072, n=64, p=64)) == ERR_UNSUP
+    # attention: one head of K/V (or Q) must stay below 2^24 rows of 128 bytes
+    wide = L(f=2, n=256, p=(1 << 23) + 64)                # 2^24 + 128 rows
+    dense = lambda ql, kl: lib.sparse3d_dense_attn_fwd(FAKE, FAKE + 10**10, FAKE + 2 * 10**10, 1, 2, 64, ql,
+                                                       kl, 0.125, NULL, FAKE + 3 * 10**10, 1, NULL, NULL)
+    frame = lambda ql, kl: lib.sparse3d_frame_attn_fwd(FAKE, FAKE + 10**10, FAKE + 2 * 10**10, 1, 2, 64, ql,
+                                                       kl, 0.125, FAKE + 3 * 10**10, 1, NULL, NULL)
+    assert dense(L(), wide) == ERR_UNSUP
+    assert dense(wide, L()) == ERR_UNSUP
+    assert frame(L(), wide) == ERR_UNSUP
+    ok = L(f=2, n=256, p=1 << 23)                          # exactly 2^24 rows: allowed
+    assert dense(L(), ok) != ERR_UNSUP
+
+
+def _cpu(*shape, dtype=None):
+    import torch
+    return torch.zeros(*shape, dtype=dtype or torch.bfloat16)
+
+
+def test_binding_checks_shapes_and_dtypes_before_the_device():
+    """Every wrapper compares its tensors with the layouts and sizes before it touches the
+    device: a too-short operand, a dtype mismatch or an int64 index table raises here, with
+    CPU tensors, long before a kernel could read past an allocation."""
+    import torch
+    lay = (2, 256, 256, 0)
+    q = _cpu(2, 512, 64)
+    with pytest.raises(ValueError, match="shape"):
+        S.sparse3d_tile_scores(q, _cpu(2, 448, 64), lay)                  # k shorter than its layout
+    with pytest.raises(ValueError, match="shape"):
+        S.sparse3d_tile_scores(_cpu(2, 512, 32), _cpu(2, 512, 32), lay)   # head_dim 32
+    with pytest.raises(TypeError, match="dtype"):
+        S.sparse3d_tile_scores(q, _cpu(2, 512, 64, dtype=torch.float32), lay)
+    with pytest.raises(TypeError, match="dtype"):
+        S.sparse3d_tile_scores(_cpu(2, 512, 64, dtype=torch.float16), _cpu(2, 512, 64, dtype=torch.float16), lay)
+    with pytest.raises(TypeError, match="dtype"):
+        S.sparse3d_select_topk(_cpu(2, 8, 8), 4, 4)                          # bf16 scores
+    idx, cnt = _cpu(2, 8, 8, dtype=torch.int32), _cpu(2, 8, dtype=torch.int32)
+    attn = lambda **kw: S.sparse3d_sparse_attn_fwd(kw.get("q", q), kw.get("k", q), kw.get("v", q), lay, lay,
+                                                    kw.get("idx", idx), kw.get("cnt", cnt),
+                                                    kbar=kw.get("kbar"), vbar=kw.get("vbar"),
+                                                    out_dtype=kw.get("out_dtype"))
+    with pytest.raises(TypeError, match="idx"):
+        attn(idx=_cpu(2, 8, 8, dtype=torch.int64))
+    with pytest.raises(TypeError, match="cnt"):
+        attn(cnt=_cpu(2, 8, dtype=torch.int64))
+    with pytest.raises(ValueError, match="cnt"):
+        attn(cnt=_cpu(2, 7, dtype=torch.int32))
+    with pytest.raises(ValueError, match="idx"):
+        attn(idx=_cpu(3, 8, 8, dtype=torch.int32))
+    with pytest.raises(ValueError, match="v has shape"):
+        attn(v=_cpu(2, 256, 64))
+    with pytest.raises(TypeError, match="v has dtype"):
+        attn(v=_cpu(2, 512, 64, dtype=torch.float32))
+    with pytest.raises(ValueError, match="kbar"):
+        attn(kbar=_cpu(2, 7, 64), vbar=_cpu(2, 8, 64))
+    with pytest.raises(TypeError, match="kbar"):
+        attn(kbar=_cpu(2, 8, 64, dtype=torch.float32), vbar=_cpu(2, 8, 64, dtype=torch.float32))
+    with pytest.raises(TypeError, match="out_dtype"):
+        attn(out_dtype=torch.float16)
+    with pytest.raises(ValueError, match="device"):
+        attn()                                                              # right shapes, host memory
+    with pytest.raises(ValueError, match="shape"):
+        S.sparse3d_dense_attn_fwd(q, _cpu(2, 500, 64), q, lay)
+    with pytest.raises(ValueError, match="shape"):
+        S.sparse3d_frame_attn_fwd(q, q, _cpu(1, 512, 64), lay)
+    with pytest.raises(TypeError, match="cnt"):
+        S.sparse3d_selection_transpose(idx, _cpu(2, 8, dtype=torch.int64), 8)
+    bwd = lambda **kw: S.sparse3d_sparse_attn_bwd(q, q, q, kw.get("out", q), kw.get("dout", q),
+                                                  kw.get("lse", _cpu(2, 512, dtype=torch.float32)), lay, lay,
+                                                  idx, cnt, kw.get("t_end", _cpu(2, 8, dtype=torch.int32)),
+                                                  kw.get("t_list", _cpu(2, 64, dtype=torch.int32)))
+    with pytest.raises(ValueError, match="lse"):
+        bwd(lse=_cpu(2, 511, dtype=torch.float32))
+    with pytest.raises(TypeError, match="dout"):
+        bwd(dout=_cpu(2, 512, 64, dtype=torch.float32))
+    with pytest.raises(ValueError, match="t_list"):
+        bwd(t_list=_cpu(2, 63, dtype=torch.int32))
+    with pytest.raises(ValueError, match="device"):
+        bwd()
+    sga = S.Sga((16, 16), 2, kmean=_cpu(2, 63, dtype=torch.float32), vmean=_cpu(2, 64, dtype=torch.float32))
+    with pytest.raises(ValueError, match="kmean"):
+        S.sparse3d_dense_attn_fwd(q, q, q, lay, sga=sga)
+    with pytest.raises(TypeError):
+        S.sparse3d_cast(_cpu(4, dtype=torch.float32), torch.float16)

@@ -26,7 +26,7 @@ MUTANTS = {
     "scores_transposed": ("np.matmul(qbar, np.swapaxes(kbar, 1, 2))", "np.matmul(kbar, np.swapaxes(qbar, 1, 2))"),
     "landmark_unscaled": ("scale * (q @ kbar[h, lm].T) + landmark_bias", "(q @ kbar[h, lm].T) + landmark_bias"),
     "anchor_short": ("(anchor + 1) * tiles_per_frame)\n", "(anchor + 1) * tiles_per_frame - 1)\n"),
-    "landmarks_include_selected": ("~chosen & (kcount > 0)", "(kcount > 0)"),
+    "landmarks_include_selected": ("~chosen & (kcount > 0))[0]\n                logits", "(kcount > 0))[0]\n                logits"),
     "dense_reads_pad": ("return _inframe(lay) < lay.tokens\n\n\n# ---", "return _inframe(lay) <= lay.tokens\n\n\n# ---"),
     "lse_without_log": ("(m + np.log(den))[:, 0]", "(m + den)[:, 0]"),
     "subsample_odd_rows": ("for y in range(0, gh, window)", "for y in range(1, gh, window)"),
@@ -44,9 +44,19 @@ MUTANTS = {
                               'ml = scale * (q @ sga["kmean"][h])'),
     "sga_mean_over_all_patches": ("if y % window or x % window]", "if True]"),
     "sga_bias_count_plus_one": ("return math.log(count)", "return math.log(count + 1)"),
+    "mask_ties_to_higher_index": ("out[h] = above | (tie & (np.cumsum(tie, axis=1) <= room[:, None]))",
+                                  "out[h] = above | (tie & (np.cumsum(tie[:, ::-1], axis=1)[:, ::-1] <= room[:, None]))"),
+    "mask_takes_every_tie": ("out[h] = above | (tie & (np.cumsum(tie, axis=1) <= room[:, None]))",
+                             "out[h] = above | tie"),
     "bwd_without_rowsum": ("ds = p * (dp - Di[:, None])", "ds = p * dp"),
-    "bwd_dk_unscaled": ("np.add.at(dK[h], J, scale * (ds.T @ q))", "np.add.at(dK[h], J, ds.T @ q)"),
-    "bwd_dv_from_ds": ("np.add.at(dV[h], J, p.T @ g)", "np.add.at(dV[h], J, ds.T @ g)"),
+    "bwd_dk_unscaled": ("gk, gv = scale * (ds.T @ q), p.T @ g", "gk, gv = ds.T @ q, p.T @ g"),
+    "bwd_dv_from_ds": ("gk, gv = scale * (ds.T @ q), p.T @ g", "gk, gv = scale * (ds.T @ q), ds.T @ g"),
+    "bwd_landmark_mean_not_divided": ("dK[:, rows_t[t]] += dkb[:, t, None, :] / kcount[t]",
+                                      "dK[:, rows_t[t]] += dkb[:, t, None, :]"),
+    "bwd_landmark_bias_dropped": ("s = scale * (q @ kk.T) + bias", "s = scale * (q @ kk.T)"),
+    "bwd_landmark_value_grad_lost": ("dvb[h, lm] += gv[J.size:]", "pass"),
+    "bwd_landmarks_include_selected": ("lm = np.nonzero(~chosen & (kcount > 0))[0]\n                kk = ",
+                                       "lm = np.nonzero(kcount > 0)[0]\n                kk = "),
     "bwd_dq_transposed_keys": ("dQ[h, rows_q] = scale * (ds @ kk)", "dQ[h, rows_q] = scale * (ds @ vv)"),
     "transpose_drops_first": ("            for t in idx[h, tq, : cnt[h, tq]]:\n                out[h][int(t)].append(tq)",
                               "            for t in idx[h, tq, 1: cnt[h, tq]]:\n                out[h][int(t)].append(tq)"),

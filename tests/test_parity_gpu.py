@@ -15,8 +15,8 @@ import oracle
 from dynamic_block_sparse_tile_amd import layer as LY
 from dynamic_block_sparse_tile_amd import sparse3d as S
 from dynamic_block_sparse_tile_amd import synth
-from parity_helpers import (TOL, check_scores, check_selection, compare_outputs, dev,
-                            oracle_pool_scores, sample_tiles, say, tdt, to_dev)
+from parity_helpers import (TOL, check_scores, check_selection, check_selection_all_rows,
+                            compare_outputs, dev, oracle_pool_scores, sample_tiles, say, tdt, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -246,8 +246,9 @@ def test_k_all_tiles_equals_dense():
 
 
 def test_dense_and_frame_with_odd_tiles_per_frame():
-    # 3 tiles per frame, 4 frames: the dense call pairs query tiles across frame boundaries
-    # (two per workgroup), the frame call takes one query tile per workgroup
+    # 3 tiles per frame, 4 frames: with an odd number of tiles per frame the dense and the
+    # frame call both take one query tile per workgroup (the two-tile instance needs an even
+    # count, so that a pair never straddles a frame)
     w = _custom(4, 150, 192, 5, heads=2)
     inp = synth.make_inputs(w, seed=17)
     q, v = to_dev(inp.q, torch.bfloat16), to_dev(inp.v, torch.bfloat16)
@@ -388,13 +389,16 @@ def _full_size(name, n_tiles=48, seed=0):
     ref = oracle_pool_scores(inp, ol, okl, K=Kn, V=Vn, landmarks=w.landmarks)
     pairs = sample_tiles(w.heads, Tq, n_tiles, seed=seed)
     g_scores = scores.cpu().numpy()
-    # scores on the sampled rows, pooled summaries everywhere
-    check_scores(qbar.cpu().numpy(), kbar.cpu().numpy(),
-                 np.stack([g_scores[h, t] for h, t in pairs])[None],
-                 dict(qbar=ref["qbar"], kbar=ref["kbar"],
-                      scores=np.stack([ref["scores"][h, t] for h, t in pairs])[None]))
+    # pooled summaries and scores everywhere, one head of scores at a time
+    for h in range(w.heads):
+        check_scores(qbar[h:h + 1].cpu().numpy(), kbar[h:h + 1].cpu().numpy(), g_scores[h:h + 1],
+                     dict(qbar=ref["qbar"][h:h + 1], kbar=ref["kbar"][h:h + 1], scores=ref["scores"][h:h + 1]))
+    say(f"[full] {name}: scores checked on every row")
+    # the selection on every (head, query tile) row: the oracle's rule on the GPU's scores,
+    # and the oracle's own fp64 selection wherever the margin exceeds 1e-3
     g_idx, g_cnt = idx.cpu().numpy(), cnt.cpu().numpy()
-    nm, n = check_selection(g_scores, g_idx, g_cnt, ref["scores"], k, tpf, w.anchor, rows=pairs)
+    nm, n = check_selection_all_rows(g_scores, g_idx, g_cnt, ref["scores"], k, tpf, w.anchor)
+    say(f"[full] {name}: selection identical on all {n} rows ({nm} margin rows)")
     kw = dict(kbar=ref["kbar"], vbar=ref["vbar"], kcount=ref["kcount"]) if w.landmarks else {}
     heads = sorted({h for h, _ in pairs})
     O, _ = oracle.sparse_attend(inp.q, Kn, Vn, ol, okl, 64, g_idx, g_cnt, 0.125,
@@ -409,6 +413,11 @@ def test_full_vggt_s32():
 
 def test_full_vggt_s128():
     _full_size("vggt_s128", n_tiles=32)
+
+
+def test_full_vggt_s128_90():
+    # the 90 % sparsity point of the S = 128 workload (k calibrated to about 251)
+    _full_size("vggt_s128_90", n_tiles=32)
 
 
 def test_full_vggt_s256_landmarks():
@@ -628,11 +637,36 @@ def test_subsample_completion_sparse_with_landmarks():
 
 
 # --------------------------------------------------------------------------- backward
-def _grad_close(g, ref, what, rel=2e-2):
-    lim = rel * max(1.0, float(np.max(np.abs(ref))))
-    err = float(np.max(np.abs(g.astype(np.float64) - ref)))
-    assert err <= lim, (what, err, lim)
-    return err
+# Elementwise bound of the backward, derived from where the bf16 path rounds (u = 2^-8 bounds
+# one bf16 rounding, relative).  The softmax weights P are recomputed from the forward's lse,
+# which its bf16-rounded probabilities move by at most ln(1 + u), and are rounded to bf16 for
+# the products: |dP_ij| relative error <= 2u.  D = rowsum(dO * O) reads the stored bf16 O,
+# which is within u of the exact output's weights: |dD_i| <= 2u A_D_i.  dS = P (dP - D) is
+# rounded to bf16: |d(dS_ij)| <= 3u M_ij with M_ij = P_ij (|dP_ij - D_i| + A_D_i).  The
+# products with K, Q, dO take exact bf16 inputs and accumulate in fp32.  Hence
+#   |dQ - ref| <= 3u scale sum_j M_ij |K_j|,  |dK - ref| <= 3u scale sum_i M_ij |Q_i|,
+#   |dV - ref| <= 2u sum_i P_ij |dO_i|,       |D - ref|  <= 2u A_D_i,
+# the sums taken by the oracle in absolute-value arithmetic (``magnitudes``); the test allows
+# twice that, plus 1e-6 for fp32 accumulation.  Being worst cases, these bounds can exceed a
+# typical gradient, so each tensor must also match in relative Frobenius norm within 2^-5
+# (rounding errors of random sign cancel: a simulation of these roundings on the 8-view case
+# gives at most 0.0093, while a dropped tile or a missing term moves the norm by several %).
+_BWD_U = 2.0 ** -8
+_BWD_C = {"dQ": 3.0, "dK": 3.0, "dV": 2.0, "D": 2.0}
+
+
+def _grad_bound(g, ref, mag, what, rows=None):
+    g = g.astype(np.float64)
+    if rows is not None:
+        g, ref, mag = g[rows], ref[rows], mag[rows]
+    name = what if isinstance(what, str) else what[0]
+    lim = 2.0 * _BWD_C[name] * _BWD_U * mag + 1e-6
+    err = np.abs(g - ref)
+    assert np.all(err <= lim), (what, float(np.max(err - lim)), float(np.max(err / lim)))
+    nr = float(np.linalg.norm(ref))
+    fro = float(np.linalg.norm(g - ref)) / nr if nr > 0 else float(np.linalg.norm(g))
+    assert fro <= 2.0 ** -5, (what, fro)
+    return float(np.max(err / lim)), fro
 
 
 def _bwd_setup(w, seed, k=None):
@@ -672,11 +706,11 @@ def test_backward_vggt_s8(seed, k):
     say(f"[case] backward vggt_s8 seed={seed} k={k}")
     inp, dO, g_idx, g_cnt, t_end, t_list, (dq, dk, dv, delta), out, Tk = _bwd_setup(w, seed, k)
     ol = oracle.Layout(*w.layout)
-    rdq, rdk, rdv, rD = oracle.sparse_attend_bwd(inp.q, inp.k, inp.v, dO, ol, ol, 64, g_idx, g_cnt, 0.125)
-    _grad_close(dq.cpu().numpy(), rdq, "dq")
-    _grad_close(dk.cpu().numpy(), rdk, "dk")
-    _grad_close(dv.cpu().numpy(), rdv, "dv")
-    _grad_close(delta.cpu().numpy(), rD, "delta")
+    rdq, rdk, rdv, rD, mag = oracle.sparse_attend_bwd(inp.q, inp.k, inp.v, dO, ol, ol, 64, g_idx, g_cnt,
+                                                      0.125, magnitudes=True)
+    for n, g, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv), ("D", delta, rD)):
+        worst, fro = _grad_bound(g.cpu().numpy(), r, mag[n], n)
+        say(f"  {n}: max err / bound {worst:.3f}, relative Frobenius error {fro:.2e}")
     qv = oracle.query_rows(ol)
     assert np.all(dq.cpu().numpy()[:, ~qv] == 0)
     pad = ~oracle.query_rows(ol)
@@ -711,11 +745,13 @@ def test_backward_full_s128_sampled():
     H, Tq = g_idx.shape[0], g_idx.shape[1]
     pairs = sample_tiles(H, Tq, 6, seed=3)
     for (h, t) in pairs:                                             # dQ of sampled query tiles
-        rdq, _, _, rD = oracle.sparse_attend_bwd(inp.q, inp.k, inp.v, dO, ol, ol, 64, g_idx, g_cnt, 0.125,
-                                                 query_tiles=[t], heads=[h])
+        rdq, _, _, rD, mag = oracle.sparse_attend_bwd(inp.q, inp.k, inp.v, dO, ol, ol, 64, g_idx, g_cnt, 0.125,
+                                                      query_tiles=[t], heads=[h], magnitudes=True)
         r = slice(t * 64, (t + 1) * 64)
-        _grad_close(dq[h, r].cpu().numpy(), rdq[h, r], ("dq", h, t))
-        _grad_close(delta[h, r].cpu().numpy(), rD[h, r], ("delta", h, t))
+        if not np.any(oracle.query_rows(ol)[r]):
+            continue
+        _grad_bound(dq[h, r].cpu().numpy(), rdq[h, r], mag["dQ"][h, r], ("dQ", h, t))
+        _grad_bound(delta[h, r].cpu().numpy(), rD[h, r], mag["D"][h, r], ("D", h, t))
     te = t_end.cpu().numpy()
     tl = t_list.cpu().numpy()
     tpf = w.layout[2] // 64
@@ -723,9 +759,9 @@ def test_backward_full_s128_sampled():
     for (h, t) in key_pairs:                                         # dK, dV of sampled key tiles
         b = 0 if t == 0 else int(te[h, t - 1])
         qt = tl[h, b:int(te[h, t])].tolist()
-        _, rdk, rdv, _ = oracle.sparse_attend_bwd(inp.q, inp.k, inp.v, dO, ol, ol, 64, g_idx, g_cnt, 0.125,
-                                                  query_tiles=qt, heads=[h])
+        _, rdk, rdv, _, mag = oracle.sparse_attend_bwd(inp.q, inp.k, inp.v, dO, ol, ol, 64, g_idx, g_cnt, 0.125,
+                                                       query_tiles=qt, heads=[h], magnitudes=True)
         j = np.arange(t * 64, (t + 1) * 64)
         mem = j[oracle.member_rows(ol)[j]]
-        _grad_close(dk[h, mem].cpu().numpy(), rdk[h, mem], ("dk", h, t))
-        _grad_close(dv[h, mem].cpu().numpy(), rdv[h, mem], ("dv", h, t))
+        _grad_bound(dk[h, mem].cpu().numpy(), rdk[h, mem], mag["dK"][h, mem], ("dK", h, t))
+        _grad_bound(dv[h, mem].cpu().numpy(), rdv[h, mem], mag["dV"][h, mem], ("dV", h, t))
