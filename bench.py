@@ -244,16 +244,21 @@ def time_sga(torch, S, LY, q, v, w, reps=3):
 
 def time_backward(torch, S, LY, L, fwd_flops, reps=3):
     """Backward of the sparse attention on the bench selection: the selection transpose,
-    then dQ, dK, dV.  Algorithmic work = 2.5x the forward's (five products per pair: the
-    recomputed scores, dP, dV, dQ, dK, against the forward's two)."""
-    _, _, _, sc = L.scores()
+    then dQ, dK, dV (with landmarks also the means' gradients and their chain into the
+    member rows).  Algorithmic work = 2.5x the forward's (five products per attended pair or
+    landmark: the recomputed scores, dP, dV, dQ, dK, against the forward's two)."""
+    qbar, kbar, vbar, sc = L.scores()
     idx, cnt = L.select(sc)
-    del sc
-    out, lse = S.sparse3d_sparse_attn_fwd(L.q, L.K, L.V, L.lay, L.klay, idx, cnt, return_lse=True)
+    del sc, qbar
+    lm = {}
+    if L.w.landmarks:
+        lm = dict(kbar=S.sparse3d_cast(kbar, L.q.dtype), vbar=S.sparse3d_cast(vbar, L.q.dtype))
+    del kbar, vbar
+    out, lse = S.sparse3d_sparse_attn_fwd(L.q, L.K, L.V, L.lay, L.klay, idx, cnt, return_lse=True, **lm)
     g = torch.Generator(device=L.q.device).manual_seed(0)
     dout = torch.randn(L.q.shape, device=L.q.device, dtype=torch.float32, generator=g).to(L.q.dtype)
     t_end, t_list = S.sparse3d_selection_transpose(idx, cnt, L.Tk)
-    S.sparse3d_sparse_attn_bwd(L.q, L.K, L.V, out, dout, lse, L.lay, L.klay, idx, cnt, t_end, t_list)
+    S.sparse3d_sparse_attn_bwd(L.q, L.K, L.V, out, dout, lse, L.lay, L.klay, idx, cnt, t_end, t_list, **lm)
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -262,12 +267,12 @@ def time_backward(torch, S, LY, L, fwd_flops, reps=3):
         S.sparse3d_selection_transpose(idx, cnt, L.Tk)
     ev[1].record(st)
     for _ in range(reps):
-        S.sparse3d_sparse_attn_bwd(L.q, L.K, L.V, out, dout, lse, L.lay, L.klay, idx, cnt, t_end, t_list)
+        S.sparse3d_sparse_attn_bwd(L.q, L.K, L.V, out, dout, lse, L.lay, L.klay, idx, cnt, t_end, t_list, **lm)
     ev[2].record(st)
     torch.cuda.synchronize()
     tr_ms = ev[0].elapsed_time(ev[1]) / reps
     bw_ms = ev[1].elapsed_time(ev[2]) / reps
-    return {"transpose_ms": round(tr_ms, 4), "ms": round(bw_ms, 4),
+    return {"transpose_ms": round(tr_ms, 4), "ms": round(bw_ms, 4), "landmarks": bool(lm),
             "tflops": round(2.5 * fwd_flops / (bw_ms * 1e-3) / 1e12, 2)}
 
 
@@ -464,6 +469,7 @@ def main():
         res["frame_attention"] = {"ms": round(fms, 4), "tflops": round(fflops / (fms * 1e-3) / 1e12, 2)}
         if w.landmarks is False and w.kv_window == 1:
             res["subsampled_global_attention"] = time_sga(torch, S, LY, q, v, w)
+        if w.kv_window == 1:
             res["backward"] = time_backward(torch, S, LY, L, flops)
     if not args.no_gate and not args.no_dense and w.name == "vggt_s128":
         w90 = synth.WORKLOADS["vggt_s128_90"]

@@ -164,13 +164,16 @@ int sparse3d_sparse_attn_bwd(const void* q, const void* k, const void* v, const 
                              const float* lse, sparse3d_dtype dtype, int32_t heads, int32_t head_dim,
                              int32_t tile, const sparse3d_layout* qlay, const sparse3d_layout* klay,
                              const int32_t* idx, const int32_t* cnt, int32_t kmax, const int32_t* t_end,
-                             const int32_t* t_list, float scale, float* dq, float* dk, float* dv,
-                             float* delta, void* stream) {
+                             const int32_t* t_list, const void* kbar, const void* vbar, float landmark_bias,
+                             float scale, float* dq, float* dk, float* dv, float* delta, float* dkbar,
+                             float* dvbar, void* stream) {
     const int st = validate_attn_bwd(q, k, v, out, dout, lse, dtype, heads, head_dim, tile, qlay, klay, idx,
-                                     cnt, kmax, t_end, t_list, scale, dq, dk, dv, delta);
+                                     cnt, kmax, t_end, t_list, kbar, vbar, landmark_bias, scale, dq, dk, dv,
+                                     delta, dkbar, dvbar);
     if (st != SPARSE3D_OK) return st;
-    BwdArgs a{q, k, v, out, dout, lse, heads, to_lay(*qlay), to_lay(*klay), idx, cnt, kmax, t_end, t_list,
-              scale, dq, dk, dv, delta};
+    BwdArgs a{q,      k,     v,    out,  dout,          lse,   heads, to_lay(*qlay), to_lay(*klay),
+              idx,    cnt,   kmax, t_end, t_list,       kbar,  vbar,  landmark_bias, scale,
+              dq,     dk,    dv,   delta, kbar ? dkbar : nullptr, kbar ? dvbar : nullptr};
     S3D_HIP(launch_attn_bwd(a, static_cast<hipStream_t>(stream)));
     return SPARSE3D_OK;
 }

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(128, 2) void k_attn(AttnDev p) {
         myidx = p.idx + ((size_t)h * p.Tq + tq) * p.kmax;
         ntiles = p.Ts + c + (LM ? p.nlm : 0);
     }
-    if (LM) init_landmark_bitmap(p, c, myidx, s_lm, tid, 128);
+    if (LM) init_landmark_bitmap(p.kl, p.Tk, p.nlm, c, myidx, s_lm, tid, 128);
 
     // ---- staging assignment: thread -> rows {2rp, 2rp+1, 32+2rp, 33+2rp}, chunk c8
     //      (bf16: 16-byte chunks of 8 elements; fp32: two 16-byte chunks per c8)

@@ -150,7 +150,7 @@ __global__ __launch_bounds__(128 * QT, 3) void k_attn_bf16(AttnDev p) {
         ntiles = p.Ts + c + (LM ? p.nlm : 0);
     }
     uint32_t* s_lm = s_dyn;                          // landmark bitmap (2 nlm words), then the list
-    if (LM) init_landmark_bitmap(p, c, myidx, s_lm, tid, 128);
+    if (LM) init_landmark_bitmap(p.kl, p.Tk, p.nlm, c, myidx, s_lm, tid, 128);
     int32_t* s_idx = reinterpret_cast<int32_t*>(s_dyn + (LM ? 2 * p.nlm : 0));
     if (!DENSE) {
         // the selected-tile list, staged once in LDS so that each step's lookup is an LDS read

@@ -1,16 +1,22 @@
 // Backward of the tile-sparse attention (bf16 operands, fp32 accumulation), for training
-// after conversion (Zebra3D abstract) and sparse training (EPFL "(Full) Attention is More
-// Than You Need").  The selection is held fixed (top-k is piecewise constant).  With P the
-// softmax weights (recomputed from the forward's log-sum-exp), D = rowsum(dO * O):
+// after conversion (Zebra3D abstract: landmark summaries, post-conversion training) and
+// sparse training (EPFL "(Full) Attention is More Than You Need").  The selection is held
+// fixed (top-k is piecewise constant).  With P the softmax weights (recomputed from the
+// forward's log-sum-exp), D = rowsum(dO * O):
 //   dS = P * (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
-// Two kernels, each with the forward's operand machinery (tile_lds.h):
+// Three kernels, each with the forward's operand machinery (tile_lds.h):
 //  - k_attn_bwd_dq: one workgroup per (head, query tile) walks the query tile's list
-//    (special pseudo-tiles, then its selected tiles) like the forward and accumulates
-//    dQ^T += K^T dS^T; it also writes D.
-//  - k_attn_bwd_dkv: one workgroup per key block walks the query tiles that attend it (the
-//    selection transposed; every query tile for a special pseudo-tile) and accumulates
-//    dV^T += dO^T P and dK^T += Q^T dS.  Every key row gets exactly one writer, so the
-//    result is deterministic.
+//    (special pseudo-tiles, its selected tiles, then with landmarks the blocks of 64 tile
+//    means) like the forward and accumulates dQ^T += K^T dS^T; it also writes D.
+//  - k_attn_bwd_dkv<true> (landmarks only): one workgroup per (head, block of 64 tile means)
+//    walks every query tile and accumulates the means' gradients dvbar^T += dO^T P and
+//    dkbar^T += Q^T dS, a tile's column masked for the query tiles that selected it.
+//  - k_attn_bwd_dkv<false>: one workgroup per key block walks the query tiles that attend
+//    it (the selection transposed; every query tile for a special pseudo-tile) and
+//    accumulates dV^T += dO^T P and dK^T += Q^T dS; with landmarks it adds the means'
+//    gradients, divided by the member count, to each member row (the means are averages
+//    over the member rows).  Every output row gets exactly one writer, so the result is
+//    deterministic.
 #include <algorithm>
 
 #include "attn_common.h"
@@ -38,18 +44,25 @@ struct BwdDev {
     int kmax;
     const int32_t* t_end;
     const int32_t* t_list;
+    const void* kbar;    // landmark means [heads, Tk, 64] bf16, or null (no landmarks)
+    const void* vbar;
+    int nlm;             // blocks of 64 tile means
+    float lm_bias_l2;    // landmark logit bias in base-2 units
     float scale, scale_l2;
     float* dq;
     float* dk;
     float* dv;
     float* delta;
+    float* dkbar;        // [heads, Tk, 64], landmarks only
+    float* dvbar;
 };
 
 constexpr float LOG2E_F = 1.4426950408889634f;
 
 // Key/query row r of a 64-row block: where it lives (row within the head) and whether it
 // takes part.  kind: 0 = a frame tile t, members only (keys) or valid rows (queries);
-// 1 = special pseudo-tile t (gathered special rows of all frames).
+// 1 = special pseudo-tile t (gathered special rows of all frames); 2 = block t of the tile
+// means (rows 64 t .. 64 t + 63 of kbar/vbar), landmarks of the query tile only.
 struct Block {
     int kind, t;
     uint64_t mask;
@@ -63,12 +76,21 @@ __device__ __forceinline__ int block_row(const Lay& L, const Block& b, int r) {
     return b.t * TILE + r;
 }
 
-__device__ __forceinline__ Block key_block(const BwdDev& p, int it, int ts, const int32_t* s_idx) {
+__device__ __forceinline__ Block key_block(const BwdDev& p, int it, int ts, int c, const int32_t* s_idx,
+                                          const uint32_t* s_lm) {
     Block b;
     if (it < ts) {
         b.kind = 1;
         b.t = it;
         b.mask = range_mask(0, min(TILE, p.kl.nsp * p.kl.S - it * TILE));
+        return b;
+    }
+    if (it >= ts + c) {
+        b.kind = 2;
+        b.t = it - ts - c;
+        const uint32_t w0 = __builtin_amdgcn_readfirstlane(s_lm[2 * b.t]);
+        const uint32_t w1 = __builtin_amdgcn_readfirstlane(s_lm[2 * b.t + 1]);
+        b.mask = (uint64_t)w0 | ((uint64_t)w1 << 32);
         return b;
     }
     b.kind = 0;
@@ -124,10 +146,12 @@ __device__ __forceinline__ float dot_bf16x8(const bf16x8& a, const bf16x8& b, fl
 }  // namespace
 
 // ------------------------------------------------------------------------------ dQ
+template <bool LM>
 __global__ __launch_bounds__(128, 2) void k_attn_bwd_dq(BwdDev p) {
     __shared__ __align__(16) unsigned char s_k[2][TILE_BYTES];
     __shared__ __align__(16) unsigned char s_v[2][TILE_BYTES];
-    extern __shared__ int32_t s_idx[];
+    extern __shared__ int32_t s_idx[];                  // kmax list entries, then the bitmap
+    uint32_t* s_lm = reinterpret_cast<uint32_t*>(s_idx + p.kmax);
 
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int qc = lane & 31, g = lane >> 5;
@@ -161,20 +185,30 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dq(BwdDev p) {
     const int c = min(max(p.cnt[(size_t)h * p.Tq + tq], 0), p.kmax);
     const int32_t* myidx = p.idx + ((size_t)h * p.Tq + tq) * p.kmax;
     for (int i = tid; i < c; i += 128) s_idx[i] = myidx[i];
+    if (LM) init_landmark_bitmap(p.kl, p.Tk, p.nlm, c, myidx, s_lm, tid, 128);   // has barriers
     __syncthreads();
-    const int ntiles = p.Ts + c;
+    const int ntiles = p.Ts + c + (LM ? p.nlm : 0);
 
     const unsigned head_bytes = (unsigned)Lk * 128u;
     const __amdgpu_buffer_rsrc_t rs_k = head_rsrc(p.k, h, head_bytes);
     const __amdgpu_buffer_rsrc_t rs_v = head_rsrc(p.v, h, head_bytes);
+    // the tile means of this head: Tk rows of 128 bytes
+    const unsigned mean_bytes = (unsigned)p.Tk * 128u;
+    const __amdgpu_buffer_rsrc_t rs_kb = head_rsrc(LM ? p.kbar : p.k, h, LM ? mean_bytes : head_bytes);
+    const __amdgpu_buffer_rsrc_t rs_vb = head_rsrc(LM ? p.vbar : p.v, h, LM ? mean_bytes : head_bytes);
     TileOffsets off;
     off.init(lane);
 
     f32x16 dq0 = {}, dq1 = {};
     auto stage = [&](int it, int b) {
-        const Block kb = key_block(p, it, p.Ts, s_idx);
-        stage_block(rs_k, p.kl, kb, (lds_u8*)s_k[b], w, lane);
-        stage_block(rs_v, p.kl, kb, (lds_u8*)s_v[b], w, lane);
+        const Block kb = key_block(p, it, p.Ts, c, s_idx, s_lm);
+        if (LM && __builtin_amdgcn_readfirstlane(kb.kind) == 2) {
+            stage_block(rs_kb, p.kl, kb, (lds_u8*)s_k[b], w, lane);
+            stage_block(rs_vb, p.kl, kb, (lds_u8*)s_v[b], w, lane);
+        } else {
+            stage_block(rs_k, p.kl, kb, (lds_u8*)s_k[b], w, lane);
+            stage_block(rs_v, p.kl, kb, (lds_u8*)s_v[b], w, lane);
+        }
         return kb;
     };
     Block cur{}, nxt{};
@@ -202,12 +236,14 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dq(BwdDev p) {
             // this lane's keys 8i + 4g + (0..3) of each half, tested against constant bits
             const uint32_t w0 = __builtin_amdgcn_readfirstlane((uint32_t)cur.mask) >> (4 * g);
             const uint32_t w1 = __builtin_amdgcn_readfirstlane((uint32_t)(cur.mask >> 32)) >> (4 * g);
+            // landmark logits carry the bias
+            const float nl = (LM && __builtin_amdgcn_readfirstlane(cur.kind) == 2 ? p.lm_bias_l2 : 0.f) - lse_l2;
             f32x16 d0, d1;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const uint32_t bit = 1u << (8 * (r >> 2) + (r & 3));
-                const float pa = (w0 & bit) ? __builtin_amdgcn_exp2f(fmaf(s0[r], p.scale_l2, -lse_l2)) : 0.f;
-                const float pb = (w1 & bit) ? __builtin_amdgcn_exp2f(fmaf(s1[r], p.scale_l2, -lse_l2)) : 0.f;
+                const float pa = (w0 & bit) ? __builtin_amdgcn_exp2f(fmaf(s0[r], p.scale_l2, nl)) : 0.f;
+                const float pb = (w1 & bit) ? __builtin_amdgcn_exp2f(fmaf(s1[r], p.scale_l2, nl)) : 0.f;
                 d0[r] = pa * (p0[r] - D);
                 d1[r] = pb * (p1[r] - D);
             }
@@ -240,12 +276,19 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dq(BwdDev p) {
 }
 
 // ------------------------------------------------------------------------------ dK, dV
-// Work items: H * Ts special pseudo-tiles first (attended by every query tile, the longest
-// items), then H * Tk frame tiles, taken in launch order: workgroup i runs on XCD i % 8, so
-// the long special items spread evenly over the XCDs and all XCDs work through the same
-// head's key tiles at a time (their query tiles then share the last-level cache).  Giving
-// each XCD a contiguous range of items instead put every special item on one XCD, which
-// then carried about 40 % more work than the others.
+// MEANS = false: work items are H * Ts special pseudo-tiles first (attended by every query
+// tile, the longest items), then H * Tk frame tiles, taken in launch order: workgroup i runs
+// on XCD i % 8, so the long special items spread evenly over the XCDs and all XCDs work
+// through the same head's key tiles at a time (their query tiles then share the last-level
+// cache).  Giving each XCD a contiguous range of items instead put every special item on
+// one XCD, which then carried about 40 % more work than the others.
+// MEANS = true: work items are H * nlm blocks of 64 tile means, each walking every query
+// tile in order (all items stream the same query tiles, which then come from the cache).
+// Lane (w, kc) owns key tile t = 64 b + 32 w + kc, a landmark of every query tile that did
+// not select it; those that did are the ascending entries of t's transposed list, which the
+// lane walks in step with the loop (one comparison per query tile; the next entry loads
+// under the step's products).
+template <bool MEANS>
 __global__ __launch_bounds__(128, 2) void k_attn_bwd_dkv(BwdDev p) {
     __shared__ __align__(16) unsigned char s_q[2][TILE_BYTES];
     __shared__ __align__(16) unsigned char s_do[2][TILE_BYTES];
@@ -254,46 +297,72 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dkv(BwdDev p) {
 
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int kc = lane & 31, g = lane >> 5;
-    const int heads = gridDim.x / (p.Ts + p.Tk);
-    const int item = blockIdx.x;
-    const int nspec = heads * p.Ts;
+    const int kr = 32 * w + kc;                                  // key row within the block
+    const int Lq = p.ql.S * p.ql.P, Lk = p.kl.S * p.kl.P;
     int h;
     Block kb;
-    if (item < nspec) {
-        h = item / p.Ts;
-        kb.kind = 1;
-        kb.t = item - h * p.Ts;
-        kb.mask = range_mask(0, min(TILE, p.kl.nsp * p.kl.S - kb.t * TILE));
+    bool kvalid;
+    size_t kbase;                                                // this lane's key row (elements)
+    int sel_next = 0x7fffffff, sel_pos = 0, sel_end = 0;         // MEANS: the lane's transposed list
+    const int32_t* sel_list = nullptr;
+    if (MEANS) {
+        h = blockIdx.x / p.nlm;
+        kb.kind = 2;
+        kb.t = blockIdx.x - h * p.nlm;
+        const int t = kb.t * TILE + kr;
+        kvalid = false;
+        if (t < p.Tk) {
+            int lo, hi;
+            member_range(p.kl, t, lo, hi);
+            kvalid = hi > lo;
+            const int32_t* te = p.t_end + (size_t)h * p.Tk;
+            sel_pos = t == 0 ? 0 : te[t - 1];
+            sel_end = te[t];
+        }
+        kbase = ((size_t)h * p.Tk + min(t, p.Tk - 1)) * HD;
+        if (p.t_list) {
+            sel_list = p.t_list + (size_t)h * p.Tq * p.kmax;
+            if (sel_pos < sel_end) sel_next = sel_list[sel_pos];
+        }
     } else {
-        const int r = item - nspec;
-        h = r / p.Tk;
-        kb.kind = 0;
-        kb.t = r - h * p.Tk;
-        int lo, hi;
-        member_range(p.kl, kb.t, lo, hi);
-        kb.mask = range_mask(lo, hi);
+        const int heads = gridDim.x / (p.Ts + p.Tk);
+        const int item = blockIdx.x;
+        const int nspec = heads * p.Ts;
+        if (item < nspec) {
+            h = item / p.Ts;
+            kb.kind = 1;
+            kb.t = item - h * p.Ts;
+            kb.mask = range_mask(0, min(TILE, p.kl.nsp * p.kl.S - kb.t * TILE));
+        } else {
+            const int r = item - nspec;
+            h = r / p.Tk;
+            kb.kind = 0;
+            kb.t = r - h * p.Tk;
+            int lo, hi;
+            member_range(p.kl, kb.t, lo, hi);
+            kb.mask = range_mask(lo, hi);
+        }
+        kvalid = (kb.mask >> kr) & 1ull;
+        kbase = ((size_t)h * Lk + block_row(p.kl, kb, kr)) * HD;
     }
-    const int Lq = p.ql.S * p.ql.P, Lk = p.kl.S * p.kl.P;
-    const int kr = 32 * w + kc;                                  // key row within the block
-    const bool kvalid = (kb.mask >> kr) & 1ull;
-    const int krow = block_row(p.kl, kb, kr);                    // row within the head
     // a wave with no key row in this block stages and meets the barriers but skips the
     // products (its accumulators stay zero)
     const bool wk = __ballot(kvalid) != 0ull;
-    const size_t kbase = ((size_t)h * Lk + krow) * HD;
 
+    const void* ksrc = MEANS ? p.kbar : p.k;
+    const void* vsrc = MEANS ? p.vbar : p.v;
     bf16x8 kop[4], vop[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        kop[s] = load_b(p.k, kbase + 16 * s + 8 * g, kvalid);
-        vop[s] = load_b(p.v, kbase + 16 * s + 8 * g, kvalid);
+        kop[s] = load_b(ksrc, kbase + 16 * s + 8 * g, kvalid);
+        vop[s] = load_b(vsrc, kbase + 16 * s + 8 * g, kvalid);
     }
     __builtin_amdgcn_s_waitcnt(0);
 
     // the query tiles that attend this block
     int nq, q0 = 0;
     const int32_t* qlist = nullptr;
-    if (kb.kind == 1) {
+    if (MEANS || kb.kind == 1) {
         nq = p.Tq;
     } else {
         const int32_t* te = p.t_end + (size_t)h * p.Tk;
@@ -301,7 +370,9 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dkv(BwdDev p) {
         nq = te[kb.t] - q0;
         qlist = p.t_list + (size_t)h * p.Tq * p.kmax + q0;
     }
-    auto qtile = [&](int i) { return kb.kind == 1 ? i : __builtin_amdgcn_readfirstlane(qlist[i]); };
+    auto qtile = [&](int i) {
+        return (MEANS || kb.kind == 1) ? i : __builtin_amdgcn_readfirstlane(qlist[i]);
+    };
 
     const unsigned head_bytes = (unsigned)Lq * 128u;
     const __amdgpu_buffer_rsrc_t rs_q = head_rsrc(p.q, h, head_bytes);
@@ -349,6 +420,21 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dkv(BwdDev p) {
             stage(tn, b ^ 1);
             fetch_rows(tn, rowval);
         }
+        // exponent offset of this lane's key column: 0 for keys, the landmark bias for a
+        // tile mean that query tile i did not select, -inf (P = 0) otherwise
+        float nb = 0.f;
+        if (MEANS) {
+            while (sel_next < i) {                               // a tile listed twice in a row
+                ++sel_pos;
+                sel_next = sel_pos < sel_end ? sel_list[sel_pos] : 0x7fffffff;
+            }
+            const bool selected = sel_next == i;
+            if (selected) {
+                ++sel_pos;
+                sel_next = sel_pos < sel_end ? sel_list[sel_pos] : 0x7fffffff;
+            }
+            nb = (kvalid && !selected) ? p.lm_bias_l2 : -INFINITY;
+        }
         const unsigned char* qt = s_q[b];
         const unsigned char* dt = s_do[b];
         if (wk) {
@@ -378,8 +464,8 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dkv(BwdDev p) {
 #pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4) {
                     const int r = 4 * a + i4;
-                    pp0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], p.scale_l2, -lav[i4]));
-                    pp1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], p.scale_l2, -lbv[i4]));
+                    pp0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], p.scale_l2, nb - lav[i4]));
+                    pp1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], p.scale_l2, nb - lbv[i4]));
                     d0[r] = pp0[r] * (p0[r] - dav[i4]);
                     d1[r] = pp1[r] * (p1[r] - dbv[i4]);
                 }
@@ -402,15 +488,32 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dkv(BwdDev p) {
         if (i + 1 < nq) (tid < 64 ? s_lse[b ^ 1] : s_d[b ^ 1])[tid & 63] = rowval;
         __syncthreads();
     }
-    // write this lane's key row: member rows of a frame tile (pad rows get zeros; special
-    // rows inside the tile belong to the special pseudo-tiles), every special row of a
-    // pseudo-tile
-    bool write = kvalid;
-    if (kb.kind == 0 && !kvalid) {
-        const int j = krow % p.kl.P;
-        write = j >= p.kl.N;                                     // pad: zeros
+    float* dk_out = MEANS ? p.dkbar : p.dk;
+    float* dv_out = MEANS ? p.dvbar : p.dv;
+    // MEANS: every tile's row (zeros for tiles without members).  Otherwise member rows of a
+    // frame tile (pad rows get zeros; special rows inside the tile belong to the special
+    // pseudo-tiles) and every special row of a pseudo-tile.
+    bool write;
+    if (MEANS) {
+        write = kb.t * TILE + kr < p.Tk;
+    } else {
+        write = kvalid;
+        if (kb.kind == 0 && !kvalid) write = block_row(p.kl, kb, kr) % p.kl.P >= p.kl.N;   // pad
     }
     if (!write) return;
+    // with landmarks, a member row also takes its tile mean's gradient over the member count
+    const bool chain = !MEANS && p.dkbar != nullptr && kb.kind == 0 && kvalid;
+    float inv = 0.f;
+    const float* mk = nullptr;
+    const float* mv = nullptr;
+    if (chain) {
+        int lo, hi;
+        member_range(p.kl, kb.t, lo, hi);
+        inv = 1.f / (float)(hi - lo);
+        mk = p.dkbar + ((size_t)h * p.Tk + kb.t) * HD;
+        mv = p.dvbar + ((size_t)h * p.Tk + kb.t) * HD;
+    }
+    const float sk = kvalid ? p.scale : 0.f, sv = kvalid ? 1.f : 0.f;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
         const f32x16& ak = cb ? dk1 : dk0;
@@ -418,11 +521,18 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dkv(BwdDev p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int c0 = 32 * cb + 8 * j + 4 * g;
-            const float sk = kvalid ? p.scale : 0.f, sv = kvalid ? 1.f : 0.f;
-            *reinterpret_cast<float4*>(p.dk + kbase + c0) =
-                make_float4(ak[4 * j] * sk, ak[4 * j + 1] * sk, ak[4 * j + 2] * sk, ak[4 * j + 3] * sk);
-            *reinterpret_cast<float4*>(p.dv + kbase + c0) =
-                make_float4(av[4 * j] * sv, av[4 * j + 1] * sv, av[4 * j + 2] * sv, av[4 * j + 3] * sv);
+            float4 k4 = make_float4(ak[4 * j] * sk, ak[4 * j + 1] * sk, ak[4 * j + 2] * sk, ak[4 * j + 3] * sk);
+            float4 v4 = make_float4(av[4 * j] * sv, av[4 * j + 1] * sv, av[4 * j + 2] * sv, av[4 * j + 3] * sv);
+            if (chain) {
+                const float4 gk = *reinterpret_cast<const float4*>(mk + c0);
+                const float4 gv = *reinterpret_cast<const float4*>(mv + c0);
+                k4 = make_float4(fmaf(gk.x, inv, k4.x), fmaf(gk.y, inv, k4.y), fmaf(gk.z, inv, k4.z),
+                                 fmaf(gk.w, inv, k4.w));
+                v4 = make_float4(fmaf(gv.x, inv, v4.x), fmaf(gv.y, inv, v4.y), fmaf(gv.z, inv, v4.z),
+                                 fmaf(gv.w, inv, v4.w));
+            }
+            *reinterpret_cast<float4*>(dk_out + kbase + c0) = k4;
+            *reinterpret_cast<float4*>(dv_out + kbase + c0) = v4;
         }
     }
 }
@@ -596,16 +706,34 @@ hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t st) {
     d.kmax = a.kmax;
     d.t_end = a.t_end;
     d.t_list = a.t_list;
+    const bool lm = a.kbar != nullptr;
+    d.kbar = a.kbar;
+    d.vbar = a.vbar;
+    d.nlm = lm ? (d.Tk + TILE - 1) / TILE : 0;
+    d.lm_bias_l2 = a.landmark_bias * LOG2E_F;
     d.scale = a.scale;
     d.scale_l2 = a.scale * LOG2E_F;
     d.dq = a.dq;
     d.dk = a.dk;
     d.dv = a.dv;
     d.delta = a.delta;
-    hipLaunchKernelGGL(k_attn_bwd_dq, dim3((unsigned)(a.heads * d.Tq)), dim3(128), (size_t)a.kmax * 4, st, d);
+    d.dkbar = lm ? a.dkbar : nullptr;
+    d.dvbar = lm ? a.dvbar : nullptr;
+    const size_t shm = ((size_t)a.kmax + 2 * (size_t)d.nlm) * 4;
+    const dim3 gq((unsigned)(a.heads * d.Tq));
+    if (lm)
+        hipLaunchKernelGGL(k_attn_bwd_dq<true>, gq, dim3(128), shm, st, d);
+    else
+        hipLaunchKernelGGL(k_attn_bwd_dq<false>, gq, dim3(128), shm, st, d);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_attn_bwd_dkv, dim3((unsigned)(a.heads * (d.Ts + d.Tk))), dim3(128), 0, st, d);
+    // the means' gradients first: the dK/dV kernel adds them to the member rows
+    if (lm) {
+        hipLaunchKernelGGL(k_attn_bwd_dkv<true>, dim3((unsigned)(a.heads * d.nlm)), dim3(128), 0, st, d);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_attn_bwd_dkv<false>, dim3((unsigned)(a.heads * (d.Ts + d.Tk))), dim3(128), 0, st, d);
     return hipGetLastError();
 }
 

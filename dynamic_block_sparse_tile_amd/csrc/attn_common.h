@@ -145,17 +145,18 @@ __device__ __forceinline__ int src_row(const AttnDev& p, const TileDesc& d, int 
 }
 
 
-__device__ __forceinline__ void init_landmark_bitmap(const AttnDev& p, int c, const int32_t* myidx,
+// Bitmap of the landmarks of one query tile, 2 * nlm words: bit t set <=> key tile t has
+// member rows and is not among the c entries of `list` (the tile's selection).
+__device__ __forceinline__ void init_landmark_bitmap(const Lay& kl, int Tk, int nlm, int c, const int32_t* list,
                                                      uint32_t* s_lm, int tid, int nthreads) {
-    // bit t set <=> key tile t has member rows and is not selected (a landmark)
-    const int nw = 2 * p.nlm;
+    const int nw = 2 * nlm;
     for (int i = tid; i < nw; i += nthreads) {
         uint32_t bits = 0;
         for (int b = 0; b < 32; ++b) {
             const int t = i * 32 + b;
-            if (t < p.Tk) {
+            if (t < Tk) {
                 int lo, hi;
-                member_range(p.kl, t, lo, hi);
+                member_range(kl, t, lo, hi);
                 if (hi > lo) bits |= 1u << b;
             }
         }
@@ -163,8 +164,8 @@ __device__ __forceinline__ void init_landmark_bitmap(const AttnDev& p, int c, co
     }
     __syncthreads();
     for (int i = tid; i < c; i += nthreads) {
-        const int t = myidx[i];
-        if (t >= 0 && t < p.Tk) atomicAnd(&s_lm[t >> 5], ~(1u << (t & 31)));
+        const int t = list[i];
+        if (t >= 0 && t < Tk) atomicAnd(&s_lm[t >> 5], ~(1u << (t & 31)));
     }
     __syncthreads();
 }

@@ -60,11 +60,16 @@ struct BwdArgs {
     int kmax;
     const int32_t* t_end;
     const int32_t* t_list;
+    const void* kbar;   // landmark means (bf16); landmarks on iff non-null
+    const void* vbar;
+    float landmark_bias;
     float scale;
     float* dq;
     float* dk;
     float* dv;
     float* delta;
+    float* dkbar;       // gradients of the means (landmarks only)
+    float* dvbar;
 };
 hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t st);
 hipError_t launch_selection_transpose(const int32_t* idx, const int32_t* cnt, int heads, int tq, int tk,

@@ -219,24 +219,34 @@ int validate_attn_bwd(const void* q, const void* k, const void* v, const void* o
                       const float* lse, int dtype, int32_t heads, int32_t head_dim, int32_t tile,
                       const sparse3d_layout* qlay, const sparse3d_layout* klay, const int32_t* idx,
                       const int32_t* cnt, int32_t kmax, const int32_t* t_end, const int32_t* t_list,
-                      float scale, const float* dq, const float* dk, const float* dv, const float* delta) {
+                      const void* kbar, const void* vbar, float landmark_bias, float scale,
+                      const float* dq, const float* dk, const float* dv, const float* delta,
+                      const float* dkbar, const float* dvbar) {
     if (!out || !dout || !lse || !t_end || !dq || !dk || !dv || !delta) return SPARSE3D_ERR_NULL;
     if (kmax > 0 && !t_list) return SPARSE3D_ERR_NULL;
+    const bool lm = kbar != nullptr;
+    if (lm && (!dkbar || !dvbar)) return SPARSE3D_ERR_NULL;
     S3D_TRY(validate_attn(true, q, k, v, dtype, heads, head_dim, tile, qlay, klay, idx, cnt, kmax,
-                          nullptr, nullptr, dq, SPARSE3D_F32, nullptr));
+                          kbar, vbar, dq, SPARSE3D_F32, nullptr));
     if (dtype != SPARSE3D_BF16) return SPARSE3D_ERR_UNSUPPORTED;
-    if (kmax > kMaxBwdList || lay_tiles(*qlay) > kMaxTransposeQ) return SPARSE3D_ERR_UNSUPPORTED;
-    S3D_TRY(check_logit_params(scale, 0.f));
+    if (kmax > (lm ? kMaxBwdListLm : kMaxBwdList) || lay_tiles(*qlay) > kMaxTransposeQ)
+        return SPARSE3D_ERR_UNSUPPORTED;
+    S3D_TRY(check_logit_params(scale, lm ? landmark_bias : 0.f));
     const size_t qb = size_t(heads) * lay_rows(*qlay) * head_dim;     // elements
     const size_t kb = size_t(heads) * lay_rows(*klay) * head_dim;
+    const size_t mb = lm ? size_t(heads) * lay_tiles(*klay) * head_dim : 0;
     const size_t lb = size_t(heads) * lay_rows(*qlay) * 4;
     const size_t ib = size_t(heads) * lay_tiles(*qlay) * kmax * 4;
     const size_t cb = size_t(heads) * lay_tiles(*qlay) * 4, eb = size_t(heads) * lay_tiles(*klay) * 4;
-    const void* p[14] = {q, k, v, out, dout, lse, idx, cnt, t_end, t_list, dq, dk, dv, delta};
-    const size_t n[14] = {qb * 2, kb * 2, kb * 2, qb * 2, qb * 2, lb, ib, cb, eb, ib, qb * 4, kb * 4, kb * 4, lb};
-    // outputs (the last four) against everything else and each other; q may equal k (self-attention)
-    for (int i = 10; i < 14; ++i)
-        for (int j = 0; j < 14; ++j)
+    // inputs first, then the outputs
+    constexpr int NIN = 12, NP = 18;
+    const void* p[NP] = {q,  k,  v,  out,  dout,  lse,   idx,   cnt,   t_end,  t_list,
+                         kbar, vbar, dq, dk, dv, delta, lm ? dkbar : nullptr, lm ? dvbar : nullptr};
+    const size_t n[NP] = {qb * 2, kb * 2, kb * 2, qb * 2, qb * 2, lb,     ib,     cb, eb,
+                          ib,     mb * 2, mb * 2, qb * 4, kb * 4, kb * 4, lb, mb * 4, mb * 4};
+    // every output against everything else; inputs may share memory (q may equal k)
+    for (int i = NIN; i < NP; ++i)
+        for (int j = 0; j < NP; ++j)
             if (j != i && overlaps(p[i], n[i], p[j], n[j])) return SPARSE3D_ERR_ALIAS;
     return SPARSE3D_OK;
 }

@@ -65,10 +65,15 @@ int validate_attn_bwd(const void* q, const void* k, const void* v, const void* o
                       const float* lse, int dtype, int32_t heads, int32_t head_dim, int32_t tile,
                       const sparse3d_layout* qlay, const sparse3d_layout* klay, const int32_t* idx,
                       const int32_t* cnt, int32_t kmax, const int32_t* t_end, const int32_t* t_list,
-                      float scale, const float* dq, const float* dk, const float* dv, const float* delta);
+                      const void* kbar, const void* vbar, float landmark_bias, float scale,
+                      const float* dq, const float* dk, const float* dv, const float* delta,
+                      const float* dkbar, const float* dvbar);
 
-// Longest tile list the backward's dQ kernel stages in LDS.
+// Longest tile list the backward's dQ kernel stages in LDS (32 KiB of tile buffers beside
+// it); with landmarks the landmark bitmap (at most kMaxTopkTiles / 8 bytes) shares that
+// room, so the list is shorter.
 constexpr int kMaxBwdList = 8000;
+constexpr int kMaxBwdListLm = 7800;
 // Most query tiles the selection transpose sorts per key tile (LDS bitonic sort).
 constexpr int kMaxTransposeQ = 16384;
 

@@ -71,7 +71,8 @@ _SIGS = {
                                  _vp], ctypes.c_int),
     "sparse3d_selection_transpose": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
     "sparse3d_sparse_attn_bwd": ([_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32, _LP, _LP,
-                                  _vp, _vp, _i32, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+                                  _vp, _vp, _i32, _vp, _vp, _vp, _vp, _f32, _f32, _vp, _vp, _vp, _vp,
+                                  _vp, _vp, _vp], ctypes.c_int),
     "sparse3d_subsample_layout": ([_LP, _i32, _i32, _i32, _i32, _LP], ctypes.c_int),
     "sparse3d_grid_subsample_kv": ([_vp, _vp, ctypes.c_int, _i32, _i32, _LP, _i32, _i32, _i32,
                                     _vp, _vp, _LP, _vp], ctypes.c_int),
@@ -414,9 +415,11 @@ def sparse3d_selection_transpose(idx: torch.Tensor, cnt: torch.Tensor, k_tiles: 
 
 
 def sparse3d_sparse_attn_bwd(q, k, v, out, dout, lse, qlay, klay, idx, cnt, t_end, t_list,
+                             kbar=None, vbar=None, landmark_bias: float = LN64,
                              scale: Optional[float] = None):
-    """Gradients of the sparse attention (no landmarks), selection fixed.
-    Returns (dq, dk, dv, delta), fp32."""
+    """Gradients of the sparse attention, selection fixed.  Returns (dq, dk, dv, delta), fp32;
+    with landmarks (kbar/vbar as given to the forward) (dq, dk, dv, delta, dkbar, dvbar),
+    where dk/dv already include the means' gradients spread over the member rows."""
     H = _operands(q, k, v, qlay, klay)
     if idx.dim() != 3:
         raise ValueError(f"idx must be [heads, q_tiles, kmax], got shape {tuple(idx.shape)}")
@@ -428,23 +431,33 @@ def sparse3d_sparse_attn_bwd(q, k, v, out, dout, lse, qlay, klay, idx, cnt, t_en
     _expect(lse, "lse", q.shape[:2], _F32)
     _expect(t_end, "t_end", (H, Tk), _I32)
     _expect(t_list, "t_list", (H, Tq * idx.shape[2]), _I32)
-    _same_device(q, out, dout, lse, idx, cnt, t_end, t_list)
+    if (kbar is None) != (vbar is None):
+        raise ValueError("kbar and vbar go together")
+    _expect(kbar, "kbar", (H, Tk, HEAD_DIM), (q.dtype,))
+    _expect(vbar, "vbar", (H, Tk, HEAD_DIM), (q.dtype,))
+    _same_device(q, out, dout, lse, idx, cnt, t_end, t_list, kbar, vbar)
     for x, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout"), (lse, "lse"),
                  (idx, "idx"), (cnt, "cnt"), (t_end, "t_end"), (t_list, "t_list")):
         _dev(x, n)
+    if kbar is not None:
+        _dev(kbar, "kbar"), _dev(vbar, "vbar")
     scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else scale
     f = dict(device=q.device, dtype=torch.float32)
     dq = torch.empty(q.shape, **f)
     dk = torch.empty(k.shape, **f)
     dv = torch.empty(v.shape, **f)
     delta = torch.empty(q.shape[:2], **f)
+    dkbar = torch.empty((H, Tk, HEAD_DIM), **f) if kbar is not None else None
+    dvbar = torch.empty((H, Tk, HEAD_DIM), **f) if kbar is not None else None
     ql, kl = _lay(qlay), _lay(klay)
     kmax = idx.shape[2]
     _check(library().sparse3d_sparse_attn_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _dt(q), H, q.shape[2], TILE,
         ctypes.byref(ql), ctypes.byref(kl), _ptr(idx) if kmax > 0 else None, _ptr(cnt), kmax,
-        _ptr(t_end), _ptr(t_list) if kmax > 0 else None, scale, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta),
-        _stream(q)))
+        _ptr(t_end), _ptr(t_list) if kmax > 0 else None, _ptr(kbar), _ptr(vbar), landmark_bias, scale,
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), _ptr(dkbar), _ptr(dvbar), _stream(q)))
+    if kbar is not None:
+        return dq, dk, dv, delta, dkbar, dvbar
     return dq, dk, dv, delta
 
 

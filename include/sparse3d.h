@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define SPARSE3D_ABI_VERSION 3
+#define SPARSE3D_ABI_VERSION 4
 
 typedef enum { SPARSE3D_F32 = 0, SPARSE3D_BF16 = 1 } sparse3d_dtype;
 
@@ -194,26 +194,40 @@ int sparse3d_selection_transpose(const int32_t* idx, const int32_t* cnt, int32_t
                                  void* stream);
 
 /*
- * Backward of sparse3d_sparse_attn_fwd without landmarks, for training through the sparse
- * layer (Zebra3D abstract: post-conversion training; EPFL "(Full) Attention is More Than
- * You Need": sparse training).  The selection is held fixed (top-k is piecewise constant,
- * no gradient flows into the scores).  Inputs: q, k, v, the forward's out and the output
- * cotangent dout (all bf16, layouts as in the forward), the forward's lse, the selection
- * idx/cnt and its transpose t_end/t_list (sparse3d_selection_transpose).  With P the
- * softmax weights and D = rowsum(dout * out):
+ * Backward of sparse3d_sparse_attn_fwd, for training through the sparse layer (Zebra3D
+ * abstract: landmark summaries, post-conversion training; EPFL "(Full) Attention is More
+ * Than You Need": sparse training).  The selection is held fixed (top-k is piecewise
+ * constant, no gradient flows into the scores).  Inputs: q, k, v, the forward's out and the
+ * output cotangent dout (all bf16, layouts as in the forward), the forward's lse, the
+ * selection idx/cnt and its transpose t_end/t_list (sparse3d_selection_transpose).  With P
+ * the softmax weights and D = rowsum(dout * out):
  *   dS = P * (dout V^T - D),  dq = scale dS K,  dk = scale dS^T Q,  dv = P^T dout
  * (special keys are attended by every query, member keys by the query tiles that selected
  * their tile).  Outputs, fp32 and fully overwritten: dq [heads, Lq, 64] (0 on rows that
  * are not valid queries), dk and dv [heads, Lk, 64] (0 on pad rows and on keys nobody
- * attends), delta [heads, Lq] = D (0 on invalid rows).  bf16 operands only
- * (SPARSE3D_ERR_UNSUPPORTED for F32), kmax <= 8000, Tq <= 16384.  Deterministic.
+ * attends), delta [heads, Lq] = D (0 on invalid rows).
+ *
+ * Landmarks (kbar and vbar non-NULL, as passed to the forward, with its landmark_bias):
+ * each tile t with member rows that a query tile did not select is one more key of its
+ * rows, kbar[h,t] with value vbar[h,t] and the logit bias.  dkbar and dvbar [heads, Tk, 64]
+ * fp32 (required then, fully overwritten) receive the gradients with respect to the means,
+ *   dkbar[t] = scale sum_i dS_it q_i,  dvbar[t] = sum_i P_it dout_i
+ * (0 for tiles without member rows), and since the forward's means are the averages of
+ * K and V over the tile's member rows M(t), dk and dv of every member row also receive
+ * dkbar[t] / |M(t)| and dvbar[t] / |M(t)|: dk and dv are then the gradients with respect
+ * to K and V through both routes.  dkbar/dvbar NULL with landmarks on: SPARSE3D_ERR_NULL.
+ *
+ * bf16 operands only (SPARSE3D_ERR_UNSUPPORTED for F32), kmax <= 8000 (7800 with
+ * landmarks), Tq <= 16384.  Deterministic: every output element has one writer and a
+ * fixed summation order.
  */
 int sparse3d_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                              const float* lse, sparse3d_dtype dtype, int32_t heads, int32_t head_dim,
                              int32_t tile, const sparse3d_layout* qlay, const sparse3d_layout* klay,
                              const int32_t* idx, const int32_t* cnt, int32_t kmax, const int32_t* t_end,
-                             const int32_t* t_list, float scale, float* dq, float* dk, float* dv,
-                             float* delta, void* stream);
+                             const int32_t* t_list, const void* kbar, const void* vbar, float landmark_bias,
+                             float scale, float* dq, float* dk, float* dv, float* delta, float* dkbar,
+                             float* dvbar, void* stream);
 
 /*
  * The mean key and mean value of every patch row the grid subsample (grid_h, grid_w,

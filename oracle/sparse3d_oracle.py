@@ -311,7 +311,8 @@ def sparse_attend_bwd(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarra
     softmax weights and of dS propagates (same shapes as the gradients):
       M_ij = P_ij (|dP_ij - D_i| + A_D_i),  A_D_i = sum_c |dO_ic| (|O_ic| + sum_j P_ij |V_jc|),
       dQ: scale sum_j M_ij |K_j|;  dK: scale sum_i M_ij |Q_i|;  dV: sum_i P_ij |dO_i|;  D: A_D
-    (landmark columns chained to member rows like the gradients)."""
+    (landmark columns chained to member rows like the gradients, and, with landmarks, kept
+    per mean as "dkbar" / "dvbar")."""
     H, Lq, d = Q.shape
     Tk = klay.rows // tile
     qv = query_rows(qlay)
@@ -374,18 +375,21 @@ def sparse_attend_bwd(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarra
                 mag["D"][h, rows_q] = AD
     if kbar is not None:
         # the mean pool: each member row of tile t receives 1/|M(t)| of the mean's gradient
+        # (heads that were not processed have no mean gradients)
         rows_t = [t * tile + np.nonzero(mem[t])[0] for t in range(Tk)]
-        for t in range(Tk):
-            if kcount[t] > 0:
-                dK[:, rows_t[t]] += dkb[:, t, None, :] / kcount[t]
-                dV[:, rows_t[t]] += dvb[:, t, None, :] / kcount[t]
-                if magnitudes:
-                    mag["dK"][:, rows_t[t]] += mkb[:, t, None, :] / kcount[t]
-                    mag["dV"][:, rows_t[t]] += mvb[:, t, None, :] / kcount[t]
+        for h in (range(H) if heads is None else heads):
+            for t in range(Tk):
+                if kcount[t] > 0:
+                    dK[h, rows_t[t]] += dkb[h, t] / kcount[t]
+                    dV[h, rows_t[t]] += dvb[h, t] / kcount[t]
+                    if magnitudes:
+                        mag["dK"][h, rows_t[t]] += mkb[h, t] / kcount[t]
+                        mag["dV"][h, rows_t[t]] += mvb[h, t] / kcount[t]
     res = (dQ, dK, dV, D)
     if means:
         res = res + (dkb, dvb)
     if magnitudes:
+        mag["dkbar"], mag["dvbar"] = mkb, mvb
         res = res + (mag,)
     return res
 

@@ -753,10 +753,28 @@ def pin_backward_magnitudes_bound_the_gradients(o):
     for lm in (False, True):
         Q, K, V, dO, lay, idx, cnt, kbar, vbar, kc = _landmark_bwd_case(o, 2, 60, 64, 5, 16, 2, seed=9)
         kw = dict(kbar=kbar, vbar=vbar, kcount=kc) if lm else {}
-        *g, mag = o.sparse_attend_bwd(Q, K, V, dO, lay, lay, 16, idx, cnt, 0.3, magnitudes=True, **kw)
-        for x, n in zip(g, ("dQ", "dK", "dV", "D")):
+        *g, mag = o.sparse_attend_bwd(Q, K, V, dO, lay, lay, 16, idx, cnt, 0.3, magnitudes=True, means=True, **kw)
+        for x, n in zip(g, ("dQ", "dK", "dV", "D", "dkbar", "dvbar")):
             assert np.all(np.abs(x) <= mag[n] * (1 + 1e-12) + 1e-300), n
             assert np.all(mag[n][x != 0] > 0), n
+
+
+def pin_backward_gradient_sums(o):
+    """Sums fixed by the softmax: each valid row's weights over all its keys (landmark
+    means included) add to 1, so the value gradients of all keys add to the sum of the
+    cotangents of the valid rows; dS_i sums to P_i . dP_i - D_i = 0 over a row, so the key
+    gradients add to 0.  Through the mean pool a mean's gradient reaches its member rows
+    divided by their count, so the sums over K and V rows are the same as over the keys."""
+    for lm in (False, True):
+        for (S, N, P, nsp, tile, k) in [(2, 60, 64, 5, 16, 2), (3, 40, 48, 2, 16, 1)]:
+            Q, K, V, dO, lay, idx, cnt, kbar, vbar, kc = _landmark_bwd_case(o, S, N, P, nsp, tile, k, seed=N + 7)
+            kw = dict(kbar=kbar, vbar=vbar, kcount=kc) if lm else {}
+            dQ, dK, dV, D, dkb, dvb = o.sparse_attend_bwd(Q, K, V, dO, lay, lay, tile, idx, cnt, 0.3, means=True,
+                                                          **kw)
+            qv = (np.arange(lay.rows) % lay.stride) < lay.tokens
+            for h in range(Q.shape[0]):
+                assert np.allclose(dV[h].sum(axis=0), dO[h][qv].sum(axis=0), rtol=0, atol=1e-10)
+                assert np.allclose(dK[h].sum(axis=0), 0.0, rtol=0, atol=1e-10)
 
 
 def pin_select_mask_equals_per_row_rule(o):
@@ -797,6 +815,7 @@ def pin_selection_transpose(o):
 
 
 ALL_PINS = [
+    pin_backward_gradient_sums,
     pin_block_mean_identity, pin_tile_constant_pool, pin_symmetric_scores,
     pin_select_brute_force, pin_select_invariants,
     pin_dense_matches_library, pin_all_tiles_is_dense, pin_closed_forms,

@@ -1,6 +1,7 @@
 """The C ABI on the CPU: the library loads, exports every declared symbol, and
 rejects bad arguments on the host before touching the GPU."""
 import ctypes
+import math
 import os
 import re
 
@@ -41,7 +42,7 @@ def test_library_resolves_every_symbol_at_load():
 
 
 def test_version_and_status(lib):
-    assert lib.sparse3d_abi_version() == 3
+    assert lib.sparse3d_abi_version() == 4
     for st in range(6):
         assert lib.sparse3d_status_string(st)
     assert lib.sparse3d_status_string(99) == b"unknown status"
@@ -207,10 +208,11 @@ def test_backward_validation(lib):
     ql = L()
     def bwd(q=FAKE, out=FAKE + 3 * 10**9, dout=FAKE + 4 * 10**9, lse=FAKE + 5 * 10**9, dt=1, kmax=8,
             dq=FAKE + 9 * 10**9, dk=FAKE + 10 * 10**9, dv=FAKE + 11 * 10**9, delta=FAKE + 12 * 10**9,
-            scale=0.125, d=64):
+            scale=0.125, d=64, kbar=NULL, vbar=NULL, bias=math.log(64.0), dkbar=NULL, dvbar=NULL):
         return lib.sparse3d_sparse_attn_bwd(q, FAKE + 10**9, FAKE + 2 * 10**9, out, dout, lse, dt, 2, d, 64,
                                             ql, ql, FAKE + 6 * 10**9, FAKE + 7 * 10**9, kmax,
-                                            FAKE + 8 * 10**9, FAKE + 13 * 10**9, scale, dq, dk, dv, delta, NULL)
+                                            FAKE + 8 * 10**9, FAKE + 13 * 10**9, kbar, vbar, bias, scale,
+                                            dq, dk, dv, delta, dkbar, dvbar, NULL)
     assert bwd(out=NULL) == ERR_NULL
     assert bwd(lse=NULL) == ERR_NULL
     assert bwd(delta=NULL) == ERR_NULL
@@ -220,6 +222,24 @@ def test_backward_validation(lib):
     assert bwd(dq=FAKE + 64) == ERR_ALIAS                                  # dq inside q
     assert bwd(dk=FAKE + 9 * 10**9 + 64) == ERR_ALIAS                     # dk inside dq
     assert bwd(delta=FAKE + 5 * 10**9 + 4) == ERR_ALIAS                   # delta inside lse
+    assert bwd(kmax=8001) == ERR_UNSUP
+    # landmarks: means in, their gradients out
+    lm = dict(kbar=FAKE + 14 * 10**9, vbar=FAKE + 15 * 10**9, dkbar=FAKE + 16 * 10**9, dvbar=FAKE + 17 * 10**9)
+    # a call that passed every check would launch on these fake addresses: the cases that
+    # must get past a check end on the aliasing test, which comes last
+    late = dict(delta=FAKE + 5 * 10**9 + 4)                                # delta inside lse
+    assert bwd(**lm, **late) == ERR_ALIAS
+    assert bwd(**{**lm, "vbar": NULL}) == ERR_NULL                         # kbar without vbar
+    assert bwd(**{**lm, "dkbar": NULL}) == ERR_NULL                        # no room for the gradients
+    assert bwd(**{**lm, "dvbar": NULL}) == ERR_NULL
+    assert bwd(**{**lm, "bias": math.inf}) == ERR_UNSUP
+    assert bwd(bias=math.inf, **late) == ERR_ALIAS                         # no landmarks: bias unused
+    assert bwd(**{**lm, "kmax": 7801}) == ERR_UNSUP                        # list + bitmap exceed LDS
+    assert bwd(**{**lm, "kmax": 7800}, **late) == ERR_ALIAS
+    assert bwd(**{**lm, "dkbar": FAKE + 14 * 10**9 + 128}) == ERR_ALIAS   # dkbar inside kbar
+    assert bwd(**{**lm, "dvbar": FAKE + 16 * 10**9 + 4}) == ERR_ALIAS     # dvbar inside dkbar
+    assert bwd(**{**lm, "dk": FAKE + 17 * 10**9}) == ERR_ALIAS            # dk on dvbar
+    assert bwd(**{**lm, "dq": FAKE + 15 * 10**9}) == ERR_ALIAS            # dq on vbar
 
 
 def test_cast_validation(lib):
@@ -341,6 +361,14 @@ def test_binding_checks_shapes_and_dtypes_before_the_device():
         bwd(t_list=_cpu(2, 63, dtype=torch.int32))
     with pytest.raises(ValueError, match="device"):
         bwd()
+    with pytest.raises(ValueError, match="kbar and vbar"):
+        S.sparse3d_sparse_attn_bwd(q, q, q, q, q, _cpu(2, 512, dtype=torch.float32), lay, lay, idx, cnt,
+                                   _cpu(2, 8, dtype=torch.int32), _cpu(2, 64, dtype=torch.int32),
+                                   kbar=_cpu(2, 8, 64))
+    with pytest.raises(TypeError, match="vbar"):
+        S.sparse3d_sparse_attn_bwd(q, q, q, q, q, _cpu(2, 512, dtype=torch.float32), lay, lay, idx, cnt,
+                                   _cpu(2, 8, dtype=torch.int32), _cpu(2, 64, dtype=torch.int32),
+                                   kbar=_cpu(2, 8, 64), vbar=_cpu(2, 8, 64, dtype=torch.float32))
     sga = S.Sga((16, 16), 2, kmean=_cpu(2, 63, dtype=torch.float32), vmean=_cpu(2, 64, dtype=torch.float32))
     with pytest.raises(ValueError, match="kmean"):
         S.sparse3d_dense_attn_fwd(q, q, q, lay, sga=sga)

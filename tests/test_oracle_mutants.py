@@ -51,8 +51,8 @@ MUTANTS = {
     "bwd_without_rowsum": ("ds = p * (dp - Di[:, None])", "ds = p * dp"),
     "bwd_dk_unscaled": ("gk, gv = scale * (ds.T @ q), p.T @ g", "gk, gv = ds.T @ q, p.T @ g"),
     "bwd_dv_from_ds": ("gk, gv = scale * (ds.T @ q), p.T @ g", "gk, gv = scale * (ds.T @ q), ds.T @ g"),
-    "bwd_landmark_mean_not_divided": ("dK[:, rows_t[t]] += dkb[:, t, None, :] / kcount[t]",
-                                      "dK[:, rows_t[t]] += dkb[:, t, None, :]"),
+    "bwd_landmark_mean_not_divided": ("dK[h, rows_t[t]] += dkb[h, t] / kcount[t]",
+                                      "dK[h, rows_t[t]] += dkb[h, t]"),
     "bwd_landmark_bias_dropped": ("s = scale * (q @ kk.T) + bias", "s = scale * (q @ kk.T)"),
     "bwd_landmark_value_grad_lost": ("dvb[h, lm] += gv[J.size:]", "pass"),
     "bwd_landmarks_include_selected": ("lm = np.nonzero(~chosen & (kcount > 0))[0]\n                kk = ",

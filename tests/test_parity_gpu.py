@@ -765,3 +765,133 @@ def test_backward_full_s128_sampled():
         mem = j[oracle.member_rows(ol)[j]]
         _grad_bound(dk[h, mem].cpu().numpy(), rdk[h, mem], mag["dK"][h, mem], ("dK", h, t))
         _grad_bound(dv[h, mem].cpu().numpy(), rdv[h, mem], mag["dV"][h, mem], ("dV", h, t))
+
+
+# ----------------------------------------------------------------- backward with landmarks
+# The landmark keys are the tile means kbar/vbar, rounded to bf16 once (the precision the
+# matrix cores read) and handed to both sides, so the bound above covers them unchanged: a
+# landmark column enters dQ, D and its own gradients exactly like a key, dkbar like dK
+# (constant 3) and dvbar like dV (constant 2); the chain into member rows divides by the
+# member count in fp32, and the oracle's magnitudes carry the same chain.
+_BWD_C.update({"dkbar": 3.0, "dvbar": 2.0})
+
+
+def _bwd_lm_setup(w, seed, k=None):
+    inp = synth.make_inputs(w, seed=seed)
+    q, v = to_dev(inp.q, torch.bfloat16), to_dev(inp.v, torch.bfloat16)
+    lay = w.layout
+    ol = oracle.Layout(*lay)
+    tpf = lay[2] // 64
+    kb, kc = oracle.tile_pool(inp.k, ol, 64, "key")
+    vb, _ = oracle.tile_pool(inp.v, ol, 64, "key")
+    kb16 = synth.round_bf16(kb.astype(np.float32))
+    vb16 = synth.round_bf16(vb.astype(np.float32))
+    kbar, vbar = to_dev(kb16, torch.bfloat16), to_dev(vb16, torch.bfloat16)
+    _, _, _, sc = S.sparse3d_tile_scores(q, q, lay)
+    idx, cnt = S.sparse3d_select_topk(sc, w.k if k is None else k, tpf, w.anchor)
+    out, lse = S.sparse3d_sparse_attn_fwd(q, q, v, lay, lay, idx, cnt, kbar=kbar, vbar=vbar, return_lse=True)
+    rng = np.random.default_rng(seed + 100)
+    dO = synth.round_bf16(rng.standard_normal(inp.q.shape).astype(np.float32))
+    dout = to_dev(dO, torch.bfloat16)
+    t_end, t_list = S.sparse3d_selection_transpose(idx, cnt, sc.shape[2])
+    grads = S.sparse3d_sparse_attn_bwd(q, q, v, out, dout, lse, lay, lay, idx, cnt, t_end, t_list,
+                                       kbar=kbar, vbar=vbar)
+    torch.cuda.synchronize()
+    means = dict(kbar=kb16.astype(np.float64), vbar=vb16.astype(np.float64), kcount=kc)
+    return inp, dO, idx.cpu().numpy(), cnt.cpu().numpy(), t_end, t_list, grads, means, ol
+
+
+def _sum_invariants(dO, ol, dk, dv):
+    """Whole-tensor properties of the gradients that hold at any size (pinned on the oracle):
+    every valid row's softmax weights sum to 1, so the value gradients of all keys (landmark
+    means included, through the chain into member rows) sum to the cotangents of the valid
+    rows, and the rows of dS sum to 0, so the key gradients sum to 0.  Rounding errors of
+    random sign stay far below 2^-5 of the norm of what is summed; a key block or the chain
+    left out moves the sums by a sizeable fraction of it."""
+    qv = oracle.query_rows(ol)
+    for h in range(dk.shape[0]):
+        g = dO[h][qv].astype(np.float64)
+        want_v, got_v = g.sum(axis=0), dv[h].astype(np.float64).sum(axis=0)
+        tol_v = 2.0 ** -5 * np.sqrt((g ** 2).sum(axis=0))
+        assert np.all(np.abs(got_v - want_v) <= tol_v), (h, float(np.max(np.abs(got_v - want_v) / tol_v)))
+        kk = dk[h].astype(np.float64)
+        got_k, tol_k = kk.sum(axis=0), 2.0 ** -5 * np.sqrt((kk ** 2).sum(axis=0))
+        assert np.all(np.abs(got_k) <= tol_k), (h, float(np.max(np.abs(got_k) / tol_k)))
+
+
+@pytest.mark.parametrize("seed,k,heads", [(21, None, None), (22, 0, [0, 5]), (23, 60, [3, 9])])
+def test_backward_landmarks_vggt_s8(seed, k, heads):
+    # heads = None: every head; otherwise those heads, each complete
+    w = synth.WORKLOADS["vggt_s8"]
+    say(f"[case] backward with landmarks vggt_s8 seed={seed} k={k} heads={heads}")
+    inp, dO, g_idx, g_cnt, *_, grads, means, ol = _bwd_lm_setup(w, seed, k)
+    dq, dk, dv, delta, dkbar, dvbar = (x.cpu().numpy() for x in grads)
+    rdq, rdk, rdv, rD, rdkb, rdvb, mag = oracle.sparse_attend_bwd(
+        inp.q, inp.k, inp.v, dO, ol, ol, 64, g_idx, g_cnt, 0.125, **means, heads=heads, means=True,
+        magnitudes=True)
+    hs = list(range(w.heads)) if heads is None else heads
+    for n, g, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv), ("D", delta, rD),
+                    ("dkbar", dkbar, rdkb), ("dvbar", dvbar, rdvb)):
+        worst, fro = _grad_bound(g[hs], r[hs], mag[n][hs], n)
+        say(f"  {n}: max err / bound {worst:.3f}, relative Frobenius error {fro:.2e}")
+    qv = oracle.query_rows(ol)
+    assert np.all(dq[:, ~qv] == 0) and np.all(dk[:, ~qv] == 0) and np.all(dv[:, ~qv] == 0)
+    empty = means["kcount"] == 0
+    assert np.all(dkbar[:, empty] == 0) and np.all(dvbar[:, empty] == 0)
+    _sum_invariants(dO, ol, dk, dv)
+
+
+def test_backward_landmarks_vggt_s32_one_head():
+    # 32 views at about 90 % sparsity: 704 query tiles per head with ragged member ranges;
+    # head 1 checked completely (every query tile contributes to its key and mean gradients)
+    w = synth.WORKLOADS["vggt_s32"]
+    say("[case] backward with landmarks vggt_s32 (k=45), head 1 complete")
+    inp, dO, g_idx, g_cnt, *_, grads, means, ol = _bwd_lm_setup(w, seed=24, k=45)
+    ref = oracle.sparse_attend_bwd(inp.q, inp.k, inp.v, dO, ol, ol, 64, g_idx, g_cnt, 0.125, **means,
+                                   heads=[1], means=True, magnitudes=True)
+    rdq, rdk, rdv, rD, rdkb, rdvb, mag = ref
+    for n, g, r in zip(("dQ", "dK", "dV", "D", "dkbar", "dvbar"), grads, (rdq, rdk, rdv, rD, rdkb, rdvb)):
+        worst, fro = _grad_bound(g[1].cpu().numpy(), r[1], mag[n][1], n)
+        say(f"  {n}: max err / bound {worst:.3f}, relative Frobenius error {fro:.2e}")
+    _sum_invariants(dO, ol, grads[1].cpu().numpy(), grads[2].cpu().numpy())
+
+
+@pytest.mark.timeout(300)
+def test_backward_landmarks_full_s256_sampled():
+    # 256 views, about 96 % sparsity with landmarks (k = 180 of 5632 tiles): dQ and D on
+    # sampled query tiles; on sampled key tiles the direct part of dK/dV (what the chain did
+    # not add: the query tiles that selected a tile never see its mean); the means' gradients
+    # through the whole-tensor sums.  The oracle's inputs at this size take most of the time.
+    w = synth.WORKLOADS["vggt_s256_lm"]
+    say("[case] backward with landmarks vggt_s256_lm (k=180), sampled tiles + sums")
+    inp, dO, g_idx, g_cnt, t_end, t_list, grads, means, ol = _bwd_lm_setup(w, seed=0, k=180)
+    dq, dk, dv, delta, dkbar, dvbar = grads
+    H, Tq = g_idx.shape[0], g_idx.shape[1]
+    pairs = sample_tiles(H, Tq, 6, seed=5)
+    hs, ts = sorted({h for h, _ in pairs}), sorted({t for _, t in pairs})
+    rdq, _, _, rD, mag = oracle.sparse_attend_bwd(inp.q, inp.k, inp.v, dO, ol, ol, 64, g_idx, g_cnt, 0.125,
+                                                  **means, query_tiles=ts, heads=hs, magnitudes=True)
+    for (h, t) in pairs:
+        r = slice(t * 64, (t + 1) * 64)
+        _grad_bound(dq[h, r].cpu().numpy(), rdq[h, r], mag["dQ"][h, r], ("dQ", h, t))
+        _grad_bound(delta[h, r].cpu().numpy(), rD[h, r], mag["D"][h, r], ("D", h, t))
+    say("  dQ, D: sampled query tiles ok")
+    del rdq, rD, mag
+    te, tl = t_end.cpu().numpy(), t_list.cpu().numpy()
+    tpf = w.layout[2] // 64
+    kc = means["kcount"]
+    for (h, t) in [(2, 3 * tpf + 7), (H - 1, Tq - 2)]:            # not the anchor frame
+        b = 0 if t == 0 else int(te[h, t - 1])
+        qt = tl[h, b:int(te[h, t])].tolist()
+        _, rdk, rdv, _, mag = oracle.sparse_attend_bwd(inp.q, inp.k, inp.v, dO, ol, ol, 64, g_idx, g_cnt, 0.125,
+                                                       **means, query_tiles=qt, heads=[h], magnitudes=True)
+        j = np.arange(t * 64, (t + 1) * 64)
+        mem = j[oracle.member_rows(ol)[j]]
+        gk = dk[h, mem].cpu().numpy().astype(np.float64) - dkbar[h, t].cpu().numpy().astype(np.float64) / kc[t]
+        gv = dv[h, mem].cpu().numpy().astype(np.float64) - dvbar[h, t].cpu().numpy().astype(np.float64) / kc[t]
+        _grad_bound(gk, rdk[h, mem], mag["dK"][h, mem], ("dK", h, t))
+        _grad_bound(gv, rdv[h, mem], mag["dV"][h, mem], ("dV", h, t))
+        del rdk, rdv, mag
+    say("  dK, dV: direct part on sampled key tiles ok")
+    _sum_invariants(dO, ol, dk.cpu().numpy(), dv.cpu().numpy())
+    say("  sums of dK, dV ok")
