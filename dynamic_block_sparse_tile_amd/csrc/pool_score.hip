@@ -81,6 +81,7 @@ __global__ __launch_bounds__(256) void k_tile_pool(const void* __restrict__ x, i
 // The product is formed transposed (keys as accumulator rows), so a lane holds four runs
 // of four consecutive scores of one query row and writes each with one 16-byte store.
 constexpr int SC_T = 128;               // queries x keys per workgroup
+constexpr int SC_STG = 68;              // staged score row stride (floats): conflict-free b128
 __device__ __forceinline__ void split_bf16x8(const float* x, bf16x8& hi, bf16x8& lo) {
     uint32_t hw[4], lw[4];
 #pragma unroll
@@ -100,6 +101,7 @@ __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restric
                                                           Lay ql, Lay kl, float scale,
                                                           float* __restrict__ scores) {
     __shared__ uint64_t s_empty[2][2];                 // [query rows | key columns][64-bit half]
+    __shared__ __align__(16) float s_stage[4][32 * SC_STG];   // per wave: 32 rows x 64 keys
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int col = lane & 31, g = lane >> 5;
     const int h = blockIdx.z;
@@ -161,15 +163,17 @@ __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restric
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         scores + ((size_t)h * Tq + (size_t)r0) * (size_t)Tk, 0, (int)slice, 0x00020000);
     const bool any_empty = (s_empty[0][0] | s_empty[0][1] | s_empty[1][0] | s_empty[1][1]) != 0ull;
+    // Each wave stages its 32 x 64 block of one row band through LDS and stores it row by
+    // row: one 16-byte store per lane then covers 4 rows x 256 contiguous bytes (whole cache
+    // lines), where the accumulator layout would spread it over 32 rows x 32 bytes.
+    float* stg = s_stage[w];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         // lane: query row r (its column of sigma^T); keys 8 (i / 4) + 4 g + i % 4 of the block
-        const int r = r0 + 32 * rb + col;
         const bool qempty = (qe >> (32 * rb + col)) & 1ull;
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
-            // sigma^T = kbar qbar^T: keys are the accumulator rows, so four consecutive keys
-            // of the lane's query row are one 16-byte store
+            // sigma^T = kbar qbar^T: keys are the accumulator rows
             f32x16 acc = {};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {           // small terms first
@@ -181,8 +185,6 @@ __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restric
             for (int ks = 0; ks < 4; ++ks)
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[cb][ks], ah[rb][ks], acc, 0, 0, 0);
             const uint32_t kw = (uint32_t)(ke >> (32 * cb)) >> (4 * g);
-            const int cbase = c0 + 32 * cb + 4 * g;
-            const unsigned voff = ((unsigned)(r - r0) * (unsigned)Tk + (unsigned)cbase) * 4u;
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 float v[4];
@@ -191,20 +193,37 @@ __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restric
                     v[j] = acc[4 * a + j] * scale;
                     if (any_empty && (qempty || ((kw >> (8 * a + j)) & 1u))) v[j] = -INFINITY;
                 }
-                if (cbase + 8 * a + 3 < Tk) {
-                    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-                    const u32x4 pk = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                                      __float_as_uint(v[3])};
-                    __builtin_amdgcn_raw_buffer_store_b128(pk, rs, (int)voff, 32 * a, 0);
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)            // a ragged last column block
-                        if (cbase + 8 * a + j < Tk)
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[j]), rs, (int)voff,
-                                                                  32 * a + 4 * j, 0);
-                }
+                *reinterpret_cast<float4*>(stg + col * SC_STG + 32 * cb + 8 * a + 4 * g) =
+                    make_float4(v[0], v[1], v[2], v[3]);
             }
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // lanes 16 i .. 16 i + 15: row 4 s + i of the band, keys 4 (lane % 16) .. + 3
+        const int ch = lane & 15;
+        const int cbase = c0 + 4 * ch;
+#pragma unroll
+        for (int sr = 0; sr < 8; ++sr) {
+            const int row = 4 * sr + (lane >> 4);
+            const float4 v = *reinterpret_cast<const float4*>(stg + row * SC_STG + 4 * ch);
+            const unsigned voff = ((unsigned)(32 * rb + row) * (unsigned)Tk + (unsigned)cbase) * 4u;
+            if (cbase + 3 < Tk) {
+                typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                const u32x4 pk = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                                  __float_as_uint(v.w)};
+                __builtin_amdgcn_raw_buffer_store_b128(pk, rs, (int)voff, 0, 0);
+            } else {
+                const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)                // a ragged last column block
+                    if (cbase + j < Tk)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(vv[j]), rs, (int)voff, 4 * j, 0);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();                   // the band is read before the next overwrites it
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 

@@ -15,6 +15,7 @@
 
 #include "device.h"
 #include "launch.h"
+#include "tile_lds.h"
 
 namespace s3d {
 
@@ -225,40 +226,70 @@ __global__ __launch_bounds__(TK_THREADS) void k_select_topk(const float* __restr
     if (tid == 0) cnt[row] = min(total, kmax);
 }
 
-// The same selection with one wave per score row (rows of at most 64 * E tiles): the keys
-// stay in registers (tile i * 64 + lane in slot i) and every count is a ballot and a scalar
-// popcount, so a row needs no LDS histogram and no barrier.  The k-th largest key T is
-// bracketed by bisection, keeping count(key >= lo) >= k > count(key > hi); once at most 64
-// keys remain inside the bracket they are gathered, one per lane, and ordered by a bitonic
-// network across the lanes, which yields T directly.
-// Selection and compaction then run over the slots in tile order with ballot prefix
-// counts, exactly as in the workgroup kernel (keys above T, the lowest-index ties, the
-// anchor frame); when exactly k keys are >= T (the bracket counts tell) there is no tie to
-// rank and every key >= T is taken.
+// The same selection with one wave per score row (rows of at most 256 G tiles): the keys stay
+// in registers, lane l holding the four consecutive tiles 256 g + 4 l .. + 3 of each group g
+// (one 16-byte load per group), and every count is a ballot and a scalar popcount, so a row
+// needs no histogram and no barrier.  The k-th largest key T is bracketed by bisection,
+// keeping count(key >= lo) >= k > count(key > hi).  Once at most 256 keys lie inside the
+// bracket they are compacted into LDS, four per lane, and the bisection continues on them
+// alone (count(key >= t) = count(key > hi at that moment) + candidates >= t); once at most
+// 64 remain they are gathered one per lane and ordered by a bitonic network across the
+// lanes, which yields T directly.  Selection and compaction then run over the groups in
+// tile order, positions from ballots and lane prefix counts (v_mbcnt): keys above T, the
+// lowest-index ties, and the anchor tiles.  When exactly k keys are >= T (the bracket
+// counts tell) there is no tie to rank and every key >= T is taken.
 constexpr int TKW_WAVES = 4;            // rows per workgroup
-// FULL: the row fills every slot (Tk = 64 E), so no slot needs a range check.
-template <int E, bool FULL>
+constexpr int TKW_CAND = 256;           // bracket size at which the candidates move to LDS
+// FULL: the row fills every slot (Tk = 256 G), so no slot needs a range check.  Rows start
+// 16-byte aligned (Tk a multiple of 4 and an aligned matrix; the launcher checks).
+template <int G, bool FULL>
 __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float* __restrict__ scores, int Tk,
                                                                      int Tq, int rows, KBudget kb, int tpf,
                                                                      int anchor, int32_t* __restrict__ idx,
                                                                      int32_t* __restrict__ cnt, int kmax) {
-    __shared__ uint32_t s_cand[TKW_WAVES][64];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ uint32_t s_cand[TKW_WAVES][TKW_CAND];
+    // the row is wave-uniform: in a scalar register, its buffer resource needs no lane loop
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row = blockIdx.x * TKW_WAVES + wave;
     if (row >= rows) return;                        // whole wave leaves together
     const int k = kb.k[row / Tq];
-    const float* src = scores + (size_t)row * Tk;
-    uint32_t key[E];
-    float f[E];
+    // the row through a buffer resource: slots past Tk read zeros (and are masked below)
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(scores) + (size_t)row * Tk, 0, Tk * 4, tl::BUF_RSRC_WORD3);
+    // the raw scores: float order equals key order for every non-NaN value (-0 == +0 as
+    // the keys fold them, -inf lowest); padding slots hold NaN, which no comparison takes
+    float x[G][4];
+    {
+        typedef float f32x4v __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int i = 0; i < E; ++i) f[i] = src[min(i * 64 + lane, Tk - 1)];   // all loads in flight at once
+        for (int g = 0; g < G; ++g) {               // all loads in flight at once
+            const f32x4v v = __builtin_bit_cast(f32x4v, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, 1024 * g, 0));
+            x[g][0] = v[0];
+            x[g][1] = v[1];
+            x[g][2] = v[2];
+            x[g][3] = v[3];
+        }
+    }
+    if (!FULL) {
+        const int lim = Tk - 4 * lane;              // slot (g, j) holds a tile iff 256 g + j < lim
 #pragma unroll
-    for (int i = 0; i < E; ++i) key[i] = FULL || i * 64 + lane < Tk ? order_key(f[i]) : 0u;   // pad slots rank lowest
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (256 * g + j >= lim) x[g][j] = __builtin_nanf("");
+    }
+    // count(key >= t) for a key t (its float: the keys' order on non-NaN values)
     auto count_ge = [&](uint32_t t) {
+        const float tf = key_float(t);
         int c = 0;
 #pragma unroll
-        for (int i = 0; i < E; ++i) c += __popcll(__ballot(key[i] >= t));
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c += __popcll(__ballot(x[g][j] >= tf));
         return c;
+    };
+    auto lanes_below = [&](uint64_t m) {
+        return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
     };
     // mode: 0 = nothing from top-k, 1 = every tile, 2 = threshold T with ties
     const int mode = k <= 0 ? 0 : (k >= Tk ? 1 : 2);
@@ -266,37 +297,71 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
     int greater = 0;
     bool take_ge = false;                           // exactly k keys are >= T: no tie to break
     if (mode == 2) {
-        uint32_t lo = 0xffffffffu, hi = 0u;
+        float mn = INFINITY, mx = -INFINITY;        // NaN padding is ignored by min / max
 #pragma unroll
-        for (int i = 0; i < E; ++i) {
-            if (FULL || i * 64 + lane < Tk) {
-                lo = min(lo, key[i]);
-                hi = max(hi, key[i]);
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                mn = fminf(mn, x[g][j]);
+                mx = fmaxf(mx, x[g][j]);
             }
-        }
-        lo = wave_min(lo);
-        hi = wave_max(hi);
+        uint32_t lo = wave_min(order_key(mn)), hi = wave_max(order_key(mx));
         int c_lo = Tk, c_hi = 0;                    // count(key >= lo), count(key > hi)
+        // candidates in LDS: cand[j] = candidate 4 lane + j (valid when below ncand);
+        // c_base = count(key > bracket top) when they were taken
+        int ncand = -1, c_base = 0;
+        float cand[4] = {0.f, 0.f, 0.f, 0.f};
+        float* s_c = reinterpret_cast<float*>(s_cand[wave]);
         // The probe halves the bracket in value (the midpoint of the two floats) while that
         // keeps shrinking the candidate count by at least a quarter, else in key order: on
         // score rows the value midpoint needs about half the passes of key bisection, and
         // the alternation bounds rows whose values span many binades.
         bool by_key = false;
         while (lo != hi) {
-            if (c_lo - c_hi <= 64) {
-                // gather the keys inside [lo, hi] and rank them across the lanes
+            const int inside = c_lo - c_hi;
+            if (inside <= 64 || (ncand < 0 && inside <= TKW_CAND)) {
+                // compact the values inside [lo, hi] into LDS (at most 256 of them); the upper
+                // bound as "below key hi + 1" (hi stays below the key of NaN, so no wrap), since
+                // key_float maps the unused key just below +0 to -0
+                const float flo = key_float(lo), fup = key_float(hi + 1);
                 int base = 0;
+                if (ncand < 0) {
 #pragma unroll
-                for (int i = 0; i < E; ++i) {
-                    const bool in = (FULL || i * 64 + lane < Tk) && key[i] >= lo && key[i] <= hi;
-                    const uint64_t m = __ballot(in);
-                    const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                    if (in) s_cand[wave][pos] = key[i];
-                    base += __popcll(m);
+                    for (int g = 0; g < G; ++g)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const bool in = x[g][j] >= flo && !(x[g][j] >= fup);
+                            const uint64_t m = __ballot(in);
+                            const int at = base + lanes_below(m);
+                            if (in && at < TKW_CAND) s_c[at] = x[g][j];
+                            base += __popcll(m);
+                        }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const bool in = 4 * lane + j < ncand && cand[j] >= flo && !(cand[j] >= fup);
+                        const uint64_t m = __ballot(in);
+                        const int at = base + lanes_below(m);
+                        if (in && at < TKW_CAND) s_c[at] = cand[j];
+                        base += __popcll(m);
+                    }
                 }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
-                uint32_t v = lane < base ? s_cand[wave][lane] : 0u;
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                if (inside > 64) {
+                    // continue the bisection on the candidates alone
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) cand[j] = 4 * lane + j < base ? s_c[4 * lane + j] : 0.f;
+                    ncand = base;
+                    c_base = c_hi;
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();         // read before a later gather overwrites
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    continue;
+                }
+                // at most 64 left: rank their keys across the lanes (pad lanes rank lowest)
+                uint32_t v = lane < base ? order_key(s_c[lane]) : 0u;
 #pragma unroll
                 for (int size = 2; size <= 64; size <<= 1) {
 #pragma unroll
@@ -308,7 +373,7 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
                 }
                 lo = (uint32_t)__shfl((int)v, k - c_hi - 1);   // rank k - c_hi among the candidates
                 hi = lo;
-                take_ge = c_hi + __popcll(__ballot(v >= lo)) == k;   // pad lanes hold 0 < lo
+                take_ge = c_hi + __popcll(__ballot(lane < base && v >= lo)) == k;
                 break;
             }
             uint32_t mid = lo + (uint32_t)(((uint64_t)hi - lo + 1) >> 1);
@@ -317,8 +382,16 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
                 if (__builtin_isfinite(fl) && __builtin_isfinite(fh))
                     mid = min(max(order_key(0.5f * fl + 0.5f * fh), lo + 1), hi);
             }
-            const int before = c_lo - c_hi;
-            const int c = count_ge(mid);
+            const int before = inside;
+            int c;
+            if (ncand < 0) {
+                c = count_ge(mid);
+            } else {
+                const float tf = key_float(mid);
+                c = c_base;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) c += __popcll(__ballot(4 * lane + j < ncand && cand[j] >= tf));
+            }
             if (c >= k) {
                 lo = mid;
                 c_lo = c;
@@ -331,50 +404,81 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
         }
         T = lo;
         if (!take_ge) {
+            const float tf = key_float(T);
 #pragma unroll
-            for (int i = 0; i < E; ++i) greater += __popcll(__ballot((FULL || i * 64 + lane < Tk) && key[i] > T));
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) greater += __popcll(__ballot(x[g][j] > tf));
         }
     }
-    int ties_before = 0;                            // keys == T in earlier slots
+    const float Tf = key_float(T);
+    int ties_before = 0;                            // keys == T in earlier groups
     const int need_eq = mode == 2 ? k - greater : 0;   // ties to take, lowest index first
-    const int a0 = anchor >= 0 ? anchor * tpf : 0, a1 = anchor >= 0 ? a0 + tpf : 0;
+    const int a0 = anchor >= 0 ? anchor * tpf : 0, a1 = anchor >= 0 ? min(a0 + tpf, Tk) : 0;
     int32_t* out = idx + (size_t)row * kmax;
     int base = 0;
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
-        const int t = i * 64 + lane;
-        const bool valid = FULL || t < Tk;
-        bool sel = valid && t >= a0 && t < a1;
-        if (mode == 1) sel = valid;
-        else if (mode == 2 && take_ge) {
-            sel = sel || (valid && key[i] >= T);
-        } else if (mode == 2) {
-            const uint64_t eqm = __ballot(valid && key[i] == T);
-            const int eq_rank = ties_before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eqm >> 32),
-                                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)eqm, 0u));
-            ties_before += __popcll(eqm);
-            if (valid && key[i] > T) sel = true;
-            else if (valid && key[i] == T && eq_rank < need_eq) sel = true;
+    for (int g = 0; g < G; ++g) {
+        const int t0 = 256 * g + 4 * lane;
+        bool sel[4], eq[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // padding holds NaN, which fails every comparison below; only "every tile" and
+            // the anchor range need the bound
+            sel[j] = t0 + j >= a0 && t0 + j < a1;
+            eq[j] = false;
+            if (mode == 1) sel[j] = FULL || t0 + j < Tk;
+            else if (mode == 2 && take_ge) sel[j] = sel[j] || x[g][j] >= Tf;
+            else if (mode == 2) {
+                sel[j] = sel[j] || x[g][j] > Tf;
+                eq[j] = x[g][j] == Tf;
+            }
         }
-        const uint64_t sm = __ballot(sel);
-        const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(sm >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)sm, 0u));
-        if (sel && pos < kmax) out[pos] = t;
-        base += __popcll(sm);
+        if (mode == 2 && !take_ge) {
+            // tie ranks in tile order: earlier groups, lower lanes, then this lane's lower j
+            int run = ties_before, tot = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint64_t em = __ballot(eq[j]);
+                run += lanes_below(em);
+                tot += __popcll(em);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (eq[j]) {
+                    sel[j] = sel[j] || run < need_eq;
+                    ++run;
+                }
+            ties_before += tot;
+        }
+        int pos = base, tot = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint64_t sm = __ballot(sel[j]);
+            pos += lanes_below(sm);
+            tot += __popcll(sm);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (sel[j]) {
+                if (pos < kmax) out[pos] = t0 + j;
+                ++pos;
+            }
+        base += tot;
     }
     for (int q = base + lane; q < kmax; q += 64) out[q] = -1;
     if (lane == 0) cnt[row] = min(base, kmax);
 }
 
-template <int E>
+template <int G>
 static void launch_wave(bool full, dim3 grid, dim3 block, hipStream_t st, const float* scores, int tk, int tq,
                         int rows, const KBudget& kb, int tpf, int anchor, int32_t* ix, int32_t* cn, int kmax) {
     if (full)
-        hipLaunchKernelGGL((k_select_topk_wave<E, true>), grid, block, 0, st, scores, tk, tq, rows, kb, tpf, anchor, ix,
-                           cn, kmax);
+        hipLaunchKernelGGL((k_select_topk_wave<G, true>), grid, block, 0, st, scores, tk, tq, rows, kb, tpf, anchor,
+                           ix, cn, kmax);
     else
-        hipLaunchKernelGGL((k_select_topk_wave<E, false>), grid, block, 0, st, scores, tk, tq, rows, kb, tpf, anchor, ix,
-                           cn, kmax);
+        hipLaunchKernelGGL((k_select_topk_wave<G, false>), grid, block, 0, st, scores, tk, tq, rows, kb, tpf,
+                           anchor, ix, cn, kmax);
 }
 
 hipError_t launch_select_topk(const float* scores, int heads, int tq, int tk, const int32_t* k_heads,
@@ -388,23 +492,25 @@ hipError_t launch_select_topk(const float* scores, int heads, int tq, int tk, co
         const int rows = nh * tq;
         int32_t* ix = kmax > 0 ? idx + r0 * kmax : idx;
         const dim3 wgrid((unsigned)((rows + TKW_WAVES - 1) / TKW_WAVES)), wblock(64 * TKW_WAVES);
-        // one wave per row while the keys fit 48 registers per lane; longer rows (fewer per
-        // launch, and each would hold too many registers) use a workgroup per row
-        if (tk <= 64 * 16)
-            launch_wave<16>(tk == 64 * 16, wgrid, wblock, st, scores + r0 * tk, tk, tq, rows, kb, tpf, anchor, ix,
-                           cnt + r0, kmax);
-        else if (tk <= 64 * 32)
-            launch_wave<32>(tk == 64 * 32, wgrid, wblock, st, scores + r0 * tk, tk, tq, rows, kb, tpf, anchor, ix,
-                           cnt + r0, kmax);
-        else if (tk <= 64 * 44)
-            launch_wave<44>(tk == 64 * 44, wgrid, wblock, st, scores + r0 * tk, tk, tq, rows, kb, tpf, anchor, ix,
-                           cnt + r0, kmax);
-        else if (tk <= 64 * 48)
-            launch_wave<48>(tk == 64 * 48, wgrid, wblock, st, scores + r0 * tk, tk, tq, rows, kb, tpf, anchor, ix,
-                           cnt + r0, kmax);
+        const float* sc = scores + r0 * tk;
+        // one wave per row while the keys fit 96 registers per lane (G groups of 256 tiles, the
+        // smallest that holds the row) and the rows allow 16-byte loads; otherwise a
+        // workgroup per row
+        const bool vec = tk % 4 == 0 && reinterpret_cast<uintptr_t>(sc) % 16 == 0;
+        const int g = (tk + 255) / 256;
+        int32_t* cn = cnt + r0;
+#define S3D_WAVE(GG) launch_wave<GG>(tk == 256 * (GG), wgrid, wblock, st, sc, tk, tq, rows, kb, tpf, anchor, ix, cn, kmax)
+        if (vec && g <= 2) S3D_WAVE(2);
+        else if (vec && g <= 4) S3D_WAVE(4);
+        else if (vec && g <= 8) S3D_WAVE(8);
+        else if (vec && g <= 11) S3D_WAVE(11);
+        else if (vec && g <= 16) S3D_WAVE(16);
+        else if (vec && g <= 22) S3D_WAVE(22);
+        else if (vec && g <= 24) S3D_WAVE(24);
         else
             hipLaunchKernelGGL(k_select_topk, dim3((unsigned)rows), dim3(TK_THREADS), shm, st,
-                               scores + r0 * tk, tk, tq, kb, tpf, anchor, ix, cnt + r0, kmax);
+                               sc, tk, tq, kb, tpf, anchor, ix, cn, kmax);
+#undef S3D_WAVE
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -165,11 +165,15 @@ def test_rising_logits_move_the_reference():
 def test_select_topk_hard_rows():
     # Score rows built to stress the k-th-largest search: heavy ties, values spread over
     # many binades (with overflow to +inf), masked (-inf) entries, constant rows and signed
-    # zeros, at lengths that take each wave width and the workgroup kernel.  Compared with
-    # the oracle's rule applied to the same fp32 scores.
+    # zeros, at lengths that take each wave width (full rows: 512, 1024, 2048, 2816, 4096,
+    # 5632, 6144; the others ragged) and the workgroup kernel (1001: not a multiple of 4;
+    # 6500: longer than a wave holds; and a matrix that starts 4 bytes past an aligned
+    # address).  Compared with the oracle's rule applied to the same fp32 scores.
     rng = np.random.default_rng(21)
-    for Tk in (100, 1000, 1024, 2000, 2048, 2816, 3000, 3072, 5000):   # 1024, 2048, 2816, 3072: full rows
-        tpf = 22 if Tk % 22 == 0 else (20 if Tk % 20 == 0 else 16)
+    for Tk in (100, 512, 1000, 1001, 1024, 2000, 2048, 2816, 3000, 3072, 4096, 5000, 5632, 6144, 6500, -1000):
+        shifted = Tk < 0
+        Tk = abs(Tk)
+        tpf = 22 if Tk % 22 == 0 else (20 if Tk % 20 == 0 else (16 if Tk % 16 == 0 else 1))
         rows = [rng.standard_normal(Tk),
                 rng.integers(-3, 3, Tk).astype(np.float64),
                 np.exp(rng.normal(0.0, 20.0, Tk)),
@@ -184,7 +188,12 @@ def test_select_topk_hard_rows():
         with np.errstate(over="ignore"):
             sc = np.stack(rows).astype(np.float32)[None]
         g = to_dev(sc, torch.float32)
-        say(f"[case] select hard rows Tk={Tk}")
+        if shifted:                                   # same values, 4 bytes past alignment
+            buf = torch.empty(g.numel() + 1, device=g.device, dtype=torch.float32)
+            g = buf[1:].view(g.shape)
+            g.copy_(to_dev(sc, torch.float32))
+            assert g.data_ptr() % 16 == 4
+        say(f"[case] select hard rows Tk={Tk}{' (shifted)' if shifted else ''}")
         for k in (1, 5, 138, Tk - 1, Tk, Tk + 3):
             for anchor in (-1, 0):
                 idx, cnt = S.sparse3d_select_topk(g, k, tpf, anchor)
