@@ -72,16 +72,24 @@ __global__ __launch_bounds__(256) void k_tile_pool(const void* __restrict__ x, i
 }
 
 // Tile scores on the matrix cores: sigma = scale * qbar . kbar (-inf where either tile has
-// no rows), a 128 x 128 block per workgroup of four waves, each wave a 64 x 64 quarter as
-// 2 x 2 accumulators of v_mfma_f32_32x32x16_bf16.  The fp32 means are split into two bf16
-// terms, x = hi + lo with hi = bf16(x) and lo = bf16(x - hi) (x - hi - lo is below 2^-17 |x|),
-// and the product takes all four cross terms, exact products accumulated in fp32: the
-// scores agree with the fp32 dot product to about 1e-6 relative, while the kernel, bound by
-// writing the score matrix, runs several times faster than fp32 FMAs on the vector ALU.
-// The product is formed transposed (keys as accumulator rows), so a lane holds four runs
-// of four consecutive scores of one query row and writes each with one 16-byte store.
-constexpr int SC_T = 128;               // queries x keys per workgroup
-constexpr int SC_STG = 68;              // staged score row stride (floats): conflict-free b128
+// no rows).  The fp32 means are split into two bf16 terms, x = hi + lo with hi = bf16(x) and
+// lo = bf16(x - hi) (x - hi - lo is below 2^-17 |x|), and the product takes all four cross
+// terms, exact products accumulated in fp32 (small terms first): the scores agree with the
+// fp32 dot product to about 1e-6 relative, and the matrix cores leave the kernel bound by
+// writing the score matrix.
+// A workgroup of four waves owns 128 query tiles (32 per wave, their hi/lo operands held in
+// registers) and walks a range of key blocks of 64 tiles: each block's means are loaded
+// once for the workgroup, split, and written to LDS (double-buffered; the next block's
+// loads are in flight while the current one is multiplied).  The product is formed
+// transposed (keys as the accumulator rows); each wave stages its 32 x 32 results through
+// LDS and stores whole 128-byte lines, eight query rows per store instruction, while the
+// matrix cores go on with the next products.
+constexpr int SC_Q = 128;               // query tiles per workgroup (4 waves x 32)
+constexpr int SC_K = 64;                // key tiles per block
+constexpr int SC_STG = 36;              // staged score row stride (floats): conflict-free b128 writes
+// Score stores carry the non-temporal hint: the matrix is read once, by the selection, and
+// streaming it past the caches measured 0.116 against 0.132 ms at 2816 x 2816 tiles x 16 heads.
+constexpr int SC_NT = 2;
 __device__ __forceinline__ void split_bf16x8(const float* x, bf16x8& hi, bf16x8& lo) {
     uint32_t hw[4], lw[4];
 #pragma unroll
@@ -96,94 +104,114 @@ __device__ __forceinline__ void split_bf16x8(const float* x, bf16x8& hi, bf16x8&
     hi = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
     lo = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
 }
+// byte offset of dims 8c .. 8c + 7 of key row r in a [64 keys][64 dims] bf16 block: 16-byte
+// chunks XOR-swizzled so that 16 lanes reading 16 consecutive keys hit 16 distinct bank groups
+__device__ __forceinline__ int sc_koff(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+
 __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restrict__ qbar,
                                                           const float* __restrict__ kbar, int Tq, int Tk,
-                                                          Lay ql, Lay kl, float scale,
+                                                          Lay ql, Lay kl, float scale, int kblocks,
                                                           float* __restrict__ scores) {
-    __shared__ uint64_t s_empty[2][2];                 // [query rows | key columns][64-bit half]
-    __shared__ __align__(16) float s_stage[4][32 * SC_STG];   // per wave: 32 rows x 64 keys
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    __shared__ __align__(16) unsigned char s_kh[2][SC_K * 128];   // key means, bf16 hi terms
+    __shared__ __align__(16) unsigned char s_kl[2][SC_K * 128];   // and lo terms
+    __shared__ __align__(16) float s_stage[4][32 * SC_STG];       // per wave: 32 rows x 32 keys
+    __shared__ uint64_t s_kempty[2];                              // key tiles without members
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, g = lane >> 5;
     const int h = blockIdx.z;
-    const int tq0 = blockIdx.y * SC_T, tk0 = blockIdx.x * SC_T;
-    // tiles of this block without rows (their scores are -inf), one ballot per 64 tiles
-    {
-        const int i = tid & 127;
-        bool e;
-        if (tid < 128) {
-            e = tq0 + i < Tq && valid_rows(ql, tq0 + i) == 0;
-        } else {
-            int lo = 0, hi = 1;
-            if (tk0 + i < Tk) member_range(kl, tk0 + i, lo, hi);
-            e = hi <= lo;
-        }
-        const uint64_t m = __ballot(e);
-        if (lane == 0) s_empty[w >> 1][w & 1] = m;
-    }
-    const int r0 = tq0 + 64 * (w >> 1), c0 = tk0 + 64 * (w & 1);
+    const int r0 = blockIdx.y * SC_Q + 32 * w;                    // this wave's first query tile
+    const int kb0 = blockIdx.x * kblocks * SC_K;                  // first key tile of the range
+    const int nkb = min(kblocks, (Tk - kb0 + SC_K - 1) / SC_K);   // key blocks in the range
     const float* qb = qbar + (size_t)h * Tq * HD;
     const float* kb = kbar + (size_t)h * Tk * HD;
-    // operands: row (or key) 32 b + col of this wave's quarter, dims 16 ks + 8 g .. +8
-    bf16x8 ah[2][4], al[2][4], bh[2][4], bl[2][4];
+
+    // query operands: row r0 + col, dims 16 ks + 8 g .. + 8, split once
+    bf16x8 ah[4], al[4];
+    const int r = r0 + col;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int r = r0 + 32 * b + col, c = c0 + 32 * b + col;
+    for (int ks = 0; ks < 4; ++ks) {
+        float x[8];
+        if (r < Tq) {
+            const float4* p = reinterpret_cast<const float4*>(qb + (size_t)r * HD + 16 * ks + 8 * g);
+            const float4 u = p[0], v = p[1];
+            x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+        } else {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            float x[8], y[8];
-            if (r < Tq) {
-                const float4* p = reinterpret_cast<const float4*>(qb + (size_t)r * HD + 16 * ks + 8 * g);
-                const float4 u = p[0], v = p[1];
-                x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) x[i] = 0.f;
-            }
-            if (c < Tk) {
-                const float4* p = reinterpret_cast<const float4*>(kb + (size_t)c * HD + 16 * ks + 8 * g);
-                const float4 u = p[0], v = p[1];
-                y[0] = u.x; y[1] = u.y; y[2] = u.z; y[3] = u.w; y[4] = v.x; y[5] = v.y; y[6] = v.z; y[7] = v.w;
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) y[i] = 0.f;
-            }
-            split_bf16x8(x, ah[b][ks], al[b][ks]);
-            split_bf16x8(y, bh[b][ks], bl[b][ks]);
+            for (int i = 0; i < 8; ++i) x[i] = 0.f;
         }
+        split_bf16x8(x, ah[ks], al[ks]);
+    }
+    const bool qempty = r < Tq && valid_rows(ql, r) == 0;
+    const bool any_qempty = __ballot(qempty) != 0ull;
+
+    // staging of a key block: thread t takes key t / 4, dims 16 (t % 4) .. + 16
+    const int sk = tid >> 2, sd = tid & 3;
+    float4 raw[4];
+    auto load_block = [&](int s) {
+        const int key = kb0 + s * SC_K + sk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            raw[i] = key < Tk ? reinterpret_cast<const float4*>(kb + (size_t)key * HD + 16 * sd)[i]
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+    };
+    auto write_block = [&](int s, int buf) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const float x[8] = {raw[2 * half].x, raw[2 * half].y, raw[2 * half].z, raw[2 * half].w,
+                                raw[2 * half + 1].x, raw[2 * half + 1].y, raw[2 * half + 1].z, raw[2 * half + 1].w};
+            bf16x8 hi, lo;
+            split_bf16x8(x, hi, lo);
+            const int off = sc_koff(sk, 2 * sd + half);
+            *reinterpret_cast<bf16x8*>(s_kh[buf] + off) = hi;
+            *reinterpret_cast<bf16x8*>(s_kl[buf] + off) = lo;
+        }
+        if (w == 0) {                                 // key tiles of the block without members
+            const int key = kb0 + s * SC_K + lane;
+            int lo = 0, hi = 1;
+            if (key < Tk) member_range(kl, key, lo, hi);
+            const uint64_t m = __ballot(hi <= lo);
+            if (lane == 0) s_kempty[buf] = m;
+        }
+    };
+    // rows past Tq fall outside this wave's store resource (based at its first row in 64-bit
+    // arithmetic; offsets below 32 * Tk * 4 bytes, which the host's Tk cap keeps in 32 bits)
+    const long long rows_here = (long long)Tq - r0 < 0 ? 0 : ((long long)Tq - r0 < 32 ? (long long)Tq - r0 : 32);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        scores + ((size_t)h * Tq + (size_t)(r0 < Tq ? r0 : 0)) * (size_t)Tk, 0, (int)(rows_here * Tk * 4), 0x00020000);
+    float* stg = s_stage[w];
+
+    if (nkb > 0) {
+        load_block(0);
+        write_block(0, 0);
     }
     __syncthreads();
-    const uint64_t qe = s_empty[0][w >> 1];            // this wave's 64 query rows
-    const uint64_t ke = s_empty[1][w & 1];             // this wave's 64 key columns
-    // stores through a buffer resource over this wave's 64 query rows of the head's [Tq, Tk]
-    // slice, based at its first row in 64-bit arithmetic: rows past Tq (last block row) fall
-    // outside the resource and are dropped, and the offsets inside it stay below
-    // 64 * Tk * 4 bytes (the host caps Tk at 2^23, so they fit 32 bits at any Tq)
-    const long long rows_here = (long long)Tq - r0 < 0 ? 0 : ((long long)Tq - r0 < 64 ? (long long)Tq - r0 : 64);
-    const unsigned slice = (unsigned)(rows_here * Tk * 4);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        scores + ((size_t)h * Tq + (size_t)r0) * (size_t)Tk, 0, (int)slice, 0x00020000);
-    const bool any_empty = (s_empty[0][0] | s_empty[0][1] | s_empty[1][0] | s_empty[1][1]) != 0ull;
-    // Each wave stages its 32 x 64 block of one row band through LDS and stores it row by
-    // row: one 16-byte store per lane then covers 4 rows x 256 contiguous bytes (whole cache
-    // lines), where the accumulator layout would spread it over 32 rows x 32 bytes.
-    float* stg = s_stage[w];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        // lane: query row r (its column of sigma^T); keys 8 (i / 4) + 4 g + i % 4 of the block
-        const bool qempty = (qe >> (32 * rb + col)) & 1ull;
+    for (int s = 0; s < nkb; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < nkb) load_block(s + 1);          // lands while this block is multiplied
+        const uint64_t ke = s_kempty[buf];
+        const bool any_empty = any_qempty || ke != 0ull;
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
-            // sigma^T = kbar qbar^T: keys are the accumulator rows
+            // sigma^T = kbar qbar^T: key rows 32 cb + col of the block, dims 16 ks + 8 g
+            bf16x8 bh[4], bl[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int off = sc_koff(32 * cb + col, 2 * ks + g);
+                bh[ks] = *reinterpret_cast<const bf16x8*>(s_kh[buf] + off);
+                bl[ks] = *reinterpret_cast<const bf16x8*>(s_kl[buf] + off);
+            }
             f32x16 acc = {};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {           // small terms first
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bl[cb][ks], al[rb][ks], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[cb][ks], al[rb][ks], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bl[cb][ks], ah[rb][ks], acc, 0, 0, 0);
+            for (int ks = 0; ks < 4; ++ks) {         // small terms first
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bl[ks], al[ks], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[ks], al[ks], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bl[ks], ah[ks], acc, 0, 0, 0);
             }
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[cb][ks], ah[rb][ks], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[ks], ah[ks], acc, 0, 0, 0);
+            // lane: query row r0 + col; keys 8 a + 4 g + j of the 32 (accumulator rows)
             const uint32_t kw = (uint32_t)(ke >> (32 * cb)) >> (4 * g);
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
@@ -193,37 +221,38 @@ __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restric
                     v[j] = acc[4 * a + j] * scale;
                     if (any_empty && (qempty || ((kw >> (8 * a + j)) & 1u))) v[j] = -INFINITY;
                 }
-                *reinterpret_cast<float4*>(stg + col * SC_STG + 32 * cb + 8 * a + 4 * g) =
-                    make_float4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<float4*>(stg + col * SC_STG + 8 * a + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
             }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // lanes 16 i .. 16 i + 15: row 4 s + i of the band, keys 4 (lane % 16) .. + 3
-        const int ch = lane & 15;
-        const int cbase = c0 + 4 * ch;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // lanes 8 i .. 8 i + 7: query row 8 q + i, keys 4 (lane % 8) .. + 3 of the 32
+            const int ch = lane & 7;
+            const int cbase = kb0 + s * SC_K + 32 * cb + 4 * ch;
 #pragma unroll
-        for (int sr = 0; sr < 8; ++sr) {
-            const int row = 4 * sr + (lane >> 4);
-            const float4 v = *reinterpret_cast<const float4*>(stg + row * SC_STG + 4 * ch);
-            const unsigned voff = ((unsigned)(32 * rb + row) * (unsigned)Tk + (unsigned)cbase) * 4u;
-            if (cbase + 3 < Tk) {
-                typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-                const u32x4 pk = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
-                                  __float_as_uint(v.w)};
-                __builtin_amdgcn_raw_buffer_store_b128(pk, rs, (int)voff, 0, 0);
-            } else {
-                const float vv[4] = {v.x, v.y, v.z, v.w};
+            for (int q = 0; q < 4; ++q) {
+                const int row = 8 * q + (lane >> 3);
+                const float4 v = *reinterpret_cast<const float4*>(stg + row * SC_STG + 4 * ch);
+                const unsigned voff = ((unsigned)row * (unsigned)Tk + (unsigned)cbase) * 4u;
+                if (cbase + 3 < Tk) {
+                    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                    const u32x4 pk = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                                      __float_as_uint(v.w)};
+                    __builtin_amdgcn_raw_buffer_store_b128(pk, rs, (int)voff, 0, SC_NT);
+                } else {
+                    const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                for (int j = 0; j < 4; ++j)                // a ragged last column block
-                    if (cbase + j < Tk)
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(vv[j]), rs, (int)voff, 4 * j, 0);
+                    for (int j = 0; j < 4; ++j)         // a ragged last key block
+                        if (cbase + j < Tk)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(vv[j]), rs, (int)voff, 4 * j, SC_NT);
+                }
             }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();         // read before the next stage overwrites it
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();                   // the band is read before the next overwrites it
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (s + 1 < nkb) write_block(s + 1, buf ^ 1);
+        __syncthreads();
     }
 }
 
@@ -244,13 +273,17 @@ hipError_t launch_tile_scores(const float* qbar, const float* kbar, int heads, L
                               float scale, float* scores, hipStream_t st) {
     const int Tq = ql.S * ql.P / TILE, Tk = kl.S * kl.P / TILE;
     const Lay lq{ql.S, ql.N, ql.P, ql.nsp}, lk{kl.S, kl.N, kl.P, kl.nsp};
-    const dim3 grid((Tk + SC_T - 1) / SC_T, (Tq + SC_T - 1) / SC_T, heads), block(256);
-    hipLaunchKernelGGL(k_tile_scores_mfma, grid, block, 0, st, qbar, kbar, Tq, Tk, lq, lk, scale, scores);
+    // split each head's key blocks into ranges so that the grid holds about 2048 workgroups
+    const int qblocks = (Tq + SC_Q - 1) / SC_Q, kblocks_all = (Tk + SC_K - 1) / SC_K;
+    const long long per = (long long)qblocks * heads;
+    const int nsplit = (int)std::max(1LL, std::min<long long>(kblocks_all, (2048 + per - 1) / per));
+    const int kblocks = (kblocks_all + nsplit - 1) / nsplit;
+    const dim3 grid((unsigned)((kblocks_all + kblocks - 1) / kblocks), (unsigned)qblocks, (unsigned)heads);
+    hipLaunchKernelGGL(k_tile_scores_mfma, grid, dim3(256), 0, st, qbar, kbar, Tq, Tk, lq, lk, scale, kblocks,
+                       scores);
     return hipGetLastError();
 }
 
-// fp32 -> bf16, round to nearest even; one value per thread, grid-stride (no alignment
-// requirement on either pointer).
 __global__ void k_cast_bf16(const float* __restrict__ src, int64_t n, __bf16* __restrict__ dst) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         dst[i] = (__bf16)src[i];

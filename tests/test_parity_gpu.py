@@ -904,3 +904,89 @@ def test_backward_landmarks_full_s256_sampled():
     say("  dK, dV: direct part on sampled key tiles ok")
     _sum_invariants(dO, ol, dk.cpu().numpy(), dv.cpu().numpy())
     say("  sums of dK, dV ok")
+
+
+# ----------------------------------------------------------------- output bounds (canaries)
+_GUARD = 4096
+_PAT = 0xA5
+
+
+class _Guarded:
+    """An output buffer of `nbytes` between two guard regions of a known byte pattern."""
+
+    def __init__(self, nbytes):
+        self.n = int(nbytes)
+        self.buf = torch.full((self.n + 2 * _GUARD,), _PAT, dtype=torch.uint8, device=dev())
+
+    @property
+    def ptr(self):
+        return self.buf.data_ptr() + _GUARD
+
+    def check(self, name):
+        b = self.buf.cpu().numpy()
+        assert np.all(b[:_GUARD] == _PAT), f"{name}: bytes written before the buffer"
+        assert np.all(b[_GUARD + self.n:] == _PAT), f"{name}: bytes written past the buffer"
+        assert np.any(b[_GUARD:_GUARD + self.n] != _PAT), f"{name}: nothing written"
+
+
+def test_outputs_stay_inside_their_buffers():
+    # every entry point, called through the C ABI on one small ragged layer (4 views of 1374
+    # tokens, 2 heads, landmarks on), writes only inside the output buffers it was given
+    say("[case] canary guards around every output")
+    import ctypes
+    lib = S.library()
+    H, d = 2, 64
+    lay = (4, 1374, 1408, 5)
+    L = lay[0] * lay[2]
+    Tq = Tk = L // 64
+    tpf = lay[2] // 64
+    k, anchor = 12, 0
+    kmax = S.kmax_for(Tk, k, tpf, anchor)
+    rng = np.random.default_rng(31)
+    q = to_dev(rng.standard_normal((H, L, d)).astype(np.float32), torch.bfloat16)
+    v = to_dev(rng.standard_normal((H, L, d)).astype(np.float32), torch.bfloat16)
+    dout = to_dev(rng.standard_normal((H, L, d)).astype(np.float32), torch.bfloat16)
+    st = torch.cuda.current_stream().cuda_stream
+    ql = S._Layout(*lay)
+    rl = ctypes.byref(ql)
+    g = {n: _Guarded(b) for n, b in dict(
+        qbar=H * Tq * d * 4, kbar=H * Tk * d * 4, vbar=H * Tk * d * 4, scores=H * Tq * Tk * 4,
+        idx=H * Tq * kmax * 4, cnt=H * Tq * 4, idx_h=H * Tq * kmax * 4, cnt_h=H * Tq * 4,
+        kb16=H * Tk * d * 2, vb16=H * Tk * d * 2, out=H * L * d * 2, lse=H * L * 4,
+        dense_out=H * L * d * 4, dense_lse=H * L * 4, frame_out=H * L * d * 2, frame_lse=H * L * 4,
+        t_end=H * Tk * 4, t_list=H * Tq * kmax * 4, dq=H * L * d * 4, dk=H * L * d * 4, dv=H * L * d * 4,
+        delta=H * L * 4, dkbar=H * Tk * d * 4, dvbar=H * Tk * d * 4, kmean=H * d * 4, vmean=H * d * 4).items()}
+    P = {n: x.ptr for n, x in g.items()}
+    ok = lambda status: S._check(status)
+    ok(lib.sparse3d_tile_scores(q.data_ptr(), q.data_ptr(), v.data_ptr(), S.BF16, H, d, 64, rl, rl, 0.125,
+                                P["qbar"], P["kbar"], P["vbar"], P["scores"], st))
+    ok(lib.sparse3d_select_topk(P["scores"], H, Tq, Tk, k, tpf, anchor, P["idx"], P["cnt"], kmax, st))
+    kh = (ctypes.c_int32 * H)(k, k - 5)
+    ok(lib.sparse3d_select_topk_per_head(P["scores"], H, Tq, Tk, kh, tpf, anchor, P["idx_h"], P["cnt_h"], kmax, st))
+    ok(lib.sparse3d_cast(P["kbar"], H * Tk * d, S.BF16, P["kb16"], st))
+    ok(lib.sparse3d_cast(P["vbar"], H * Tk * d, S.BF16, P["vb16"], st))
+    ok(lib.sparse3d_sparse_attn_fwd(q.data_ptr(), q.data_ptr(), v.data_ptr(), S.BF16, H, d, 64, rl, rl, P["idx"],
+                                    P["cnt"], kmax, P["kb16"], P["vb16"], math.log(64.0), 0.125, None, P["out"],
+                                    S.BF16, P["lse"], st))
+    ok(lib.sparse3d_dense_attn_fwd(q.data_ptr(), q.data_ptr(), v.data_ptr(), S.BF16, H, d, rl, rl, 0.125, None,
+                                   P["dense_out"], S.F32, P["dense_lse"], st))
+    ok(lib.sparse3d_frame_attn_fwd(q.data_ptr(), q.data_ptr(), v.data_ptr(), S.BF16, H, d, rl, rl, 0.125,
+                                   P["frame_out"], S.BF16, P["frame_lse"], st))
+    ok(lib.sparse3d_selection_transpose(P["idx"], P["cnt"], H, Tq, Tk, kmax, P["t_end"], P["t_list"], st))
+    ok(lib.sparse3d_sparse_attn_bwd(q.data_ptr(), q.data_ptr(), v.data_ptr(), P["out"], dout.data_ptr(), P["lse"],
+                                    S.BF16, H, d, 64, rl, rl, P["idx"], P["cnt"], kmax, P["t_end"], P["t_list"],
+                                    P["kb16"], P["vb16"], math.log(64.0), 0.125, P["dq"], P["dk"], P["dv"],
+                                    P["delta"], P["dkbar"], P["dvbar"], st))
+    ok(lib.sparse3d_discarded_mean(q.data_ptr(), v.data_ptr(), S.BF16, H, d, rl, 37, 37, 2, P["kmean"],
+                                   P["vmean"], st))
+    sl = S._Layout()
+    ok(lib.sparse3d_subsample_layout(rl, 37, 37, 2, 64, ctypes.byref(sl)))
+    rows_out = sl.frames * sl.stride
+    ko, vo = _Guarded(H * rows_out * d * 2), _Guarded(H * rows_out * d * 2)
+    ok(lib.sparse3d_grid_subsample_kv(q.data_ptr(), v.data_ptr(), S.BF16, H, d, rl, 37, 37, 2, ko.ptr, vo.ptr,
+                                      ctypes.byref(sl), st))
+    torch.cuda.synchronize()
+    for n, x in g.items():
+        x.check(n)
+    ko.check("k_out")
+    vo.check("v_out")
