@@ -27,11 +27,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "sparse global-attn effective TFLOP/s + ms/layer at S=128 frames, % bf16 MFMA peak"
-PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak (published)
-PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-ATTN_SRCS = [os.path.join(ROOT, "dynamic_block_sparse_tile_amd", "csrc", f)
-             for f in ("attn_bf16.hip", "attn_common.h", "device.h")]
+PEAK_TFLOPS = {"bf16": 2500.0,   # MI355X dense matrix peaks (published): bf16
+               "f32": 157.3}     # fp32 (the fp32 path runs on v_mfma_f32_32x32x2_f32)
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E (published)
+N_XCD, N_SIMD = 8, 1024          # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "dynamic_block_sparse_tile_amd", "csrc")
+# the configurations of the pages' workloads, smallest first; the default run is vggt_s128
+CONFIGS = ["tiny_s2", "vggt_s8", "vggt_s32", "vggt_s128", "vggt_s128_90", "vggt_s256_lm",
+           "vggt_s256_lm_sub2"]
 
 
 def log(msg):
@@ -53,50 +57,216 @@ def parse():
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first run a plain elementwise copy of this many MiB (fp32) twice, as a "
                          "known-size reference for the HBM byte counters")
-    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="no GPU work: turn the counter files of a FETCH_SIZE run and a WRITE_SIZE "
-                         "run (rocprofv3 --pmc, both with --copy-mb) into profiles/traffic.json")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="one JSON line per configuration: " + ", ".join(CONFIGS))
+    ap.add_argument("--top-k", type=int, default=None, help="fixed k instead of the calibrated one")
+    ap.add_argument("--run-info", metavar="PATH",
+                    help="write the layer's algorithmic work per kernel dispatch (for --counters-from)")
+    ap.add_argument("--profile-commands", metavar="OUTDIR",
+                    help="no GPU work: print the rocprofv3 passes that --counters-from reads")
+    ap.add_argument("--counters-from", metavar="OUTDIR",
+                    help="no GPU work: turn the rocprofv3 passes under OUTDIR into "
+                         "profiles/counters_<workload>.json and .md")
     return ap.parse_args()
 
 
-ATTN_KERNEL = "k_attn_bf16<false, false, false, false, 1>"     # the sparse bf16 attention kernel
+def kernel_source_sha256() -> str:
+    """Hash of every kernel source: counters taken before a change to any of them are stale."""
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
 
 
-def write_traffic(fetch_csv, write_csv, copy_mb, workload):
-    """HBM bytes per attention launch from two counter runs.  Each counter is scaled by
-    what it reads for the plain copy of known size in the same run (the largest elementwise
-    launch: copy_mb MiB read and written)."""
+# rocprofv3 passes over one short benchmark run (the layer kernels plus a plain copy of
+# known size, the reference that scales the byte counters); pass name -> profiler options
+COUNTER_PASSES = [
+    ("trace", "--kernel-trace --stats"),
+    ("fetch", "--pmc FETCH_SIZE"),
+    ("write", "--pmc WRITE_SIZE"),
+    ("sq", "--pmc SQ_WAVE_CYCLES SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_BUSY_CYCLES "
+           "SQ_INSTS_VALU SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE"),
+]
+PROFILE_COPY_MB = 1024
+
+
+def profile_commands(workload: str, outdir: str) -> list:
+    bench = (f"python3 {os.path.join(ROOT, 'bench.py')} --workload {workload} --steps 2 --warmup 1 "
+             f"--no-cpu-baseline --no-dense --no-gate --copy-mb {PROFILE_COPY_MB}")
+    cmds = []
+    for name, opts in COUNTER_PASSES:
+        d = os.path.join(outdir, name)
+        info = f" --run-info {os.path.join(outdir, 'run_info.json')}" if name == "trace" else ""
+        regex = "" if name == "trace" else " --kernel-include-regex 's3d::|elementwise'"
+        cmds.append(f"timeout -s KILL 300 rocprofv3 {opts}{regex} --output-format csv -d {d} -o run -- "
+                    f"{bench}{info}")
+    return cmds
+
+
+def kernel_family(name: str):
+    """Which step of the layer a kernel name belongs to (None: not a layer kernel)."""
+    if "elementwise" in name:
+        return "copy"
+    if "s3d::" not in name:
+        return None
+    if "k_tile_pool" in name:
+        # template arguments <bf16, key_rows>
+        return "pool_key" if name.split("<", 1)[1].split(">", 1)[0].replace(" ", "").endswith("true") else "pool_query"
+    for key, fam in (("k_tile_scores", "score"), ("k_select_topk", "select"), ("k_cast_bf16", "cast"),
+                     ("k_grid_subsample", "subsample"), ("k_attn_bwd", None), ("k_attn", "attention")):
+        if key in name:
+            return fam
+    return None
+
+
+def write_counters(outdir: str):
+    """Per-kernel figures of one layer from the rocprofv3 passes under outdir: mean duration
+    (kernel trace), HBM bytes per dispatch (FETCH_SIZE / WRITE_SIZE, each scaled by what the
+    counter reads for the plain copy of known size), counted and algorithmic GB/s against
+    the 8 TB/s peak, and for the attention kernel the shader clock, matrix-core busy share
+    (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles) and FLOP rate against the matrix peak."""
     import csv
+    import glob
     from collections import defaultdict
 
-    def per_dispatch(path, counter):
-        vals, names = defaultdict(float), {}
-        for row in csv.DictReader(open(path)):
-            if row["Counter_Name"] == counter:
-                vals[row["Dispatch_Id"]] += float(row["Counter_Value"])
-                names[row["Dispatch_Id"]] = row["Kernel_Name"]
-        attn = [v for d, v in vals.items() if ATTN_KERNEL in names[d]]
-        copy = [v for d, v in vals.items() if "elementwise" in names[d]]
-        if not attn or not copy:
-            raise SystemExit(f"{path}: no {ATTN_KERNEL} or copy dispatch with {counter}")
-        return sum(attn) / len(attn), max(copy), len(attn)
+    info = json.load(open(os.path.join(outdir, "run_info.json")))
+    stats = glob.glob(os.path.join(outdir, "trace", "**", "*kernel_stats.csv"), recursive=True)
+    if not stats:
+        raise SystemExit(f"{outdir}/trace: no kernel_stats.csv")
+    dur = {}                                            # name -> (calls, mean ns)
+    for row in csv.DictReader(open(stats[0])):
+        dur[row["Name"]] = (int(row["Calls"]), float(row["AverageNs"]))
 
-    copy_bytes = copy_mb * (1 << 20)
-    out = {"workload": workload, "kernel": ATTN_KERNEL, "attn_source_sha256": attn_source_sha256(),
-           "copy_reference_bytes": copy_bytes}
-    total = 0.0
-    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
-        a, c, n = per_dispatch(path, counter)
-        scale = copy_bytes / (c * 1024.0)
-        out[key] = {"counter": counter, "attn_kib_per_launch": a, "launches": n, "copy_kib": c,
-                    "scale": round(scale, 4), "bytes_per_launch": round(a * 1024.0 * scale)}
-        total += a * 1024.0 * scale
-    out["bytes_per_launch"] = round(total)
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
+    def counters(pass_name):
+        files = glob.glob(os.path.join(outdir, pass_name, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"{outdir}/{pass_name}: no counter_collection.csv")
+        per = defaultdict(lambda: defaultdict(float))   # (name, counter) -> dispatch -> value
+        span = {}
+        for row in csv.DictReader(open(files[0])):
+            per[(row["Kernel_Name"], row["Counter_Name"])][row["Dispatch_Id"]] += float(row["Counter_Value"])
+            span[row["Dispatch_Id"]] = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-9
+        return per, span
+
+    fetch, _ = counters("fetch")
+    write, _ = counters("write")
+    sq, span = counters("sq")
+
+    def mean_of(per, name, counter):
+        v = per.get((name, counter))
+        return sum(v.values()) / len(v) if v else None
+
+    copy_bytes = PROFILE_COPY_MB * (1 << 20)
+    scale = {}
+    for cname, per in (("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
+        copies = [max(v.values()) for (n, c), v in per.items() if c == cname and kernel_family(n) == "copy"]
+        if not copies:
+            raise SystemExit(f"no copy reference dispatch with {cname}")
+        scale[cname] = copy_bytes / (max(copies) * 1024.0)   # known bytes per counted KiB
+
+    alg = info["alg_per_dispatch"]
+    kernels = []
+    for name, (calls, ns) in sorted(dur.items(), key=lambda x: -x[1][0] * x[1][1]):
+        fam = kernel_family(name)
+        if fam in (None, "copy"):
+            continue
+        sec = ns * 1e-9
+        fb = mean_of(fetch, name, "FETCH_SIZE")
+        wb = mean_of(write, name, "WRITE_SIZE")
+        k = {"name": name, "family": fam, "dispatches": calls, "avg_ms": round(sec * 1e3, 4),
+             "per_layer": info["dispatches_per_layer"].get(fam, 0)}
+        if fb is not None and wb is not None:
+            byt = fb * 1024.0 * scale["FETCH_SIZE"] + wb * 1024.0 * scale["WRITE_SIZE"]
+            k.update(fetch_bytes=round(fb * 1024.0 * scale["FETCH_SIZE"]),
+                     write_bytes=round(wb * 1024.0 * scale["WRITE_SIZE"]),
+                     counted_gbs=round(byt / sec / 1e9, 1), counted_frac_hbm=round(byt / sec / 1e9 / PEAK_HBM_GBS, 4))
+        if fam != "attention" and fam in alg:
+            k.update(alg_bytes=alg[fam], alg_gbs=round(alg[fam] / sec / 1e9, 1),
+                     alg_frac_hbm=round(alg[fam] / sec / 1e9 / PEAK_HBM_GBS, 4))
+        grbm = sq.get((name, "GRBM_GUI_ACTIVE"))
+        if grbm:
+            # cycles per XCD over the dispatch's own span in that pass
+            clocks = [grbm[d] / N_XCD / span[d] for d in grbm if span.get(d, 0) > 0]
+            cyc = sum(grbm.values()) / len(grbm) / N_XCD
+            k["clock_ghz"] = round(sum(clocks) / len(clocks) / 1e9, 3) if clocks else None
+            busy = mean_of(sq, name, "SQ_VALU_MFMA_BUSY_CYCLES")
+            anyi = mean_of(sq, name, "SQ_ACTIVE_INST_ANY")
+            valu = mean_of(sq, name, "SQ_ACTIVE_INST_VALU")
+            wavec = mean_of(sq, name, "SQ_WAVE_CYCLES")
+            if busy is not None:
+                k["mfma_busy"] = round(busy / (cyc * N_SIMD), 4)
+            if anyi and valu is not None:
+                k["valu_share_of_issue"] = round(valu / anyi, 4)
+            if anyi and wavec:
+                k["issue_share_of_wave_cycles"] = round(anyi / wavec, 4)
+        if fam == "attention":
+            flops = info["attn_flops_per_launch"]
+            peak = PEAK_TFLOPS[info["dtype"]]
+            k.update(flops=flops, tflops=round(flops / sec / 1e12, 2), frac_peak=round(flops / sec / 1e12 / peak, 4))
+            if k.get("clock_ghz"):
+                # the same peak at the clock the kernel actually ran (peak is quoted at 2.4 GHz)
+                k["frac_peak_at_clock"] = round(k["tflops"] / (peak * k["clock_ghz"] / 2.4), 4)
+        kernels.append(k)
+    fam_ms = defaultdict(float)
+    for fam, n in info["dispatches_per_layer"].items():
+        ks = [k for k in kernels if k["family"] == fam]
+        if ks:                                          # instances of one family: mean over dispatches
+            tot = sum(k["avg_ms"] * k["dispatches"] for k in ks) / sum(k["dispatches"] for k in ks)
+            fam_ms[fam] = round(n * tot, 4)
+    out = {"workload": info["workload"], "kernel_source_sha256": kernel_source_sha256(),
+           "run": info, "copy_reference_bytes": copy_bytes,
+           "counter_scale": {c: round(v, 4) for c, v in scale.items()},
+           "commands": profile_commands(info["workload"], outdir), "kernels": kernels,
+           "layer_ms_by_family": dict(fam_ms)}
+    os.makedirs(PROFILES, exist_ok=True)
+    base = os.path.join(PROFILES, f"counters_{info['workload']}")
+    with open(base + ".json", "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
-    print(json.dumps(out))
+    with open(base + ".md", "w") as f:
+        f.write(counters_markdown(out))
+    print(json.dumps({"written": [base + ".json", base + ".md"]}))
+
+
+def counters_markdown(c) -> str:
+    """The generated summary of counters_<workload>.json."""
+    run = c["run"]
+    L = [f"# Kernel counters: one layer of {c['workload']} (generated by `bench.py --counters-from`)", "",
+         f"{run['heads']} heads, {run['q_tiles']} query tiles x {run['k_tiles']} key tiles per head, "
+         f"k = {run['top_k']}, landmarks {run['landmarks']}, dtype {run['dtype']}.  Durations from the kernel "
+         f"trace; bytes from FETCH_SIZE and WRITE_SIZE per dispatch, scaled by what each counter reads for "
+         f"a plain copy of {c['copy_reference_bytes'] >> 20} MiB read + written "
+         f"(FETCH_SIZE x{c['counter_scale']['FETCH_SIZE']}, WRITE_SIZE x{c['counter_scale']['WRITE_SIZE']}); "
+         f"peaks: HBM {PEAK_HBM_GBS / 1000:g} TB/s, matrix {PEAK_TFLOPS[run['dtype']]:g} TFLOP/s "
+         f"({run['dtype']}, quoted at 2.4 GHz).", "",
+         "Commands (`$R` = repository root, run from /tmp with TMPDIR=/tmp):", "", "```"]
+    for cmd in c["commands"]:
+        L.append(cmd.replace(ROOT, "$R"))
+    L.append(f"python3 $R/bench.py --counters-from {c['commands'][0].split(' -d ')[1].split('/trace')[0].replace(ROOT, '$R')}")
+    L += ["```", "", "| kernel | step | dispatches | ms | counted GB/s | of 8 TB/s | algorithmic GB/s | of 8 TB/s | clock GHz | MFMA busy | VALU share of issue |",
+          "|---|---|---|---|---|---|---|---|---|---|---|"]
+
+    def f(x, fmt="{:.4g}"):
+        return "—" if x is None else fmt.format(x)
+    for k in c["kernels"]:
+        L.append(f"| `{k['name'][:70]}` | {k['family']} | {k['dispatches']} | {k['avg_ms']:.4f} | "
+                 f"{f(k.get('counted_gbs'), '{:.0f}')} | {f(k.get('counted_frac_hbm'), '{:.1%}')} | "
+                 f"{f(k.get('alg_gbs'), '{:.0f}')} | {f(k.get('alg_frac_hbm'), '{:.1%}')} | "
+                 f"{f(k.get('clock_ghz'), '{:.2f}')} | {f(k.get('mfma_busy'), '{:.1%}')} | "
+                 f"{f(k.get('valu_share_of_issue'), '{:.1%}')} |")
+    for k in c["kernels"]:
+        if k["family"] == "attention":
+            L += ["", f"Attention `{k['name'][:70]}`: {k['flops']:.4g} FLOP per launch in {k['avg_ms']:.3f} ms = "
+                  f"{k['tflops']:.1f} TFLOP/s, {k['frac_peak']:.1%} of the published peak"
+                  + (f", {k['frac_peak_at_clock']:.1%} of the peak at the {k['clock_ghz']:.2f} GHz it ran"
+                     if k.get("frac_peak_at_clock") else "")
+                  + (f"; HBM traffic {(k['fetch_bytes'] + k['write_bytes']) / 1e9:.2f} GB per launch."
+                     if "fetch_bytes" in k else ".")]
+    L += ["", "Per layer (dispatches per layer x mean duration): " +
+          ", ".join(f"{fam} {ms:.4f} ms" for fam, ms in c["layer_ms_by_family"].items()), ""]
+    return "\n".join(L)
 
 
 class Layer:
@@ -194,13 +364,6 @@ def time_dense(torch, S, q, v, lay, reps):
     return a.elapsed_time(b) / reps
 
 
-def attn_source_sha256() -> str:
-    h = hashlib.sha256()
-    for f in ATTN_SRCS:
-        h.update(open(f, "rb").read())
-    return h.hexdigest()
-
-
 def time_frame(torch, S, q, v, lay, reps):
     """Mean time of the frame-attention call (every query over its own frame)."""
     S.sparse3d_frame_attn_fwd(q, q, v, lay)
@@ -276,17 +439,16 @@ def time_backward(torch, S, LY, L, fwd_flops, reps=3):
             "tflops": round(2.5 * fwd_flops / (bw_ms * 1e-3) / 1e12, 2)}
 
 
-def traffic_entry():
-    """Per-launch HBM bytes of the attention kernel from committed counter runs, or None
-    when the kernel source changed after the counters were taken."""
+def counters_entry(workload: str):
+    """The committed counter summary of this workload, or None when any kernel source changed
+    after the counters were taken."""
     try:
-        t = json.load(open(TRAFFIC_FILE))
+        c = json.load(open(os.path.join(PROFILES, f"counters_{workload}.json")))
     except (OSError, ValueError):
         return None
-    sha = attn_source_sha256()
-    if t.get("attn_source_sha256") != sha:
+    if c.get("kernel_source_sha256") != kernel_source_sha256():
         return None
-    return t
+    return c
 
 
 def rocminfo_peak():
@@ -372,10 +534,143 @@ def cpu_baseline(w, inp, k, budget_s, LY):
                 layer_seconds=t_layer)
 
 
+def alg_per_dispatch(w, L, kmax: int, attn_flops: int) -> dict:
+    """Algorithmic bytes each kernel dispatch of the layer must move (FLOPs for attention):
+    operands read once, outputs written once."""
+    eb = 2 if w.dtype == "bf16" else 4
+    H, d = w.heads, w.head_dim
+    rows_q, rows_k = w.rows, L.klay[0] * L.klay[2]
+    out = {"pool_query": H * rows_q * d * eb + H * L.Tq * d * 4,
+           "pool_key": H * rows_k * d * eb + H * L.Tk * d * 4,
+           "score": H * L.Tq * L.Tk * 4 + H * (L.Tq + L.Tk) * d * 4,
+           "select": H * L.Tq * L.Tk * 4 + H * L.Tq * (kmax + 1) * 4,
+           "cast": H * L.Tk * d * (4 + eb),
+           "attention": attn_flops}
+    if w.kv_window > 1:
+        kept = L.klay[0] * L.klay[1]                   # valid rows after the subsample
+        out["subsample"] = 2 * H * kept * d * eb + 2 * H * rows_k * d * eb
+    return out
+
+
+def bench_workload(args, w, torch, S, LY, synth, dev, single: bool) -> dict:
+    log(f"workload {w.name}: S={w.frames} N={w.tokens} H={w.heads}; generating inputs")
+    inp = synth.make_inputs(w, seed=args.seed)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q = torch.from_numpy(inp.q).to(dev, dt)
+    v = torch.from_numpy(inp.v).to(dev, dt)
+    torch.cuda.synchronize()
+    L = Layer(S, LY, w, q, v, seed_k=args.top_k)
+    log(f"k={L.k}; timing {args.steps} steps after {args.warmup} warmup")
+    torch.cuda.synchronize()
+    r = run_layer(torch, L, args.steps, args.warmup)
+    rows = L.rows
+    lm_count = 0
+    flops = LY.selected_flops(r["total_cnt"], rows, L.ts)
+    if w.landmarks:
+        # landmarks per (head, query tile) = non-empty unselected tiles; every key tile of
+        # these layouts has members, so it is Tk - cnt
+        lm_count = rows * L.Tk - r["total_cnt"]
+        flops += lm_count * 64 * 4 * 64
+    sparsity = LY.measured_sparsity(r["total_cnt"], rows, L.ts, L.Tk)
+    peak = PEAK_TFLOPS[w.dtype]
+    value = flops / (r["ms_per_step"] * 1e-3) / 1e12
+    attn_tflops = flops / (r["attn_ms"] * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded multi-view latent-bank tokens)",
+        "config": {"workload": w.name, "frames": w.frames, "tokens_per_frame": w.tokens,
+                   "stride": w.stride, "specials": w.specials, "heads": w.heads,
+                   "head_dim": w.head_dim, "tile": w.tile, "top_k": L.k,
+                   "target_sparsity": w.target_sparsity, "measured_sparsity": round(sparsity, 5),
+                   "landmarks": w.landmarks, "kv_window": w.kv_window, "anchor_frame": w.anchor,
+                   "seed": args.seed},
+        f"pct_{w.dtype}_peak_layer": round(100 * value / peak, 2),
+        "kernels_ms": {"grid_subsample": round(r["sub_ms"], 4), "tile_scores": round(r["scores_ms"], 4),
+                       "select_topk": round(r["select_ms"], 4), "sparse_attn": round(r["attn_ms"], 4)},
+        "selected_flops": flops,
+        "valid_pair_flops": LY.valid_pair_flops(r["idx"].cpu().numpy(), r["cnt"].cpu().numpy(),
+                                                w.layout, L.klay),
+    }
+    alg = alg_per_dispatch(w, L, r["kmax"], flops)
+    # pool + score are one library call (timed together); select is one call
+    ps_bytes = alg["pool_query"] + alg["pool_key"] * (2 if w.landmarks else 1) + alg["score"]
+    res["kernels_gbs"] = {
+        "tile_scores": round(ps_bytes / (r["scores_ms"] * 1e-3) / 1e9, 1),
+        "select_topk": round(alg["select"] / (r["select_ms"] * 1e-3) / 1e9, 1)}
+    res["kernels_frac_hbm"] = {n: round(g / PEAK_HBM_GBS, 4) for n, g in res["kernels_gbs"].items()}
+    if args.run_info:
+        per_layer = {"pool_query": 1, "pool_key": 2 if w.landmarks else 1, "score": 1, "select": 1,
+                     "attention": 1}
+        if w.landmarks and w.dtype == "bf16":
+            per_layer["cast"] = 2
+        if w.kv_window > 1:
+            per_layer["subsample"] = 1
+        with open(args.run_info, "w") as f:
+            json.dump({"workload": w.name, "dtype": w.dtype, "heads": w.heads, "q_tiles": L.Tq,
+                       "k_tiles": L.Tk, "top_k": L.k, "kmax": r["kmax"], "landmarks": w.landmarks,
+                       "layers": args.steps + args.warmup, "attn_flops_per_launch": flops,
+                       "alg_per_dispatch": alg, "dispatches_per_layer": per_layer}, f, indent=1)
+    # roofline of the dominant kernel (sparse attention): algorithmic FLOPs per launch
+    # over its mean launch time, measured with events on its stream during the timed steps
+    c = counters_entry(w.name)
+    attn_c = next((k for k in c["kernels"] if k["family"] == "attention"), None) if c else None
+    res["roofline"] = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
+                       "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
+                       "traffic": (attn_c["fetch_bytes"] + attn_c["write_bytes"]
+                                   if attn_c and "fetch_bytes" in attn_c else None)}
+    if c:
+        # per-kernel split from the committed counters of this workload (same kernel sources)
+        res["counters"] = {k["family"]: {kk: k.get(kk) for kk in ("avg_ms", "counted_gbs", "counted_frac_hbm",
+                                                                     "alg_gbs", "alg_frac_hbm", "mfma_busy",
+                                                                     "clock_ghz") if k.get(kk) is not None}
+                           for k in c["kernels"] if k["family"] in ("pool_query", "pool_key", "score",
+                                                                   "select", "attention")}
+    dev_peak = rocminfo_peak() if w.dtype == "bf16" else None
+    if dev_peak:
+        dev_peak["attn_frac"] = round(attn_tflops / dev_peak["peak_tflops"], 4)
+        res["peak_rocminfo"] = dev_peak
+    if not args.no_dense:
+        log("timing the dense kernel")
+        dms = time_dense(torch, S, q, v, w.layout, args.dense_reps)
+        dflops = LY.pair_flops() * w.heads * L.Tq * (w.rows // 64)
+        res["dense"] = {"ms": round(dms, 3), "tflops": round(dflops / (dms * 1e-3) / 1e12, 2),
+                        "speedup_layer_vs_dense": round(dms / r["ms_per_step"], 2)}
+        # frame attention (early layers, every query over its own frame) on the same inputs
+        fms = time_frame(torch, S, q, v, w.layout, 5)
+        fflops = LY.pair_flops() * w.heads * L.Tq * (w.stride // 64)
+        res["frame_attention"] = {"ms": round(fms, 4), "tflops": round(fflops / (fms * 1e-3) / 1e12, 2)}
+        if w.landmarks is False and w.kv_window == 1:
+            res["subsampled_global_attention"] = time_sga(torch, S, LY, q, v, w)
+        if w.kv_window == 1 and w.dtype == "bf16":
+            log("timing the backward")
+            res["backward"] = time_backward(torch, S, LY, L, flops)
+    if single and not args.no_gate and not args.no_dense and w.name == "vggt_s128":
+        w90 = synth.WORKLOADS["vggt_s128_90"]
+        L90 = Layer(S, LY, w90, q, v)
+        r90 = run_layer(torch, L90, max(5, args.steps // 2), 1)
+        sp90 = LY.measured_sparsity(r90["total_cnt"], rows, L90.ts, L90.Tk)
+        f90 = LY.selected_flops(r90["total_cnt"], rows, L90.ts)
+        res["sparsity_90"] = {"top_k": L90.k, "measured_sparsity": round(sp90, 5),
+                              "ms_per_layer": round(r90["ms_per_step"], 4),
+                              "attn_ms": round(r90["attn_ms"], 4),
+                              "tflops_layer": round(f90 / (r90["ms_per_step"] * 1e-3) / 1e12, 2),
+                              "speedup_vs_dense": round(res["dense"]["ms"] / r90["ms_per_step"], 2)}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(w, inp, L.k, args.cpu_budget, LY)
+    del r, L, q, v, inp
+    return res
+
+
 def main():
     args = parse()
-    if args.traffic_from:
-        write_traffic(*args.traffic_from, args.copy_mb or 1024, args.workload)
+    if args.profile_commands:
+        print("\n".join(profile_commands(args.workload, args.profile_commands)))
+        return
+    if args.counters_from:
+        write_counters(args.counters_from)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the layer shards by "
@@ -399,93 +694,11 @@ def main():
         torch.cuda.synchronize()
         log(f"copy reference: {args.copy_mb} MiB read + {args.copy_mb} MiB written per launch")
         del src, dst
-    w = synth.WORKLOADS[args.workload]
-    log(f"workload {w.name}: S={w.frames} N={w.tokens} H={w.heads}; generating inputs")
-    inp = synth.make_inputs(w, seed=args.seed)
-    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    q = torch.from_numpy(inp.q).to(dev, dt)
-    v = torch.from_numpy(inp.v).to(dev, dt)
-    torch.cuda.synchronize()
-    L = Layer(S, LY, w, q, v)
-    log(f"k={L.k}; timing {args.steps} steps after {args.warmup} warmup")
-    torch.cuda.synchronize()
-    r = run_layer(torch, L, args.steps, args.warmup)
-    rows = L.rows
-    lm_count = 0
-    flops = LY.selected_flops(r["total_cnt"], rows, L.ts)
-    if w.landmarks:
-        # landmarks per (head, query tile) = non-empty unselected tiles; every key tile of
-        # these layouts has members, so it is Tk - cnt
-        lm_count = rows * L.Tk - r["total_cnt"]
-        flops += lm_count * 64 * 4 * 64
-    sparsity = LY.measured_sparsity(r["total_cnt"], rows, L.ts, L.Tk)
-    value = flops / (r["ms_per_step"] * 1e-3) / 1e12
-    attn_tflops = flops / (r["attn_ms"] * 1e-3) / 1e12
-    res = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
-        "data": "synthetic (seeded multi-view latent-bank tokens)",
-        "config": {"workload": w.name, "frames": w.frames, "tokens_per_frame": w.tokens,
-                   "stride": w.stride, "specials": w.specials, "heads": w.heads,
-                   "head_dim": w.head_dim, "tile": w.tile, "top_k": L.k,
-                   "target_sparsity": w.target_sparsity, "measured_sparsity": round(sparsity, 5),
-                   "landmarks": w.landmarks, "kv_window": w.kv_window, "anchor_frame": w.anchor,
-                   "seed": args.seed},
-        "pct_bf16_peak_layer": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "kernels_ms": {"grid_subsample": round(r["sub_ms"], 4), "tile_scores": round(r["scores_ms"], 4),
-                       "select_topk": round(r["select_ms"], 4), "sparse_attn": round(r["attn_ms"], 4)},
-        "selected_flops": flops,
-        "valid_pair_flops": LY.valid_pair_flops(r["idx"].cpu().numpy(), r["cnt"].cpu().numpy(),
-                                                w.layout, L.klay),
-    }
-    Lq = w.rows
-    bytes_in = 2 * w.heads * Lq * 64 * (2 if w.dtype == "bf16" else 4)
-    sc_bytes = 4 * w.heads * L.Tq * L.Tk
-    res["kernels_gbs"] = {
-        "tile_scores": round((bytes_in * (1.5 if w.landmarks else 1.0) + sc_bytes) / (r["scores_ms"] * 1e-3) / 1e9, 1),
-        "select_topk": round((sc_bytes + 4 * rows * (r["kmax"] + 1)) / (r["select_ms"] * 1e-3) / 1e9, 1),
-    }
-    # roofline of the dominant kernel (sparse attention): algorithmic FLOPs per launch
-    # over its mean launch time, measured with events on its stream during the timed steps
-    tr = traffic_entry()
-    res["roofline"] = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                       "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                       "traffic": (tr["bytes_per_launch"] if tr and tr.get("workload") == w.name else None)}
-    dev_peak = rocminfo_peak()
-    if dev_peak:
-        dev_peak["attn_frac"] = round(attn_tflops / dev_peak["peak_tflops"], 4)
-        res["peak_rocminfo"] = dev_peak
-    if not args.no_dense:
-        log("timing the dense kernel")
-        dms = time_dense(torch, S, q, v, w.layout, args.dense_reps)
-        dflops = LY.pair_flops() * w.heads * L.Tq * (w.rows // 64)
-        res["dense"] = {"ms": round(dms, 3), "tflops": round(dflops / (dms * 1e-3) / 1e12, 2),
-                        "speedup_layer_vs_dense": round(dms / r["ms_per_step"], 2)}
-    if not args.no_dense:
-        # frame attention (early layers, every query over its own frame) on the same inputs
-        fms = time_frame(torch, S, q, v, w.layout, 5)
-        fflops = LY.pair_flops() * w.heads * L.Tq * (w.stride // 64)
-        res["frame_attention"] = {"ms": round(fms, 4), "tflops": round(fflops / (fms * 1e-3) / 1e12, 2)}
-        if w.landmarks is False and w.kv_window == 1:
-            res["subsampled_global_attention"] = time_sga(torch, S, LY, q, v, w)
-        if w.kv_window == 1:
-            res["backward"] = time_backward(torch, S, LY, L, flops)
-    if not args.no_gate and not args.no_dense and w.name == "vggt_s128":
-        w90 = synth.WORKLOADS["vggt_s128_90"]
-        L90 = Layer(S, LY, w90, q, v)
-        r90 = run_layer(torch, L90, max(5, args.steps // 2), 1)
-        sp90 = LY.measured_sparsity(r90["total_cnt"], rows, L90.ts, L90.Tk)
-        f90 = LY.selected_flops(r90["total_cnt"], rows, L90.ts)
-        res["sparsity_90"] = {"top_k": L90.k, "measured_sparsity": round(sp90, 5),
-                              "ms_per_layer": round(r90["ms_per_step"], 4),
-                              "attn_ms": round(r90["attn_ms"], 4),
-                              "tflops_layer": round(f90 / (r90["ms_per_step"] * 1e-3) / 1e12, 2),
-                              "speedup_vs_dense": round(res["dense"]["ms"] / r90["ms_per_step"], 2)}
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample")
-        res["cpu_baseline"] = cpu_baseline(w, inp, L.k, args.cpu_budget, LY)
-    print(json.dumps(res), flush=True)
+    names = CONFIGS if args.all_configs else [args.workload]
+    for name in names:
+        res = bench_workload(args, synth.WORKLOADS[name], torch, S, LY, synth, dev, single=not args.all_configs)
+        print(json.dumps(res), flush=True)
+        torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

@@ -1,0 +1,98 @@
+"""The counter reader of bench.py on small hand-made rocprofv3 outputs (no GPU): scaling of
+the byte counters by the copy reference, GB/s, clock, matrix-core busy share, FLOP rate."""
+import csv
+import json
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+ATTN = "void s3d::k_attn_bf16<false, false, false, false, 1>(s3d::AttnDev)"
+POOLQ = "void s3d::k_tile_pool<true, false>(void const*, int, s3d::Lay, float*)"
+POOLK = "void s3d::k_tile_pool<true, true>(void const*, int, s3d::Lay, float*)"
+SEL = "void s3d::k_select_topk_wave<44, true>(float const*, int)"
+COPY = "void at::native::vectorized_elementwise_kernel<4, at::native::CUDAFunctor_add<float> >(int)"
+BWD = "void s3d::k_attn_bwd_dq<false>(s3d::BwdDev)"
+
+
+def _pmc(path, rows):
+    os.makedirs(path)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
+                    "End_Timestamp"])
+        for r in rows:
+            w.writerow(r)
+
+
+def test_counter_reader(tmp_path, monkeypatch):
+    d = tmp_path / "prof"
+    os.makedirs(d / "trace")
+    with open(d / "trace" / "run_kernel_stats.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs"])
+        w.writerow([ATTN, 3, 30e6, 10e6])              # 10 ms
+        w.writerow([POOLQ, 3, 3e5, 1e5])               # 0.1 ms
+        w.writerow([POOLK, 3, 3e5, 1e5])
+        w.writerow([SEL, 9, 1.8e6, 2e5])               # 0.2 ms (calibration launches too)
+        w.writerow([COPY, 2, 1e6, 5e5])
+        w.writerow([BWD, 1, 1e6, 1e6])                 # not a layer kernel
+    mib = bench.PROFILE_COPY_MB * 1024                  # KiB moved each way by the copy
+    # FETCH_SIZE counts half the bytes (scale 2), WRITE_SIZE all (scale 1)
+    _pmc(str(d / "fetch"), [[1, COPY, "FETCH_SIZE", mib / 2, 0, 1], [2, ATTN, "FETCH_SIZE", 5e6, 0, 1],
+                            [3, ATTN, "FETCH_SIZE", 7e6, 0, 1], [4, SEL, "FETCH_SIZE", 2.5e5, 0, 1]])
+    _pmc(str(d / "write"), [[1, COPY, "WRITE_SIZE", mib, 0, 1], [2, ATTN, "WRITE_SIZE", 1e5, 0, 1],
+                            [3, ATTN, "WRITE_SIZE", 1e5, 0, 1], [4, SEL, "WRITE_SIZE", 1e3, 0, 1]])
+    # the attention dispatch in the counter pass: 10 ms at 2.0 GHz on every XCD
+    cyc = 2.0e9 * 10e-3
+    _pmc(str(d / "sq"), [[7, ATTN, "GRBM_GUI_ACTIVE", cyc * bench.N_XCD, 0, 10_000_000],
+                         [7, ATTN, "SQ_VALU_MFMA_BUSY_CYCLES", 0.4 * cyc * bench.N_SIMD, 0, 10_000_000],
+                         [7, ATTN, "SQ_ACTIVE_INST_ANY", 100.0, 0, 10_000_000],
+                         [7, ATTN, "SQ_ACTIVE_INST_VALU", 55.0, 0, 10_000_000],
+                         [7, ATTN, "SQ_WAVE_CYCLES", 400.0, 0, 10_000_000]])
+    info = {"workload": "fake", "dtype": "bf16", "heads": 2, "q_tiles": 4, "k_tiles": 4, "top_k": 1,
+            "kmax": 2, "landmarks": False, "layers": 3, "attn_flops_per_launch": 8e12,
+            "alg_per_dispatch": {"pool_query": 4e8, "pool_key": 4e8, "score": 1e9, "select": 1e9,
+                                 "cast": 0, "attention": 8e12},
+            "dispatches_per_layer": {"pool_query": 1, "pool_key": 1, "score": 1, "select": 1, "attention": 1}}
+    json.dump(info, open(d / "run_info.json", "w"))
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    bench.write_counters(str(d))
+    c = json.load(open(tmp_path / "profiles" / "counters_fake.json"))
+    assert c["counter_scale"] == {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
+    k = {x["family"]: x for x in c["kernels"]}
+    assert set(k) == {"attention", "pool_query", "pool_key", "select"}   # backward and copy left out
+    a = k["attention"]
+    assert a["fetch_bytes"] == round(6e6 * 1024 * 2) and a["write_bytes"] == round(1e5 * 1024)
+    assert a["counted_gbs"] == pytest.approx((6e6 * 2 + 1e5) * 1024 / 10e-3 / 1e9, rel=1e-3)
+    assert a["tflops"] == pytest.approx(800.0) and a["frac_peak"] == pytest.approx(0.32)
+    assert a["clock_ghz"] == pytest.approx(2.0) and a["mfma_busy"] == pytest.approx(0.4)
+    assert a["frac_peak_at_clock"] == pytest.approx(800.0 / (2500.0 * 2.0 / 2.4), rel=1e-3)
+    assert a["valu_share_of_issue"] == pytest.approx(0.55)
+    assert a["issue_share_of_wave_cycles"] == pytest.approx(0.25)
+    s = k["select"]
+    assert s["alg_gbs"] == pytest.approx(1e9 / 2e-4 / 1e9) and s["alg_frac_hbm"] == pytest.approx(0.625)
+    assert s["counted_gbs"] == pytest.approx((2.5e5 * 2 + 1e3) * 1024 / 2e-4 / 1e9, rel=1e-3)
+    assert "counted_gbs" not in k["pool_query"]                          # no counter rows for it
+    assert c["layer_ms_by_family"] == {"pool_query": 0.1, "pool_key": 0.1, "select": 0.2, "attention": 10.0}
+    md = open(tmp_path / "profiles" / "counters_fake.md").read()
+    assert "rocprofv3 --pmc FETCH_SIZE" in md and "| attention |" in md
+
+
+def test_kernel_family():
+    assert bench.kernel_family(POOLQ) == "pool_query"
+    assert bench.kernel_family(POOLK) == "pool_key"
+    assert bench.kernel_family("void s3d::k_tile_scores_mfma(float const*)") == "score"
+    assert bench.kernel_family(SEL) == "select"
+    assert bench.kernel_family("void s3d::k_select_topk(float const*)") == "select"
+    assert bench.kernel_family(ATTN) == "attention"
+    assert bench.kernel_family("void s3d::k_attn<true, true, false>(s3d::AttnDev)") == "attention"
+    assert bench.kernel_family(BWD) is None
+    assert bench.kernel_family("void s3d::k_attn_bwd_dkv<true>(s3d::BwdDev)") is None
+    assert bench.kernel_family("void s3d::k_cast_bf16(float const*, long, __bf16*)") == "cast"
+    assert bench.kernel_family(COPY) == "copy"
+    assert bench.kernel_family("void other::kernel()") is None
