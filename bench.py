@@ -7,9 +7,11 @@ Inputs are resident in HBM before the timed region starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload vggt_s128]
 
-Prints one JSON line.  ``value`` is the effective TFLOP/s of the layer: the
-algorithmic FLOPs of every attended (query tile, key tile) pair divided by the
-wall time of the whole step.
+Prints one JSON line (one per configuration with --all-configs).  ``value`` is
+the effective TFLOP/s of the layer: the algorithmic FLOPs of every attended
+(query tile, key tile) pair divided by the wall time of the whole step.  Before
+the warmup steps the GPU runs 0.3 s of dense matrix work, so that host-only phases
+(input generation, the CPU baseline) do not leave it at idle clocks.
 """
 from __future__ import annotations
 
@@ -552,6 +554,20 @@ def alg_per_dispatch(w, L, kmax: int, attn_flops: int) -> dict:
     return out
 
 
+def spin_up(torch, dev, seconds: float = 0.3):
+    """Bring the GPU out of its idle clocks before the warmup steps: a few hundred
+    milliseconds of dense matrix work (seconds of host-only work, such as input generation
+    or the CPU baseline, leave it idle; a small layer's warmup steps alone do not ramp it
+    up, and the timed steps then ran several times slower)."""
+    a = torch.randn(4096, 4096, device=dev, dtype=torch.bfloat16)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            b = a @ a
+        torch.cuda.synchronize()
+    del a, b
+
+
 def bench_workload(args, w, torch, S, LY, synth, dev, single: bool) -> dict:
     log(f"workload {w.name}: S={w.frames} N={w.tokens} H={w.heads}; generating inputs")
     inp = synth.make_inputs(w, seed=args.seed)
@@ -561,7 +577,7 @@ def bench_workload(args, w, torch, S, LY, synth, dev, single: bool) -> dict:
     torch.cuda.synchronize()
     L = Layer(S, LY, w, q, v, seed_k=args.top_k)
     log(f"k={L.k}; timing {args.steps} steps after {args.warmup} warmup")
-    torch.cuda.synchronize()
+    spin_up(torch, dev)
     r = run_layer(torch, L, args.steps, args.warmup)
     rows = L.rows
     lm_count = 0
