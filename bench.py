@@ -487,7 +487,8 @@ def cpu_model():
 
 
 def cpu_baseline(w, inp, k, budget_s, LY):
-    """The fp64 oracle on a bounded sample of the same workload, scaled to TFLOP/s."""
+    """The fp64 oracle on a bounded sample of the same workload (subsampled keys and the
+    landmark term where the workload has them), scaled to TFLOP/s."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -499,15 +500,23 @@ def cpu_baseline(w, inp, k, budget_s, LY):
     H = w.heads
     heads = [0]                                        # pool/score/select/attend for one head
     t0 = time.perf_counter()
-    qbar, qc = oracle.tile_pool(inp.q[:1], lay, 64, "query")
-    kbar, kc = oracle.tile_pool(inp.k[:1], lay, 64, "key")
+    Q, K, V, klay = inp.q[:1], inp.k[:1], inp.v[:1], lay
+    if w.kv_window > 1:
+        K, V, klay = oracle.subsample_keys(K, V, lay, w.grid, w.kv_window, 64)
+    qbar, qc = oracle.tile_pool(Q, lay, 64, "query")
+    kbar, kc = oracle.tile_pool(K, klay, 64, "key")
+    lm = {}
+    if w.landmarks:
+        vbar, _ = oracle.tile_pool(V, klay, 64, "key")
+        lm = dict(kbar=kbar, vbar=vbar, kcount=kc)
     sig = oracle.tile_scores(qbar, qc, kbar, kc, 0.125)
     t_ps = time.perf_counter() - t0
     Tq, Tk = sig.shape[1], sig.shape[2]
-    tpf = w.stride // 64
+    tpf = klay.stride // 64
+    nonempty = kc > 0
     rng = np.random.default_rng(0)
     order = rng.permutation(Tq)
-    done, t_att, cnt_sum = 0, 0.0, 0
+    done, t_att, cnt_sum, lm_sum = 0, 0.0, 0, 0
     kmax = oracle.kmax_for(Tk, k, tpf, w.anchor)
     while done < Tq and (t_ps + t_att) < budget_s:
         chunk = order[done:done + 8]
@@ -518,21 +527,24 @@ def cpu_baseline(w, inp, k, budget_s, LY):
             sel = oracle.select_tiles(sig[0, t], k, tpf, w.anchor)
             cnt[0, t] = len(sel)
             idx[0, t, :len(sel)] = sel
-        oracle.sparse_attend(inp.q, inp.k, inp.v, lay, lay, 64, idx, cnt, 0.125,
-                             query_tiles=chunk, heads=heads)
+            if w.landmarks:
+                lm_sum += int(nonempty.sum() - nonempty[sel].sum())
+        oracle.sparse_attend(Q, K, V, lay, klay, 64, idx, cnt, 0.125, query_tiles=chunk, heads=heads, **lm)
         t_att += time.perf_counter() - t1
         cnt_sum += int(cnt.sum())
         done += len(chunk)
     # whole layer = H heads x (pool+score for a head + Tq tiles of select+attend)
     t_layer = H * (t_ps + t_att * Tq / done)
-    ts = LY.special_tiles(w.layout)
-    flops_sample = LY.selected_flops(cnt_sum, done, ts)
+    ts = LY.special_tiles(tuple(klay))
+    # landmarks: 4 * 64 FLOP per (query row, landmark), 64 rows per query tile
+    flops_sample = LY.selected_flops(cnt_sum, done, ts) + lm_sum * 64 * 4 * 64
     flops_layer = flops_sample * (H * Tq / done)
     return dict(value=flops_layer / t_layer / 1e12, unit="TFLOP/s", cores=int(min(threads, cores)),
                 kind="oracle", cpu_model=cpu_model(),
-                sample=(f"head 0: full pool+score ({t_ps:.1f}s), select+attend on {done} of {Tq} "
-                        f"query tiles ({t_att:.1f}s); layer time extrapolated x{H} heads, "
-                        f"x{Tq / done:.1f} tiles = {t_layer:.0f}s"),
+                sample=(f"head 0: full pool+score ({t_ps:.1f}s), select+attend"
+                        f"{' with landmarks' if w.landmarks else ''} on {done} of {Tq} query tiles "
+                        f"({t_att:.1f}s); layer time extrapolated x{H} heads, x{Tq / done:.1f} tiles = "
+                        f"{t_layer:.0f}s"),
                 layer_seconds=t_layer)
 
 
