@@ -302,16 +302,18 @@ class Layer:
                                                                   self.w.grid, self.w.kv_window)
 
     def scores(self):
+        """(qbar, kbar, vbar, scores): with landmarks, kbar/vbar are the means in the operand
+        dtype that the pooling pass writes alongside the fp32 ones."""
         lm = self.w.landmarks
-        return self.S.sparse3d_tile_scores(self.q, self.K, self.lay, self.klay, v=self.V if lm else None)
+        r = self.S.sparse3d_tile_scores(self.q, self.K, self.lay, self.klay, v=self.V if lm else None,
+                                        operand_means=lm)
+        return (r[0], r[4], r[5], r[3]) if lm else r
 
     def select(self, scores):
         return self.S.sparse3d_select_topk(scores, self.k, self.tpf, self.w.anchor)
 
     def attend(self, idx, cnt, kbar, vbar):
         lm = self.w.landmarks
-        if lm and self.q.dtype != kbar.dtype:        # landmark means in the operand precision
-            kbar, vbar = self.S.sparse3d_cast(kbar, self.q.dtype), self.S.sparse3d_cast(vbar, self.q.dtype)
         return self.S.sparse3d_sparse_attn_fwd(self.q, self.K, self.V, self.lay, self.klay, idx, cnt,
                                                kbar=kbar if lm else None, vbar=vbar if lm else None)
 
@@ -415,9 +417,7 @@ def time_backward(torch, S, LY, L, fwd_flops, reps=3):
     qbar, kbar, vbar, sc = L.scores()
     idx, cnt = L.select(sc)
     del sc, qbar
-    lm = {}
-    if L.w.landmarks:
-        lm = dict(kbar=S.sparse3d_cast(kbar, L.q.dtype), vbar=S.sparse3d_cast(vbar, L.q.dtype))
+    lm = dict(kbar=kbar, vbar=vbar) if L.w.landmarks else {}     # operand-dtype means
     del kbar, vbar
     out, lse = S.sparse3d_sparse_attn_fwd(L.q, L.K, L.V, L.lay, L.klay, idx, cnt, return_lse=True, **lm)
     g = torch.Generator(device=L.q.device).manual_seed(0)
@@ -555,7 +555,8 @@ def alg_per_dispatch(w, L, kmax: int, attn_flops: int) -> dict:
     H, d = w.heads, w.head_dim
     rows_q, rows_k = w.rows, L.klay[0] * L.klay[2]
     out = {"pool_query": H * rows_q * d * eb + H * L.Tq * d * 4,
-           "pool_key": H * rows_k * d * eb + H * L.Tk * d * 4,
+           # with landmarks the key/value pools also write the means in the operand dtype
+           "pool_key": H * rows_k * d * eb + H * L.Tk * d * 4 + (H * L.Tk * d * eb if w.landmarks else 0),
            "score": H * L.Tq * L.Tk * 4 + H * (L.Tq + L.Tk) * d * 4,
            "select": H * L.Tq * L.Tk * 4 + H * L.Tq * (kmax + 1) * 4,
            "cast": H * L.Tk * d * (4 + eb),
@@ -631,8 +632,6 @@ def bench_workload(args, w, torch, S, LY, synth, dev, single: bool) -> dict:
     if args.run_info:
         per_layer = {"pool_query": 1, "pool_key": 2 if w.landmarks else 1, "score": 1, "select": 1,
                      "attention": 1}
-        if w.landmarks and w.dtype == "bf16":
-            per_layer["cast"] = 2
         if w.kv_window > 1:
             per_layer["subsample"] = 1
         with open(args.run_info, "w") as f:

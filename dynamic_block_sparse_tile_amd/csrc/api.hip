@@ -35,15 +35,16 @@ const char* sparse3d_status_string(int status) {
 int sparse3d_tile_scores(const void* q, const void* k, const void* v, sparse3d_dtype dtype,
                          int32_t heads, int32_t head_dim, int32_t tile,
                          const sparse3d_layout* qlay, const sparse3d_layout* klay, float scale,
-                         float* qbar, float* kbar, float* vbar, float* scores, void* stream) {
+                         float* qbar, float* kbar, float* vbar, float* scores, void* kbar_op,
+                         void* vbar_op, void* stream) {
     const int st = validate_tile_scores(q, k, v, dtype, heads, head_dim, tile, qlay, klay, qbar,
-                                        kbar, vbar, scores);
+                                        kbar, vbar, scores, kbar_op, vbar_op);
     if (st != SPARSE3D_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const LayH ql = to_lay(*qlay), kl = to_lay(*klay);
-    S3D_HIP(launch_tile_pool(q, dtype, heads, ql, false, qbar, s));
-    S3D_HIP(launch_tile_pool(k, dtype, heads, kl, true, kbar, s));
-    if (v) S3D_HIP(launch_tile_pool(v, dtype, heads, kl, true, vbar, s));
+    S3D_HIP(launch_tile_pool(q, dtype, heads, ql, false, qbar, nullptr, s));
+    S3D_HIP(launch_tile_pool(k, dtype, heads, kl, true, kbar, kbar_op, s));
+    if (v) S3D_HIP(launch_tile_pool(v, dtype, heads, kl, true, vbar, vbar_op, s));
     S3D_HIP(launch_tile_scores(qbar, kbar, heads, ql, kl, scale, scores, s));
     return SPARSE3D_OK;
 }

@@ -15,8 +15,8 @@ struct LayH {
 };
 inline LayH to_lay(const sparse3d_layout& l) { return {l.frames, l.tokens, l.stride, l.specials}; }
 
-hipError_t launch_tile_pool(const void* x, int dtype, int heads, LayH lay, bool key_rows,
-                            float* out, hipStream_t st);
+hipError_t launch_tile_pool(const void* x, int dtype, int heads, LayH lay, bool key_rows, float* out,
+                            void* out_op, hipStream_t st);
 hipError_t launch_tile_scores(const float* qbar, const float* kbar, int heads, LayH ql, LayH kl,
                               float scale, float* scores, hipStream_t st);
 // k_heads: host array of one budget per head

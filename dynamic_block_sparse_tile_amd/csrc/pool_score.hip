@@ -16,9 +16,11 @@ namespace s3d {
 // c8 = lane%8); a wave load covers 8 consecutive rows = 1 KiB of bf16, so every
 // access is a full 128-byte line.  Sums run in fp32: sequentially over the rows of a
 // lane, then a fixed butterfly over the 8 row groups, so results are reproducible.
+// out_op (optional): the same means rounded to the operand dtype (bf16: round to nearest
+// even, as sparse3d_cast), the form the bf16 attention reads landmark means in.
 template <bool BF16, bool KEY>
 __global__ __launch_bounds__(256) void k_tile_pool(const void* __restrict__ x, int T, Lay L,
-                                                   float* __restrict__ out) {
+                                                   float* __restrict__ out, void* __restrict__ out_op) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wave;
     const int h = blockIdx.y;
@@ -65,9 +67,21 @@ __global__ __launch_bounds__(256) void k_tile_pool(const void* __restrict__ x, i
         float r[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) r[e] = n > 0 ? acc[e] / (float)n : 0.f;
-        float4* o = reinterpret_cast<float4*>(out + ((size_t)h * T + t) * HD + c8 * 8);
+        const size_t e0 = ((size_t)h * T + t) * HD + c8 * 8;
+        float4* o = reinterpret_cast<float4*>(out + e0);
         o[0] = make_float4(r[0], r[1], r[2], r[3]);
         o[1] = make_float4(r[4], r[5], r[6], r[7]);
+        if (out_op) {
+            if (BF16) {
+                *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out_op) + e0) =
+                    make_uint4(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]),
+                               pack_bf16x2(r[6], r[7]));
+            } else {
+                float4* c = reinterpret_cast<float4*>(static_cast<float*>(out_op) + e0);
+                c[0] = o[0];
+                c[1] = o[1];
+            }
+        }
     }
 }
 
@@ -257,15 +271,15 @@ __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restric
 }
 
 hipError_t launch_tile_pool(const void* x, int dtype, int heads, LayH lay, bool key_rows, float* out,
-                            hipStream_t st) {
+                            void* out_op, hipStream_t st) {
     const int T = lay.S * lay.P / TILE;
     const Lay L{lay.S, lay.N, lay.P, lay.nsp};
     const dim3 grid((T + 3) / 4, heads), block(256);
     const bool bf16 = dtype == SPARSE3D_BF16;
-    if (bf16 && key_rows) hipLaunchKernelGGL((k_tile_pool<true, true>), grid, block, 0, st, x, T, L, out);
-    else if (bf16) hipLaunchKernelGGL((k_tile_pool<true, false>), grid, block, 0, st, x, T, L, out);
-    else if (key_rows) hipLaunchKernelGGL((k_tile_pool<false, true>), grid, block, 0, st, x, T, L, out);
-    else hipLaunchKernelGGL((k_tile_pool<false, false>), grid, block, 0, st, x, T, L, out);
+    if (bf16 && key_rows) hipLaunchKernelGGL((k_tile_pool<true, true>), grid, block, 0, st, x, T, L, out, out_op);
+    else if (bf16) hipLaunchKernelGGL((k_tile_pool<true, false>), grid, block, 0, st, x, T, L, out, out_op);
+    else if (key_rows) hipLaunchKernelGGL((k_tile_pool<false, true>), grid, block, 0, st, x, T, L, out, out_op);
+    else hipLaunchKernelGGL((k_tile_pool<false, false>), grid, block, 0, st, x, T, L, out, out_op);
     return hipGetLastError();
 }
 

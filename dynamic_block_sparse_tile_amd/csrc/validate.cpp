@@ -51,9 +51,10 @@ int check_logit_params(float scale, float landmark_bias) {
 int validate_tile_scores(const void* q, const void* k, const void* v, int dtype, int32_t heads,
                          int32_t head_dim, int32_t tile, const sparse3d_layout* qlay,
                          const sparse3d_layout* klay, const float* qbar, const float* kbar,
-                         const float* vbar, const float* scores) {
+                         const float* vbar, const float* scores, const void* kbar_op, const void* vbar_op) {
     if (!q || !k || !qbar || !kbar || !scores) return SPARSE3D_ERR_NULL;
     if ((v == nullptr) != (vbar == nullptr)) return SPARSE3D_ERR_NULL;
+    if (vbar_op && !v) return SPARSE3D_ERR_NULL;         // value means need the values
     S3D_TRY(check_dtype(dtype));
     S3D_TRY(check_heads_dims(heads, head_dim, tile));
     S3D_TRY(check_layout(qlay));
@@ -68,14 +69,16 @@ int validate_tile_scores(const void* q, const void* k, const void* v, int dtype,
     const size_t Tq = lay_tiles(*qlay), Tk = lay_tiles(*klay);
     const size_t qbar_b = size_t(heads) * Tq * head_dim * 4;
     const size_t kbar_b = size_t(heads) * Tk * head_dim * 4;
+    const size_t op_b = size_t(heads) * Tk * head_dim * eb;   // means in the operand dtype
     const size_t sc_b = size_t(heads) * Tq * Tk * 4;
-    const void* outs[4] = {qbar, kbar, vbar, scores};
-    const size_t outn[4] = {qbar_b, kbar_b, vbar ? kbar_b : 0, sc_b};
-    for (int i = 0; i < 4; ++i) {
+    constexpr int NO = 6;
+    const void* outs[NO] = {qbar, kbar, vbar, scores, kbar_op, vbar_op};
+    const size_t outn[NO] = {qbar_b, kbar_b, vbar ? kbar_b : 0, sc_b, op_b, op_b};
+    for (int i = 0; i < NO; ++i) {
         if (overlaps(outs[i], outn[i], q, qb) || overlaps(outs[i], outn[i], k, kb) ||
             overlaps(outs[i], outn[i], v, kb))
             return SPARSE3D_ERR_ALIAS;
-        for (int j = i + 1; j < 4; ++j)
+        for (int j = i + 1; j < NO; ++j)
             if (overlaps(outs[i], outn[i], outs[j], outn[j])) return SPARSE3D_ERR_ALIAS;
     }
     return SPARSE3D_OK;

@@ -36,7 +36,8 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb);
 int validate_tile_scores(const void* q, const void* k, const void* v, int dtype, int32_t heads,
                          int32_t head_dim, int32_t tile, const sparse3d_layout* qlay,
                          const sparse3d_layout* klay, const float* qbar, const float* kbar,
-                         const float* vbar, const float* scores);
+                         const float* vbar, const float* scores, const void* kbar_op = nullptr,
+                         const void* vbar_op = nullptr);
 
 int validate_select_topk(const float* scores, int32_t heads, int32_t q_tiles, int32_t k_tiles,
                          int32_t k, int32_t tiles_per_frame, int32_t anchor_frame,

@@ -113,12 +113,13 @@ def sparse_global_attention(q, k, v, qlay, klay=None, *, top_k: int, anchor_fram
     """One dynamic tile-sparse global-attention layer (three library calls)."""
     klay = qlay if klay is None else klay
     scale = 1.0 / math.sqrt(q.shape[2]) if scale is None else scale
-    qbar, kbar, vbar, scores = S.sparse3d_tile_scores(q, k, qlay, klay, v=v if landmarks else None,
-                                                      scale=scale)
+    # with landmarks the pooling pass also writes the means in the operand dtype (the
+    # precision the attention reads them in)
+    sc = S.sparse3d_tile_scores(q, k, qlay, klay, v=v if landmarks else None, scale=scale,
+                                operand_means=landmarks)
+    qbar, kbar, vbar, scores = sc[:4]
+    km, vm = sc[4:] if landmarks else (None, None)
     idx, cnt = S.sparse3d_select_topk(scores, top_k, tiles_per_frame(klay), anchor_frame)
-    km, vm = (kbar, vbar) if q.dtype == torch.float32 else (None, None)
-    if landmarks and q.dtype != torch.float32:          # the operand precision of the means
-        km, vm = S.sparse3d_cast(kbar, q.dtype), S.sparse3d_cast(vbar, q.dtype)
     res = S.sparse3d_sparse_attn_fwd(q, k, v, qlay, klay, idx, cnt,
                                      kbar=km if landmarks else None, vbar=vm if landmarks else None,
                                      landmark_bias=landmark_bias, scale=scale,

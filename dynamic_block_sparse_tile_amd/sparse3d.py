@@ -59,7 +59,7 @@ _SIGS = {
     "sparse3d_abi_version": ([], ctypes.c_int),
     "sparse3d_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "sparse3d_tile_scores": ([_vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32, _LP, _LP, _f32,
-                              _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+                              _vp, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "sparse3d_select_topk": ([_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp],
                              ctypes.c_int),
     "sparse3d_sparse_attn_fwd": ([_vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32, _LP, _LP, _vp,
@@ -220,8 +220,11 @@ def _tiles(lay) -> int:
 
 
 def sparse3d_tile_scores(q: torch.Tensor, k: torch.Tensor, qlay, klay=None,
-                         v: Optional[torch.Tensor] = None, scale: Optional[float] = None):
-    """Pooled tile summaries and tile scores.  Returns (qbar, kbar, vbar|None, scores)."""
+                         v: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                         operand_means: bool = False):
+    """Pooled tile summaries and tile scores.  Returns (qbar, kbar, vbar|None, scores); with
+    ``operand_means`` also (kbar_op, vbar_op|None), the key/value means in q's dtype (the
+    landmark means the attention calls take), written by the same pooling pass."""
     klay = qlay if klay is None else klay
     H = _operands(q, k, v, qlay, klay)
     _dev(q, "q"), _dev(k, "k")
@@ -234,10 +237,16 @@ def sparse3d_tile_scores(q: torch.Tensor, k: torch.Tensor, qlay, klay=None,
     kbar = torch.empty((H, Tk, HEAD_DIM), **f)
     vbar = torch.empty((H, Tk, HEAD_DIM), **f) if v is not None else None
     scores = torch.empty((H, Tq, Tk), **f)
+    kop = vop = None
+    if operand_means:
+        kop = torch.empty((H, Tk, HEAD_DIM), device=q.device, dtype=q.dtype)
+        vop = torch.empty((H, Tk, HEAD_DIM), device=q.device, dtype=q.dtype) if v is not None else None
     ql, kl = _lay(qlay), _lay(klay)
     _check(library().sparse3d_tile_scores(
         _ptr(q), _ptr(k), _ptr(v), _dt(q), H, q.shape[2], TILE, ctypes.byref(ql), ctypes.byref(kl),
-        scale, _ptr(qbar), _ptr(kbar), _ptr(vbar), _ptr(scores), _stream(q)))
+        scale, _ptr(qbar), _ptr(kbar), _ptr(vbar), _ptr(scores), _ptr(kop), _ptr(vop), _stream(q)))
+    if operand_means:
+        return qbar, kbar, vbar, scores, kop, vop
     return qbar, kbar, vbar, scores
 
 

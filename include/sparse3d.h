@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define SPARSE3D_ABI_VERSION 4
+#define SPARSE3D_ABI_VERSION 5
 
 typedef enum { SPARSE3D_F32 = 0, SPARSE3D_BF16 = 1 } sparse3d_dtype;
 
@@ -108,11 +108,17 @@ const char* sparse3d_status_string(int status);
  * each fp32 mean split into two bf16 terms and all four cross products accumulated in
  * fp32, within about 1e-6 (relative) of the fp32 dot product.  v and vbar must be both
  * NULL or both non-NULL.
+ *
+ * kbar_op, vbar_op (optional, NULL to skip; vbar_op needs v): the key and value means again,
+ * in the operand dtype ([heads, Tk, 64] of `dtype`; for BF16 rounded to nearest even, the
+ * same values sparse3d_cast gives).  These are the landmark means the attention calls take,
+ * written by the same pooling pass, so a bf16 landmark layer needs no separate cast.
  */
 int sparse3d_tile_scores(const void* q, const void* k, const void* v, sparse3d_dtype dtype,
                          int32_t heads, int32_t head_dim, int32_t tile,
                          const sparse3d_layout* qlay, const sparse3d_layout* klay, float scale,
-                         float* qbar, float* kbar, float* vbar, float* scores, void* stream);
+                         float* qbar, float* kbar, float* vbar, float* scores, void* kbar_op,
+                         void* vbar_op, void* stream);
 
 /*
  * Per query tile: the k key tiles with the largest score (larger first; equal scores,
@@ -150,8 +156,9 @@ int sparse3d_select_topk_per_head(const float* scores, int32_t heads, int32_t q_
  * is not selected and has member rows adds one more logit scale * q_i . kbar[h,t] +
  * landmark_bias with value vbar[h,t].  kbar and vbar are the key/value tile means
  * [heads, Tk, 64] in the operand dtype: for F32 the fp32 means sparse3d_tile_scores
- * writes, for BF16 those means rounded to bf16 (sparse3d_cast), which is the precision
- * the matrix cores take them in.
+ * writes, for BF16 those means rounded to bf16 (the kbar_op/vbar_op outputs of
+ * sparse3d_tile_scores, or sparse3d_cast of the fp32 means), which is the precision the
+ * matrix cores take them in.
  *   out[h,i,:] = sum_j softmax_j * value_j   (fp32 statistics and accumulation)
  *   lse[h,i]   = natural-log log-sum-exp of the logits (optional, float [heads, Lq])
  * Rows that are not valid queries get out = 0 and lse = 0; a valid query with nothing

@@ -69,7 +69,8 @@ int main() {
         check(check_heads_dims(pick(kInts), pick(kInts), pick(kInts)));
         check(check_logit_params(pick(kFloats), pick(kFloats)));
         check(validate_tile_scores(ptr(), ptr(), next() % 2 ? ptr() : nullptr, dtype(), pick(kInts), 64, 64, pa,
-                                   pb, fptr(), fptr(), next() % 2 ? fptr() : nullptr, fptr()));
+                                   pb, fptr(), fptr(), next() % 2 ? fptr() : nullptr, fptr(),
+                                   next() % 2 ? ptr() : nullptr, next() % 2 ? ptr() : nullptr));
         check(validate_select_topk(fptr(), pick(kInts), pick(kInts), pick(kInts), pick(kInts), pick(kInts),
                                    pick(kInts), iptr(), iptr(), pick(kInts)));
         check(validate_attn(next() % 2, ptr(), ptr(), ptr(), dtype(), pick(kInts), 64, 64, pa, pb, iptr(),

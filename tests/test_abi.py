@@ -42,7 +42,7 @@ def test_library_resolves_every_symbol_at_load():
 
 
 def test_version_and_status(lib):
-    assert lib.sparse3d_abi_version() == 4
+    assert lib.sparse3d_abi_version() == 5
     for st in range(6):
         assert lib.sparse3d_status_string(st)
     assert lib.sparse3d_status_string(99) == b"unknown status"
@@ -53,9 +53,9 @@ def L(f=2, n=256, p=256, s=0):
 
 
 def scores_call(lib, q=FAKE, k=FAKE, v=NULL, dt=1, H=2, d=64, tile=64, ql=None, kl=None,
-                qbar=FAKE + 10**9, kbar=FAKE + 2 * 10**9, vbar=NULL, sc=FAKE + 3 * 10**9):
+                qbar=FAKE + 10**9, kbar=FAKE + 2 * 10**9, vbar=NULL, sc=FAKE + 3 * 10**9, kop=NULL, vop=NULL):
     return lib.sparse3d_tile_scores(q, k, v, dt, H, d, tile, ql or L(), kl or L(), 0.125,
-                                    qbar, kbar, vbar, sc, NULL)
+                                    qbar, kbar, vbar, sc, kop, vop, NULL)
 
 
 def test_tile_scores_validation(lib):
@@ -72,7 +72,13 @@ def test_tile_scores_validation(lib):
     assert scores_call(lib, kl=L(f=3, n=256, p=256)) == ERR_SHAPE       # frame counts differ
     assert scores_call(lib, sc=FAKE + 100) == ERR_ALIAS                 # scores overlaps q
     assert lib.sparse3d_tile_scores(FAKE, FAKE, NULL, 1, 2, 64, 64, NULL, L(), 0.1, FAKE + 10**9,
-                                    FAKE + 2 * 10**9, NULL, FAKE + 3 * 10**9, NULL) == ERR_NULL
+                                    FAKE + 2 * 10**9, NULL, FAKE + 3 * 10**9, NULL, NULL, NULL) == ERR_NULL
+    # the means in the operand dtype: value means need the values, no overlap with anything
+    assert scores_call(lib, vop=FAKE + 5 * 10**9) == ERR_NULL
+    assert scores_call(lib, kop=FAKE + 2 * 10**9 + 64) == ERR_ALIAS      # inside kbar
+    assert scores_call(lib, kop=FAKE + 64) == ERR_ALIAS                  # inside q
+    assert scores_call(lib, v=FAKE + 4 * 10**9, vbar=FAKE + 5 * 10**9, kop=FAKE + 6 * 10**9,
+                       vop=FAKE + 6 * 10**9 + 32) == ERR_ALIAS            # kop and vop overlap
 
 
 def topk_call(lib, sc=FAKE, H=2, tq=8, tk=8, k=4, tpf=4, anchor=0, idx=FAKE + 10**9,

@@ -374,15 +374,18 @@ def _full_size(name, n_tiles=48, seed=0):
     K, V = q, v
     if w.kv_window > 1:
         K, V, klay = S.sparse3d_grid_subsample_kv(q, v, lay, w.grid, w.kv_window)
-    qbar, kbar, vbar, scores = S.sparse3d_tile_scores(q, K, lay, klay, v=V if w.landmarks else None)
+    qbar, kbar, vbar, scores, km, vm = S.sparse3d_tile_scores(q, K, lay, klay, v=V if w.landmarks else None,
+                                                              operand_means=True)
     tpf = klay[2] // 64
     Tq, Tk = scores.shape[1], scores.shape[2]
     ts = LY.special_tiles(klay)
     k = LY.calibrate_k(LY.device_count_fn(scores, tpf, w.anchor), w.heads * Tq, ts, Tk,
                        w.target_sparsity)
     idx, cnt = S.sparse3d_select_topk(scores, k, tpf, w.anchor)
-    km = S.sparse3d_cast(kbar, q.dtype) if w.landmarks else None
-    vm = S.sparse3d_cast(vbar, q.dtype) if w.landmarks else None
+    if w.landmarks:                                   # the pooling pass's means equal the cast
+        assert torch.equal(km, S.sparse3d_cast(kbar, q.dtype)) and torch.equal(vm, S.sparse3d_cast(vbar, q.dtype))
+    else:
+        km = vm = None
     out = S.sparse3d_sparse_attn_fwd(q, K, V, lay, klay, idx, cnt, kbar=km, vbar=vm)
     torch.cuda.synchronize()
     sp = LY.measured_sparsity(int(cnt.sum()), w.heads * Tq, ts, Tk)
@@ -955,11 +958,12 @@ def test_outputs_stay_inside_their_buffers():
         kb16=H * Tk * d * 2, vb16=H * Tk * d * 2, out=H * L * d * 2, lse=H * L * 4,
         dense_out=H * L * d * 4, dense_lse=H * L * 4, frame_out=H * L * d * 2, frame_lse=H * L * 4,
         t_end=H * Tk * 4, t_list=H * Tq * kmax * 4, dq=H * L * d * 4, dk=H * L * d * 4, dv=H * L * d * 4,
-        delta=H * L * 4, dkbar=H * Tk * d * 4, dvbar=H * Tk * d * 4, kmean=H * d * 4, vmean=H * d * 4).items()}
+        delta=H * L * 4, dkbar=H * Tk * d * 4, dvbar=H * Tk * d * 4, kmean=H * d * 4, vmean=H * d * 4,
+        kop=H * Tk * d * 2, vop=H * Tk * d * 2).items()}
     P = {n: x.ptr for n, x in g.items()}
     ok = lambda status: S._check(status)
     ok(lib.sparse3d_tile_scores(q.data_ptr(), q.data_ptr(), v.data_ptr(), S.BF16, H, d, 64, rl, rl, 0.125,
-                                P["qbar"], P["kbar"], P["vbar"], P["scores"], st))
+                                P["qbar"], P["kbar"], P["vbar"], P["scores"], P["kop"], P["vop"], st))
     ok(lib.sparse3d_select_topk(P["scores"], H, Tq, Tk, k, tpf, anchor, P["idx"], P["cnt"], kmax, st))
     kh = (ctypes.c_int32 * H)(k, k - 5)
     ok(lib.sparse3d_select_topk_per_head(P["scores"], H, Tq, Tk, kh, tpf, anchor, P["idx_h"], P["cnt_h"], kmax, st))
@@ -990,3 +994,6 @@ def test_outputs_stay_inside_their_buffers():
         x.check(n)
     ko.check("k_out")
     vo.check("v_out")
+    # the pooling pass's operand-dtype means equal the cast of its fp32 means, bit for bit
+    for a, b in (("kop", "kb16"), ("vop", "vb16")):
+        assert torch.equal(g[a].buf[_GUARD:_GUARD + g[a].n], g[b].buf[_GUARD:_GUARD + g[b].n]), a
