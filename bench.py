@@ -134,6 +134,8 @@ def write_counters(outdir: str):
     from collections import defaultdict
 
     info = json.load(open(os.path.join(outdir, "run_info.json")))
+    if "kernel_source_sha256" not in info:
+        raise SystemExit(f"{outdir}/run_info.json records no kernel source hash")
     stats = glob.glob(os.path.join(outdir, "trace", "**", "*kernel_stats.csv"), recursive=True)
     if not stats:
         raise SystemExit(f"{outdir}/trace: no kernel_stats.csv")
@@ -217,7 +219,8 @@ def write_counters(outdir: str):
         if ks:                                          # instances of one family: mean over dispatches
             tot = sum(k["avg_ms"] * k["dispatches"] for k in ks) / sum(k["dispatches"] for k in ks)
             fam_ms[fam] = round(n * tot, 4)
-    out = {"workload": info["workload"], "kernel_source_sha256": kernel_source_sha256(),
+    # the hash of the kernel sources the counters were measured with (recorded by the run)
+    out = {"workload": info["workload"], "kernel_source_sha256": info["kernel_source_sha256"],
            "run": info, "copy_reference_bytes": copy_bytes,
            "counter_scale": {c: round(v, 4) for c, v in scale.items()},
            "commands": profile_commands(info["workload"], outdir), "kernels": kernels,
@@ -229,7 +232,26 @@ def write_counters(outdir: str):
         f.write("\n")
     with open(base + ".md", "w") as f:
         f.write(counters_markdown(out))
-    print(json.dumps({"written": [base + ".json", base + ".md"]}))
+    trace = os.path.join(PROFILES, f"trace_{info['workload']}.md")
+    with open(trace, "w") as f:
+        f.write(trace_markdown(info["workload"], stats[0], profile_commands(info["workload"], outdir)[0]))
+    print(json.dumps({"written": [base + ".json", base + ".md", trace]}))
+
+
+def trace_markdown(workload: str, stats_csv: str, command: str) -> str:
+    """The kernel-trace summary (rocprofv3 --kernel-trace --stats) of the profiled bench run."""
+    import csv
+    rows = [r for r in csv.DictReader(open(stats_csv))]
+    L = [f"# Kernel trace: {workload} (generated by `bench.py --counters-from` from the trace pass)", "",
+         "Command (`$R` = repository root, run from /tmp with TMPDIR=/tmp):", "", "```",
+         command.replace(ROOT, "$R"), "```", "",
+         "| kernel | calls | mean ms | min ms | max ms | total ms |", "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        L.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
+                 f"{float(r['MinNs']) / 1e6:.4f} | {float(r['MaxNs']) / 1e6:.4f} | "
+                 f"{float(r['TotalDurationNs']) / 1e6:.3f} |")
+    L.append("")
+    return "\n".join(L)
 
 
 def counters_markdown(c) -> str:
@@ -635,7 +657,8 @@ def bench_workload(args, w, torch, S, LY, synth, dev, single: bool) -> dict:
         if w.kv_window > 1:
             per_layer["subsample"] = 1
         with open(args.run_info, "w") as f:
-            json.dump({"workload": w.name, "dtype": w.dtype, "heads": w.heads, "q_tiles": L.Tq,
+            json.dump({"workload": w.name, "kernel_source_sha256": kernel_source_sha256(),
+                       "dtype": w.dtype, "heads": w.heads, "q_tiles": L.Tq,
                        "k_tiles": L.Tk, "top_k": L.k, "kmax": r["kmax"], "landmarks": w.landmarks,
                        "layers": args.steps + args.warmup, "attn_flops_per_launch": flops,
                        "alg_per_dispatch": alg, "dispatches_per_layer": per_layer}, f, indent=1)

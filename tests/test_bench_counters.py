@@ -34,13 +34,13 @@ def test_counter_reader(tmp_path, monkeypatch):
     os.makedirs(d / "trace")
     with open(d / "trace" / "run_kernel_stats.csv", "w", newline="") as f:
         w = csv.writer(f)
-        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs"])
-        w.writerow([ATTN, 3, 30e6, 10e6])              # 10 ms
-        w.writerow([POOLQ, 3, 3e5, 1e5])               # 0.1 ms
-        w.writerow([POOLK, 3, 3e5, 1e5])
-        w.writerow([SEL, 9, 1.8e6, 2e5])               # 0.2 ms (calibration launches too)
-        w.writerow([COPY, 2, 1e6, 5e5])
-        w.writerow([BWD, 1, 1e6, 1e6])                 # not a layer kernel
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "MinNs", "MaxNs"])
+        w.writerow([ATTN, 3, 30e6, 10e6, 9e6, 11e6])   # 10 ms
+        w.writerow([POOLQ, 3, 3e5, 1e5, 1e5, 1e5])     # 0.1 ms
+        w.writerow([POOLK, 3, 3e5, 1e5, 1e5, 1e5])
+        w.writerow([SEL, 9, 1.8e6, 2e5, 2e5, 2e5])     # 0.2 ms (calibration launches too)
+        w.writerow([COPY, 2, 1e6, 5e5, 5e5, 5e5])
+        w.writerow([BWD, 1, 1e6, 1e6, 1e6, 1e6])       # not a layer kernel
     mib = bench.PROFILE_COPY_MB * 1024                  # KiB moved each way by the copy
     # FETCH_SIZE counts half the bytes (scale 2), WRITE_SIZE all (scale 1)
     _pmc(str(d / "fetch"), [[1, COPY, "FETCH_SIZE", mib / 2, 0, 1], [2, ATTN, "FETCH_SIZE", 5e6, 0, 1],
@@ -54,7 +54,7 @@ def test_counter_reader(tmp_path, monkeypatch):
                          [7, ATTN, "SQ_ACTIVE_INST_ANY", 100.0, 0, 10_000_000],
                          [7, ATTN, "SQ_ACTIVE_INST_VALU", 55.0, 0, 10_000_000],
                          [7, ATTN, "SQ_WAVE_CYCLES", 400.0, 0, 10_000_000]])
-    info = {"workload": "fake", "dtype": "bf16", "heads": 2, "q_tiles": 4, "k_tiles": 4, "top_k": 1,
+    info = {"workload": "fake", "kernel_source_sha256": "abc", "dtype": "bf16", "heads": 2, "q_tiles": 4, "k_tiles": 4, "top_k": 1,
             "kmax": 2, "landmarks": False, "layers": 3, "attn_flops_per_launch": 8e12,
             "alg_per_dispatch": {"pool_query": 4e8, "pool_key": 4e8, "score": 1e9, "select": 1e9,
                                  "cast": 0, "attention": 8e12},
@@ -81,6 +81,9 @@ def test_counter_reader(tmp_path, monkeypatch):
     assert c["layer_ms_by_family"] == {"pool_query": 0.1, "pool_key": 0.1, "select": 0.2, "attention": 10.0}
     md = open(tmp_path / "profiles" / "counters_fake.md").read()
     assert "rocprofv3 --pmc FETCH_SIZE" in md and "| attention |" in md
+    assert c["kernel_source_sha256"] == "abc"                  # the run's, not the current sources'
+    tr = open(tmp_path / "profiles" / "trace_fake.md").read()
+    assert "--kernel-trace --stats" in tr and "k_attn_bf16" in tr
 
 
 def test_kernel_family():
