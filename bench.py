@@ -190,7 +190,9 @@ def write_counters(outdir: str):
             k.update(alg_bytes=alg[fam], alg_gbs=round(alg[fam] / sec / 1e9, 1),
                      alg_frac_hbm=round(alg[fam] / sec / 1e9 / PEAK_HBM_GBS, 4))
         grbm = sq.get((name, "GRBM_GUI_ACTIVE"))
-        if grbm:
+        # the clock (and the busy share that uses it) only for dispatches of at least 0.1 ms:
+        # on shorter ones the active-cycle count and the dispatch timestamps do not line up
+        if grbm and sec >= 1e-4:
             # cycles per XCD over the dispatch's own span in that pass
             clocks = [grbm[d] / N_XCD / span[d] for d in grbm if span.get(d, 0) > 0]
             cyc = sum(grbm.values()) / len(grbm) / N_XCD
@@ -265,7 +267,8 @@ def counters_markdown(c) -> str:
          f"(FETCH_SIZE x{c['counter_scale']['FETCH_SIZE']}, WRITE_SIZE x{c['counter_scale']['WRITE_SIZE']}); "
          f"peaks: HBM {PEAK_HBM_GBS / 1000:g} TB/s, matrix {PEAK_TFLOPS[run['dtype']]:g} TFLOP/s "
          f"({run['dtype']}, quoted at 2.4 GHz).", "",
-         "Commands (`$R` = repository root, run from /tmp with TMPDIR=/tmp):", "", "```"]
+         "The shader clock and the matrix-core busy share are given for dispatches of at least 0.1 ms.",
+         "", "Commands (`$R` = repository root, run from /tmp with TMPDIR=/tmp):", "", "```"]
     for cmd in c["commands"]:
         L.append(cmd.replace(ROOT, "$R"))
     L.append(f"python3 $R/bench.py --counters-from {c['commands'][0].split(' -d ')[1].split('/trace')[0].replace(ROOT, '$R')}")
