@@ -225,7 +225,8 @@ def write_counters(outdir: str):
     out = {"workload": info["workload"], "kernel_source_sha256": info["kernel_source_sha256"],
            "run": info, "copy_reference_bytes": copy_bytes,
            "counter_scale": {c: round(v, 4) for c, v in scale.items()},
-           "commands": profile_commands(info["workload"], outdir), "kernels": kernels,
+           "commands": [c.replace(ROOT, "$R") for c in profile_commands(info["workload"], outdir)],
+           "kernels": kernels,
            "layer_ms_by_family": dict(fam_ms)}
     os.makedirs(PROFILES, exist_ok=True)
     base = os.path.join(PROFILES, f"counters_{info['workload']}")
@@ -270,8 +271,8 @@ def counters_markdown(c) -> str:
          "The shader clock and the matrix-core busy share are given for dispatches of at least 0.1 ms.",
          "", "Commands (`$R` = repository root, run from /tmp with TMPDIR=/tmp):", "", "```"]
     for cmd in c["commands"]:
-        L.append(cmd.replace(ROOT, "$R"))
-    L.append(f"python3 $R/bench.py --counters-from {c['commands'][0].split(' -d ')[1].split('/trace')[0].replace(ROOT, '$R')}")
+        L.append(cmd)
+    L.append(f"python3 $R/bench.py --counters-from {c['commands'][0].split(' -d ')[1].split('/trace')[0]}")
     L += ["```", "", "| kernel | step | dispatches | ms | counted GB/s | of 8 TB/s | algorithmic GB/s | of 8 TB/s | clock GHz | MFMA busy | VALU share of issue |",
           "|---|---|---|---|---|---|---|---|---|---|---|"]
 
