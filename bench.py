@@ -370,12 +370,14 @@ def run_layer(torch, L, steps, warmup):
         out = L.attend(idx, cnt, kbar, vbar)
         e[4].record(st)
     end.record(st)
+    enq = time.perf_counter() - t0                  # host time to enqueue the K steps
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(end) / steps
     per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev])
     total_cnt = int(cnt.sum().item())
-    return dict(ms_per_step=ms, wall_ms=1e3 * wall / steps, sub_ms=float(per[:, 0].mean()),
+    return dict(ms_per_step=ms, wall_ms=1e3 * wall / steps, enqueue_ms=1e3 * enq / steps,
+                sub_ms=float(per[:, 0].mean()),
                 scores_ms=float(per[:, 1].mean()), select_ms=float(per[:, 2].mean()),
                 attn_ms=float(per[:, 3].mean()), total_cnt=total_cnt, out=out, idx=idx, cnt=cnt,
                 kmax=int(idx.shape[2]))
@@ -644,6 +646,8 @@ def bench_workload(args, w, torch, S, LY, synth, dev, single: bool) -> dict:
         f"pct_{w.dtype}_peak_layer": round(100 * value / peak, 2),
         "kernels_ms": {"grid_subsample": round(r["sub_ms"], 4), "tile_scores": round(r["scores_ms"], 4),
                        "select_topk": round(r["select_ms"], 4), "sparse_attn": round(r["attn_ms"], 4)},
+        # host time to enqueue one step: close to ms_per_step means the step was launch-bound
+        "enqueue_ms_per_step": round(r["enqueue_ms"], 4),
         "selected_flops": flops,
         "valid_pair_flops": LY.valid_pair_flops(r["idx"].cpu().numpy(), r["cnt"].cpu().numpy(),
                                                 w.layout, L.klay),
@@ -748,11 +752,26 @@ def main():
         torch.cuda.synchronize()
         log(f"copy reference: {args.copy_mb} MiB read + {args.copy_mb} MiB written per launch")
         del src, dst
-    names = CONFIGS if args.all_configs else [args.workload]
-    for name in names:
-        res = bench_workload(args, synth.WORKLOADS[name], torch, S, LY, synth, dev, single=not args.all_configs)
+    if not args.all_configs:
+        res = bench_workload(args, synth.WORKLOADS[args.workload], torch, S, LY, synth, dev, single=True)
         print(json.dumps(res), flush=True)
+        return
+    # every configuration's GPU timing first, then the CPU baselines: the oracle's BLAS threads
+    # keep the host busy for a while after each call, which slowed the launches of the next
+    # configuration (a 1.1 ms layer measured 4.6 ms that way)
+    results = []
+    cpu = args.no_cpu_baseline
+    args.no_cpu_baseline = True
+    for name in CONFIGS:
+        results.append(bench_workload(args, synth.WORKLOADS[name], torch, S, LY, synth, dev, single=False))
         torch.cuda.empty_cache()
+    for name, res in zip(CONFIGS, results):
+        if not cpu:
+            w = synth.WORKLOADS[name]
+            log(f"timing the CPU oracle on a bounded sample of {name}")
+            res["cpu_baseline"] = cpu_baseline(w, synth.make_inputs(w, seed=args.seed), res["config"]["top_k"],
+                                               args.cpu_budget, LY)
+        print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":
