@@ -997,3 +997,58 @@ def test_outputs_stay_inside_their_buffers():
     # the pooling pass's operand-dtype means equal the cast of its fp32 means, bit for bit
     for a, b in (("kop", "kb16"), ("vop", "vb16")):
         assert torch.equal(g[a].buf[_GUARD:_GUARD + g[a].n], g[b].buf[_GUARD:_GUARD + g[b].n]), a
+
+
+def test_rejected_calls_launch_nothing():
+    # every wrapper checks shapes and dtypes of device tensors before it touches the device,
+    # and a call the library refuses writes nothing (its output keeps a sentinel)
+    say("[case] rejected calls on device tensors")
+    import ctypes
+    d = dev()
+    lay = (2, 256, 256, 0)
+    q = torch.randn((2, 512, 64), device=d).to(torch.bfloat16)
+    sc = torch.zeros((2, 8, 8), device=d)
+    idx = torch.zeros((2, 8, 8), dtype=torch.int32, device=d)
+    cnt = torch.full((2, 8), 4, dtype=torch.int32, device=d)
+    with pytest.raises(ValueError):
+        S.sparse3d_tile_scores(q, q[:, :448].contiguous(), lay)               # k shorter than its layout
+    with pytest.raises(TypeError):
+        S.sparse3d_tile_scores(q, q.float(), lay)                            # k dtype differs from q
+    with pytest.raises(TypeError):
+        S.sparse3d_select_topk(sc.double(), 4, 4, 0)                         # scores must be fp32
+    with pytest.raises(TypeError):
+        S.sparse3d_sparse_attn_fwd(q, q, q, lay, lay, idx.long(), cnt)       # idx must be int32
+    with pytest.raises(ValueError):
+        S.sparse3d_sparse_attn_fwd(q, q, q, lay, lay, idx, cnt[:, :7].contiguous())
+    with pytest.raises(ValueError):
+        S.sparse3d_dense_attn_fwd(q, q, q[:, :500].contiguous(), lay)
+    with pytest.raises(ValueError, match="kbar and vbar"):
+        S.sparse3d_sparse_attn_fwd(q, q, q, lay, lay, idx, cnt, kbar=torch.zeros((2, 8, 64), device=d, dtype=q.dtype))
+    lse = torch.zeros((2, 512), device=d)
+    with pytest.raises(ValueError):
+        S.sparse3d_sparse_attn_bwd(q, q, q, q, q, lse[:, :511].contiguous(), lay, lay, idx, cnt,
+                                   torch.zeros((2, 8), dtype=torch.int32, device=d),
+                                   torch.zeros((2, 64), dtype=torch.int32, device=d))
+    torch.cuda.synchronize()
+    # the C ABI with real device buffers: refused calls leave the output untouched
+    lib = S.library()
+    out = torch.full((2, 512, 64), 7.0, device=d)
+    ql = S._Layout(*lay)
+    rl = ctypes.byref(ql)
+    st = torch.cuda.current_stream().cuda_stream
+    bad = [
+        dict(scale=0.0, out=out.data_ptr(), status=3),                # scale must be > 0
+        dict(scale=0.125, out=q.data_ptr(), status=5),                # out aliases q
+        dict(scale=float("nan"), out=out.data_ptr(), status=3),
+    ]
+    for b in bad:
+        r = lib.sparse3d_sparse_attn_fwd(q.data_ptr(), q.data_ptr(), q.data_ptr(), S.BF16, 2, 64, 64, rl, rl,
+                                         idx.data_ptr(), cnt.data_ptr(), 8, None, None, math.log(64.0), b["scale"],
+                                         None, b["out"], S.F32, None, st)
+        assert r == b["status"], (b, r)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+    # and a valid call afterwards still runs
+    o = S.sparse3d_sparse_attn_fwd(q, q, q, lay, lay, idx, cnt)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
