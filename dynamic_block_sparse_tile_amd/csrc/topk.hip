@@ -247,7 +247,8 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
                                                                      int Tq, int rows, KBudget kb, int tpf,
                                                                      int anchor, int32_t* __restrict__ idx,
                                                                      int32_t* __restrict__ cnt, int kmax) {
-    __shared__ uint32_t s_cand[TKW_WAVES][TKW_CAND];
+    // TKW_CAND candidate slots, then one dump slot per lane for lanes that have nothing to write
+    __shared__ uint32_t s_cand[TKW_WAVES][TKW_CAND + 64];
     // the row is wave-uniform: in a scalar register, its buffer resource needs no lane loop
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row = blockIdx.x * TKW_WAVES + wave;
@@ -288,9 +289,11 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
             for (int j = 0; j < 4; ++j) c += __popcll(__ballot(x[g][j] >= tf));
         return c;
     };
-    auto lanes_below = [&](uint64_t m) {
-        return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    // b + the number of lanes below this one whose bit in m is set
+    auto below_from = [&](uint64_t m, int b) {
+        return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)b));
     };
+    auto lanes_below = [&](uint64_t m) { return below_from(m, 0); };
     // mode: 0 = nothing from top-k, 1 = every tile, 2 = threshold T with ties
     const int mode = k <= 0 ? 0 : (k >= Tk ? 1 : 2);
     uint32_t T = 0;
@@ -305,7 +308,10 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
                 mn = fminf(mn, x[g][j]);
                 mx = fmaxf(mx, x[g][j]);
             }
-        uint32_t lo = wave_min(order_key(mn)), hi = wave_max(order_key(mx));
+        // readfirstlane: the reductions end in lane shuffles, and a bracket the compiler
+        // sees as per-lane would put the whole bisection under exec masks
+        uint32_t lo = __builtin_amdgcn_readfirstlane(wave_min(order_key(mn)));
+        uint32_t hi = __builtin_amdgcn_readfirstlane(wave_max(order_key(mx)));
         int c_lo = Tk, c_hi = 0;                    // count(key >= lo), count(key > hi)
         // candidates in LDS: cand[j] = candidate 4 lane + j (valid when below ncand);
         // c_base = count(key > bracket top) when they were taken
@@ -317,12 +323,23 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
         // score rows the value midpoint needs about half the passes of key bisection, and
         // the alternation bounds rows whose values span many binades.
         bool by_key = false;
-        while (lo != hi) {
+        for (;;) {
+            // every loop-carried value is wave-uniform; saying so keeps the loop's branches
+            // scalar (the compiler cannot prove it through the LDS and lane-shuffle steps)
+            lo = __builtin_amdgcn_readfirstlane(lo);
+            hi = __builtin_amdgcn_readfirstlane(hi);
+            c_lo = __builtin_amdgcn_readfirstlane(c_lo);
+            c_hi = __builtin_amdgcn_readfirstlane(c_hi);
+            ncand = __builtin_amdgcn_readfirstlane(ncand);
+            c_base = __builtin_amdgcn_readfirstlane(c_base);
+            if (lo == hi) break;
             const int inside = c_lo - c_hi;
             if (inside <= 64 || (ncand < 0 && inside <= TKW_CAND)) {
                 // compact the values inside [lo, hi] into LDS (at most 256 of them); the upper
                 // bound as "below key hi + 1" (hi stays below the key of NaN, so no wrap), since
-                // key_float maps the unused key just below +0 to -0
+                // key_float maps the unused key just below +0 to -0.  The same comparisons gave
+                // c_hi = count(key > hi) exactly and c_lo >= count(key >= lo), so at most
+                // inside <= TKW_CAND values pass and every write index stays inside s_c.
                 const float flo = key_float(lo), fup = key_float(hi + 1);
                 int base = 0;
                 if (ncand < 0) {
@@ -330,10 +347,11 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
                     for (int g = 0; g < G; ++g)
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            const bool in = x[g][j] >= flo && !(x[g][j] >= fup);
-                            const uint64_t m = __ballot(in);
-                            const int at = base + lanes_below(m);
-                            if (in && at < TKW_CAND) s_c[at] = x[g][j];
+                            // one ballot per comparison, combined on the scalar unit; every
+                            // lane writes (outside the bracket to its dump slot), so the
+                            // store needs no exec mask
+                            const uint64_t m = __ballot(x[g][j] >= flo) & ~__ballot(x[g][j] >= fup);
+                            s_c[__builtin_amdgcn_inverse_ballot_w64(m) ? below_from(m, base) : TKW_CAND + lane] = x[g][j];
                             base += __popcll(m);
                         }
                 } else {
@@ -341,8 +359,7 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
                     for (int j = 0; j < 4; ++j) {
                         const bool in = 4 * lane + j < ncand && cand[j] >= flo && !(cand[j] >= fup);
                         const uint64_t m = __ballot(in);
-                        const int at = base + lanes_below(m);
-                        if (in && at < TKW_CAND) s_c[at] = cand[j];
+                        if (in) s_c[below_from(m, base)] = cand[j];
                         base += __popcll(m);
                     }
                 }
@@ -371,7 +388,8 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
                         v = (lower == desc) ? max(v, o) : min(v, o);
                     }
                 }
-                lo = (uint32_t)__shfl((int)v, k - c_hi - 1);   // rank k - c_hi among the candidates
+                // rank k - c_hi among the candidates (one lane's key, the same in every lane)
+                lo = __builtin_amdgcn_readfirstlane((uint32_t)__shfl((int)v, k - c_hi - 1));
                 hi = lo;
                 take_ge = c_hi + __popcll(__ballot(lane < base && v >= lo)) == k;
                 break;
@@ -412,11 +430,42 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
         }
     }
     const float Tf = key_float(T);
-    int ties_before = 0;                            // keys == T in earlier groups
-    const int need_eq = mode == 2 ? k - greater : 0;   // ties to take, lowest index first
     const int a0 = anchor >= 0 ? anchor * tpf : 0, a1 = anchor >= 0 ? min(a0 + tpf, Tk) : 0;
     int32_t* out = idx + (size_t)row * kmax;
     int base = 0;
+    if (mode == 2 && take_ge) {
+        // No tie to rank: the row takes every key >= T (exactly k of them) and the anchor
+        // tiles.  The selection stays in 64-bit lane masks (scalar registers), turned back
+        // into lane predicates where a store needs them; a lane's first slot of a group goes
+        // after every selected slot of the lower lanes.  Stores go through a buffer
+        // resource of min(kmax, Tk) entries, which drops anything past kmax.
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(out, 0, min(kmax, Tk) * 4,
+                                                                            tl::BUF_RSRC_WORD3);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int t0 = 256 * g + 4 * lane;
+            uint64_t m[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) m[j] = __ballot(x[g][j] >= Tf);
+            if (a0 < 256 * g + 256 && a1 > 256 * g) {   // the group meets the anchor frame
+#pragma unroll
+                for (int j = 0; j < 4; ++j) m[j] |= __ballot(t0 + j >= a0 && t0 + j < a1);
+            }
+            uint32_t off = 4u * (uint32_t)below_from(m[3], below_from(m[2], below_from(m[1], below_from(m[0], base))));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (__builtin_amdgcn_inverse_ballot_w64(m[j])) {
+                    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(t0 + j), ro, (int)off, 0, 0);
+                    off += 4u;
+                }
+            base += __popcll(m[0]) + __popcll(m[1]) + __popcll(m[2]) + __popcll(m[3]);
+        }
+        for (int q = base + lane; q < kmax; q += 64) out[q] = -1;
+        if (lane == 0) cnt[row] = min(base, kmax);
+        return;
+    }
+    int ties_before = 0;                            // keys == T in earlier groups
+    const int need_eq = mode == 2 ? k - greater : 0;   // ties to take, lowest index first
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         const int t0 = 256 * g + 4 * lane;

@@ -194,8 +194,12 @@ def test_select_topk_hard_rows():
             g.copy_(to_dev(sc, torch.float32))
             assert g.data_ptr() % 16 == 4
         say(f"[case] select hard rows Tk={Tk}{' (shifted)' if shifted else ''}")
+        # anchor frames: none, the first, one whose tiles straddle a 256-tile group boundary
+        # (frame 11 of 22-tile frames covers tiles 242..263) where it exists, and the last
+        nf = Tk // tpf
+        anchors = sorted({a for a in (-1, 0, 11, nf - 1) if a < nf})
         for k in (1, 5, 138, Tk - 1, Tk, Tk + 3):
-            for anchor in (-1, 0):
+            for anchor in anchors:
                 idx, cnt = S.sparse3d_select_topk(g, k, tpf, anchor)
                 gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
                 for t in range(sc.shape[1]):
