@@ -226,307 +226,313 @@ __global__ __launch_bounds__(TK_THREADS) void k_select_topk(const float* __restr
     if (tid == 0) cnt[row] = min(total, kmax);
 }
 
-// The same selection with one wave per score row (rows of at most 256 G tiles): the keys stay
-// in registers, lane l holding the four consecutive tiles 256 g + 4 l .. + 3 of each group g
-// (one 16-byte load per group), and every count is a ballot and a scalar popcount, so a row
-// needs no histogram and no barrier.  The k-th largest key T is bracketed by bisection,
-// keeping count(key >= lo) >= k > count(key > hi).  Once at most 256 keys lie inside the
-// bracket they are compacted into LDS, four per lane, and the bisection continues on them
-// alone (count(key >= t) = count(key > hi at that moment) + candidates >= t); once at most
-// 64 remain they are gathered one per lane and ordered by a bitonic network across the
-// lanes, which yields T directly.  Selection and compaction then run over the groups in
-// tile order, positions from ballots and lane prefix counts (v_mbcnt): keys above T, the
-// lowest-index ties, and the anchor tiles.  When exactly k keys are >= T (the bracket
-// counts tell) there is no tie to rank and every key >= T is taken.
+// The same selection with one wave per score row (rows of at most 64 NS tiles).  Lane l holds
+// the scores of tiles 64 s + l for slots s = 0 .. NS-1 in registers, so a ballot over one slot
+// lists that slot's tiles in ascending order, and every count is a ballot and a scalar
+// popcount: a row needs no histogram and no barrier.
+//
+// The k-th largest key T is bracketed by bisection, keeping count(key >= lo) >= k >
+// count(key > hi).  The probe halves the bracket in value (the midpoint of its two floats)
+// while that shrinks the count inside by at least a quarter, else in key order: on score rows
+// the value midpoint needs about half the passes of key bisection, and the alternation bounds
+// rows whose values span many binades.  Once at most TKW_LIST keys (with the anchor tiles) lie
+// at or above lo, they move with their tile numbers into an LDS list in tile order, and
+// everything after runs on the list alone: every key >= lo is in it, so its counts are the
+// row's counts.  Once at most 64 keys lie inside the bracket they are gathered one per lane
+// and ordered by a bitonic network, which yields T.  The output is then one pass over the
+// list: keys above T, the lowest-index keys equal to T (k in all), and the anchor tiles, in
+// tile order.  Rows whose budget is too large for the list bisect the full row to T and emit
+// from the registers the same way.  Rows that take nothing from the top k (k <= 0) or every
+// tile (k >= Tk) need no search.
+//
+// Scores are compared as floats: float order equals key order for every non-NaN value (-0 ==
+// +0 as the keys fold them, -inf lowest).  Padding slots and NaN scores fail every comparison,
+// so top-k never takes them (anchor tiles are taken whatever their score).
 constexpr int TKW_WAVES = 4;            // rows per workgroup
-constexpr int TKW_CAND = 256;           // bracket size at which the candidates move to LDS
-// FULL: the row fills every slot (Tk = 256 G), so no slot needs a range check.  Rows start
-// 16-byte aligned (Tk a multiple of 4 and an aligned matrix; the launcher checks).
-template <int G, bool FULL>
+constexpr int TKW_LIST = 512;           // list entries per row
+
+// Wave-wide minimum and maximum through DPP (quad swaps, row mirrors, row broadcasts), read
+// from the last lane: a value in a scalar register.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_min(uint32_t v) {
+    return min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xF, false));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ uint32_t wave_min_uniform(uint32_t v) {
+    v = dpp_min<0xB1, 0xF>(v);          // quad_perm [1,0,3,2]
+    v = dpp_min<0x4E, 0xF>(v);          // quad_perm [2,3,0,1]
+    v = dpp_min<0x141, 0xF>(v);         // row_half_mirror
+    v = dpp_min<0x140, 0xF>(v);         // row_mirror: every lane holds its row's minimum
+    v = dpp_min<0x142, 0xA>(v);         // row_bcast:15 into rows 1 and 3
+    v = dpp_min<0x143, 0xC>(v);         // row_bcast:31 into rows 2 and 3
+    return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ uint32_t wave_max_uniform(uint32_t v) {
+    v = dpp_max<0xB1, 0xF>(v);
+    v = dpp_max<0x4E, 0xF>(v);
+    v = dpp_max<0x141, 0xF>(v);
+    v = dpp_max<0x140, 0xF>(v);
+    v = dpp_max<0x142, 0xA>(v);
+    v = dpp_max<0x143, 0xC>(v);
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// The bisection state of one row (every field wave-uniform).
+struct Bracket {
+    uint32_t lo, hi;        // key bracket of T
+    int c_lo, c_hi;         // c_lo >= count(key >= lo) (exact once lo moved), c_hi = count(key > hi)
+    bool by_key;            // the next probe halves in key order
+    __device__ __forceinline__ void uniform() {
+        lo = __builtin_amdgcn_readfirstlane(lo);
+        hi = __builtin_amdgcn_readfirstlane(hi);
+        c_lo = __builtin_amdgcn_readfirstlane(c_lo);
+        c_hi = __builtin_amdgcn_readfirstlane(c_hi);
+    }
+    __device__ __forceinline__ uint32_t probe() const {
+        uint32_t mid = lo + (uint32_t)(((uint64_t)hi - lo + 1) >> 1);
+        if (!by_key) {
+            const float fl = key_float(lo), fh = key_float(hi);
+            if (__builtin_isfinite(fl) && __builtin_isfinite(fh))
+                mid = min(max(order_key(0.5f * fl + 0.5f * fh), lo + 1), hi);
+        }
+        return mid;                                 // in [lo + 1, hi]: every step shrinks
+    }
+    // c = count(key >= mid)
+    __device__ __forceinline__ void update(uint32_t mid, int c, int k) {
+        const int before = c_lo - c_hi;
+        if (c >= k) {
+            lo = mid;
+            c_lo = c;
+        } else {
+            hi = mid - 1;
+            c_hi = c;
+        }
+        by_key = !by_key && 4 * (c_lo - c_hi) > 3 * before;
+    }
+};
+
+// Emit the selection of one row from NV slots of (score, tile) per lane, in tile order across
+// (slot, lane): keys > Tf, the first need_eq keys == Tf, and tiles in [a0, a0 + na).  Slots
+// with valid false take nothing.  Returns the selected count (stores stop at kmax).
+template <int NV, typename Get>
+__device__ __forceinline__ int emit_selection(Get get, int nslots, float Tf, int need_eq, int a0, int na,
+                                              int32_t* out, int kmax) {
+    int base = 0, ties = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        if (i >= nslots) break;                     // uniform
+        float v;
+        int t;
+        bool valid;
+        get(i, v, t, valid);
+        const bool eq = v == Tf;
+        const uint64_t em = __ballot(eq);
+        const bool sel = v > Tf || (eq && ties + lanes_below(em) < need_eq) ||
+                         (valid && (uint32_t)(t - a0) < (uint32_t)na);
+        ties += __popcll(em);
+        const uint64_t sm = __ballot(sel);
+        const int pos = base + lanes_below(sm);
+        if (sel && pos < kmax) out[pos] = t;
+        base += __popcll(sm);
+    }
+    return base;
+}
+
+template <int NS, bool FULL>
 __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float* __restrict__ scores, int Tk,
                                                                      int Tq, int rows, KBudget kb, int tpf,
                                                                      int anchor, int32_t* __restrict__ idx,
                                                                      int32_t* __restrict__ cnt, int kmax) {
-    // TKW_CAND candidate slots, then one dump slot per lane for lanes that have nothing to write
-    __shared__ uint32_t s_cand[TKW_WAVES][TKW_CAND + 64];
+    // per row: the list (values and tiles at a fixed distance, so one address serves both)
+    // and the gathered bracket (64 entries, then one dump slot per lane)
+    struct List {
+        float v[TKW_LIST];
+        int32_t t[TKW_LIST];
+    };
+    __shared__ List s_list[TKW_WAVES];
+    __shared__ float s_gat[TKW_WAVES][128];
     // the row is wave-uniform: in a scalar register, its buffer resource needs no lane loop
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row = blockIdx.x * TKW_WAVES + wave;
     if (row >= rows) return;                        // whole wave leaves together
     const int k = kb.k[row / Tq];
+    int32_t* out = idx + (size_t)row * kmax;
+    const int a0 = anchor >= 0 ? anchor * tpf : 0, a1 = anchor >= 0 ? min(a0 + tpf, Tk) : 0, na = a1 - a0;
+    auto finish = [&](int n) {
+        for (int q = n + lane; q < kmax; q += 64) out[q] = -1;
+        if (lane == 0) cnt[row] = min(n, kmax);
+    };
+    if (k <= 0 || k >= Tk) {
+        // only the anchor frame, or every tile (the anchor frame among them)
+        const int n = k <= 0 ? na : Tk, first = k <= 0 ? a0 : 0;
+        for (int q = lane; q < min(n, kmax); q += 64) out[q] = first + q;
+        finish(n);
+        return;
+    }
     // the row through a buffer resource: slots past Tk read zeros (and are masked below)
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(scores) + (size_t)row * Tk, 0, Tk * 4, tl::BUF_RSRC_WORD3);
-    // the raw scores: float order equals key order for every non-NaN value (-0 == +0 as
-    // the keys fold them, -inf lowest); padding slots hold NaN, which no comparison takes
-    float x[G][4];
-    {
-        typedef float f32x4v __attribute__((ext_vector_type(4)));
+    float x[NS];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {               // all loads in flight at once
-            const f32x4v v = __builtin_bit_cast(f32x4v, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, 1024 * g, 0));
-            x[g][0] = v[0];
-            x[g][1] = v[1];
-            x[g][2] = v[2];
-            x[g][3] = v[3];
-        }
-    }
+    for (int s = 0; s < NS; ++s)                    // all loads in flight at once
+        x[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * lane + 256 * s, 0, 0));
     if (!FULL) {
-        const int lim = Tk - 4 * lane;              // slot (g, j) holds a tile iff 256 g + j < lim
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (256 * g + j >= lim) x[g][j] = __builtin_nanf("");
+        for (int s = 0; s < NS; ++s)
+            if (64 * s + lane >= Tk) x[s] = __builtin_nanf("");
     }
-    // count(key >= t) for a key t (its float: the keys' order on non-NaN values)
-    auto count_ge = [&](uint32_t t) {
-        const float tf = key_float(t);
-        int c = 0;
+    float mn = INFINITY, mx = -INFINITY;            // NaN is ignored by min / max
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) c += __popcll(__ballot(x[g][j] >= tf));
-        return c;
-    };
-    // b + the number of lanes below this one whose bit in m is set
-    auto below_from = [&](uint64_t m, int b) {
-        return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)b));
-    };
-    auto lanes_below = [&](uint64_t m) { return below_from(m, 0); };
-    // mode: 0 = nothing from top-k, 1 = every tile, 2 = threshold T with ties
-    const int mode = k <= 0 ? 0 : (k >= Tk ? 1 : 2);
-    uint32_t T = 0;
-    int greater = 0;
-    bool take_ge = false;                           // exactly k keys are >= T: no tie to break
-    if (mode == 2) {
-        float mn = INFINITY, mx = -INFINITY;        // NaN padding is ignored by min / max
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                mn = fminf(mn, x[g][j]);
-                mx = fmaxf(mx, x[g][j]);
-            }
-        // readfirstlane: the reductions end in lane shuffles, and a bracket the compiler
-        // sees as per-lane would put the whole bisection under exec masks
-        uint32_t lo = __builtin_amdgcn_readfirstlane(wave_min(order_key(mn)));
-        uint32_t hi = __builtin_amdgcn_readfirstlane(wave_max(order_key(mx)));
-        int c_lo = Tk, c_hi = 0;                    // count(key >= lo), count(key > hi)
-        // candidates in LDS: cand[j] = candidate 4 lane + j (valid when below ncand);
-        // c_base = count(key > bracket top) when they were taken
-        int ncand = -1, c_base = 0;
-        float cand[4] = {0.f, 0.f, 0.f, 0.f};
-        float* s_c = reinterpret_cast<float*>(s_cand[wave]);
-        // The probe halves the bracket in value (the midpoint of the two floats) while that
-        // keeps shrinking the candidate count by at least a quarter, else in key order: on
-        // score rows the value midpoint needs about half the passes of key bisection, and
-        // the alternation bounds rows whose values span many binades.
-        bool by_key = false;
-        for (;;) {
-            // every loop-carried value is wave-uniform; saying so keeps the loop's branches
-            // scalar (the compiler cannot prove it through the LDS and lane-shuffle steps)
-            lo = __builtin_amdgcn_readfirstlane(lo);
-            hi = __builtin_amdgcn_readfirstlane(hi);
-            c_lo = __builtin_amdgcn_readfirstlane(c_lo);
-            c_hi = __builtin_amdgcn_readfirstlane(c_hi);
-            ncand = __builtin_amdgcn_readfirstlane(ncand);
-            c_base = __builtin_amdgcn_readfirstlane(c_base);
-            if (lo == hi) break;
-            const int inside = c_lo - c_hi;
-            if (inside <= 64 || (ncand < 0 && inside <= TKW_CAND)) {
-                // compact the values inside [lo, hi] into LDS (at most 256 of them); the upper
-                // bound as "below key hi + 1" (hi stays below the key of NaN, so no wrap), since
-                // key_float maps the unused key just below +0 to -0.  The same comparisons gave
-                // c_hi = count(key > hi) exactly and c_lo >= count(key >= lo), so at most
-                // inside <= TKW_CAND values pass and every write index stays inside s_c.
-                const float flo = key_float(lo), fup = key_float(hi + 1);
-                int base = 0;
-                if (ncand < 0) {
-#pragma unroll
-                    for (int g = 0; g < G; ++g)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            // one ballot per comparison, combined on the scalar unit; every
-                            // lane writes (outside the bracket to its dump slot), so the
-                            // store needs no exec mask
-                            const uint64_t m = __ballot(x[g][j] >= flo) & ~__ballot(x[g][j] >= fup);
-                            s_c[__builtin_amdgcn_inverse_ballot_w64(m) ? below_from(m, base) : TKW_CAND + lane] = x[g][j];
-                            base += __popcll(m);
-                        }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const bool in = 4 * lane + j < ncand && cand[j] >= flo && !(cand[j] >= fup);
-                        const uint64_t m = __ballot(in);
-                        if (in) s_c[below_from(m, base)] = cand[j];
-                        base += __popcll(m);
-                    }
-                }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                if (inside > 64) {
-                    // continue the bisection on the candidates alone
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) cand[j] = 4 * lane + j < base ? s_c[4 * lane + j] : 0.f;
-                    ncand = base;
-                    c_base = c_hi;
-                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                    __builtin_amdgcn_wave_barrier();         // read before a later gather overwrites
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                    continue;
-                }
-                // at most 64 left: rank their keys across the lanes (pad lanes rank lowest)
-                uint32_t v = lane < base ? order_key(s_c[lane]) : 0u;
-#pragma unroll
-                for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-                    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                        const uint32_t o = (uint32_t)__shfl_xor((int)v, stride);
-                        const bool desc = (lane & size) == 0, lower = (lane & stride) == 0;
-                        v = (lower == desc) ? max(v, o) : min(v, o);
-                    }
-                }
-                // rank k - c_hi among the candidates (one lane's key, the same in every lane)
-                lo = __builtin_amdgcn_readfirstlane((uint32_t)__shfl((int)v, k - c_hi - 1));
-                hi = lo;
-                take_ge = c_hi + __popcll(__ballot(lane < base && v >= lo)) == k;
-                break;
-            }
-            uint32_t mid = lo + (uint32_t)(((uint64_t)hi - lo + 1) >> 1);
-            if (!by_key) {
-                const float fl = key_float(lo), fh = key_float(hi);
-                if (__builtin_isfinite(fl) && __builtin_isfinite(fh))
-                    mid = min(max(order_key(0.5f * fl + 0.5f * fh), lo + 1), hi);
-            }
-            const int before = inside;
-            int c;
-            if (ncand < 0) {
-                c = count_ge(mid);
-            } else {
-                const float tf = key_float(mid);
-                c = c_base;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) c += __popcll(__ballot(4 * lane + j < ncand && cand[j] >= tf));
-            }
-            if (c >= k) {
-                lo = mid;
-                c_lo = c;
-            } else {
-                hi = mid - 1;
-                c_hi = c;
-            }
-            by_key = !by_key && 4 * (c_lo - c_hi) > 3 * before;
-            if (lo == hi) take_ge = c_lo == k;      // converged: c_lo = count(key >= T)
-        }
-        T = lo;
-        if (!take_ge) {
-            const float tf = key_float(T);
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) greater += __popcll(__ballot(x[g][j] > tf));
-        }
+    for (int s = 0; s < NS; ++s) {
+        mn = fminf(mn, x[s]);
+        mx = fmaxf(mx, x[s]);
     }
-    const float Tf = key_float(T);
-    const int a0 = anchor >= 0 ? anchor * tpf : 0, a1 = anchor >= 0 ? min(a0 + tpf, Tk) : 0;
-    int32_t* out = idx + (size_t)row * kmax;
-    int base = 0;
-    if (mode == 2 && take_ge) {
-        // No tie to rank: the row takes every key >= T (exactly k of them) and the anchor
-        // tiles.  The selection stays in 64-bit lane masks (scalar registers), turned back
-        // into lane predicates where a store needs them; a lane's first slot of a group goes
-        // after every selected slot of the lower lanes.  Stores go through a buffer
-        // resource of min(kmax, Tk) entries, which drops anything past kmax.
-        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(out, 0, min(kmax, Tk) * 4,
-                                                                            tl::BUF_RSRC_WORD3);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const int t0 = 256 * g + 4 * lane;
-            uint64_t m[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) m[j] = __ballot(x[g][j] >= Tf);
-            if (a0 < 256 * g + 256 && a1 > 256 * g) {   // the group meets the anchor frame
-#pragma unroll
-                for (int j = 0; j < 4; ++j) m[j] |= __ballot(t0 + j >= a0 && t0 + j < a1);
-            }
-            uint32_t off = 4u * (uint32_t)below_from(m[3], below_from(m[2], below_from(m[1], below_from(m[0], base))));
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (__builtin_amdgcn_inverse_ballot_w64(m[j])) {
-                    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(t0 + j), ro, (int)off, 0, 0);
-                    off += 4u;
-                }
-            base += __popcll(m[0]) + __popcll(m[1]) + __popcll(m[2]) + __popcll(m[3]);
-        }
-        for (int q = base + lane; q < kmax; q += 64) out[q] = -1;
-        if (lane == 0) cnt[row] = min(base, kmax);
+    Bracket b{wave_min_uniform(order_key(mn)), wave_max_uniform(order_key(mx)), Tk, 0, false};
+    if (b.lo > b.hi) {                              // no score that is not NaN: the anchor frame only
+        emit_selection<NS>([&](int s, float& v, int& t, bool& valid) { v = x[s]; t = 64 * s + lane; valid = t < Tk; },
+                           NS, INFINITY, 0, a0, na, out, kmax);
+        finish(na);
         return;
     }
-    int ties_before = 0;                            // keys == T in earlier groups
-    const int need_eq = mode == 2 ? k - greater : 0;   // ties to take, lowest index first
+    // bisect the full row while the keys at or above lo overflow the list
+    for (;;) {
+        b.uniform();
+        if (b.lo == b.hi || b.c_lo <= TKW_LIST) break;
+        const uint32_t mid = b.probe();
+        const float tf = key_float(mid);
+        int c = 0;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const int t0 = 256 * g + 4 * lane;
-        bool sel[4], eq[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            // padding holds NaN, which fails every comparison below; only "every tile" and
-            // the anchor range need the bound
-            sel[j] = t0 + j >= a0 && t0 + j < a1;
-            eq[j] = false;
-            if (mode == 1) sel[j] = FULL || t0 + j < Tk;
-            else if (mode == 2 && take_ge) sel[j] = sel[j] || x[g][j] >= Tf;
-            else if (mode == 2) {
-                sel[j] = sel[j] || x[g][j] > Tf;
-                eq[j] = x[g][j] == Tf;
-            }
-        }
-        if (mode == 2 && !take_ge) {
-            // tie ranks in tile order: earlier groups, lower lanes, then this lane's lower j
-            int run = ties_before, tot = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint64_t em = __ballot(eq[j]);
-                run += lanes_below(em);
-                tot += __popcll(em);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (eq[j]) {
-                    sel[j] = sel[j] || run < need_eq;
-                    ++run;
-                }
-            ties_before += tot;
-        }
-        int pos = base, tot = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint64_t sm = __ballot(sel[j]);
-            pos += lanes_below(sm);
-            tot += __popcll(sm);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (sel[j]) {
-                if (pos < kmax) out[pos] = t0 + j;
-                ++pos;
-            }
-        base += tot;
+        for (int s = 0; s < NS; ++s) c += __popcll(__ballot(x[s] >= tf));
+        b.update(mid, c, k);
     }
-    for (int q = base + lane; q < kmax; q += 64) out[q] = -1;
-    if (lane == 0) cnt[row] = min(base, kmax);
+    if (b.c_lo > TKW_LIST) {
+        // converged on the full row with more keys >= T than the list holds
+        const float Tf = key_float(b.lo);
+        int greater = 0;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) greater += __popcll(__ballot(x[s] > Tf));
+        const int n = emit_selection<NS>(
+            [&](int s, float& v, int& t, bool& valid) { v = x[s]; t = 64 * s + lane; valid = t < Tk; },
+            NS, Tf, k - greater, a0, na, out, kmax);
+        finish(n);
+        return;
+    }
+    // the list: every key >= lo, in tile order.  c_lo >= count(key >= lo), so at most c_lo <=
+    // TKW_LIST entries are written and every write stays inside.
+    float* s_v = s_list[wave].v;
+    int32_t* s_t = s_list[wave].t;
+    int n = 0;
+    {
+        const float flo = key_float(b.lo);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const uint64_t m = __ballot(x[s] >= flo);
+            if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+                const int p = lanes_below(m);
+                (s_v + n)[p] = x[s];
+                (s_t + n)[p] = 64 * s + lane;
+            }
+            n += __popcll(m);
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    constexpr int NL = TKW_LIST / 64;
+    float lv[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) lv[i] = 64 * i + lane < n ? s_v[64 * i + lane] : __builtin_nanf("");
+    // bisect on the list while more than 64 keys lie inside the bracket
+    for (;;) {
+        b.uniform();
+        if (b.lo == b.hi || b.c_lo - b.c_hi <= 64) break;
+        const uint32_t mid = b.probe();
+        const float tf = key_float(mid);
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) c += __popcll(__ballot(lv[i] >= tf));
+        b.update(mid, c, k);
+    }
+    if (b.lo != b.hi) {
+        // gather the keys inside [lo, hi] (at most 64: c_hi is exact and c_lo bounds count(key
+        // >= lo)), one per lane, and rank them: T has rank k - c_hi among them.  The upper bound
+        // as "below key hi + 1" (hi stays below the key of NaN, so no wrap), since key_float
+        // maps the unused key just below +0 to -0.
+        const float glo = key_float(b.lo), gup = key_float(b.hi + 1);
+        float* s_g = s_gat[wave];
+        int ng = 0;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const uint64_t m = __ballot(lv[i] >= glo) & ~__ballot(lv[i] >= gup);
+            s_g[__builtin_amdgcn_inverse_ballot_w64(m) ? ng + lanes_below(m) : 64 + lane] = lv[i];
+            ng += __popcll(m);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        uint32_t v = lane < ng ? order_key(s_g[lane]) : 0u;   // pad lanes rank lowest
+#pragma unroll
+        for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                const uint32_t o = (uint32_t)__shfl_xor((int)v, stride);
+                const bool desc = (lane & size) == 0, lower = (lane & stride) == 0;
+                v = (lower == desc) ? max(v, o) : min(v, o);
+            }
+        }
+        b.lo = __builtin_amdgcn_readfirstlane((uint32_t)__shfl((int)v, k - b.c_hi - 1));
+    }
+    // Emit: S = the keys > T and the first k - count(key > T) keys == T, all in the list.  In
+    // the sorted output the anchor frame A = [a0, a1) is one run starting after the members of
+    // S below a0, and members of S after A move by the anchor tiles S does not hold.
+    const float Tf = key_float(b.lo);
+    int greater = 0;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) greater += __popcll(__ballot(lv[i] > Tf));
+    const int need_eq = k - greater;
+    uint64_t sm[NL];
+    int ties = 0, before_a = 0, in_a = 0;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const bool eq = lv[i] == Tf;
+        const uint64_t em = __ballot(eq);
+        const bool sel = lv[i] > Tf || (eq && ties + lanes_below(em) < need_eq);
+        ties += __popcll(em);
+        sm[i] = __ballot(sel);
+        const int t = s_t[64 * i + lane];           // read past n: stale, and not selected
+        before_a += __popcll(__ballot(sel && t < a0));
+        in_a += __popcll(__ballot(sel && t >= a0 && t < a1));
+    }
+    const int shift = na - in_a;                    // anchor tiles S does not hold
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int t = s_t[64 * i + lane];
+        const int pos = base + lanes_below(sm[i]) + (t >= a1 ? shift : 0);
+        if (__builtin_amdgcn_inverse_ballot_w64(sm[i]) && (uint32_t)(t - a0) >= (uint32_t)na && pos < kmax)
+            out[pos] = t;
+        base += __popcll(sm[i]);
+    }
+    for (int q = lane; q < na; q += 64)
+        if (before_a + q < kmax) out[before_a + q] = a0 + q;
+    finish(base + shift);
 }
 
-template <int G>
+template <int NS>
 static void launch_wave(bool full, dim3 grid, dim3 block, hipStream_t st, const float* scores, int tk, int tq,
                         int rows, const KBudget& kb, int tpf, int anchor, int32_t* ix, int32_t* cn, int kmax) {
     if (full)
-        hipLaunchKernelGGL((k_select_topk_wave<G, true>), grid, block, 0, st, scores, tk, tq, rows, kb, tpf, anchor,
+        hipLaunchKernelGGL((k_select_topk_wave<NS, true>), grid, block, 0, st, scores, tk, tq, rows, kb, tpf, anchor,
                            ix, cn, kmax);
     else
-        hipLaunchKernelGGL((k_select_topk_wave<G, false>), grid, block, 0, st, scores, tk, tq, rows, kb, tpf,
+        hipLaunchKernelGGL((k_select_topk_wave<NS, false>), grid, block, 0, st, scores, tk, tq, rows, kb, tpf,
                            anchor, ix, cn, kmax);
 }
 
@@ -542,20 +548,18 @@ hipError_t launch_select_topk(const float* scores, int heads, int tq, int tk, co
         int32_t* ix = kmax > 0 ? idx + r0 * kmax : idx;
         const dim3 wgrid((unsigned)((rows + TKW_WAVES - 1) / TKW_WAVES)), wblock(64 * TKW_WAVES);
         const float* sc = scores + r0 * tk;
-        // one wave per row while the keys fit 96 registers per lane (G groups of 256 tiles, the
-        // smallest that holds the row) and the rows allow 16-byte loads; otherwise a
-        // workgroup per row
-        const bool vec = tk % 4 == 0 && reinterpret_cast<uintptr_t>(sc) % 16 == 0;
-        const int g = (tk + 255) / 256;
+        // one wave per row while the scores fit 96 registers per lane (NS slots of 64 tiles, the
+        // fewest of these that hold the row); otherwise a workgroup per row
+        const int ns = (tk + 63) / 64;
         int32_t* cn = cnt + r0;
-#define S3D_WAVE(GG) launch_wave<GG>(tk == 256 * (GG), wgrid, wblock, st, sc, tk, tq, rows, kb, tpf, anchor, ix, cn, kmax)
-        if (vec && g <= 2) S3D_WAVE(2);
-        else if (vec && g <= 4) S3D_WAVE(4);
-        else if (vec && g <= 8) S3D_WAVE(8);
-        else if (vec && g <= 11) S3D_WAVE(11);
-        else if (vec && g <= 16) S3D_WAVE(16);
-        else if (vec && g <= 22) S3D_WAVE(22);
-        else if (vec && g <= 24) S3D_WAVE(24);
+#define S3D_WAVE(N) launch_wave<N>(tk == 64 * (N), wgrid, wblock, st, sc, tk, tq, rows, kb, tpf, anchor, ix, cn, kmax)
+        if (ns <= 8) S3D_WAVE(8);
+        else if (ns <= 16) S3D_WAVE(16);
+        else if (ns <= 32) S3D_WAVE(32);
+        else if (ns <= 44) S3D_WAVE(44);
+        else if (ns <= 64) S3D_WAVE(64);
+        else if (ns <= 88) S3D_WAVE(88);
+        else if (ns <= 96) S3D_WAVE(96);
         else
             hipLaunchKernelGGL(k_select_topk, dim3((unsigned)rows), dim3(TK_THREADS), shm, st,
                                sc, tk, tq, kb, tpf, anchor, ix, cn, kmax);

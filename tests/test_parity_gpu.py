@@ -166,9 +166,11 @@ def test_select_topk_hard_rows():
     # Score rows built to stress the k-th-largest search: heavy ties, values spread over
     # many binades (with overflow to +inf), masked (-inf) entries, constant rows and signed
     # zeros, at lengths that take each wave width (full rows: 512, 1024, 2048, 2816, 4096,
-    # 5632, 6144; the others ragged) and the workgroup kernel (1001: not a multiple of 4;
-    # 6500: longer than a wave holds; and a matrix that starts 4 bytes past an aligned
-    # address).  Compared with the oracle's rule applied to the same fp32 scores.
+    # 5632, 6144; the others ragged, and a matrix that starts 4 bytes past an aligned
+    # address) and the workgroup kernel (6500: longer than a wave holds).  Budgets up to 138
+    # finish on the short list of keys at or above the bracket; larger ones, and the rows of
+    # many equal values, bisect the whole row.  Compared with the oracle's rule applied to
+    # the same fp32 scores.
     rng = np.random.default_rng(21)
     for Tk in (100, 512, 1000, 1001, 1024, 2000, 2048, 2816, 3000, 3072, 4096, 5000, 5632, 6144, 6500, -1000):
         shifted = Tk < 0
