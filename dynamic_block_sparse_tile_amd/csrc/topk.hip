@@ -284,6 +284,41 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Bitonic sort of one key per lane into descending lane order.  Lane pairs (l, l ^ stride)
+// exchange through DPP quad permutes (strides 1, 2), ds_swizzle (4, 8, 16) or a lane permute
+// (32); the lane that keeps the larger key in each step is fixed by (size, stride).
+constexpr uint64_t bitonic_max_lanes(int size, int stride) {
+    uint64_t m = 0;
+    for (int l = 0; l < 64; ++l)
+        if (((l & stride) == 0) == ((l & size) == 0)) m |= 1ull << l;
+    return m;
+}
+template <int STRIDE>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+    if constexpr (STRIDE == 1)
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    else if constexpr (STRIDE == 2)
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    else if constexpr (STRIDE < 32)
+        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (STRIDE << 10));    // lane ^ STRIDE in 32
+    else
+        return (uint32_t)__shfl_xor((int)v, STRIDE);
+}
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ uint32_t bitonic_merge(uint32_t v) {
+    constexpr uint64_t take_max = bitonic_max_lanes(SIZE, STRIDE);
+    const uint32_t o = lane_xor<STRIDE>(v);
+    v = __builtin_amdgcn_inverse_ballot_w64(take_max) ? max(v, o) : min(v, o);
+    if constexpr (STRIDE > 1) return bitonic_merge<SIZE, STRIDE / 2>(v);
+    else return v;
+}
+template <int SIZE>
+__device__ __forceinline__ uint32_t bitonic_sort_desc(uint32_t v) {
+    v = bitonic_merge<SIZE, SIZE / 2>(v);
+    if constexpr (SIZE < 64) return bitonic_sort_desc<SIZE * 2>(v);
+    else return v;
+}
+
 // The bisection state of one row (every field wave-uniform).
 struct Bracket {
     uint32_t lo, hi;        // key bracket of T
@@ -353,8 +388,8 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
     // per row: the list (values and tiles at a fixed distance, so one address serves both)
     // and the gathered bracket (64 entries, then one dump slot per lane)
     struct List {
-        float v[TKW_LIST];
-        int32_t t[TKW_LIST];
+        float v[TKW_LIST + 64];         // TKW_LIST entries, then one dump slot per lane
+        int32_t t[TKW_LIST + 64];
     };
     __shared__ List s_list[TKW_WAVES];
     __shared__ float s_gat[TKW_WAVES][128];
@@ -425,7 +460,8 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
         return;
     }
     // the list: every key >= lo, in tile order.  c_lo >= count(key >= lo), so at most c_lo <=
-    // TKW_LIST entries are written and every write stays inside.
+    // TKW_LIST entries are written and every write stays inside.  Every lane writes, the ones
+    // without a key for the list to their dump slot, so the writes need no exec mask.
     float* s_v = s_list[wave].v;
     int32_t* s_t = s_list[wave].t;
     int n = 0;
@@ -434,11 +470,12 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             const uint64_t m = __ballot(x[s] >= flo);
-            if (__builtin_amdgcn_inverse_ballot_w64(m)) {
-                const int p = lanes_below(m);
-                (s_v + n)[p] = x[s];
-                (s_t + n)[p] = 64 * s + lane;
-            }
+            int p = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)n));
+            asm volatile("" : "+v"(p));             // in every lane, so the choice below is a select
+            p = __builtin_amdgcn_inverse_ballot_w64(m) ? p : TKW_LIST + lane;
+            s_v[p] = x[s];
+            s_t[p] = 64 * s + lane;
             n += __popcll(m);
         }
     }
@@ -477,16 +514,7 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        uint32_t v = lane < ng ? order_key(s_g[lane]) : 0u;   // pad lanes rank lowest
-#pragma unroll
-        for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                const uint32_t o = (uint32_t)__shfl_xor((int)v, stride);
-                const bool desc = (lane & size) == 0, lower = (lane & stride) == 0;
-                v = (lower == desc) ? max(v, o) : min(v, o);
-            }
-        }
+        const uint32_t v = bitonic_sort_desc<2>(lane < ng ? order_key(s_g[lane]) : 0u);   // pads rank lowest
         b.lo = __builtin_amdgcn_readfirstlane((uint32_t)__shfl((int)v, k - b.c_hi - 1));
     }
     // Emit: S = the keys > T and the first k - count(key > T) keys == T, all in the list.  In
