@@ -385,14 +385,14 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
                                                                      int Tq, int rows, KBudget kb, int tpf,
                                                                      int anchor, int32_t* __restrict__ idx,
                                                                      int32_t* __restrict__ cnt, int kmax) {
-    // per row: the list (values and tiles at a fixed distance, so one address serves both)
-    // and the gathered bracket (64 entries, then one dump slot per lane)
+    // per row: the list (values and tiles at a fixed distance, so one address serves both).
+    // Once the values sit in registers, the value half takes the gathered bracket (64
+    // entries, then one dump slot per lane).
     struct List {
         float v[TKW_LIST + 64];         // TKW_LIST entries, then one dump slot per lane
         int32_t t[TKW_LIST + 64];
     };
     __shared__ List s_list[TKW_WAVES];
-    __shared__ float s_gat[TKW_WAVES][128];
     // the row is wave-uniform: in a scalar register, its buffer resource needs no lane loop
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row = blockIdx.x * TKW_WAVES + wave;
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(64 * TKW_WAVES) void k_select_topk_wave(const float
         // as "below key hi + 1" (hi stays below the key of NaN, so no wrap), since key_float
         // maps the unused key just below +0 to -0.
         const float glo = key_float(b.lo), gup = key_float(b.hi + 1);
-        float* s_g = s_gat[wave];
+        float* s_g = s_v;                           // the list values are in lv[] now
         int ng = 0;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
