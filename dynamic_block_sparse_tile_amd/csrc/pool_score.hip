@@ -97,7 +97,10 @@ __global__ __launch_bounds__(256) void k_tile_pool(const void* __restrict__ x, i
 // loads are in flight while the current one is multiplied).  The product is formed
 // transposed (keys as the accumulator rows); each wave stages its 32 x 32 results through
 // LDS and stores whole 128-byte lines, eight query rows per store instruction, while the
-// matrix cores go on with the next products.
+// matrix cores go on with the next products.  Stores and loads share one in-order
+// completion counter, so the next block is split into LDS after this block's products and
+// before its stores: waiting for its loads then waits only for the previous block's stores,
+// which have had the products' time to drain.
 constexpr int SC_Q = 128;               // query tiles per workgroup (4 waves x 32)
 constexpr int SC_K = 64;                // key tiles per block
 constexpr int SC_STG = 36;              // staged score row stride (floats): conflict-free b128 writes
@@ -162,12 +165,18 @@ __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restric
     // staging of a key block: thread t takes key t / 4, dims 16 (t % 4) .. + 16
     const int sk = tid >> 2, sd = tid & 3;
     float4 raw[4];
+    // the head's key means through a buffer resource: keys past Tk read zeros
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(kb), 0, Tk * HD * 4,
+                                                                        0x00020000);
     auto load_block = [&](int s) {
         const int key = kb0 + s * SC_K + sk;
+        typedef float f32x4v __attribute__((ext_vector_type(4)));
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            raw[i] = key < Tk ? reinterpret_cast<const float4*>(kb + (size_t)key * HD + 16 * sd)[i]
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int i = 0; i < 4; ++i) {
+            const f32x4v u = __builtin_bit_cast(f32x4v, __builtin_amdgcn_raw_buffer_load_b128(
+                rk, key * (HD * 4) + 64 * sd + 16 * i, 0, 0));
+            raw[i] = make_float4(u[0], u[1], u[2], u[3]);
+        }
     };
     auto write_block = [&](int s, int buf) {
 #pragma unroll
@@ -205,6 +214,10 @@ __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restric
         if (s + 1 < nkb) load_block(s + 1);          // lands while this block is multiplied
         const uint64_t ke = s_kempty[buf];
         const bool any_empty = any_qempty || ke != 0ull;
+        // both 32-key halves' products, then the next block's split into the other buffer
+        // (its loads, and the previous block's score stores issued before them, have had the
+        // products' time to land), then this block's stores
+        f32x16 accs[2];
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
             // sigma^T = kbar qbar^T: key rows 32 cb + col of the block, dims 16 ks + 8 g
@@ -225,17 +238,31 @@ __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restric
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[ks], ah[ks], acc, 0, 0, 0);
+            accs[cb] = acc;
+        }
+        if (s + 1 < nkb) write_block(s + 1, buf ^ 1);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            const f32x16& acc = accs[cb];
             // lane: query row r0 + col; keys 8 a + 4 g + j of the 32 (accumulator rows)
-            const uint32_t kw = (uint32_t)(ke >> (32 * cb)) >> (4 * g);
+            if (!any_empty) {                        // the common case: no empty tile in sight
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                float v[4];
+                for (int a = 0; a < 4; ++a)
+                    *reinterpret_cast<float4*>(stg + col * SC_STG + 8 * a + 4 * g) =
+                        make_float4(acc[4 * a] * scale, acc[4 * a + 1] * scale, acc[4 * a + 2] * scale,
+                                    acc[4 * a + 3] * scale);
+            } else {
+                const uint32_t kw = (uint32_t)(ke >> (32 * cb)) >> (4 * g);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    v[j] = acc[4 * a + j] * scale;
-                    if (any_empty && (qempty || ((kw >> (8 * a + j)) & 1u))) v[j] = -INFINITY;
+                for (int a = 0; a < 4; ++a) {
+                    float v[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        v[j] = acc[4 * a + j] * scale;
+                        if (qempty || ((kw >> (8 * a + j)) & 1u)) v[j] = -INFINITY;
+                    }
+                    *reinterpret_cast<float4*>(stg + col * SC_STG + 8 * a + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
                 }
-                *reinterpret_cast<float4*>(stg + col * SC_STG + 8 * a + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -243,12 +270,13 @@ __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restric
             // lanes 8 i .. 8 i + 7: query row 8 q + i, keys 4 (lane % 8) .. + 3 of the 32
             const int ch = lane & 7;
             const int cbase = kb0 + s * SC_K + 32 * cb + 4 * ch;
+            const bool whole = kb0 + s * SC_K + 32 * cb + 32 <= Tk;   // no ragged column in this half
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int row = 8 * q + (lane >> 3);
                 const float4 v = *reinterpret_cast<const float4*>(stg + row * SC_STG + 4 * ch);
                 const unsigned voff = ((unsigned)row * (unsigned)Tk + (unsigned)cbase) * 4u;
-                if (cbase + 3 < Tk) {
+                if (whole || cbase + 3 < Tk) {
                     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
                     const u32x4 pk = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
                                       __float_as_uint(v.w)};
@@ -265,7 +293,6 @@ __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restric
             __builtin_amdgcn_wave_barrier();         // read before the next stage overwrites it
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-        if (s + 1 < nkb) write_block(s + 1, buf ^ 1);
         __syncthreads();
     }
 }
