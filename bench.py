@@ -139,9 +139,30 @@ def write_counters(outdir: str):
     stats = glob.glob(os.path.join(outdir, "trace", "**", "*kernel_stats.csv"), recursive=True)
     if not stats:
         raise SystemExit(f"{outdir}/trace: no kernel_stats.csv")
+    # The figures of one layer come from the layers the run timed (warm-up included): the
+    # last dispatches_per_layer x layers dispatches of each kernel.  Dispatches before them
+    # (the sparsity calibration's selections at other budgets) are left out.
+    def keep(name):
+        fam = kernel_family(name)
+        n = info["dispatches_per_layer"].get(fam, 0) if fam else 0
+        return n * info.get("layers", 0)
+
     dur = {}                                            # name -> (calls, mean ns)
-    for row in csv.DictReader(open(stats[0])):
-        dur[row["Name"]] = (int(row["Calls"]), float(row["AverageNs"]))
+    traces = glob.glob(os.path.join(outdir, "trace", "**", "*kernel_trace.csv"), recursive=True)
+    if traces:
+        per_name = defaultdict(list)                    # name -> [(start, duration ns)]
+        for row in csv.DictReader(open(traces[0])):
+            t0, t1 = int(row["Start_Timestamp"]), int(row["End_Timestamp"])
+            per_name[row["Kernel_Name"]].append((t0, t1 - t0))
+        for name, ds in per_name.items():
+            ds.sort()
+            n = keep(name)
+            if n:
+                ds = ds[-n:]
+            dur[name] = (len(ds), sum(d for _, d in ds) / len(ds))
+    else:
+        for row in csv.DictReader(open(stats[0])):
+            dur[row["Name"]] = (int(row["Calls"]), float(row["AverageNs"]))
 
     def counters(pass_name):
         files = glob.glob(os.path.join(outdir, pass_name, "**", "*counter_collection.csv"), recursive=True)
@@ -160,7 +181,13 @@ def write_counters(outdir: str):
 
     def mean_of(per, name, counter):
         v = per.get((name, counter))
-        return sum(v.values()) / len(v) if v else None
+        if not v:
+            return None
+        vals = [v[d] for d in sorted(v, key=int)]
+        n = keep(name)
+        if n:
+            vals = vals[-n:]
+        return sum(vals) / len(vals)
 
     copy_bytes = PROFILE_COPY_MB * (1 << 20)
     scale = {}
@@ -194,8 +221,11 @@ def write_counters(outdir: str):
         # on shorter ones the active-cycle count and the dispatch timestamps do not line up
         if grbm and sec >= 1e-4:
             # cycles per XCD over the dispatch's own span in that pass
-            clocks = [grbm[d] / N_XCD / span[d] for d in grbm if span.get(d, 0) > 0]
-            cyc = sum(grbm.values()) / len(grbm) / N_XCD
+            ids = sorted(grbm, key=int)
+            if keep(name):
+                ids = ids[-keep(name):]
+            clocks = [grbm[d] / N_XCD / span[d] for d in ids if span.get(d, 0) > 0]
+            cyc = sum(grbm[d] for d in ids) / len(ids) / N_XCD
             k["clock_ghz"] = round(sum(clocks) / len(clocks) / 1e9, 3) if clocks else None
             busy = mean_of(sq, name, "SQ_VALU_MFMA_BUSY_CYCLES")
             anyi = mean_of(sq, name, "SQ_ACTIVE_INST_ANY")
@@ -268,7 +298,10 @@ def counters_markdown(c) -> str:
          f"(FETCH_SIZE x{c['counter_scale']['FETCH_SIZE']}, WRITE_SIZE x{c['counter_scale']['WRITE_SIZE']}); "
          f"peaks: HBM {PEAK_HBM_GBS / 1000:g} TB/s, matrix {PEAK_TFLOPS[run['dtype']]:g} TFLOP/s "
          f"({run['dtype']}, quoted at 2.4 GHz).", "",
-         "The shader clock and the matrix-core busy share are given for dispatches of at least 0.1 ms.",
+         f"Each kernel's figures are means over the dispatches of the {run.get('layers', '?')} layers the run "
+         f"timed (warm-up included), one layer's worth per layer; the sparsity calibration's selections "
+         f"before them are left out.  The shader clock and the matrix-core busy share are given for "
+         f"dispatches of at least 0.1 ms.",
          "", "Commands (`$R` = repository root, run from /tmp with TMPDIR=/tmp):", "", "```"]
     for cmd in c["commands"]:
         L.append(cmd)
