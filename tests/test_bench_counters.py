@@ -99,3 +99,41 @@ def test_kernel_family():
     assert bench.kernel_family("void s3d::k_cast_bf16(float const*, long, __bf16*)") == "cast"
     assert bench.kernel_family(COPY) == "copy"
     assert bench.kernel_family("void other::kernel()") is None
+
+
+def test_counter_reader_keeps_the_timed_layers(tmp_path, monkeypatch):
+    # nine selections: six calibration launches at other budgets (0.5 ms, 4e5 KiB fetched)
+    # before the three timed layers (0.1 ms, 1e5 KiB); only the last three may count
+    d = tmp_path / "prof"
+    os.makedirs(d / "trace")
+    with open(d / "trace" / "run_kernel_stats.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "MinNs", "MaxNs"])
+        w.writerow([SEL, 9, 3.3e6, 3.67e5, 1e5, 5e5])
+        w.writerow([COPY, 1, 5e5, 5e5, 5e5, 5e5])
+    with open(d / "trace" / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        t = 0
+        for i in range(9):
+            dt = 500_000 if i < 6 else 100_000
+            w.writerow([SEL, t, t + dt])
+            t += 10 * dt
+        w.writerow([COPY, t, t + 500_000])
+    mib = bench.PROFILE_COPY_MB * 1024
+    _pmc(str(d / "fetch"), [[0, COPY, "FETCH_SIZE", mib / 2, 0, 1]] +
+         [[i + 1, SEL, "FETCH_SIZE", 4e5 if i < 6 else 1e5, 0, 1] for i in range(9)])
+    _pmc(str(d / "write"), [[0, COPY, "WRITE_SIZE", mib, 0, 1]] +
+         [[i + 1, SEL, "WRITE_SIZE", 0.0, 0, 1] for i in range(9)])
+    _pmc(str(d / "sq"), [[0, COPY, "SQ_WAVES", 1.0, 0, 1]])
+    info = {"workload": "fake2", "kernel_source_sha256": "abc", "dtype": "bf16", "heads": 1, "q_tiles": 4,
+            "k_tiles": 4, "top_k": 1, "kmax": 2, "landmarks": False, "layers": 3, "attn_flops_per_launch": 1.0,
+            "alg_per_dispatch": {"select": 1e8}, "dispatches_per_layer": {"select": 1}}
+    json.dump(info, open(d / "run_info.json", "w"))
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    bench.write_counters(str(d))
+    c = json.load(open(tmp_path / "profiles" / "counters_fake2.json"))
+    s = {x["family"]: x for x in c["kernels"]}["select"]
+    assert s["dispatches"] == 3 and s["avg_ms"] == pytest.approx(0.1)
+    assert s["fetch_bytes"] == round(1e5 * 1024 * 2)
+    assert c["layer_ms_by_family"]["select"] == pytest.approx(0.1)
