@@ -7,7 +7,10 @@
 // Three kernels, each with the forward's operand machinery (tile_lds.h):
 //  - k_attn_bwd_dq: one workgroup per (head, query tile) walks the query tile's list
 //    (special pseudo-tiles, its selected tiles, then with landmarks the blocks of 64 tile
-//    means) like the forward and accumulates dQ^T += K^T dS^T; it also writes D.
+//    means) like the forward and accumulates dQ^T += K^T dS^T; it also writes D.  Each step
+//    forms dP for its 64 keys first (the only use of V, whose single buffer then takes the
+//    next tile), then S, dS and dQ for one half of 32 keys at a time (K is double
+//    buffered): 24 KiB of LDS and at most 168 VGPRs, three waves per SIMD.
 //  - k_attn_bwd_dkv<true> (landmarks only): one workgroup per (head, block of 64 tile means)
 //    walks every query tile and accumulates the means' gradients dvbar^T += dO^T P and
 //    dkbar^T += Q^T dS, a tile's column masked for the query tiles that selected it.
@@ -147,9 +150,11 @@ __device__ __forceinline__ float dot_bf16x8(const bf16x8& a, const bf16x8& b, fl
 
 // ------------------------------------------------------------------------------ dQ
 template <bool LM>
-__global__ __launch_bounds__(128, 2) void k_attn_bwd_dq(BwdDev p) {
+__global__ __launch_bounds__(128, 3) void k_attn_bwd_dq(BwdDev p) {
+    // K is read at both ends of a step (S, then dQ), V only at its start (dP): K is double
+    // buffered, V single, reloaded once every wave has formed its dP
     __shared__ __align__(16) unsigned char s_k[2][TILE_BYTES];
-    __shared__ __align__(16) unsigned char s_v[2][TILE_BYTES];
+    __shared__ __align__(16) unsigned char s_v[1][TILE_BYTES];
     extern __shared__ int32_t s_idx[];                  // kmax list entries, then the bitmap
     uint32_t* s_lm = reinterpret_cast<uint32_t*>(s_idx + p.kmax);
 
@@ -200,61 +205,86 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dq(BwdDev p) {
     off.init(lane);
 
     f32x16 dq0 = {}, dq1 = {};
-    auto stage = [&](int it, int b) {
+    auto stage_k = [&](int it, int b) {
         const Block kb = key_block(p, it, p.Ts, c, s_idx, s_lm);
-        if (LM && __builtin_amdgcn_readfirstlane(kb.kind) == 2) {
-            stage_block(rs_kb, p.kl, kb, (lds_u8*)s_k[b], w, lane);
-            stage_block(rs_vb, p.kl, kb, (lds_u8*)s_v[b], w, lane);
-        } else {
-            stage_block(rs_k, p.kl, kb, (lds_u8*)s_k[b], w, lane);
-            stage_block(rs_v, p.kl, kb, (lds_u8*)s_v[b], w, lane);
-        }
+        const bool mean = LM && __builtin_amdgcn_readfirstlane(kb.kind) == 2;
+        stage_block(mean ? rs_kb : rs_k, p.kl, kb, (lds_u8*)s_k[b], w, lane);
         return kb;
     };
+    auto stage_v = [&](const Block& kb) {
+        const bool mean = LM && __builtin_amdgcn_readfirstlane(kb.kind) == 2;
+        stage_block(mean ? rs_vb : rs_v, p.kl, kb, (lds_u8*)s_v[0], w, lane);
+    };
     Block cur{}, nxt{};
-    if (ntiles > 0) cur = stage(0, 0);
+    if (ntiles > 0) {
+        cur = stage_k(0, 0);
+        stage_v(cur);
+    }
     __builtin_amdgcn_s_waitcnt(0x0070);
     __syncthreads();
     for (int it = 0; it < ntiles; ++it) {
         const int b = it & 1;
-        if (it + 1 < ntiles) nxt = stage(it + 1, b ^ 1);
+        if (it + 1 < ntiles) nxt = stage_k(it + 1, b ^ 1);
         const unsigned char* kt = s_k[b];
-        const unsigned char* vt = s_v[b];
-        if (wq) {
-            f32x16 s0 = {}, s1 = {}, p0 = {}, p1 = {};
+        const unsigned char* vt = s_v[0];
+        // landmark logits carry the bias
+        const float nl = (LM && __builtin_amdgcn_readfirstlane(cur.kind) == 2 ? p.lm_bias_l2 : 0.f) - lse_l2;
+        const uint64_t km = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(cur.mask >> 32)) << 32) |
+                            __builtin_amdgcn_readfirstlane((uint32_t)cur.mask);
+        // keys 32 hk .. 32 hk + 31 of the step: S^T and dP^T (lane = query column), then
+        // dS^T = P^T (dP^T - D) with key rows outside the block's mask taking no part, then
+        // dQ^T += K^T dS^T over the half's two k-steps
+        auto products = [&](int hk, f32x16& acc, const unsigned char* t, const bf16x8 (&op)[4]) {
+            acc = f32x16{};
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
-                bf16x8 a0, a1, v0, v1;
-                read_rows(kt, off, st, a0, a1);
-                read_rows(vt, off, st, v0, v1);
-                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qop[st], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qop[st], s1, 0, 0, 0);
-                p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, dop[st], p0, 0, 0, 0);
-                p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, dop[st], p1, 0, 0, 0);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(t + off.row[st] + 4096 * hk));
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, op[st], acc, 0, 0, 0);
             }
-            // dS^T = P^T (dP^T - D); key rows outside the block's mask take no part
-            // this lane's keys 8i + 4g + (0..3) of each half, tested against constant bits
-            const uint32_t w0 = __builtin_amdgcn_readfirstlane((uint32_t)cur.mask) >> (4 * g);
-            const uint32_t w1 = __builtin_amdgcn_readfirstlane((uint32_t)(cur.mask >> 32)) >> (4 * g);
-            // landmark logits carry the bias
-            const float nl = (LM && __builtin_amdgcn_readfirstlane(cur.kind) == 2 ? p.lm_bias_l2 : 0.f) - lse_l2;
-            f32x16 d0, d1;
+        };
+        auto finish = [&](int hk, const f32x16& sk, f32x16& pk) {
+            const uint32_t wm = (uint32_t)(km >> (32 * hk));
+            if (wm == 0xffffffffu) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const uint32_t bit = 1u << (8 * (r >> 2) + (r & 3));
-                const float pa = (w0 & bit) ? __builtin_amdgcn_exp2f(fmaf(s0[r], p.scale_l2, nl)) : 0.f;
-                const float pb = (w1 & bit) ? __builtin_amdgcn_exp2f(fmaf(s1[r], p.scale_l2, nl)) : 0.f;
-                d0[r] = pa * (p0[r] - D);
-                d1[r] = pb * (p1[r] - D);
+                for (int r = 0; r < 16; ++r)
+                    pk[r] = __builtin_amdgcn_exp2f(fmaf(sk[r], p.scale_l2, nl)) * (pk[r] - D);
+            } else {
+                // this lane's keys 8i + 4g + (0..3) of the half, tested against constant bits
+                const uint32_t wl = wm >> (4 * g);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const uint32_t bit = 1u << (8 * (r >> 2) + (r & 3));
+                    const float pa = (wl & bit) ? __builtin_amdgcn_exp2f(fmaf(sk[r], p.scale_l2, nl)) : 0.f;
+                    pk[r] = pa * (pk[r] - D);
+                }
             }
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int kk = 0; kk < 2; ++kk) {
                 bf16x8 a0, a1;
-                read_tr(kt, off, ks, a0, a1);
-                const bf16x8 bs = acc_to_b(d0, d1, ks, [](float x, int, int) { return x; });
+                read_tr(kt, off, 2 * hk + kk, a0, a1);
+                const bf16x8 bs = acc_to_b(pk, pk, kk, [](float x, int, int) { return x; });
                 dq0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bs, dq0, 0, 0, 0);
                 dq1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bs, dq1, 0, 0, 0);
             }
+        };
+        f32x16 p0, p1;
+        if (wq) {                                            // dP of both halves: every V read
+            products(0, p0, vt, dop);
+            products(1, p1, vt, dop);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);          // this wave's V reads are done
+        __syncthreads();                                     // and every wave's
+        if (it + 1 < ntiles) stage_v(nxt);                   // V(it+1) into the one V buffer
+        __builtin_amdgcn_sched_barrier(0);
+        if (wq) {                                            // S, dS and dQ half by half
+            f32x16 s0;
+            products(0, s0, kt, qop);
+            finish(0, s0, p0);
+            __builtin_amdgcn_sched_barrier(0);
+            f32x16 s1;
+            products(1, s1, kt, qop);
+            finish(1, s1, p1);
         }
         cur = nxt;
         __builtin_amdgcn_s_waitcnt(0x0070);
