@@ -18,8 +18,9 @@
 //    it (the selection transposed; every query tile for a special pseudo-tile) and
 //    accumulates dV^T += dO^T P and dK^T += Q^T dS; with landmarks it adds the means'
 //    gradients, divided by the member count, to each member row (the means are averages
-//    over the member rows).  Every output row gets exactly one writer, so the result is
-//    deterministic.
+//    over the member rows).  Four waves per workgroup: two key halves times two query
+//    halves, whose partial sums are added in a fixed order at the end, so three waves share
+//    a SIMD.  Every output row gets exactly one writer, so the result is deterministic.
 #include <algorithm>
 
 #include "attn_common.h"
@@ -109,21 +110,22 @@ __device__ __forceinline__ Block key_block(const BwdDev& p, int it, int ts, int 
     return b;
 }
 
-// Stage rows of a 64-row block into LDS (this wave's 32 rows, four 8-row DMA loads);
-// rows outside `mask` load zeros.
+// Stage rows of a 64-row block into LDS (this wave's 64 / NW rows, 8-row DMA loads, NW
+// waves per workgroup); rows outside `mask` load zeros.
+template <int NW = 2>
 __device__ __forceinline__ void stage_block(const __amdgpu_buffer_rsrc_t& rs, const Lay& L, const Block& b,
                                             lds_u8* dst, int w, int lane) {
     const int srow_in = lane >> 3, sslot = lane & 7;
     const unsigned base = b.kind == 1 ? 0u : (unsigned)b.t * TILE_BYTES;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = 32 * w + 8 * j + srow_in;
+    for (int j = 0; j < 8 / NW; ++j) {
+        const int r = (64 / NW) * w + 8 * j + srow_in;
         unsigned vo = OOB_OFFSET;
         if ((b.mask >> r) & 1ull) {
             const int row_in_block = b.kind == 1 ? block_row(L, b, r) : r;
             vo = (unsigned)row_in_block * 128u + swz(r, sslot) * 16u;
         }
-        dma_buf(rs, dst + (32 * w + 8 * j) * 128, vo, __builtin_amdgcn_readfirstlane(base));
+        dma_buf(rs, dst + ((64 / NW) * w + 8 * j) * 128, vo, __builtin_amdgcn_readfirstlane(base));
     }
 }
 
@@ -319,15 +321,20 @@ __global__ __launch_bounds__(128, 3) void k_attn_bwd_dq(BwdDev p) {
 // lane walks in step with the loop (one comparison per query tile; the next entry loads
 // under the step's products).
 template <bool MEANS>
-__global__ __launch_bounds__(128, 2) void k_attn_bwd_dkv(BwdDev p) {
+__global__ __launch_bounds__(256, MEANS ? 2 : 3) void k_attn_bwd_dkv(BwdDev p) {
+    // the staging buffers (32 KiB) also carry the query halves' partial sums at the end
     __shared__ __align__(16) unsigned char s_q[2][TILE_BYTES];
     __shared__ __align__(16) unsigned char s_do[2][TILE_BYTES];
     __shared__ __align__(16) float s_lse[2][TILE];
     __shared__ __align__(16) float s_d[2][TILE];
 
+    // four waves: wave w owns key rows 32 (w & 1) .. + 31 of the block and query rows
+    // 32 (w >> 1) .. + 31 of every query tile; the two query halves' partial sums of dK and dV
+    // are added in a fixed order at the end
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int wk_half = w & 1, qh = w >> 1;
     const int kc = lane & 31, g = lane >> 5;
-    const int kr = 32 * w + kc;                                  // key row within the block
+    const int kr = 32 * wk_half + kc;                            // key row within the block
     const int Lq = p.ql.S * p.ql.P, Lk = p.kl.S * p.kl.P;
     int h;
     Block kb;
@@ -429,8 +436,8 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dkv(BwdDev p) {
         qb.kind = 0;
         qb.t = tq;
         qb.mask = range_mask(0, valid_rows(p.ql, tq));
-        stage_block(rs_q, p.ql, qb, (lds_u8*)s_q[b], w, lane);
-        stage_block(rs_do, p.ql, qb, (lds_u8*)s_do[b], w, lane);
+        stage_block<4>(rs_q, p.ql, qb, (lds_u8*)s_q[b], w, lane);
+        stage_block<4>(rs_do, p.ql, qb, (lds_u8*)s_do[b], w, lane);
     };
 
     f32x16 dk0 = {}, dk1 = {}, dv0 = {}, dv1 = {};
@@ -438,9 +445,9 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dkv(BwdDev p) {
     if (nq > 0) {
         const int t0 = qtile(0);
         stage(t0, 0);
-        fetch_rows(t0, rowval);
+        if (tid < 128) fetch_rows(t0, rowval);
         __builtin_amdgcn_s_waitcnt(0x0070);
-        (tid < 64 ? s_lse[0] : s_d[0])[tid & 63] = rowval;
+        if (tid < 128) (tid < 64 ? s_lse[0] : s_d[0])[tid & 63] = rowval;
     }
     __syncthreads();
     for (int i = 0; i < nq; ++i) {
@@ -448,7 +455,7 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dkv(BwdDev p) {
         if (i + 1 < nq) {
             const int tn = qtile(i + 1);
             stage(tn, b ^ 1);
-            fetch_rows(tn, rowval);
+            if (tid < 128) fetch_rows(tn, rowval);
         }
         // exponent offset of this lane's key column: 0 for keys, the landmark bias for a
         // tile mean that query tile i did not select, -inf (P = 0) otherwise
@@ -468,46 +475,38 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dkv(BwdDev p) {
         const unsigned char* qt = s_q[b];
         const unsigned char* dt = s_do[b];
         if (wk) {
-            // S = Q K^T and dP = dO V^T, lane = key column, rows = queries
-            f32x16 s0 = {}, s1 = {}, p0 = {}, p1 = {};
+            // S = Q K^T and dP = dO V^T over this wave's 32 query rows (lane = key column)
+            f32x16 sq = {}, pq = {};
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
-                bf16x8 a0, a1, o0, o1;
-                read_rows(qt, off, st, a0, a1);
-                read_rows(dt, off, st, o0, o1);
-                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, kop[st], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, kop[st], s1, 0, 0, 0);
-                p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o0, vop[st], p0, 0, 0, 0);
-                p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o1, vop[st], p1, 0, 0, 0);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qt + off.row[st] + 4096 * qh));
+                const bf16x8 o = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(dt + off.row[st] + 4096 * qh));
+                sq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kop[st], sq, 0, 0, 0);
+                pq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, vop[st], pq, 0, 0, 0);
             }
-            // P and dS per query row (8 (r/4) + 4 g + r % 4, +32)
-            f32x16 pp0, pp1, d0, d1;
+            // P (in sq) and dS (in pq) per query row 32 qh + 8 (r/4) + 4 g + r % 4
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                const int q4 = 8 * a + 4 * g;
+                const int q4 = 32 * qh + 8 * a + 4 * g;
                 const float4 la = *reinterpret_cast<const float4*>(&s_lse[b][q4]);
-                const float4 lb = *reinterpret_cast<const float4*>(&s_lse[b][q4 + 32]);
                 const float4 da = *reinterpret_cast<const float4*>(&s_d[b][q4]);
-                const float4 db = *reinterpret_cast<const float4*>(&s_d[b][q4 + 32]);
-                const float lav[4] = {la.x, la.y, la.z, la.w}, lbv[4] = {lb.x, lb.y, lb.z, lb.w};
-                const float dav[4] = {da.x, da.y, da.z, da.w}, dbv[4] = {db.x, db.y, db.z, db.w};
+                const float lav[4] = {la.x, la.y, la.z, la.w}, dav[4] = {da.x, da.y, da.z, da.w};
 #pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4) {
                     const int r = 4 * a + i4;
-                    pp0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], p.scale_l2, nb - lav[i4]));
-                    pp1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], p.scale_l2, nb - lbv[i4]));
-                    d0[r] = pp0[r] * (p0[r] - dav[i4]);
-                    d1[r] = pp1[r] * (p1[r] - dbv[i4]);
+                    sq[r] = __builtin_amdgcn_exp2f(fmaf(sq[r], p.scale_l2, nb - lav[i4]));
+                    pq[r] = sq[r] * (pq[r] - dav[i4]);
                 }
             }
-            // dV^T += dO^T P and dK^T += Q^T dS (k = queries)
+            // dV^T += dO^T P and dK^T += Q^T dS over the wave's queries (k-steps 2 qh, 2 qh + 1)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int kk = 0; kk < 2; ++kk) {
+                const int ks = 2 * qh + kk;
                 bf16x8 a0, a1, c0, c1;
                 read_tr(dt, off, ks, a0, a1);
                 read_tr(qt, off, ks, c0, c1);
-                const bf16x8 bp = acc_to_b(pp0, pp1, ks, [](float x, int, int) { return x; });
-                const bf16x8 bd = acc_to_b(d0, d1, ks, [](float x, int, int) { return x; });
+                const bf16x8 bp = acc_to_b(sq, sq, kk, [](float x, int, int) { return x; });
+                const bf16x8 bd = acc_to_b(pq, pq, kk, [](float x, int, int) { return x; });
                 dv0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bp, dv0, 0, 0, 0);
                 dv1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bp, dv1, 0, 0, 0);
                 dk0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c0, bd, dk0, 0, 0, 0);
@@ -515,8 +514,31 @@ __global__ __launch_bounds__(128, 2) void k_attn_bwd_dkv(BwdDev p) {
             }
         }
         __builtin_amdgcn_s_waitcnt(0x0070);
-        if (i + 1 < nq) (tid < 64 ? s_lse[b ^ 1] : s_d[b ^ 1])[tid & 63] = rowval;
+        if (i + 1 < nq && tid < 128) (tid < 64 ? s_lse[b ^ 1] : s_d[b ^ 1])[tid & 63] = rowval;
         __syncthreads();
+    }
+    // the second query half hands its partial sums to the first through the staging buffers
+    // (the loop's last barrier is behind every read of them), which adds them in this order
+    {
+        float* red = reinterpret_cast<float*>(wk_half ? &s_do[0][0] : &s_q[0][0]);   // 16 KiB per key half
+        if (qh == 1) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                red[(0 * 16 + r) * 64 + lane] = dk0[r];
+                red[(1 * 16 + r) * 64 + lane] = dk1[r];
+                red[(2 * 16 + r) * 64 + lane] = dv0[r];
+                red[(3 * 16 + r) * 64 + lane] = dv1[r];
+            }
+        }
+        __syncthreads();
+        if (qh == 1) return;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            dk0[r] += red[(0 * 16 + r) * 64 + lane];
+            dk1[r] += red[(1 * 16 + r) * 64 + lane];
+            dv0[r] += red[(2 * 16 + r) * 64 + lane];
+            dv1[r] += red[(3 * 16 + r) * 64 + lane];
+        }
     }
     float* dk_out = MEANS ? p.dkbar : p.dk;
     float* dv_out = MEANS ? p.dvbar : p.dv;
@@ -759,11 +781,11 @@ hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     // the means' gradients first: the dK/dV kernel adds them to the member rows
     if (lm) {
-        hipLaunchKernelGGL(k_attn_bwd_dkv<true>, dim3((unsigned)(a.heads * d.nlm)), dim3(128), 0, st, d);
+        hipLaunchKernelGGL(k_attn_bwd_dkv<true>, dim3((unsigned)(a.heads * d.nlm)), dim3(256), 0, st, d);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_attn_bwd_dkv<false>, dim3((unsigned)(a.heads * (d.Ts + d.Tk))), dim3(128), 0, st, d);
+    hipLaunchKernelGGL(k_attn_bwd_dkv<false>, dim3((unsigned)(a.heads * (d.Ts + d.Tk))), dim3(256), 0, st, d);
     return hipGetLastError();
 }
 
