@@ -1,6 +1,8 @@
 // Per-row top-k tile selection united with the anchor frame (SAF3R abstract: keep
 // only the most promising interactions for this input; Zebra3D abstract: tile-sparse
-// attention).  One workgroup per (head, query tile) row of the score matrix.
+// attention), for every (head, query tile) row of the score matrix.  Rows of at most
+// 6144 tiles take one wave each (k_select_topk_wave, below); longer rows one workgroup
+// each (k_select_topk), described here.
 //
 // Scores become order-preserving unsigned keys (-0 folded into +0, so equal values
 // give equal keys).  The k-th largest key T is found by a radix select whose digit
