@@ -325,6 +325,11 @@ def counters_markdown(c) -> str:
                      if k.get("frac_peak_at_clock") else "")
                   + (f"; HBM traffic {(k['fetch_bytes'] + k['write_bytes']) / 1e9:.2f} GB per launch."
                      if "fetch_bytes" in k else ".")]
+            ev = c["run"].get("events_ms", {}).get("attention")
+            if ev:
+                L += ["", f"The traced run's own bench line (events on the kernel's stream over its timed "
+                          f"steps) measured the attention launch at {ev:.3f} ms, against the trace's "
+                          f"{k['avg_ms']:.3f} ms mean."]
     L += ["", "Per layer (dispatches per layer x mean duration): " +
           ", ".join(f"{fam} {ms:.4f} ms" for fam, ms in c["layer_ms_by_family"].items()), ""]
     return "\n".join(L)
@@ -702,7 +707,11 @@ def bench_workload(args, w, torch, S, LY, synth, dev, single: bool) -> dict:
                        "dtype": w.dtype, "heads": w.heads, "q_tiles": L.Tq,
                        "k_tiles": L.Tk, "top_k": L.k, "kmax": r["kmax"], "landmarks": w.landmarks,
                        "layers": args.steps + args.warmup, "attn_flops_per_launch": flops,
-                       "alg_per_dispatch": alg, "dispatches_per_layer": per_layer}, f, indent=1)
+                       "alg_per_dispatch": alg, "dispatches_per_layer": per_layer,
+                       # the same run's own timing: events on the stream over the timed steps
+                       "events_ms": {"attention": round(r["attn_ms"], 4),
+                                     "score_call": round(r["scores_ms"], 4),
+                                     "select": round(r["select_ms"], 4)}}, f, indent=1)
     # roofline of the dominant kernel (sparse attention): algorithmic FLOPs per launch
     # over its mean launch time, measured with events on its stream during the timed steps
     c = counters_entry(w.name)
