@@ -110,7 +110,9 @@ def profile_commands(workload: str, outdir: str) -> list:
 def kernel_family(name: str):
     """Which step of the layer a kernel name belongs to (None: not a layer kernel)."""
     if "elementwise" in name:
-        return "copy"
+        # the copy reference is torch's add (src + 0 into dst); other elementwise kernels
+        # (the fill of the stream references) are not layer kernels
+        return "copy" if "_add" in name else None
     if "s3d::" not in name:
         return None
     if "k_tile_pool" in name:
@@ -633,6 +635,26 @@ def alg_per_dispatch(w, L, kmax: int, attn_flops: int) -> dict:
     return out
 
 
+def stream_refs(torch, dev, nbytes: int, reps: int = 10) -> dict:
+    """What a library store kernel reaches on a buffer the size of the score matrix: torch's
+    fill (stores only, in address order, the score kernel's kind of traffic), mean GB/s over
+    `reps` launches timed with events on the current stream.  The score kernel is quoted
+    against this rate as well as against the published 8 TB/s."""
+    buf = torch.empty(nbytes // 4, device=dev, dtype=torch.float32)
+    out = {"bytes": int(buf.numel() * 4)}
+    for _ in range(2):
+        buf.fill_(1.0)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        buf.fill_(1.0)
+    b.record()
+    torch.cuda.synchronize()
+    out["fill_gbs"] = round(out["bytes"] / (a.elapsed_time(b) / reps * 1e-3) / 1e9, 1)
+    del buf
+    return out
+
+
 def spin_up(torch, dev, seconds: float = 0.3):
     """Bring the GPU out of its idle clocks before the warmup steps: a few hundred
     milliseconds of dense matrix work (seconds of host-only work, such as input generation
@@ -697,6 +719,7 @@ def bench_workload(args, w, torch, S, LY, synth, dev, single: bool) -> dict:
         "tile_scores": round(ps_bytes / (r["scores_ms"] * 1e-3) / 1e9, 1),
         "select_topk": round(alg["select"] / (r["select_ms"] * 1e-3) / 1e9, 1)}
     res["kernels_frac_hbm"] = {n: round(g / PEAK_HBM_GBS, 4) for n, g in res["kernels_gbs"].items()}
+    res["stream_refs"] = stream_refs(torch, dev, w.heads * L.Tq * L.Tk * 4)
     if args.run_info:
         per_layer = {"pool_query": 1, "pool_key": 2 if w.landmarks else 1, "score": 1, "select": 1,
                      "attention": 1}

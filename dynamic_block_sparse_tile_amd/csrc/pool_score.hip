@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void k_tile_pool(const void* __restrict__ x, i
 // which have had the products' time to drain.
 constexpr int SC_Q = 128;               // query tiles per workgroup (4 waves x 32)
 constexpr int SC_K = 64;                // key tiles per block
-constexpr int SC_STG = 36;              // staged score row stride (floats): conflict-free b128 writes
+constexpr int SC_RESIDENT = 3 * 256;     // workgroups resident at once on the 256 compute units
 // Score stores carry the non-temporal hint: the matrix is read once, by the selection, and
 // streaming it past the caches measured 0.116 against 0.132 ms at 2816 x 2816 tiles x 16 heads.
 constexpr int SC_NT = 2;
@@ -124,6 +124,10 @@ __device__ __forceinline__ void split_bf16x8(const float* x, bf16x8& hi, bf16x8&
 // byte offset of dims 8c .. 8c + 7 of key row r in a [64 keys][64 dims] bf16 block: 16-byte
 // chunks XOR-swizzled so that 16 lanes reading 16 consecutive keys hit 16 distinct bank groups
 __device__ __forceinline__ int sc_koff(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+// byte offset of keys 4c .. 4c + 3 of query row r in a wave's [32 rows][32 keys] fp32 staging
+// block, with the same swizzle: the accumulator writes (16 rows, one chunk each) and the row
+// reads (two rows, eight chunks each) both touch 16 distinct bank groups per 16 lanes
+__device__ __forceinline__ int sc_soff(int r, int c) { return sc_koff(r, c); }
 
 __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restrict__ qbar,
                                                           const float* __restrict__ kbar, int Tq, int Tk,
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restric
                                                           float* __restrict__ scores) {
     __shared__ __align__(16) unsigned char s_kh[2][SC_K * 128];   // key means, bf16 hi terms
     __shared__ __align__(16) unsigned char s_kl[2][SC_K * 128];   // and lo terms
-    __shared__ __align__(16) float s_stage[4][32 * SC_STG];       // per wave: 32 rows x 32 keys
+    __shared__ __align__(16) unsigned char s_stage[4][32 * 128];  // per wave: 32 rows x 32 keys
     __shared__ uint64_t s_kempty[2];                              // key tiles without members
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -202,7 +206,7 @@ __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restric
     const long long rows_here = (long long)Tq - r0 < 0 ? 0 : ((long long)Tq - r0 < 32 ? (long long)Tq - r0 : 32);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         scores + ((size_t)h * Tq + (size_t)(r0 < Tq ? r0 : 0)) * (size_t)Tk, 0, (int)(rows_here * Tk * 4), 0x00020000);
-    float* stg = s_stage[w];
+    unsigned char* stg = s_stage[w];
 
     if (nkb > 0) {
         load_block(0);
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restric
             if (!any_empty) {                        // the common case: no empty tile in sight
 #pragma unroll
                 for (int a = 0; a < 4; ++a)
-                    *reinterpret_cast<float4*>(stg + col * SC_STG + 8 * a + 4 * g) =
+                    *reinterpret_cast<float4*>(stg + sc_soff(col, 2 * a + g)) =
                         make_float4(acc[4 * a] * scale, acc[4 * a + 1] * scale, acc[4 * a + 2] * scale,
                                     acc[4 * a + 3] * scale);
             } else {
@@ -261,7 +265,7 @@ __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restric
                         v[j] = acc[4 * a + j] * scale;
                         if (qempty || ((kw >> (8 * a + j)) & 1u)) v[j] = -INFINITY;
                     }
-                    *reinterpret_cast<float4*>(stg + col * SC_STG + 8 * a + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
+                    *reinterpret_cast<float4*>(stg + sc_soff(col, 2 * a + g)) = make_float4(v[0], v[1], v[2], v[3]);
                 }
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -271,22 +275,25 @@ __global__ __launch_bounds__(256) void k_tile_scores_mfma(const float* __restric
             const int ch = lane & 7;
             const int cbase = kb0 + s * SC_K + 32 * cb + 4 * ch;
             const bool whole = kb0 + s * SC_K + 32 * cb + 32 <= Tk;   // no ragged column in this half
+            typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+            u32x4 v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                v[q] = *reinterpret_cast<const u32x4*>(stg + sc_soff(8 * q + (lane >> 3), ch));
+            // the four 16-byte reads all issue before the first store: left to itself the
+            // compiler splits each around the ragged-column branch into 12- and 4-byte reads,
+            // which conflict on the LDS banks and are each waited for alone
+            asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int row = 8 * q + (lane >> 3);
-                const float4 v = *reinterpret_cast<const float4*>(stg + row * SC_STG + 4 * ch);
                 const unsigned voff = ((unsigned)row * (unsigned)Tk + (unsigned)cbase) * 4u;
                 if (whole || cbase + 3 < Tk) {
-                    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-                    const u32x4 pk = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
-                                      __float_as_uint(v.w)};
-                    __builtin_amdgcn_raw_buffer_store_b128(pk, rs, (int)voff, 0, SC_NT);
+                    __builtin_amdgcn_raw_buffer_store_b128(v[q], rs, (int)voff, 0, SC_NT);
                 } else {
-                    const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                     for (int j = 0; j < 4; ++j)         // a ragged last key block
-                        if (cbase + j < Tk)
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(vv[j]), rs, (int)voff, 4 * j, SC_NT);
+                        if (cbase + j < Tk) __builtin_amdgcn_raw_buffer_store_b32(v[q][j], rs, (int)voff, 4 * j, SC_NT);
                 }
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -314,10 +321,13 @@ hipError_t launch_tile_scores(const float* qbar, const float* kbar, int heads, L
                               float scale, float* scores, hipStream_t st) {
     const int Tq = ql.S * ql.P / TILE, Tk = kl.S * kl.P / TILE;
     const Lay lq{ql.S, ql.N, ql.P, ql.nsp}, lk{kl.S, kl.N, kl.P, kl.nsp};
-    // split each head's key blocks into ranges so that the grid holds about 2048 workgroups
+    // split each head's key blocks into as many ranges as one round of resident workgroups
+    // holds (three per compute unit, bound by LDS): every workgroup then starts at once and
+    // none waits for a second round (at 5632 x 5632 tiles x 16 heads one range per query
+    // block, 0.41-0.42 ms, against 0.42-0.44 ms with about 2048 workgroups)
     const int qblocks = (Tq + SC_Q - 1) / SC_Q, kblocks_all = (Tk + SC_K - 1) / SC_K;
     const long long per = (long long)qblocks * heads;
-    const int nsplit = (int)std::max(1LL, std::min<long long>(kblocks_all, (2048 + per - 1) / per));
+    const int nsplit = (int)std::max(1LL, std::min<long long>(kblocks_all, SC_RESIDENT / per));
     const int kblocks = (kblocks_all + nsplit - 1) / nsplit;
     const dim3 grid((unsigned)((kblocks_all + kblocks - 1) / kblocks), (unsigned)qblocks, (unsigned)heads);
     hipLaunchKernelGGL(k_tile_scores_mfma, grid, dim3(256), 0, st, qbar, kbar, Tq, Tk, lq, lk, scale, kblocks,

@@ -98,6 +98,8 @@ def test_kernel_family():
     assert bench.kernel_family("void s3d::k_attn_bwd_dkv<true>(s3d::BwdDev)") is None
     assert bench.kernel_family("void s3d::k_cast_bf16(float const*, long, __bf16*)") == "cast"
     assert bench.kernel_family(COPY) == "copy"
+    assert bench.kernel_family("void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float>, "
+                               "std::array<char*, 1ul> >(int, at::native::FillFunctor<float>, std::array<char*, 1ul>)") is None
     assert bench.kernel_family("void other::kernel()") is None
 
 
