@@ -90,6 +90,10 @@ COUNTER_PASSES = [
     ("write", "--pmc WRITE_SIZE"),
     ("sq", "--pmc SQ_WAVE_CYCLES SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_BUSY_CYCLES "
            "SQ_INSTS_VALU SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE"),
+    # where the waves spend their cycles: waiting on counters (memory, LDS, barriers), waiting
+    # for an instruction to issue, matrix/vector overlap, LDS bank conflicts
+    ("wait", "--pmc SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
+             "SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT"),
 ]
 PROFILE_COPY_MB = 1024
 
@@ -180,6 +184,9 @@ def write_counters(outdir: str):
     fetch, _ = counters("fetch")
     write, _ = counters("write")
     sq, span = counters("sq")
+    # the wait pass is optional (profiles taken before it existed have four passes)
+    wait = counters("wait")[0] if glob.glob(os.path.join(outdir, "wait", "**", "*counter_collection.csv"),
+                                          recursive=True) else {}
 
     def mean_of(per, name, counter):
         v = per.get((name, counter))
@@ -239,6 +246,20 @@ def write_counters(outdir: str):
                 k["valu_share_of_issue"] = round(valu / anyi, 4)
             if anyi and wavec:
                 k["issue_share_of_wave_cycles"] = round(anyi / wavec, 4)
+        if wait and sec >= 1e-4:
+            w = {c: mean_of(wait, name, c) for c in ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+                                                      "SQ_ACTIVE_INST_ANY", "SQ_VALU_MFMA_BUSY_CYCLES",
+                                                      "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_LDS_IDX_ACTIVE",
+                                                      "SQ_LDS_BANK_CONFLICT")}
+            if w["SQ_WAVE_CYCLES"]:
+                for key, c in (("wait_counter_share", "SQ_WAIT_ANY"), ("wait_issue_share", "SQ_WAIT_INST_ANY"),
+                               ("issue_share", "SQ_ACTIVE_INST_ANY")):
+                    if w[c] is not None:
+                        k[key] = round(w[c] / w["SQ_WAVE_CYCLES"], 4)
+            if w["SQ_VALU_MFMA_BUSY_CYCLES"] and w["SQ_VALU_MFMA_COEXEC_CYCLES"] is not None:
+                k["coexec_share_of_mfma_busy"] = round(w["SQ_VALU_MFMA_COEXEC_CYCLES"] / w["SQ_VALU_MFMA_BUSY_CYCLES"], 4)
+            if w["SQ_LDS_IDX_ACTIVE"] and w["SQ_LDS_BANK_CONFLICT"] is not None:
+                k["lds_conflict_share"] = round(w["SQ_LDS_BANK_CONFLICT"] / w["SQ_LDS_IDX_ACTIVE"], 4)
         if fam == "attention":
             flops = info["attn_flops_per_launch"]
             peak = PEAK_TFLOPS[info["dtype"]]
@@ -319,6 +340,19 @@ def counters_markdown(c) -> str:
                  f"{f(k.get('alg_gbs'), '{:.0f}')} | {f(k.get('alg_frac_hbm'), '{:.1%}')} | "
                  f"{f(k.get('clock_ghz'), '{:.2f}')} | {f(k.get('mfma_busy'), '{:.1%}')} | "
                  f"{f(k.get('valu_share_of_issue'), '{:.1%}')} |")
+    if any("wait_counter_share" in k for k in c["kernels"]):
+        L += ["", "Where the waves of each kernel (dispatches of at least 0.1 ms) spend their cycles, from the "
+              "wait pass: shares of SQ_WAVE_CYCLES spent in s_waitcnt or a barrier (SQ_WAIT_ANY), waiting for "
+              "an instruction to issue (SQ_WAIT_INST_ANY) and issuing (SQ_ACTIVE_INST_ANY); the share of "
+              "matrix-core busy cycles with vector work issued alongside (SQ_VALU_MFMA_COEXEC_CYCLES over "
+              "SQ_VALU_MFMA_BUSY_CYCLES); LDS bank-conflict cycles over LDS-active cycles.", "",
+              "| kernel | step | waiting on counters | waiting to issue | issuing | vector under matrix | LDS conflicts |",
+              "|---|---|---|---|---|---|---|"]
+        for k in c["kernels"]:
+            if "wait_counter_share" in k:
+                L.append(f"| `{k['name'][:70]}` | {k['family']} | {f(k.get('wait_counter_share'), '{:.1%}')} | "
+                         f"{f(k.get('wait_issue_share'), '{:.1%}')} | {f(k.get('issue_share'), '{:.1%}')} | "
+                         f"{f(k.get('coexec_share_of_mfma_busy'), '{:.1%}')} | {f(k.get('lds_conflict_share'), '{:.1%}')} |")
     for k in c["kernels"]:
         if k["family"] == "attention":
             L += ["", f"Attention `{k['name'][:70]}`: {k['flops']:.4g} FLOP per launch in {k['avg_ms']:.3f} ms = "

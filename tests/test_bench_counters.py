@@ -54,6 +54,16 @@ def test_counter_reader(tmp_path, monkeypatch):
                          [7, ATTN, "SQ_ACTIVE_INST_ANY", 100.0, 0, 10_000_000],
                          [7, ATTN, "SQ_ACTIVE_INST_VALU", 55.0, 0, 10_000_000],
                          [7, ATTN, "SQ_WAVE_CYCLES", 400.0, 0, 10_000_000]])
+    # the wait pass: 30 % of wave cycles in s_waitcnt, 20 % waiting to issue, 40 % of the matrix
+    # core's busy cycles with vector work alongside, a quarter of LDS cycles in bank conflicts
+    _pmc(str(d / "wait"), [[7, ATTN, "SQ_WAVE_CYCLES", 1000.0, 0, 10_000_000],
+                           [7, ATTN, "SQ_WAIT_ANY", 300.0, 0, 10_000_000],
+                           [7, ATTN, "SQ_WAIT_INST_ANY", 200.0, 0, 10_000_000],
+                           [7, ATTN, "SQ_ACTIVE_INST_ANY", 250.0, 0, 10_000_000],
+                           [7, ATTN, "SQ_VALU_MFMA_BUSY_CYCLES", 500.0, 0, 10_000_000],
+                           [7, ATTN, "SQ_VALU_MFMA_COEXEC_CYCLES", 200.0, 0, 10_000_000],
+                           [7, ATTN, "SQ_LDS_IDX_ACTIVE", 80.0, 0, 10_000_000],
+                           [7, ATTN, "SQ_LDS_BANK_CONFLICT", 20.0, 0, 10_000_000]])
     info = {"workload": "fake", "kernel_source_sha256": "abc", "dtype": "bf16", "heads": 2, "q_tiles": 4, "k_tiles": 4, "top_k": 1,
             "kmax": 2, "landmarks": False, "layers": 3, "attn_flops_per_launch": 8e12,
             "alg_per_dispatch": {"pool_query": 4e8, "pool_key": 4e8, "score": 1e9, "select": 1e9,
@@ -73,6 +83,9 @@ def test_counter_reader(tmp_path, monkeypatch):
     assert a["clock_ghz"] == pytest.approx(2.0) and a["mfma_busy"] == pytest.approx(0.4)
     assert a["frac_peak_at_clock"] == pytest.approx(800.0 / (2500.0 * 2.0 / 2.4), rel=1e-3)
     assert a["valu_share_of_issue"] == pytest.approx(0.55)
+    assert a["wait_counter_share"] == pytest.approx(0.3) and a["wait_issue_share"] == pytest.approx(0.2)
+    assert a["issue_share"] == pytest.approx(0.25) and a["coexec_share_of_mfma_busy"] == pytest.approx(0.4)
+    assert a["lds_conflict_share"] == pytest.approx(0.25)
     assert a["issue_share_of_wave_cycles"] == pytest.approx(0.25)
     s = k["select"]
     assert s["alg_gbs"] == pytest.approx(1e9 / 2e-4 / 1e9) and s["alg_frac_hbm"] == pytest.approx(0.625)
@@ -81,6 +94,7 @@ def test_counter_reader(tmp_path, monkeypatch):
     assert c["layer_ms_by_family"] == {"pool_query": 0.1, "pool_key": 0.1, "select": 0.2, "attention": 10.0}
     md = open(tmp_path / "profiles" / "counters_fake.md").read()
     assert "rocprofv3 --pmc FETCH_SIZE" in md and "| attention |" in md
+    assert "| 30.0% | 20.0% | 25.0% | 40.0% | 25.0% |" in md
     assert c["kernel_source_sha256"] == "abc"                  # the run's, not the current sources'
     tr = open(tmp_path / "profiles" / "trace_fake.md").read()
     assert "--kernel-trace --stats" in tr and "k_attn_bf16" in tr
