@@ -45,6 +45,16 @@ __device__ __forceinline__ float keep_lanes(float x, uint64_t lanes) {
     return r;
 }
 
+// Global row (within the head) of special token e, numbering every frame's special tokens
+// in frame order: frame e / nsp, in-frame position e % nsp.  The quotient is one fp32 FMA
+// and a truncation, exact while e < 2^21: (e + 1/2) / nsp lies at least 1 / (2 nsp) from
+// an integer, and the rounded product is within a relative 2^-23 of it.  (An integer
+// division by the runtime nsp costs about 26 vector instructions per row.)
+__device__ __forceinline__ unsigned spec_src_row(unsigned e, unsigned nsp, float inv_nsp, unsigned P) {
+    const unsigned f = (unsigned)fmaf((float)e, inv_nsp, 0.5f * inv_nsp);
+    return f * P + (e - f * nsp);
+}
+
 // all ones if bit b of w is set, else zero
 __device__ __forceinline__ uint32_t bit_to_word(uint32_t w, int b) {
     return (uint32_t)((int32_t)(w << (31 - b)) >> 31);
@@ -197,11 +207,22 @@ __global__ __launch_bounds__(128 * QT, 3) void k_attn_bf16(AttnDev p) {
         soff[j] = srow[j] * 128 + swz(srow[j], sslot) * 16;
     }
     auto desc = [&](int it) { return describe<DENSE, LM, !DENSE>(p, it, c, myidx, s_idx, s_lm, rot, t0); };
+    // special rows by the fp32 quotient while every special row number is below 2^21
+    const bool spec_fast = 64 * p.Ts <= (1 << 21);
+    const float inv_nsp = 1.0f / (float)p.kl.nsp;
     auto plan = [&](const TileDesc& dd, unsigned (&voff)[NJ], unsigned& base) {
         const TileDesc d = uniform(dd);
         const bool spec = d.kind == KIND_SPEC;
         base = spec ? 0u : (unsigned)d.t * TILE_BYTES;
-        if (spec) {
+        if (spec && spec_fast) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int r = srow[j];
+                const unsigned srcr = spec_src_row((unsigned)(d.t * TILE + r), (unsigned)p.kl.nsp, inv_nsp, (unsigned)p.kl.P);
+                const unsigned o = srcr * 128u + swz(r, sslot) * 16u;
+                voff[j] = ((d.mask >> r) & 1ull) ? o : OOB_OFFSET;
+            }
+        } else if (spec) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const int r = srow[j];
@@ -271,15 +292,21 @@ __global__ __launch_bounds__(128 * QT, 3) void k_attn_bf16(AttnDev p) {
                 __builtin_amdgcn_sched_barrier(0);
                 asm volatile("s_nop 7\n\ts_nop 7");
                 const uint32_t mlo = (uint32_t)cur.mask, mhi = (uint32_t)(cur.mask >> 32);
+                // Only a half holding both keys and non-keys needs the masks: a full half has
+                // none to mask, and the sparse paths skip a half without keys before reading
+                // its scores (the dense paths take the max over both halves, so there a half
+                // without keys is masked too).
+                auto mask_half = [&](f32x16& sc, uint32_t mh) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int cr = 8 * (r >> 2) + (r & 3);
-                    // each 32-bit half of a lane mask is one row bit sign-extended (s_bfe_i32)
-                    const uint64_t k0 = (uint64_t)bit_to_word(mlo, cr) | ((uint64_t)bit_to_word(mlo, cr + 4) << 32);
-                    const uint64_t k1 = (uint64_t)bit_to_word(mhi, cr) | ((uint64_t)bit_to_word(mhi, cr + 4) << 32);
-                    s0[r] = keep_lanes(s0[r], k0);
-                    s1[r] = keep_lanes(s1[r], k1);
-                }
+                    for (int r = 0; r < 16; ++r) {
+                        const int cr = 8 * (r >> 2) + (r & 3);
+                        // each 32-bit half of a lane mask is one row bit sign-extended (s_bfe_i32)
+                        const uint64_t km = (uint64_t)bit_to_word(mh, cr) | ((uint64_t)bit_to_word(mh, cr + 4) << 32);
+                        sc[r] = keep_lanes(sc[r], km);
+                    }
+                };
+                if (mlo != ~0u && (DENSE || mlo != 0u)) mask_half(s0, mlo);
+                if (mhi != ~0u && (DENSE || mhi != 0u)) mask_half(s1, mhi);
             }
             if constexpr (DENSE) {
                 // every workgroup sweeps the keys in the same order, so the probabilities are

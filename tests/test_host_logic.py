@@ -67,3 +67,18 @@ def test_valid_pair_flops_brute_force():
                         keys += nsp <= kpos < N                # patch tokens of the tile only
                 total += keys
     assert LY.valid_pair_flops(idx, cnt, lay, lay) == total * 4 * 64
+
+
+def test_special_row_quotient_by_fp32_multiply():
+    # The bf16 attention kernel finds the frame of special token e (e // nsp) as
+    # trunc(fma(e, fl(1/nsp), fl(1/nsp) / 2)) in fp32 for every e < 2^21.  Replayed here
+    # exactly: e * inv + inv / 2 is exact in fp64 (at most 46 significant bits), and one
+    # rounding to fp32 is the fma's.  Every e below 2^21, for special counts 1..130 and a
+    # few larger ones.
+    e = np.arange(1 << 21, dtype=np.float64)
+    ei = np.arange(1 << 21, dtype=np.int64)
+    for nsp in list(range(1, 131)) + [255, 256, 257, 1000, 4095]:
+        inv = np.float32(1.0) / np.float32(nsp)
+        f = (e * np.float64(inv) + np.float64(inv) * 0.5).astype(np.float32)
+        q = np.trunc(f.astype(np.float64)).astype(np.int64)
+        assert np.array_equal(q, ei // nsp), nsp
