@@ -46,12 +46,13 @@ __device__ __forceinline__ float keep_lanes(float x, uint64_t lanes) {
 }
 
 // Global row (within the head) of special token e, numbering every frame's special tokens
-// in frame order: frame e / nsp, in-frame position e % nsp.  The quotient is one fp32 FMA
-// and a truncation, exact while e < 2^21: (e + 1/2) / nsp lies at least 1 / (2 nsp) from
-// an integer, and the rounded product is within a relative 2^-23 of it.  (An integer
-// division by the runtime nsp costs about 26 vector instructions per row.)
-__device__ __forceinline__ unsigned spec_src_row(unsigned e, unsigned nsp, float inv_nsp, unsigned P) {
-    const unsigned f = (unsigned)fmaf((float)e, inv_nsp, 0.5f * inv_nsp);
+// in frame order: frame e / nsp, in-frame position e % nsp.  The quotient is one fp64 FMA
+// and a truncation, trunc((e + 1/2) * fl(1/nsp)): (e + 1/2) / nsp lies at least 1 / (2 nsp)
+// from an integer, and the computed product is within a relative 2^-51 of it, far inside
+// that margin for every 32-bit e.  (An integer division by the runtime nsp costs about 26
+// vector instructions per row.)
+__device__ __forceinline__ unsigned spec_src_row(unsigned e, unsigned nsp, double inv_nsp, unsigned P) {
+    const unsigned f = (unsigned)fma((double)e, inv_nsp, 0.5 * inv_nsp);
     return f * P + (e - f * nsp);
 }
 
@@ -207,26 +208,25 @@ __global__ __launch_bounds__(128 * QT, 3) void k_attn_bf16(AttnDev p) {
         soff[j] = srow[j] * 128 + swz(srow[j], sslot) * 16;
     }
     auto desc = [&](int it) { return describe<DENSE, LM, !DENSE>(p, it, c, myidx, s_idx, s_lm, rot, t0); };
-    // special rows by the fp32 quotient while every special row number is below 2^21
-    const bool spec_fast = 64 * p.Ts <= (1 << 21);
-    const float inv_nsp = 1.0f / (float)p.kl.nsp;
+    // 1 / nsp for the special rows' quotient, uniform, so kept in scalar registers
+    double inv_nsp;
+    {
+        const double x = 1.0 / (double)p.kl.nsp;
+        const uint64_t u = __builtin_bit_cast(uint64_t, x);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+        inv_nsp = __builtin_bit_cast(double, (uint64_t)lo | ((uint64_t)hi << 32));
+    }
     auto plan = [&](const TileDesc& dd, unsigned (&voff)[NJ], unsigned& base) {
         const TileDesc d = uniform(dd);
         const bool spec = d.kind == KIND_SPEC;
         base = spec ? 0u : (unsigned)d.t * TILE_BYTES;
-        if (spec && spec_fast) {
+        if (spec) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const int r = srow[j];
                 const unsigned srcr = spec_src_row((unsigned)(d.t * TILE + r), (unsigned)p.kl.nsp, inv_nsp, (unsigned)p.kl.P);
                 const unsigned o = srcr * 128u + swz(r, sslot) * 16u;
-                voff[j] = ((d.mask >> r) & 1ull) ? o : OOB_OFFSET;
-            }
-        } else if (spec) {
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int r = srow[j];
-                const unsigned o = (unsigned)src_row(p, d, r) * 128u + swz(r, sslot) * 16u;
                 voff[j] = ((d.mask >> r) & 1ull) ? o : OOB_OFFSET;
             }
         } else if (d.mask == ~0ull) {

@@ -69,16 +69,21 @@ def test_valid_pair_flops_brute_force():
     assert LY.valid_pair_flops(idx, cnt, lay, lay) == total * 4 * 64
 
 
-def test_special_row_quotient_by_fp32_multiply():
+def test_special_row_quotient_by_fp64_fma():
     # The bf16 attention kernel finds the frame of special token e (e // nsp) as
-    # trunc(fma(e, fl(1/nsp), fl(1/nsp) / 2)) in fp32 for every e < 2^21.  Replayed here
-    # exactly: e * inv + inv / 2 is exact in fp64 (at most 46 significant bits), and one
-    # rounding to fp32 is the fma's.  Every e below 2^21, for special counts 1..130 and a
-    # few larger ones.
-    e = np.arange(1 << 21, dtype=np.float64)
-    ei = np.arange(1 << 21, dtype=np.int64)
-    for nsp in list(range(1, 131)) + [255, 256, 257, 1000, 4095]:
-        inv = np.float32(1.0) / np.float32(nsp)
-        f = (e * np.float64(inv) + np.float64(inv) * 0.5).astype(np.float32)
-        q = np.trunc(f.astype(np.float64)).astype(np.int64)
-        assert np.array_equal(q, ei // nsp), nsp
+    # trunc(fma(e, fl(1/nsp), fl(1/nsp) / 2)) in fp64.  The fma is replayed exactly (the exact
+    # rational e * inv + inv / 2, rounded once to the nearest double), on the e where a
+    # truncation would first go wrong, just below and at every multiple of nsp, up to 2^31.
+    from fractions import Fraction
+    rng = np.random.default_rng(3)
+    for nsp in [1, 2, 3, 5, 7, 64, 70, 127, 1000, 65535, 1 << 20, (1 << 30) + 7]:
+        inv = 1.0 / nsp
+        half = inv * 0.5
+        qs = np.unique(np.concatenate([np.arange(1, 200), rng.integers(1, max(2, (1 << 31) // nsp), 300),
+                                       [(1 << 31) // nsp - 1]]))
+        for q in qs:
+            for e in (int(q) * nsp - 1, int(q) * nsp):
+                if not 0 <= e < (1 << 31):
+                    continue
+                f = float(Fraction(e) * Fraction(inv) + Fraction(half))
+                assert int(f) == e // nsp, (nsp, e)
