@@ -135,6 +135,15 @@ def test_specials_span_tiles():
     run_full_case(_custom(2, 150, 192, 70, k=2), landmarks=True)
 
 
+@pytest.mark.parametrize("specials", [1, 3, 64, 65])
+def test_special_counts(specials):
+    # The special pseudo-tiles gather every frame's special tokens in frame order, and each
+    # staged row finds its frame as the quotient of its index by the special count: one
+    # per frame, a count that leaves pseudo-tile rows unfilled, a frame's worth that fills a
+    # pseudo-tile exactly, and one that spills into the next (5 frames: 1 to 6 pseudo-tiles)
+    run_full_case(_custom(5, specials + 100, 192, specials, k=2))
+
+
 def test_rising_logits_move_the_reference():
     # Every frame's tokens scaled by 2^frame (exact in bf16): scores grow by factors of up to
     # 2^(2*3) across frames, spanning ~100 base-2 units, so the sparse kernel's running
