@@ -99,6 +99,11 @@ constexpr float RESCALE_THRESHOLD = 8.0f;
 // Sparse attention: largest sum of one half tile's probabilities (16 per lane) taken
 // without moving the reference max.
 constexpr float PROB_SUM_LIMIT = 65536.0f;
+// Sparse attention: the reference of a row that has seen no key yet.  Finite and far below
+// any score, so the first probabilities against it overflow to +inf, the half's sum check
+// fails and the half forms its max: no separate test for rows without a reference.  (A
+// row that never sees a key ends with it and is treated as having no reference.)
+constexpr float M_NONE = -0x1p126f;
 
 
 // SGA: the subsample completion (own key of dropped positions, mean pair) is applied to
@@ -135,7 +140,10 @@ __global__ __launch_bounds__(128 * QT, 3) void k_attn_bf16(AttnDev p) {
     // last tile) still stages its half of every tile and meets every barrier, but skips the
     // products.  (Dense and frame attention keep every wave busy: there the workgroups sweep
     // the keys in lockstep and share them through L2, and one finishing early was slower.)
-    const bool wq = DENSE || __ballot(qvalid) != 0ull;
+    // (an int from readfirstlane: kept as a bool, the compiler re-derives it on the vector
+    // unit in every step)
+    int wq = DENSE ? 1 : __builtin_amdgcn_readfirstlane((int)(__ballot(qvalid) != 0ull));
+    asm volatile("" : "+s"(wq));
 
     bf16x8 qop[4];
     {
@@ -246,7 +254,10 @@ __global__ __launch_bounds__(128 * QT, 3) void k_attn_bf16(AttnDev p) {
     TileOffsets to;
     to.init(lane);
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float m = -INFINITY, l = 0.f;
+    // m: running reference (base 2) of the lane's row; negm = -m, kept beside it so that the
+    // sparse paths' probabilities need no per-step negation
+    float m = DENSE ? -INFINITY : M_NONE, l = 0.f;
+    float negm = -M_NONE;
     f32x16 o0 = {}, o1 = {};
 
     auto step = [&](int it, TileDesc& dcur, const unsigned char* vcur, unsigned char* vnext) {
@@ -282,8 +293,12 @@ __global__ __launch_bounds__(128 * QT, 3) void k_attn_bf16(AttnDev p) {
         __builtin_amdgcn_s_barrier();                       // every wave has read K(it)
         dma4(nlmk ? rs_lk : rs_k, (lds_u8*)s_k, vk, bk);    // K(it+1)
         __builtin_amdgcn_sched_barrier(0);
+        // the two 32-key halves of the row mask as scalars (left to itself the compiler folds a
+        // test of the upper half back into a 64-bit compare, which runs on the vector unit)
+        uint32_t mlo = (uint32_t)cur.mask, mhi = (uint32_t)(cur.mask >> 32);
+        asm volatile("" : "+s"(mlo), "+s"(mhi));
         if (wq) {
-            if (cur.mask != ~0ull) {
+            if ((mlo & mhi) != ~0u) {
                 // slot r of a lane in half-wave g holds key 8 (r / 4) + 4 g + r % 4 (+32 in s1): its
                 // lane mask takes one row bit for lanes 0-31 and another for lanes 32-63, formed
                 // on the scalar unit from the uniform row mask.  The scores come from the matrix
@@ -291,7 +306,6 @@ __global__ __launch_bounds__(128 * QT, 3) void k_attn_bf16(AttnDev p) {
                 // cycles keep them clear of the products' write-back
                 __builtin_amdgcn_sched_barrier(0);
                 asm volatile("s_nop 7\n\ts_nop 7");
-                const uint32_t mlo = (uint32_t)cur.mask, mhi = (uint32_t)(cur.mask >> 32);
                 // Only a half holding both keys and non-keys needs the masks: a full half has
                 // none to mask, and the sparse paths skip a half without keys before reading
                 // its scores (the dense paths take the max over both halves, so there a half
@@ -328,7 +342,7 @@ __global__ __launch_bounds__(128 * QT, 3) void k_attn_bf16(AttnDev p) {
                 const float off = -(m == -INFINITY ? 0.f : m);
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
-                    if ((uint32_t)(cur.mask >> (32 * (ks >> 1))) == 0u) continue;   // no key in this half
+                    if ((ks < 2 ? mlo : mhi) == 0u) continue;   // no key in this half
                     const f32x16& sp = (ks < 2) ? s0 : s1;
                     const int j0 = 2 * (ks & 1);
                     bf16x8 va0, va1;
@@ -352,15 +366,16 @@ __global__ __launch_bounds__(128 * QT, 3) void k_attn_bf16(AttnDev p) {
                 // Probabilities are taken against the running reference m without first forming
                 // the tile's row max.  Each half tile (32 keys) checks afterwards that its rounded
                 // probabilities sum to at most 2^16 (then none exceeds 2^16: nothing overflowed,
-                // and the accumulators keep ample range); only a half that fails, or any half while a
-                // row has no reference yet, forms the max of its scores, moves the reference
-                // (rescaling O and l) and recomputes.  Rounding is relative, so the reference only
-                // has to keep the probabilities in range, not equal the running max.
-                const bool fresh = __ballot(m == -INFINITY) != 0;
-                const float bias = (LM && cur.kind == KIND_LM) ? p.lm_bias_l2 : 0.f;   // landmark logit bias
+                // and the accumulators keep ample range); only a half that fails (as every half
+                // does while a row has no reference yet, see M_NONE) forms the max of its scores,
+                // moves the reference (rescaling O and l) and recomputes.  Rounding is relative, so
+                // the reference only has to keep the probabilities in range, not equal the running
+                // max.
+                const bool lmk = LM && cur.kind == KIND_LM;
+                const float bias = lmk ? p.lm_bias_l2 : 0.f;   // landmark logit bias
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
-                    if ((uint32_t)(cur.mask >> (32 * hf)) == 0u) continue;   // no key in this half
+                    if ((hf ? mhi : mlo) == 0u) continue;   // no key in this half
                     // this half's V operands, requested before the exponentials so that the LDS
                     // reads overlap them
                     bf16x8 va[2][2];
@@ -370,8 +385,7 @@ __global__ __launch_bounds__(128 * QT, 3) void k_attn_bf16(AttnDev p) {
                     bf16x8 pb[2];
                     float lh;
                     auto probs = [&]() {
-                        const float off = bias - (m == -INFINITY ? 0.f : m);
-                        lh = 0.f;
+                        const float off = lmk ? negm + bias : negm;
 #pragma unroll
                         for (int kk = 0; kk < 2; ++kk) {
                             float pv[8];
@@ -381,7 +395,7 @@ __global__ __launch_bounds__(128 * QT, 3) void k_attn_bf16(AttnDev p) {
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
                                 pp[i] = bf16x2{(__bf16)pv[2 * i], (__bf16)pv[2 * i + 1]};
-                                lh = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, lh, false);
+                                lh = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, (kk | i) ? lh : 0.f, false);
                             }
                             pb[kk] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
                                                              __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
@@ -389,19 +403,22 @@ __global__ __launch_bounds__(128 * QT, 3) void k_attn_bf16(AttnDev p) {
                         }
                     };
                     probs();
-                    if (fresh || __ballot(!(lh <= PROB_SUM_LIMIT))) {
+                    if (__ballot(!(lh <= PROB_SUM_LIMIT))) {
                         float mx = sp[0];
 #pragma unroll
                         for (int i = 1; i < 15; i += 2) mx = max3f(mx, sp[i], sp[i + 1]);
                         mx = fmaxf(mx, sp[15]);
                         const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
                         mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-                        const float mnew = fmaxf(m, mx == -INFINITY ? -INFINITY : fmaf(mx, p.scale_l2, bias));
-                        const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
+                        // (a half of -inf scores leaves m alone: fma(-inf, scale, bias) = -inf;
+                        // from M_NONE, alpha = 2^(M_NONE - mnew) is 0 or, m unmoved, 1 on a zero O)
+                        const float mnew = fmaxf(m, fmaf(mx, p.scale_l2, bias));
+                        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
                         l *= alpha;
                         o0 *= alpha;
                         o1 *= alpha;
                         m = mnew;
+                        negm = -mnew;
                         probs();
                     }
                     l += lh;
@@ -437,6 +454,7 @@ __global__ __launch_bounds__(128 * QT, 3) void k_attn_bf16(AttnDev p) {
     }
     if (it < ntiles) step(it, d, s_v0, s_v1);
 
+    if (!DENSE && m == M_NONE) m = -INFINITY;         // the row saw no key
     float ltot = l + __shfl_xor(l, 32);
     if (SGA) sga_finish<false>(p, h, qrow, qvalid, g, m, ltot, o0, o1);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
