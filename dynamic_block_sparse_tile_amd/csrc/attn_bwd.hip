@@ -155,8 +155,12 @@ template <bool LM>
 __global__ __launch_bounds__(128, 3) void k_attn_bwd_dq(BwdDev p) {
     // K is read at both ends of a step (S, then dQ), V only at its start (dP): K is double
     // buffered, V single, reloaded once every wave has formed its dP
-    __shared__ __align__(16) unsigned char s_k[2][TILE_BYTES];
-    __shared__ __align__(16) unsigned char s_v[1][TILE_BYTES];
+    // (one array per buffer: with both K buffers in one array indexed by the step's parity
+    // the compiler cannot tell the buffer being read from the one being loaded, and waits
+    // for the next tile's loads before reading this one)
+    __shared__ __align__(16) unsigned char s_k0[TILE_BYTES];
+    __shared__ __align__(16) unsigned char s_k1[TILE_BYTES];
+    __shared__ __align__(16) unsigned char s_v[TILE_BYTES];
     extern __shared__ int32_t s_idx[];                  // kmax list entries, then the bitmap
     uint32_t* s_lm = reinterpret_cast<uint32_t*>(s_idx + p.kmax);
 
@@ -207,28 +211,27 @@ __global__ __launch_bounds__(128, 3) void k_attn_bwd_dq(BwdDev p) {
     off.init(lane);
 
     f32x16 dq0 = {}, dq1 = {};
-    auto stage_k = [&](int it, int b) {
+    auto stage_k = [&](int it, unsigned char* dst) {
         const Block kb = key_block(p, it, p.Ts, c, s_idx, s_lm);
         const bool mean = LM && __builtin_amdgcn_readfirstlane(kb.kind) == 2;
-        stage_block(mean ? rs_kb : rs_k, p.kl, kb, (lds_u8*)s_k[b], w, lane);
+        stage_block(mean ? rs_kb : rs_k, p.kl, kb, (lds_u8*)dst, w, lane);
         return kb;
     };
     auto stage_v = [&](const Block& kb) {
         const bool mean = LM && __builtin_amdgcn_readfirstlane(kb.kind) == 2;
-        stage_block(mean ? rs_vb : rs_v, p.kl, kb, (lds_u8*)s_v[0], w, lane);
+        stage_block(mean ? rs_vb : rs_v, p.kl, kb, (lds_u8*)s_v, w, lane);
     };
     Block cur{}, nxt{};
     if (ntiles > 0) {
-        cur = stage_k(0, 0);
+        cur = stage_k(0, s_k0);
         stage_v(cur);
     }
     __builtin_amdgcn_s_waitcnt(0x0070);
     __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-        const int b = it & 1;
-        if (it + 1 < ntiles) nxt = stage_k(it + 1, b ^ 1);
-        const unsigned char* kt = s_k[b];
-        const unsigned char* vt = s_v[0];
+    // step it reads K(it) from kt while K(it+1) loads into kn (steps alternate the buffers)
+    auto kstep = [&](int it, const unsigned char* kt, unsigned char* kn) __attribute__((always_inline)) {
+        if (it + 1 < ntiles) nxt = stage_k(it + 1, kn);
+        const unsigned char* vt = s_v;
         // landmark logits carry the bias
         const float nl = (LM && __builtin_amdgcn_readfirstlane(cur.kind) == 2 ? p.lm_bias_l2 : 0.f) - lse_l2;
         const uint64_t km = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(cur.mask >> 32)) << 32) |
@@ -276,7 +279,8 @@ __global__ __launch_bounds__(128, 3) void k_attn_bwd_dq(BwdDev p) {
         }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);          // this wave's V reads are done
-        __syncthreads();                                     // and every wave's
+        // and every wave's (a plain barrier: __syncthreads would also wait for K(it+1)'s loads)
+        __builtin_amdgcn_s_barrier();
         if (it + 1 < ntiles) stage_v(nxt);                   // V(it+1) into the one V buffer
         __builtin_amdgcn_sched_barrier(0);
         if (wq) {                                            // S, dS and dQ half by half
@@ -291,7 +295,13 @@ __global__ __launch_bounds__(128, 3) void k_attn_bwd_dq(BwdDev p) {
         cur = nxt;
         __builtin_amdgcn_s_waitcnt(0x0070);
         __syncthreads();
+    };
+    int it = 0;
+    for (; it + 1 < ntiles; it += 2) {
+        kstep(it, s_k0, s_k1);
+        kstep(it + 1, s_k1, s_k0);
     }
+    if (it < ntiles) kstep(it, s_k0, s_k1);
     // dQ = scale * dQ^T accumulators: lane holds query qc, dims 8 (r/4) + 4 g + r % 4 (+32)
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
@@ -407,8 +417,12 @@ __global__ __launch_bounds__(256, MEANS ? 2 : 3) void k_attn_bwd_dkv(BwdDev p) {
         nq = te[kb.t] - q0;
         qlist = p.t_list + (size_t)h * p.Tq * p.kmax + q0;
     }
+    // the list through the constant address space: a uniform index makes a scalar load, which
+    // does not wait behind the vector loads in flight
+    typedef __attribute__((address_space(4))) const int32_t cint32;
+    cint32* const qlist_s = (cint32*)qlist;
     auto qtile = [&](int i) {
-        return (MEANS || kb.kind == 1) ? i : __builtin_amdgcn_readfirstlane(qlist[i]);
+        return (MEANS || kb.kind == 1) ? i : (int)qlist_s[i];
     };
 
     const unsigned head_bytes = (unsigned)Lq * 128u;
@@ -418,18 +432,22 @@ __global__ __launch_bounds__(256, MEANS ? 2 : 3) void k_attn_bwd_dkv(BwdDev p) {
     off.init(lane);
     const int tpfq = p.ql.P / TILE;
 
-    // lse (base 2, +inf where P must be 0) and D of the 64 rows of a query tile, one value
-    // per thread of the first 64 (lse) and last 64 (D) lanes
+    // lse and D of the 64 rows of a query tile, one value per thread of the first 64 (lse,
+    // +inf for rows that are not queries) and last 64 (D) lanes.  The value is stored as
+    // loaded and converted (row_value) when it goes to LDS at the end of the step: converted
+    // at once, its use would wait for the load, and so (loads complete in order) for the
+    // staging loads of the next tile issued just before it.
     auto fetch_rows = [&](int tq, float& val) {
         const int r = tid & 63;
         const int row = tq * TILE + r;
         const bool ok = (tq % tpfq) * TILE + r < p.ql.N;
-        if (tid < 64) {
-            const float l = ok ? p.lse[(size_t)h * Lq + row] : INFINITY;
-            val = (ok && l > -INFINITY) ? l * LOG2E_F : INFINITY;
-        } else {
-            val = ok ? p.delta[(size_t)h * Lq + row] : 0.f;
-        }
+        if (tid < 64) val = ok ? p.lse[(size_t)h * Lq + row] : INFINITY;
+        else val = ok ? p.delta[(size_t)h * Lq + row] : 0.f;
+    };
+    // as the steps read them: lse in base 2 (+inf, so P = 0, for a row with nothing attended
+    // or not a query), D as it is
+    auto row_value = [&](float val) {
+        return tid < 64 ? (val > -INFINITY ? val * LOG2E_F : INFINITY) : val;
     };
     auto stage = [&](int tq, int b) {
         Block qb;
@@ -447,7 +465,7 @@ __global__ __launch_bounds__(256, MEANS ? 2 : 3) void k_attn_bwd_dkv(BwdDev p) {
         stage(t0, 0);
         if (tid < 128) fetch_rows(t0, rowval);
         __builtin_amdgcn_s_waitcnt(0x0070);
-        if (tid < 128) (tid < 64 ? s_lse[0] : s_d[0])[tid & 63] = rowval;
+        if (tid < 128) (tid < 64 ? s_lse[0] : s_d[0])[tid & 63] = row_value(rowval);
     }
     __syncthreads();
     for (int i = 0; i < nq; ++i) {
@@ -514,7 +532,7 @@ __global__ __launch_bounds__(256, MEANS ? 2 : 3) void k_attn_bwd_dkv(BwdDev p) {
             }
         }
         __builtin_amdgcn_s_waitcnt(0x0070);
-        if (i + 1 < nq && tid < 128) (tid < 64 ? s_lse[b ^ 1] : s_d[b ^ 1])[tid & 63] = rowval;
+        if (i + 1 < nq && tid < 128) (tid < 64 ? s_lse[b ^ 1] : s_d[b ^ 1])[tid & 63] = row_value(rowval);
         __syncthreads();
     }
     // the second query half hands its partial sums to the first through the staging buffers
